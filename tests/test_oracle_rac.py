@@ -1,0 +1,138 @@
+"""Pins for the oracle's Residual Activation Compensation (CPU only).
+
+RAC as the pages describe it (technical summary, section 2.2-B; AI-Wiki
+"Methodology"): find the channels whose first-pass FP4 error is largest, keep a
+binary mask of the top k% of them, quantize their residual a second time and
+add that correction to the quantized path.  Pins: brute-force top-k over all
+subsets, selection invariants, the k=0 and k=100 reductions, the residual
+tensor scale computed two ways, and the error-never-grows theorem at the
+activation level.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import quads_oracle as O
+from fp4_quantized_moe_amd import synthetic as S
+
+
+def test_nsel_integer_floor():
+    assert O.rac_nsel(2048, 50) == 1024
+    assert O.rac_nsel(768, 50) == 384
+    assert O.rac_nsel(256, 33) == 84
+    assert O.rac_nsel(100, 0) == 0
+    assert O.rac_nsel(100, 100) == 100
+    assert O.rac_kpad(84) == 96 and O.rac_kpad(0) == 0 and O.rac_kpad(16) == 16
+    with pytest.raises(ValueError):
+        O.rac_nsel(16, 101)
+
+
+def test_select_brute_force_all_subsets():
+    """P8: the selected set maximizes the score multiset and, among equal
+    scores, prefers lower indices -- checked over all subsets for tiny K with
+    injected ties."""
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        K = int(rng.integers(4, 13))
+        sc = rng.integers(0, 4, K).astype(np.float32)  # many ties
+        for k in (0, 10, 25, 40, 50):
+            nsel = O.rac_nsel(K, k)
+            sel, n = O.rac_select(sc, k)
+            assert n == nsel
+            best = None
+            for sub in itertools.combinations(range(K), nsel):
+                key = (sorted((-sc[list(sub)]).tolist()), list(sub))
+                if best is None or key < best:
+                    best = key
+            assert list(sel[:nsel]) == best[1], (sc, k)
+
+
+def test_select_invariants():
+    """P10: |S| = nsel, strictly ascending, and no unselected channel outranks
+    a selected one."""
+    rng = np.random.default_rng(32)
+    sc = np.floor(rng.random(2048) * 300).astype(np.float32)
+    for k in (1, 25, 50, 99):
+        sel, nsel = O.rac_select(sc, k)
+        s = sel[:nsel]
+        assert len(s) == nsel and np.all(np.diff(s) > 0)
+        chosen = np.zeros(2048, bool)
+        chosen[s] = True
+        worst_sel = min((sc[c], -c) for c in s)
+        for c in np.nonzero(~chosen)[0]:
+            assert (sc[c], -c) < worst_sel
+        assert (sel[nsel:] == 0).all()
+
+
+def _dense(seed=41, M=64, K=256):
+    rng = np.random.default_rng(seed)
+    return S.activation(rng, M, K, 4, 20.0, bf16=False).f32
+
+
+def test_k0_and_k100_reductions():
+    """P5/P6: k=0 selects nothing (the plain W4A4 path); k=100 selects every
+    channel in order and the residual is the whole ΔX."""
+    x = _dense()
+    q = O.quantize_nvfp4(x)
+    sc = O.rac_scores(x, q)
+    sel0, n0 = O.rac_select(sc, 0)
+    assert n0 == 0 and sel0.size == 0
+    sel1, n1 = O.rac_select(sc, 100)
+    assert np.array_equal(sel1, np.arange(x.shape[1]))
+    r = O.rac_quantize_residual(x, q, sel1, n1)
+    assert np.array_equal(r.codes, O.quantize_nvfp4(O.rac_residual(x, q)).codes)
+
+
+def test_residual_scale_two_ways():
+    """P9: the residual tensor's amax is the largest selected score."""
+    x = _dense(42)
+    q = O.quantize_nvfp4(x)
+    sc = O.rac_scores(x, q)
+    for k in (10, 50, 100):
+        sel, n = O.rac_select(sc, k)
+        r = O.rac_quantize_residual(x, q, sel, n)
+        a = sc[sel[:n]].max()
+        assert r.g == np.float32(a / np.float32(2688.0))
+        assert a == sc.max()
+
+
+def test_scores_are_column_max_of_abs_residual():
+    x = _dense(43, 8, 32)
+    q = O.quantize_nvfp4(x)
+    sc = O.rac_scores(x, q)
+    for c in range(32):
+        m = 0.0
+        for r in range(8):
+            m = max(m, abs(float(np.float32(x[r, c]) - np.float32(q.dq[r, c]))))
+        assert sc[c] == np.float32(m)
+
+
+def test_activation_error_never_grows():
+    """P7 (activation level, a theorem): adding the second-pass residual never
+    moves an element farther from x than the first pass left it, up to one
+    fp32 rounding."""
+    for seed, k in [(44, 25), (45, 50), (46, 100)]:
+        x = _dense(seed)
+        q = O.quantize_nvfp4(x)
+        sel, n = O.rac_select(O.rac_scores(x, q), k)
+        r = O.rac_quantize_residual(x, q, sel, n)
+        comp = O.rac_compensated_activation(x, q, r, sel, n)
+        e0 = np.abs(x.astype(np.float64) - q.dq)
+        e1 = np.abs(x.astype(np.float64) - comp)
+        ulp = np.spacing(np.abs(comp).astype(np.float32)).astype(np.float64)
+        assert (e1 <= e0 + ulp).all()
+        # the selected channels' error shrinks in aggregate
+        assert e1[:, sel[:n]].sum() < e0[:, sel[:n]].sum()
+
+
+def test_residual_pad_columns_are_zero():
+    x = _dense(47, 16, 256)
+    q = O.quantize_nvfp4(x)
+    sel, n = O.rac_select(O.rac_scores(x, q), 33)  # nsel 84 -> kpad 96
+    r = O.rac_quantize_residual(x, q, sel, n)
+    code = O.unpack_nibbles(r.codes)
+    assert sel.size == 96 and (sel[n:] == 0).all()
+    assert (code[:, n:] == 0).all()
+    # the last block holds 4 real + 12 pad entries: the scale comes from the real ones
+    assert O.dequant_exact(r.codes, r.scales, r.g)[:, n:].max() == 0
