@@ -1,0 +1,298 @@
+"""ctypes binding of libquads (include/quads.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+library.  PyTorch provides device memory (torch.empty on the GPU) and the
+current HIP stream.  If the library is missing or a call fails, an exception
+is raised -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libquads.so")
+
+F32, BF16 = 0, 1
+GSCALE_GIVEN, WANT_SCORES = 1, 2
+OPERANDS_W4A4, OPERANDS_BF16 = 0, 1
+EPI_NONE, EPI_SWIGLU = 0, 1
+
+_c_i64, _c_i32, _c_u32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
+
+
+class QuadsError(RuntimeError):
+    pass
+
+
+class _NVFP4(ctypes.Structure):
+    _fields_ = [("codes", _vp), ("scales", _vp), ("gscale", _vp),
+                ("batch", _c_i64), ("rows", _c_i64), ("cols", _c_i64)]
+
+
+class _GemmArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _c_u32), ("operand_mode", _c_i32), ("epilogue", _c_i32), ("y_dtype", _c_i32),
+        ("num_experts", _c_i32), ("n_seg", _c_i32),
+        ("num_rows", _c_i64), ("act_rows", _c_i64), ("N", _c_i64), ("K", _c_i64),
+        ("x_codes", _vp), ("x_scales", _vp), ("x_gscale", _vp),
+        ("r_codes", _vp), ("r_scales", _vp), ("r_gscale", _vp), ("sel_idx", _vp), ("kpad", _c_i64),
+        ("w_codes", _vp), ("w_scales", _vp), ("w_gscale", _vp),
+        ("x_bf16", _vp), ("w_bf16", _vp),
+        ("row_token", _vp), ("expert_offsets", _vp),
+        ("y", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = [
+    "quads_last_error", "quads_version", "quads_rac_nsel", "quads_rac_kpad",
+    "quads_quantize_workspace_bytes", "quads_quantize_nvfp4",
+    "quads_rac_select_workspace_bytes", "quads_rac_select",
+    "quads_moe_gemm_workspace_bytes", "quads_moe_w4a4_gemm",
+    "quads_weight_qdq_workspace_bytes", "quads_weight_qdq",
+    "quads_moe_route_workspace_bytes", "quads_moe_route", "quads_moe_combine",
+]
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libquads.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise QuadsError(f"{path} not found: build it with `python -m fp4_quantized_moe_amd.build`")
+    L = ctypes.CDLL(path)
+    L.quads_last_error.restype = ctypes.c_char_p
+    L.quads_version.restype = ctypes.c_char_p
+    L.quads_rac_nsel.restype = _c_i64
+    L.quads_rac_nsel.argtypes = [_c_i64, _c_i32]
+    L.quads_rac_kpad.restype = _c_i64
+    L.quads_rac_kpad.argtypes = [_c_i64]
+    L.quads_quantize_workspace_bytes.restype = ctypes.c_size_t
+    L.quads_quantize_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
+    L.quads_quantize_nvfp4.restype = ctypes.c_int
+    L.quads_quantize_nvfp4.argtypes = [_vp, ctypes.c_int, _NVFP4, _c_u32, _vp, _vp, ctypes.c_size_t, _vp]
+    L.quads_rac_select_workspace_bytes.restype = ctypes.c_size_t
+    L.quads_rac_select_workspace_bytes.argtypes = [_c_i64, _c_i64]
+    L.quads_rac_select.restype = ctypes.c_int
+    L.quads_rac_select.argtypes = [_vp, ctypes.c_int, ctypes.POINTER(_NVFP4), _vp, _c_i32, _vp, _NVFP4,
+                                   _vp, ctypes.c_size_t, _vp]
+    L.quads_moe_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.quads_moe_gemm_workspace_bytes.argtypes = [ctypes.POINTER(_GemmArgs)]
+    L.quads_moe_w4a4_gemm.restype = ctypes.c_int
+    L.quads_moe_w4a4_gemm.argtypes = [ctypes.POINTER(_GemmArgs), _vp]
+    L.quads_weight_qdq_workspace_bytes.restype = ctypes.c_size_t
+    L.quads_weight_qdq_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
+    L.quads_weight_qdq.restype = ctypes.c_int
+    L.quads_weight_qdq.argtypes = [_vp, _c_i64, _c_i64, _c_i64, _vp, ctypes.POINTER(_NVFP4), _c_u32, _vp,
+                                   ctypes.c_size_t, _vp]
+    L.quads_moe_route_workspace_bytes.restype = ctypes.c_size_t
+    L.quads_moe_route_workspace_bytes.argtypes = [_c_i64, _c_i32]
+    L.quads_moe_route.restype = ctypes.c_int
+    L.quads_moe_route.argtypes = [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.quads_moe_combine.restype = ctypes.c_int
+    L.quads_moe_combine.argtypes = [_vp, _c_i64, _c_i32, _c_i64, _vp, _vp, _vp, _vp]
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().quads_last_error().decode()
+        raise QuadsError(f"{what} failed with status {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise QuadsError(f"unsupported dtype {t.dtype}")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise QuadsError("tensors must be contiguous and on the GPU")
+
+
+def _workspace(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class NVFP4Tensor:
+    """Packed codes [batch, rows, cols/2] u8, E4M3 scales [batch, rows, cols/16]
+    u8 and FP32 tensor scales [batch] (batch axis omitted when batch == 1)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    gscale: torch.Tensor
+    batch: int
+    rows: int
+    cols: int
+
+    def c_struct(self):
+        return _NVFP4(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr(),
+                      self.batch, self.rows, self.cols)
+
+
+def empty_nvfp4(batch, rows, cols, device):
+    shape = (rows,) if batch == 1 else (batch, rows)
+    return NVFP4Tensor(torch.empty(*shape, cols // 2, dtype=torch.uint8, device=device),
+                       torch.empty(*shape, cols // 16, dtype=torch.uint8, device=device),
+                       torch.empty(batch, dtype=torch.float32, device=device), batch, rows, cols)
+
+
+def rac_nsel(cols: int, k_percent: int) -> int:
+    return int(load().quads_rac_nsel(cols, k_percent))
+
+
+def rac_kpad(nsel: int) -> int:
+    return int(load().quads_rac_kpad(nsel))
+
+
+def quantize_nvfp4(x: torch.Tensor, want_scores: bool = False, gscale: torch.Tensor | None = None,
+                   out: NVFP4Tensor | None = None):
+    """x: [rows, cols] or [batch, rows, cols] (bf16/fp32) -> (NVFP4Tensor, scores or None)."""
+    L = load()
+    _require_cuda(x)
+    batch, rows, cols = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+    q = out if out is not None else empty_nvfp4(batch, rows, cols, x.device)
+    flags = 0
+    if gscale is not None:
+        q.gscale.copy_(gscale.reshape(-1))
+        flags |= GSCALE_GIVEN
+    scores = None
+    if want_scores:
+        scores = torch.empty(cols, dtype=torch.float32, device=x.device)
+        flags |= WANT_SCORES
+    ws = _workspace(L.quads_quantize_workspace_bytes(batch, rows, cols), x.device)
+    _check(L.quads_quantize_nvfp4(_ptr(x), _dtype_code(x), q.c_struct(), flags, _ptr(scores), _ptr(ws),
+                                  ws.numel(), _stream()), "quads_quantize_nvfp4")
+    return q, scores
+
+
+def rac_select(x: torch.Tensor, xq: NVFP4Tensor, scores: torch.Tensor, k_percent: int):
+    """-> (sel_idx int32 [kpad], residual NVFP4Tensor [rows, kpad], nsel)."""
+    L = load()
+    _require_cuda(x, scores)
+    rows, cols = xq.rows, xq.cols
+    nsel = rac_nsel(cols, k_percent)
+    if nsel < 0:
+        raise QuadsError(f"invalid k_percent {k_percent}")
+    kpad = rac_kpad(nsel)
+    sel = torch.empty(max(kpad, 1), dtype=torch.int32, device=x.device)
+    res = empty_nvfp4(1, rows, kpad, x.device) if kpad else NVFP4Tensor(
+        torch.empty(rows, 0, dtype=torch.uint8, device=x.device),
+        torch.empty(rows, 0, dtype=torch.uint8, device=x.device),
+        torch.empty(1, dtype=torch.float32, device=x.device), 1, rows, 0)
+    xs = xq.c_struct()
+    _check(L.quads_rac_select(_ptr(x), _dtype_code(x), ctypes.byref(xs), _ptr(scores), k_percent, _ptr(sel),
+                              res.c_struct(), None, 0, _stream()), "quads_rac_select")
+    return sel[:kpad], res, nsel
+
+
+def moe_w4a4_gemm(*, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
+                  expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
+                  sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
+                  x_bf16=None, w_bf16=None, y=None):
+    """Grouped expert GEMM (see quads.h).  W4A4 mode when `x` is given,
+    bf16-operand (trainer W4A16) mode when `x_bf16`/`w_bf16` are given."""
+    L = load()
+    E = int(expert_offsets.numel()) - 1
+    bf16_mode = x_bf16 is not None
+    dev = expert_offsets.device
+    if y is None:
+        if epilogue == EPI_SWIGLU:
+            y = torch.empty(num_rows, N // 2, dtype=torch.bfloat16, device=dev)
+        else:
+            y = torch.empty(num_rows, N, dtype=y_dtype, device=dev)
+    a = _GemmArgs()
+    a.struct_size = ctypes.sizeof(_GemmArgs)
+    a.operand_mode = OPERANDS_BF16 if bf16_mode else OPERANDS_W4A4
+    a.epilogue = epilogue
+    a.y_dtype = BF16 if y.dtype == torch.bfloat16 else F32
+    a.num_experts = E
+    a.n_seg = n_seg
+    a.num_rows = num_rows
+    a.N, a.K = N, K
+    if bf16_mode:
+        _require_cuda(x_bf16, w_bf16)
+        a.act_rows = x_bf16.shape[0]
+        a.x_bf16, a.w_bf16 = x_bf16.data_ptr(), w_bf16.data_ptr()
+    else:
+        a.act_rows = x.rows
+        a.x_codes, a.x_scales, a.x_gscale = x.codes.data_ptr(), x.scales.data_ptr(), x.gscale.data_ptr()
+        a.w_codes, a.w_scales, a.w_gscale = w_codes.data_ptr(), w_scales.data_ptr(), w_gscale.data_ptr()
+        if res is not None and res.cols > 0:
+            a.r_codes, a.r_scales, a.r_gscale = res.codes.data_ptr(), res.scales.data_ptr(), res.gscale.data_ptr()
+            a.sel_idx = sel_idx.data_ptr()
+            a.kpad = res.cols
+    a.row_token = None if row_token is None else row_token.data_ptr()
+    a.expert_offsets = expert_offsets.data_ptr()
+    a.y = y.data_ptr()
+    nbytes = L.quads_moe_gemm_workspace_bytes(ctypes.byref(a))
+    if nbytes == 0:
+        _check(L.quads_moe_w4a4_gemm(ctypes.byref(a), _stream()), "quads_moe_w4a4_gemm")
+    ws = _workspace(nbytes, dev)
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
+    _check(L.quads_moe_w4a4_gemm(ctypes.byref(a), _stream()), "quads_moe_w4a4_gemm")
+    return y
+
+
+def weight_qdq(w: torch.Tensor, export: bool = False):
+    """w: bf16 [rows, cols] or [batch, rows, cols] -> (bf16 QDQ tensor, NVFP4Tensor or None)."""
+    L = load()
+    _require_cuda(w)
+    if w.dtype != torch.bfloat16:
+        raise QuadsError("weight_qdq expects bf16 master weights")
+    batch, rows, cols = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+    out = torch.empty_like(w)
+    q = empty_nvfp4(batch, rows, cols, w.device) if export else None
+    qs = q.c_struct() if q is not None else None
+    ws = _workspace(L.quads_weight_qdq_workspace_bytes(batch, rows, cols), w.device)
+    _check(L.quads_weight_qdq(_ptr(w), batch, rows, cols, _ptr(out), ctypes.byref(qs) if qs is not None else None,
+                              0, _ptr(ws), ws.numel(), _stream()), "quads_weight_qdq")
+    return out, q
+
+
+def moe_route(logits: torch.Tensor, top: int):
+    """-> (topk_ids [T, top] i32, topk_w [T, top] f32, expert_offsets [E+1] i32,
+    row_token [T*top] i32, inverse [T, top] i32)."""
+    L = load()
+    _require_cuda(logits)
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty(T, top, dtype=torch.int32, device=dev)
+    w = torch.empty(T, top, dtype=torch.float32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    rt = torch.empty(max(T * top, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(T, top, dtype=torch.int32, device=dev)
+    ws = _workspace(L.quads_moe_route_workspace_bytes(T, E), dev)
+    _check(L.quads_moe_route(_ptr(logits), T, E, top, _ptr(ids), _ptr(w), _ptr(offs), _ptr(rt), _ptr(inv),
+                             _ptr(ws), ws.numel(), _stream()), "quads_moe_route")
+    return ids, w, offs, rt[:T * top], inv
+
+
+def moe_combine(y: torch.Tensor, inverse: torch.Tensor, topk_w: torch.Tensor):
+    L = load()
+    _require_cuda(y, inverse, topk_w)
+    T, top = inverse.shape
+    N = y.shape[1]
+    out = torch.empty(T, N, dtype=torch.float32, device=y.device)
+    _check(L.quads_moe_combine(_ptr(y), T, top, N, _ptr(inverse), _ptr(topk_w), _ptr(out), _stream()),
+           "quads_moe_combine")
+    return out

@@ -1,0 +1,284 @@
+// C ABI of libquads (declared in include/quads.h): argument validation,
+// workspace sizing, status codes and the thread-local error message.  Every
+// entry point only enqueues work on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/quads.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+quads_status_t fail(quads_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+quads_status_t ok() {
+  g_err[0] = '\0';
+  return QUADS_OK;
+}
+
+quads_status_t device_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(QUADS_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a >= 0 && b >= 0 && (a == 0 || b <= lim / a); }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxSelectCols = 16384;
+
+}  // namespace
+
+extern "C" {
+
+const char *quads_last_error(void) { return g_err; }
+
+const char *quads_version(void) { return "quads-gfx950 0.1"; }
+
+int64_t quads_rac_nsel(int64_t cols, int32_t k_percent) {
+  if (cols < 0 || k_percent < 0 || k_percent > 100 || cols > kMaxElems) return -1;
+  return cols * k_percent / 100;
+}
+
+int64_t quads_rac_kpad(int64_t nsel) {
+  if (nsel < 0) return -1;
+  return (nsel + 15) / 16 * 16;
+}
+
+size_t quads_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch <= 0 || rows < 0 || cols <= 0) return 0;
+  return quads::quantize_ws_bytes(batch, rows, cols);
+}
+
+quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4_t out, uint32_t flags,
+                                    float *scores, void *ws, size_t ws_bytes, void *stream) {
+  if (dt != QUADS_F32 && dt != QUADS_BF16) return fail(QUADS_ERR_ARG, "quantize: bad dtype %d", dt);
+  if (flags & ~(QUADS_GSCALE_GIVEN | QUADS_WANT_SCORES)) return fail(QUADS_ERR_ARG, "quantize: unknown flags");
+  if (out.batch < 1 || out.rows < 0 || out.cols <= 0) return fail(QUADS_ERR_SHAPE, "quantize: bad shape");
+  if (out.cols % 16) return fail(QUADS_ERR_SHAPE, "quantize: cols (%lld) must be a multiple of 16", (long long)out.cols);
+  if (!mul_ok(out.rows, out.cols, kMaxElems) || !mul_ok(out.batch, out.rows * out.cols, kMaxElems))
+    return fail(QUADS_ERR_SHAPE, "quantize: size overflow");
+  const bool want_scores = (flags & QUADS_WANT_SCORES) != 0;
+  if (want_scores && (out.batch != 1 || scores == nullptr))
+    return fail(QUADS_ERR_ARG, "quantize: QUADS_WANT_SCORES needs batch == 1 and a scores buffer");
+  if (out.rows == 0) return ok();
+  if (!x || !out.codes || !out.scales || !out.gscale) return fail(QUADS_ERR_ARG, "quantize: null pointer");
+  const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
+  if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(out.batch, out.rows, out.cols)))
+    return fail(QUADS_ERR_WORKSPACE, "quantize: workspace too small (need %zu)",
+                quads::quantize_ws_bytes(out.batch, out.rows, out.cols));
+  quads::QuantizeLaunch a{};
+  a.x = x;
+  a.x_bf16 = dt == QUADS_BF16;
+  a.batch = out.batch;
+  a.rows = out.rows;
+  a.cols = out.cols;
+  a.codes = out.codes;
+  a.scales = out.scales;
+  a.gscale = out.gscale;
+  a.gscale_given = given;
+  a.scores = want_scores ? scores : nullptr;
+  a.qdq_out = nullptr;
+  a.ws = ws;
+  return device_status(quads::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize");
+}
+
+size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  return 0;
+}
+
+quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq, const float *scores,
+                                int32_t k_percent, int32_t *sel_idx, quads_nvfp4_t res, void *ws,
+                                size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (dt != QUADS_F32 && dt != QUADS_BF16) return fail(QUADS_ERR_ARG, "rac_select: bad dtype");
+  if (!xq) return fail(QUADS_ERR_ARG, "rac_select: null xq");
+  if (k_percent < 0 || k_percent > 100) return fail(QUADS_ERR_ARG, "rac_select: k_percent %d outside [0,100]", k_percent);
+  if (xq->batch != 1 || xq->cols <= 0 || xq->cols % 16 || xq->rows < 0)
+    return fail(QUADS_ERR_SHAPE, "rac_select: xq must be one [rows, cols] tensor with cols %% 16 == 0");
+  if (xq->cols > kMaxSelectCols) return fail(QUADS_ERR_SHAPE, "rac_select: cols > %lld", (long long)kMaxSelectCols);
+  const int64_t nsel = quads_rac_nsel(xq->cols, k_percent), kpad = quads_rac_kpad(nsel);
+  if (res.cols != kpad || res.rows != xq->rows || res.batch != 1)
+    return fail(QUADS_ERR_SHAPE, "rac_select: res must be [rows=%lld, kpad=%lld]", (long long)xq->rows, (long long)kpad);
+  const int64_t row_bytes = ((xq->cols * (dt == QUADS_BF16 ? 2 : 4) + xq->cols / 2 + xq->cols / 16) + 15) / 16 * 16;
+  if (kpad * 4 + row_bytes > 64 * 1024)
+    return fail(QUADS_ERR_SHAPE, "rac_select: cols too large for the residual kernel's LDS staging");
+  if (!scores || !res.gscale || (kpad > 0 && !sel_idx))
+    return fail(QUADS_ERR_ARG, "rac_select: null pointer");
+  if (kpad > 0 && xq->rows > 0 && (!x || !xq->codes || !xq->scales || !xq->gscale || !res.codes || !res.scales))
+    return fail(QUADS_ERR_ARG, "rac_select: null pointer");
+  quads::RacLaunch a{};
+  a.x = x;
+  a.x_bf16 = dt == QUADS_BF16;
+  a.rows = xq->rows;
+  a.cols = xq->cols;
+  a.x_codes = xq->codes;
+  a.x_scales = xq->scales;
+  a.x_gscale = xq->gscale;
+  a.scores = scores;
+  a.nsel = nsel;
+  a.kpad = kpad;
+  a.sel_idx = sel_idx;
+  a.r_codes = res.codes;
+  a.r_scales = res.scales;
+  a.r_gscale = res.gscale;
+  return device_status(quads::launch_rac_select(a, static_cast<hipStream_t>(stream)), "rac_select");
+}
+
+static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch &g) {
+  if (!a) return fail(QUADS_ERR_ARG, "gemm: null args");
+  if (a->struct_size != sizeof(quads_moe_gemm_args))
+    return fail(QUADS_ERR_ARG, "gemm: struct_size %u != %zu", a->struct_size, sizeof(quads_moe_gemm_args));
+  if (a->operand_mode != QUADS_OPERANDS_W4A4 && a->operand_mode != QUADS_OPERANDS_BF16)
+    return fail(QUADS_ERR_ARG, "gemm: bad operand_mode");
+  if (a->epilogue != QUADS_EPI_NONE && a->epilogue != QUADS_EPI_SWIGLU) return fail(QUADS_ERR_ARG, "gemm: bad epilogue");
+  if (a->y_dtype != QUADS_F32 && a->y_dtype != QUADS_BF16) return fail(QUADS_ERR_ARG, "gemm: bad y_dtype");
+  if (a->num_experts < 1 || a->num_experts > 1024) return fail(QUADS_ERR_SHAPE, "gemm: num_experts outside [1,1024]");
+  if (a->n_seg < 1 || a->N <= 0 || a->N % a->n_seg) return fail(QUADS_ERR_SHAPE, "gemm: bad n_seg");
+  if (a->K <= 0 || a->K % 16) return fail(QUADS_ERR_SHAPE, "gemm: K must be a positive multiple of 16");
+  if (a->N % 128) return fail(QUADS_ERR_SHAPE, "gemm: N must be a multiple of 128");
+  if (a->epilogue == QUADS_EPI_SWIGLU && a->n_seg != 2 && a->operand_mode == QUADS_OPERANDS_W4A4)
+    return fail(QUADS_ERR_SHAPE, "gemm: SWIGLU needs n_seg == 2 (gate, up)");
+  if (a->num_rows < 0 || a->act_rows < 0 || a->num_rows > (int64_t(1) << 31) - 1 || a->act_rows > (int64_t(1) << 31) - 1)
+    return fail(QUADS_ERR_SHAPE, "gemm: row counts must fit int32");
+  if (!mul_ok(a->num_rows, a->N, kMaxElems) || !mul_ok(int64_t(a->num_experts) * a->N, a->K, kMaxElems))
+    return fail(QUADS_ERR_SHAPE, "gemm: size overflow");
+  if (!a->expert_offsets || !a->y) return fail(QUADS_ERR_ARG, "gemm: null expert_offsets or y");
+  if (a->row_token == nullptr && a->act_rows < a->num_rows)
+    return fail(QUADS_ERR_SHAPE, "gemm: identity rows need act_rows >= num_rows");
+  g = quads::GemmLaunch{};
+  g.mode = a->operand_mode == QUADS_OPERANDS_BF16 ? 1 : 0;
+  g.epilogue = a->epilogue;
+  g.y_bf16 = a->y_dtype == QUADS_BF16;
+  g.E = a->num_experts;
+  g.n_seg = a->n_seg;
+  g.num_rows = a->num_rows;
+  g.act_rows = a->act_rows;
+  g.N = a->N;
+  g.K = a->K;
+  g.row_token = a->row_token;
+  g.expert_offsets = a->expert_offsets;
+  g.y = a->y;
+  g.ws = a->ws;
+  if (g.mode == 0) {
+    if (!a->x_codes || !a->x_scales || !a->x_gscale || !a->w_codes || !a->w_scales || !a->w_gscale)
+      return fail(QUADS_ERR_ARG, "gemm: null W4A4 operand");
+    g.x_codes = a->x_codes;
+    g.x_scales = a->x_scales;
+    g.x_g = a->x_gscale;
+    g.w_codes = a->w_codes;
+    g.w_scales = a->w_scales;
+    g.w_g = a->w_gscale;
+    if (a->r_codes != nullptr && a->kpad > 0) {
+      if (a->kpad % 16 || a->kpad > 16384) return fail(QUADS_ERR_SHAPE, "gemm: kpad must be a multiple of 16, <= 16384");
+      if (!a->r_scales || !a->r_gscale || !a->sel_idx) return fail(QUADS_ERR_ARG, "gemm: null residual operand");
+      g.r_codes = a->r_codes;
+      g.r_scales = a->r_scales;
+      g.r_g = a->r_gscale;
+      g.sel_idx = a->sel_idx;
+      g.kpad = a->kpad;
+    }
+  } else {
+    if (!a->x_bf16 || !a->w_bf16) return fail(QUADS_ERR_ARG, "gemm: null bf16 operand");
+    g.x_bf16 = static_cast<const uint16_t *>(a->x_bf16);
+    g.w_bf16 = static_cast<const uint16_t *>(a->w_bf16);
+  }
+  return QUADS_OK;
+}
+
+size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a) {
+  quads::GemmLaunch g;
+  if (gemm_fill(a, g) != QUADS_OK) return 0;
+  return quads::gemm_ws_bytes(g);
+}
+
+quads_status_t quads_moe_w4a4_gemm(const quads_moe_gemm_args *a, void *stream) {
+  quads::GemmLaunch g;
+  const quads_status_t st = gemm_fill(a, g);
+  if (st != QUADS_OK) return st;
+  if (a->ws == nullptr || a->ws_bytes < quads::gemm_ws_bytes(g))
+    return fail(QUADS_ERR_WORKSPACE, "gemm: workspace too small (need %zu)", quads::gemm_ws_bytes(g));
+  return device_status(quads::launch_gemm(g, static_cast<hipStream_t>(stream)), "gemm");
+}
+
+size_t quads_weight_qdq_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  return quads_quantize_workspace_bytes(batch, rows, cols);
+}
+
+quads_status_t quads_weight_qdq(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols, void *w_out_bf16,
+                                const quads_nvfp4_t *q_out, uint32_t flags, void *ws, size_t ws_bytes,
+                                void *stream) {
+  if (flags & ~QUADS_GSCALE_GIVEN) return fail(QUADS_ERR_ARG, "weight_qdq: unknown flags");
+  if (batch < 1 || rows < 0 || cols <= 0 || cols % 16)
+    return fail(QUADS_ERR_SHAPE, "weight_qdq: bad shape (cols must be a positive multiple of 16)");
+  if (!mul_ok(rows, cols, kMaxElems) || !mul_ok(batch, rows * cols, kMaxElems))
+    return fail(QUADS_ERR_SHAPE, "weight_qdq: size overflow");
+  const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
+  if (given && (q_out == nullptr || q_out->gscale == nullptr))
+    return fail(QUADS_ERR_ARG, "weight_qdq: QUADS_GSCALE_GIVEN needs q_out->gscale");
+  if (q_out && (q_out->batch != batch || q_out->rows != rows || q_out->cols != cols))
+    return fail(QUADS_ERR_SHAPE, "weight_qdq: q_out shape mismatch");
+  if (rows == 0) return ok();
+  if (!w_bf16 || !w_out_bf16) return fail(QUADS_ERR_ARG, "weight_qdq: null pointer");
+  if (q_out && (!q_out->codes || !q_out->scales || !q_out->gscale)) return fail(QUADS_ERR_ARG, "weight_qdq: null q_out member");
+  if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(batch, rows, cols)))
+    return fail(QUADS_ERR_WORKSPACE, "weight_qdq: workspace too small (need %zu)", quads::quantize_ws_bytes(batch, rows, cols));
+  quads::QuantizeLaunch a{};
+  a.x = w_bf16;
+  a.x_bf16 = true;
+  a.batch = batch;
+  a.rows = rows;
+  a.cols = cols;
+  a.codes = q_out ? q_out->codes : nullptr;
+  a.scales = q_out ? q_out->scales : nullptr;
+  a.gscale = q_out ? q_out->gscale : nullptr;
+  a.gscale_given = given;
+  a.scores = nullptr;
+  a.qdq_out = static_cast<uint16_t *>(w_out_bf16);
+  a.ws = ws;
+  return device_status(quads::launch_quantize(a, static_cast<hipStream_t>(stream)), "weight_qdq");
+}
+
+size_t quads_moe_route_workspace_bytes(int64_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return quads::route_ws_bytes(T, E);
+}
+
+quads_status_t quads_moe_route(const float *logits, int64_t T, int32_t E, int32_t top, int32_t *topk_ids,
+                               float *topk_w, int32_t *expert_offsets, int32_t *row_token, int32_t *inverse,
+                               void *ws, size_t ws_bytes, void *stream) {
+  if (E < 1 || E > 1024) return fail(QUADS_ERR_SHAPE, "route: E outside [1,1024]");
+  if (top < 1 || top > 16 || top > E) return fail(QUADS_ERR_SHAPE, "route: top outside [1, min(E,16)]");
+  if (T < 0 || !mul_ok(T, top, (int64_t(1) << 31) - 1) || !mul_ok(T, E, kMaxElems))
+    return fail(QUADS_ERR_SHAPE, "route: T out of range");
+  if (!expert_offsets) return fail(QUADS_ERR_ARG, "route: null expert_offsets");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !row_token || !inverse)) return fail(QUADS_ERR_ARG, "route: null pointer");
+  if (ws == nullptr || ws_bytes < quads::route_ws_bytes(T, E))
+    return fail(QUADS_ERR_WORKSPACE, "route: workspace too small (need %zu)", quads::route_ws_bytes(T, E));
+  return device_status(quads::launch_route(logits, T, E, top, topk_ids, topk_w, expert_offsets, row_token, inverse, ws,
+                                           static_cast<hipStream_t>(stream)),
+                       "route");
+}
+
+quads_status_t quads_moe_combine(const float *y, int64_t T, int32_t top, int64_t N, const int32_t *inverse,
+                                 const float *topk_w, float *out, void *stream) {
+  if (T < 0 || top < 1 || top > 16 || N <= 0 || N % 4) return fail(QUADS_ERR_SHAPE, "combine: bad shape (N %% 4 == 0)");
+  if (T > 0 && (!y || !inverse || !topk_w || !out)) return fail(QUADS_ERR_ARG, "combine: null pointer");
+  return device_status(quads::launch_combine(y, T, top, N, inverse, topk_w, out, static_cast<hipStream_t>(stream)),
+                       "combine");
+}
+
+}  // extern "C"

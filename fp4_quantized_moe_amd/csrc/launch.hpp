@@ -1,0 +1,74 @@
+// Host-side launchers shared between the kernel translation units and the
+// C-ABI layer (api.hip).  Arguments are validated by the caller; launchers
+// only size grids and enqueue kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace quads {
+
+// ---- quantize.hip --------------------------------------------------------
+struct QuantizeLaunch {
+  const void *x;
+  bool x_bf16;
+  int64_t batch, rows, cols;
+  uint8_t *codes;      // may be null (QDQ without export)
+  uint8_t *scales;     // may be null
+  float *gscale;       // [batch]; input if gscale_given else output (may be null if not given)
+  bool gscale_given;
+  float *scores;       // [cols] or null
+  uint16_t *qdq_out;   // [batch, rows, cols] bf16 or null
+  void *ws;            // partials
+};
+int amax_partials_per_tensor(int64_t n_elem);
+size_t quantize_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
+hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream);
+
+// ---- rac.hip ---------------------------------------------------------------
+struct RacLaunch {
+  const void *x;
+  bool x_bf16;
+  int64_t rows, cols;
+  const uint8_t *x_codes, *x_scales;
+  const float *x_gscale;
+  const float *scores;
+  int64_t nsel, kpad;
+  int32_t *sel_idx;
+  uint8_t *r_codes, *r_scales;
+  float *r_gscale;
+};
+hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream);
+
+// ---- gemm.hip --------------------------------------------------------------
+struct GemmLaunch {
+  int mode;       // 0: W4A4 (+ residual), 1: bf16 operands
+  int epilogue;   // 0: none, 1: swiglu
+  bool y_bf16;
+  int E, n_seg;
+  int64_t num_rows, act_rows, N, K, kpad;
+  const uint8_t *x_codes, *x_scales;
+  const float *x_g;
+  const uint8_t *r_codes, *r_scales;
+  const float *r_g;
+  const int32_t *sel_idx;
+  const uint8_t *w_codes, *w_scales;
+  const float *w_g;
+  const uint16_t *x_bf16, *w_bf16;
+  const int32_t *row_token, *expert_offsets;
+  void *y;
+  void *ws;
+};
+size_t gemm_ws_bytes(const GemmLaunch &a);
+hipError_t launch_gemm(const GemmLaunch &a, hipStream_t stream);
+
+// ---- route.hip -------------------------------------------------------------
+size_t route_ws_bytes(int64_t T, int E);
+hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t *ids, float *w,
+                        int32_t *offsets, int32_t *row_token, int32_t *inverse, void *ws,
+                        hipStream_t stream);
+hipError_t launch_combine(const float *y, int64_t T, int top, int64_t N, const int32_t *inverse,
+                          const float *w, float *out, hipStream_t stream);
+
+}  // namespace quads

@@ -1,0 +1,278 @@
+// NVFP4 quantization kernels (activation quantize + RAC channel scores, and
+// the trainer weight QDQ), gfx950.
+//
+// The activation quantization is what the QUADS technical summary
+// (section 2.1) describes as recomputed online on every rollout forward; the
+// channel score (max over rows of the first-pass residual |x - dq|) is what
+// RAC (section 2.2-B) ranks channels by; the QDQ output (bf16 of dq) is the
+// trainer's fake-quantized weight (section 2.2-A).
+//
+// Two launches per call, no atomics on floats and no memset:
+//   k_amax_partial  one max|x| partial per workgroup (P per tensor); also
+//                   zeroes the score buffer when scores are requested;
+//   k_quantize      every workgroup folds its tensor's P partials into g, then
+//                   quantizes a [rows x 16*BC] tile: 16-element blocks,
+//                   one block per thread per row step, coalesced 32/64-byte
+//                   loads, 8-byte code stores, optional bf16 QDQ stores, and a
+//                   per-workgroup column max of |x - dq| merged with one u32
+//                   atomicMax per column (order-independent, so deterministic).
+#include "launch.hpp"
+#include "quads_device.hpp"
+
+namespace quads {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool BF16>
+__device__ __forceinline__ void load16(const void *base, int64_t elem, float (&v)[16]) {
+  if constexpr (BF16) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
+    const uint4 a = load_nt16(p);
+    const uint4 b = load_nt16(p + 1);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 f = load_nt16(p + i);
+      v[4 * i] = __uint_as_float(f.x);
+      v[4 * i + 1] = __uint_as_float(f.y);
+      v[4 * i + 2] = __uint_as_float(f.z);
+      v[4 * i + 3] = __uint_as_float(f.w);
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Block-wide max over kThreads threads; result valid in every thread.
+__device__ __forceinline__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_amax_partial(const void *x, int64_t n_per_tensor,
+                                                           int P, int64_t chunk, float *partials,
+                                                           float *scores, int64_t cols) {
+  __shared__ float red[kThreads / 64];
+  const int b = blockIdx.x / P, p = blockIdx.x % P;
+  const int64_t start = p * chunk;
+  const int64_t end = min(start + chunk, n_per_tensor);
+  const int64_t base = static_cast<int64_t>(b) * n_per_tensor;
+  float m = 0.0f;
+  constexpr int kVec = BF16 ? 8 : 4;  // elements per 16-byte load
+  for (int64_t i = start + static_cast<int64_t>(threadIdx.x) * kVec; i < end;
+       i += static_cast<int64_t>(kThreads) * kVec) {
+    if constexpr (BF16) {
+      const uint4 u = load_nt16(static_cast<const uint16_t *>(x) + base + i);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xFFFF0000u)));
+      }
+    } else {
+      const uint4 u = load_nt16(static_cast<const float *>(x) + base + i);
+      m = fmaxf(fmaxf(fabsf(__uint_as_float(u.x)), fabsf(__uint_as_float(u.y))),
+                fmaxf(fmaxf(fabsf(__uint_as_float(u.z)), fabsf(__uint_as_float(u.w))), m));
+    }
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  if (scores != nullptr && blockIdx.x == 0) {
+    for (int64_t c = threadIdx.x; c < cols; c += kThreads) scores[c] = 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_zero_f32(float *p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    p[i] = 0.0f;
+}
+
+struct QParams {
+  const void *x;
+  int64_t rows, cols, cb;  // cb = cols / 16
+  int BC, RG, RW;          // blocks per row step, rows per step, rows per workgroup
+  int col_chunks, row_chunks, P;
+  const float *partials;
+  float *gscale;
+  int gscale_given;
+  uint8_t *codes, *scales;
+  float *scores;
+  uint16_t *qdq;
+};
+
+template <bool BF16, bool SCORES, bool CODES, bool QDQ>
+__global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
+  __shared__ float red[kThreads / 64];
+  extern __shared__ float smax_lds[];  // [RG][BC*16] when SCORES
+  const int per_tensor = p.row_chunks * p.col_chunks;
+  const int b = blockIdx.x / per_tensor;
+  const int rem = blockIdx.x % per_tensor;
+  const int rc = rem / p.col_chunks, cc = rem % p.col_chunks;
+
+  float g;
+  if (p.gscale_given) {
+    g = p.gscale[b];
+  } else {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < p.P; i += kThreads) m = fmaxf(m, p.partials[b * p.P + i]);
+    g = tensor_scale_from_amax(block_max(m, red));
+    if (p.gscale != nullptr && rc == 0 && cc == 0 && threadIdx.x == 0) p.gscale[b] = g;
+  }
+
+  const int bcol = threadIdx.x % p.BC, rg = threadIdx.x / p.BC;
+  const int64_t gbc = static_cast<int64_t>(cc) * p.BC + bcol;
+  const bool active = rg < p.RG && gbc < p.cb;
+  float smax[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) smax[i] = 0.0f;
+
+  if (active) {
+    const int64_t r_end = min(static_cast<int64_t>(rc + 1) * p.RW, p.rows);
+    for (int64_t r = static_cast<int64_t>(rc) * p.RW + rg; r < r_end; r += p.RG) {
+      const int64_t row = static_cast<int64_t>(b) * p.rows + r;
+      float v[16];
+      load16<BF16>(p.x, row * p.cols + gbc * 16, v);
+      float dq[16];
+      const BlockQ q = quantize_block16(v, g, (SCORES || QDQ) ? dq : nullptr);
+      if constexpr (CODES) {
+        reinterpret_cast<uint2 *>(p.codes)[row * p.cb + gbc] = make_uint2(q.lo, q.hi);
+        p.scales[row * p.cb + gbc] = static_cast<uint8_t>(q.scale);
+      }
+      if constexpr (QDQ) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          w[i] = f32_to_bf16_bits(dq[2 * i]) | (f32_to_bf16_bits(dq[2 * i + 1]) << 16);
+        uint4 *o = reinterpret_cast<uint4 *>(p.qdq + row * p.cols + gbc * 16);
+        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+      if constexpr (SCORES) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) smax[i] = fmaxf(smax[i], fabsf(v[i] - dq[i]));
+      }
+    }
+  }
+
+  if constexpr (SCORES) {
+    const int width = p.BC * 16;
+    if (rg < p.RG) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) smax_lds[rg * width + bcol * 16 + i] = smax[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < width; c += kThreads) {
+      float m = 0.0f;
+      for (int k = 0; k < p.RG; ++k) m = fmaxf(m, smax_lds[k * width + c]);
+      const int64_t gc = static_cast<int64_t>(cc) * width + c;
+      if (gc < p.cols && m > 0.0f)
+        atomicMax(reinterpret_cast<unsigned int *>(p.scores) + gc, __float_as_uint(m));
+    }
+  }
+}
+
+template <bool BF16, bool SCORES, bool CODES, bool QDQ>
+void launch_q(const QParams &qp, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((k_quantize<BF16, SCORES, CODES, QDQ>), dim3(grid), dim3(kThreads), lds, s, qp);
+}
+
+}  // namespace
+
+int amax_partials_per_tensor(int64_t n_elem) {
+  int64_t p = (n_elem + 65535) / 65536;
+  if (p < 1) p = 1;
+  if (p > 1024) p = 1024;
+  return static_cast<int>(p);
+}
+
+size_t quantize_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  const int P = amax_partials_per_tensor(rows * cols);
+  return static_cast<size_t>(batch) * P * sizeof(float) + 256;
+}
+
+hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
+  const int64_t n = a.rows * a.cols;
+  const int P = amax_partials_per_tensor(n);
+  float *partials = static_cast<float *>(a.ws);
+  if (!a.gscale_given) {
+    int64_t chunk = (n + P - 1) / P;
+    chunk = (chunk + 15) / 16 * 16;
+    if (a.x_bf16)
+      hipLaunchKernelGGL(k_amax_partial<true>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n,
+                         P, chunk, partials, a.scores, a.cols);
+    else
+      hipLaunchKernelGGL(k_amax_partial<false>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x,
+                         n, P, chunk, partials, a.scores, a.cols);
+  } else if (a.scores != nullptr) {
+    hipLaunchKernelGGL(k_zero_f32, dim3(1), dim3(kThreads), 0, stream, a.scores, a.cols);
+  }
+
+  QParams qp{};
+  qp.x = a.x;
+  qp.rows = a.rows;
+  qp.cols = a.cols;
+  qp.cb = a.cols / 16;
+  qp.BC = static_cast<int>(qp.cb < 64 ? qp.cb : 64);
+  qp.RG = kThreads / qp.BC;
+  qp.col_chunks = static_cast<int>((qp.cb + qp.BC - 1) / qp.BC);
+  const int64_t steps = a.batch * ((a.rows + qp.RG - 1) / qp.RG) * qp.col_chunks;
+  int64_t iters = steps / 2048;
+  if (iters < 1) iters = 1;
+  if (iters > 16) iters = 16;
+  qp.RW = static_cast<int>(qp.RG * iters);
+  qp.row_chunks = static_cast<int>((a.rows + qp.RW - 1) / qp.RW);
+  qp.P = P;
+  qp.partials = partials;
+  qp.gscale = a.gscale;
+  qp.gscale_given = a.gscale_given ? 1 : 0;
+  qp.codes = a.codes;
+  qp.scales = a.scales;
+  qp.scores = a.scores;
+  qp.qdq = a.qdq_out;
+  const int grid = static_cast<int>(a.batch * qp.row_chunks * qp.col_chunks);
+  const bool scores = a.scores != nullptr, codes = a.codes != nullptr, qdq = a.qdq_out != nullptr;
+  const size_t lds = scores ? static_cast<size_t>(qp.RG) * qp.BC * 16 * sizeof(float) : 0;
+  if (a.x_bf16) {
+    if (scores)
+      launch_q<true, true, true, false>(qp, grid, lds, stream);
+    else if (codes && qdq)
+      launch_q<true, false, true, true>(qp, grid, lds, stream);
+    else if (qdq)
+      launch_q<true, false, false, true>(qp, grid, lds, stream);
+    else
+      launch_q<true, false, true, false>(qp, grid, lds, stream);
+  } else {
+    if (scores)
+      launch_q<false, true, true, false>(qp, grid, lds, stream);
+    else if (codes && qdq)
+      launch_q<false, false, true, true>(qp, grid, lds, stream);
+    else if (qdq)
+      launch_q<false, false, false, true>(qp, grid, lds, stream);
+    else
+      launch_q<false, false, true, false>(qp, grid, lds, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace quads

@@ -1,0 +1,185 @@
+// MoE support steps around the expert GEMM on gfx950: top-k softmax routing,
+// the (expert, token)-ordered permutation of routed rows, and the combine.
+// The pages describe experts and expert-grouped execution, not the routing
+// mechanics; this is standard top-k softmax routing with deterministic ties.
+//
+//   k_route_topk     one wave per token: softmax statistics and top-k by
+//                    repeated wave argmax (ties to the lower expert index)
+//   k_route_count    per 256-token block, per-expert counts (LDS atomics on
+//                    integers: exact and order-independent)
+//   k_route_scan     block offsets per expert and expert_offsets[E+1]
+//   k_route_scatter  rank of a token among the block's tokens that chose the
+//                    same expert (popcount over an LDS bitmap), giving
+//                    row_token and inverse without any ordering race
+//   k_combine        out[t] = sum over slots (in order) of w * y[row]
+#include "launch.hpp"
+#include "quads_device.hpp"
+
+namespace quads {
+namespace {
+
+constexpr int kTokBlk = 256;
+
+__global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t T, int E, int top,
+                                                    int32_t *ids, float *wts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *row = logits + t * E;
+  constexpr int kMaxPer = 16;  // E <= 1024
+  float v[kMaxPer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int e = q * 64 + lane;
+    v[q] = e < E ? row[e] : -INFINITY;
+    mx = fmaxf(mx, v[q]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float sum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q)
+    if (q * 64 + lane < E) sum += expf(v[q] - mx);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  uint32_t taken = 0;  // bit q: slot q of this lane already chosen
+  for (int j = 0; j < top; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      const int e = q * 64 + lane;
+      if (e < E && !((taken >> q) & 1u) && (v[q] > bv || (v[q] == bv && e < bi))) {
+        bv = v[q];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == 0) {
+      ids[t * top + j] = bi;
+      wts[t * top + j] = expf(bv - mx) / sum;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTokBlk) void k_route_count(const int32_t *ids, int64_t T, int E, int top,
+                                                         int32_t *blkcnt) {
+  extern __shared__ int32_t cnt[];
+  for (int e = threadIdx.x; e < E; e += kTokBlk) cnt[e] = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokBlk + threadIdx.x;
+  if (t < T)
+    for (int j = 0; j < top; ++j) atomicAdd(&cnt[ids[t * top + j]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kTokBlk) blkcnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t *blkcnt, int nblk, int E, int32_t *offsets) {
+  __shared__ int32_t tot[1025];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int32_t c = blkcnt[static_cast<int64_t>(b) * E + e];
+      blkcnt[static_cast<int64_t>(b) * E + e] = run;
+      run += c;
+    }
+  }
+  tot[e + 1] = e < E ? run : 0;
+  if (e == 0) tot[0] = 0;
+  __syncthreads();
+  if (e == 0)
+    for (int i = 1; i <= E; ++i) tot[i] += tot[i - 1];
+  __syncthreads();
+  if (e < E) offsets[e] = tot[e];
+  if (e == 0) offsets[E] = tot[E];
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) blkcnt[static_cast<int64_t>(b) * E + e] += tot[e];
+}
+
+__global__ __launch_bounds__(kTokBlk) void k_route_scatter(const int32_t *ids, int64_t T, int E, int top,
+                                                           const int32_t *blkoff, int32_t *row_token,
+                                                           int32_t *inverse) {
+  extern __shared__ uint32_t bits[];  // [E][kTokBlk / 32]
+  constexpr int W = kTokBlk / 32;
+  for (int i = threadIdx.x; i < E * W; i += kTokBlk) bits[i] = 0;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokBlk + tl;
+  if (t < T)
+    for (int j = 0; j < top; ++j) atomicOr(&bits[ids[t * top + j] * W + (tl >> 5)], 1u << (tl & 31));
+  __syncthreads();
+  if (t >= T) return;
+  for (int j = 0; j < top; ++j) {
+    const int e = ids[t * top + j];
+    int rank = 0;
+    for (int w = 0; w < (tl >> 5); ++w) rank += __popc(bits[e * W + w]);
+    rank += __popc(bits[e * W + (tl >> 5)] & ((1u << (tl & 31)) - 1u));
+    const int32_t pos = blkoff[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+    row_token[pos] = static_cast<int32_t>(t);
+    inverse[t * top + j] = pos;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_combine(const float *y, int64_t T, int top, int64_t N,
+                                                 const int32_t *inverse, const float *w, float *out) {
+  const int64_t n4 = N / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= T * n4) return;
+  const int64_t t = idx / n4, c = idx % n4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < top; ++j) {
+    const float wj = w[t * top + j];
+    const float4 v = reinterpret_cast<const float4 *>(y + static_cast<int64_t>(inverse[t * top + j]) * N)[c];
+    acc.x = acc.x + wj * v.x;
+    acc.y = acc.y + wj * v.y;
+    acc.z = acc.z + wj * v.z;
+    acc.w = acc.w + wj * v.w;
+  }
+  reinterpret_cast<float4 *>(out + t * N)[c] = acc;
+}
+
+}  // namespace
+
+size_t route_ws_bytes(int64_t T, int E) {
+  const int64_t nblk = (T + kTokBlk - 1) / kTokBlk;
+  return static_cast<size_t>(nblk) * E * sizeof(int32_t) + 256;
+}
+
+hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t *ids, float *w,
+                        int32_t *offsets, int32_t *row_token, int32_t *inverse, void *ws,
+                        hipStream_t stream) {
+  const int nblk = static_cast<int>((T + kTokBlk - 1) / kTokBlk);
+  int32_t *blk = static_cast<int32_t *>(ws);
+  if (T > 0) {
+    hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, top, ids, w);
+    hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kTokBlk), E * sizeof(int32_t), stream, ids, T, E,
+                       top, blk);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, blk, nblk, E, offsets);
+  if (T > 0)
+    hipLaunchKernelGGL(k_route_scatter, dim3(nblk), dim3(kTokBlk), E * (kTokBlk / 32) * sizeof(uint32_t),
+                       stream, ids, T, E, top, blk, row_token, inverse);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *y, int64_t T, int top, int64_t N, const int32_t *inverse,
+                          const float *w, float *out, hipStream_t stream) {
+  const int64_t total = T * (N / 4);
+  if (total > 0)
+    hipLaunchKernelGGL(k_combine, dim3((total + 255) / 256), dim3(256), 0, stream, y, T, top, N, inverse,
+                       w, out);
+  return hipGetLastError();
+}
+
+}  // namespace quads

@@ -1,0 +1,245 @@
+/*
+ * quads.h -- C ABI of libquads, the gfx950 (MI355X) implementation of the
+ * QUADS rollout/trainer hot path: NVFP4 activation quantization, Residual
+ * Activation Compensation (RAC), the W4A4+RAC grouped expert GEMM, and the
+ * trainer-side weight quantize-dequantize (QDQ).
+ *
+ * Method sources (three web pages about the paper "QUADS: Stabilizing NVFP4
+ * Reinforcement Learning for MoE via QUantization-error Alignment across Dual
+ * Sides"):
+ *   [Gist]  gist.science "Technische Samenvatting: QUADS" -- section 1
+ *           (NVFP4 W4A4 GEMMs; the E2M1 grid has eight levels per sign),
+ *           section 2.1 (activations are re-quantized online on every
+ *           forward; weights are aligned by sharing one QDQ path),
+ *           section 2.2-A (asymmetric W4A16 QAT: NVFP4 fake-quantized
+ *           weights, BF16 activations), section 2.2-B (RAC: a binary mask of
+ *           the top k% channels by residual magnitude, a second-pass
+ *           quantization of their residual, added to the quantized path).
+ *   [Wiki]  AI-Wiki summary, "Methodology" (the compensation is added before
+ *           the native W4A4 GEMM).
+ *
+ * NVFP4 encoding used throughout (the pages name the format, not its
+ * layout): 16-element blocks along the last (contraction) axis; one OCP FP8
+ * E4M3 block scale per block (no infinities, max 448, never NaN here); one
+ * FP32 scale g per tensor, decode direction (value = e2m1 * e4m3 * g);
+ * rounding is nearest-even with saturation; g = fl32(amax / 2688), or 1 for
+ * an all-zero tensor; block scale s = E4M3(fl32(fl32(amax_block / 6) / g));
+ * element code = sign << 3 | nearest E2M1 magnitude of fl32(|x| / fl32(dec(s) * g))
+ * (the sign bit is kept for zeros).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller (e.g. from
+ *     torch.empty on the GPU).  The library never allocates device memory;
+ *     scratch space is a caller-provided workspace whose size is returned by
+ *     the matching *_workspace_bytes() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work; they never synchronize the host.
+ *   - Layouts are row-major.  Packed codes: [rows, cols/2] bytes, element 2j
+ *     in the low nibble of byte j.  Block scales: [rows, cols/16] bytes.
+ *   - Return value: QUADS_OK or a negative quads_status_t; on error nothing is
+ *     enqueued and quads_last_error() (thread-local) describes the problem.
+ *     Nothing throws or aborts across the ABI.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified (but memory-safe)
+ *     results.
+ */
+#ifndef QUADS_H
+#define QUADS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QUADS_OK = 0,
+  QUADS_ERR_ARG = -1,       /* null pointer, bad enum, k outside [0,100] */
+  QUADS_ERR_SHAPE = -2,     /* cols % 16 != 0, size overflow, unsupported shape */
+  QUADS_ERR_WORKSPACE = -3, /* workspace missing or too small */
+  QUADS_ERR_DEVICE = -4     /* HIP launch error (message in quads_last_error) */
+} quads_status_t;
+
+typedef enum { QUADS_F32 = 0, QUADS_BF16 = 1 } quads_dtype_t;
+
+/* quads_quantize_nvfp4 flags */
+#define QUADS_GSCALE_GIVEN 1u /* use out.gscale[b] as the tensor scale instead of computing it */
+#define QUADS_WANT_SCORES 2u  /* also compute RAC channel scores (batch must be 1) */
+
+/* An NVFP4 tensor of `batch` matrices of [rows, cols] (cols % 16 == 0). */
+typedef struct {
+  uint8_t *codes;  /* [batch, rows, cols/2] */
+  uint8_t *scales; /* [batch, rows, cols/16] E4M3 */
+  float *gscale;   /* [batch] FP32 tensor scales */
+  int64_t batch, rows, cols;
+} quads_nvfp4_t;
+
+/* Thread-local description of the last error ("" if none). */
+const char *quads_last_error(void);
+
+/* Library version string. */
+const char *quads_version(void);
+
+/* ---------------------------------------------------------------------------
+ * RAC sizes.  [Gist 2.2-B]: the mask keeps the top k% of channels.  nsel =
+ * floor(cols * k / 100) in integer arithmetic; the selected-channel list is
+ * padded to kpad = nsel rounded up to a multiple of 16 with index 0 and zero
+ * residual.  Return -1 for invalid arguments (cols < 0, k outside [0,100]).
+ * ------------------------------------------------------------------------- */
+int64_t quads_rac_nsel(int64_t cols, int32_t k_percent);
+int64_t quads_rac_kpad(int64_t nsel);
+
+/* ---------------------------------------------------------------------------
+ * quads_quantize_nvfp4 -- NVFP4-quantize x ([batch, rows, cols], F32 or BF16,
+ * contiguous) into `out` (same batch/rows/cols).  Each of the `batch`
+ * matrices gets its own tensor scale (one per weight matrix; batch = 1 for an
+ * activation).  This is the online activation quantization of [Gist 2.1] and
+ * the weight quantization shared by trainer and rollout.
+ *
+ * With QUADS_WANT_SCORES (batch == 1) it also writes the RAC channel scores
+ * scores[c] = max over rows of |x - dequant(Q(x))| (FP32, [cols]), the
+ * residual magnitudes [Gist 2.2-B] ranks channels by.
+ *
+ * ws: device workspace of at least quads_quantize_workspace_bytes(batch,
+ * rows, cols) bytes (cross-workgroup amax partials).
+ * ------------------------------------------------------------------------- */
+size_t quads_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
+quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4_t out,
+                                    uint32_t flags, float *scores, void *ws, size_t ws_bytes,
+                                    void *stream);
+
+/* ---------------------------------------------------------------------------
+ * quads_rac_select -- RAC channel mask and second-pass residual quantization
+ * [Gist 2.2-B].
+ *   1. Rank channels by (scores desc, index asc); keep the first nsel =
+ *      quads_rac_nsel(cols, k_percent); write them ASCENDING to sel_idx
+ *      ([kpad] int32, pad entries 0).
+ *   2. Residual G[r, j] = x[r, sel_j] - dequant(xq)[r, sel_j] (FP32, exact
+ *      recomputation from x and xq), 0 for pad columns; quantize G to NVFP4
+ *      into `res` ([rows, kpad], batch 1) with its own tensor scale, whose
+ *      amax is the largest selected score.
+ * x / dt: the activation that produced xq (batch 1); scores from
+ * quads_quantize_nvfp4(QUADS_WANT_SCORES).  res.cols must equal kpad; with
+ * k such that kpad == 0 only res.gscale[0] = 1 is written.
+ * Channel count limit: cols <= 16384.
+ * ------------------------------------------------------------------------- */
+size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols);
+quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
+                                const float *scores, int32_t k_percent, int32_t *sel_idx,
+                                quads_nvfp4_t res, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * quads_moe_w4a4_gemm -- token-permuted grouped expert GEMM with the RAC
+ * segment (extended K), on bf16 MFMA with exact NVFP4 -> bf16 operand decode:
+ *
+ *   Y[i, n] = gw[e, seg(n)] * ( gx * sum_k W[e,n,k] X[t(i),k]
+ *                             + gr * sum_j W[e,n,sel_j] R[t(i),j] )
+ *
+ * for routed row i of expert e (expert_offsets[e] <= i < expert_offsets[e+1]),
+ * t(i) = row_token[i] (or i when row_token is NULL), W/X/R the e2m1 * e4m3
+ * block values.  This is the quantized path plus the RAC correction, which
+ * [Wiki Methodology] adds before the W4A4 GEMM and [Gist 2.2-B] adds to the
+ * quantized output: the same sum.  With r_codes == NULL (or kpad == 0) it is
+ * plain W4A4.
+ *
+ * operand_mode QUADS_OPERANDS_BF16 is the trainer's W4A16 forward [Gist
+ * 2.2-A]: x_bf16 [act_rows, K] times w_bf16 [E, N, K] (QDQ'd weights),
+ * no scales, no residual.
+ *
+ * Epilogues: QUADS_EPI_NONE writes y [num_rows, N] (F32 or BF16);
+ * QUADS_EPI_SWIGLU (n_seg must be 2: W rows [0, N/2) are the gate, [N/2, N)
+ * the up projection) writes h [num_rows, N/2] BF16 with
+ * h = silu(Y_gate) * Y_up.
+ *
+ * Shapes: K % 16 == 0, N % 64 == 0 (N % 128 == 0 for SWIGLU), num_experts
+ * in [1, 1024].  expert_offsets is a DEVICE array of num_experts + 1
+ * non-decreasing int32 with expert_offsets[0] = 0 and
+ * expert_offsets[E] = num_rows (not checked on the host: reading it would
+ * synchronize).
+ * ws: at least quads_moe_gemm_workspace_bytes(args) bytes.
+ * ------------------------------------------------------------------------- */
+#define QUADS_OPERANDS_W4A4 0
+#define QUADS_OPERANDS_BF16 1
+#define QUADS_EPI_NONE 0
+#define QUADS_EPI_SWIGLU 1
+
+typedef struct {
+  uint32_t struct_size;  /* sizeof(quads_moe_gemm_args) (ABI versioning) */
+  int32_t operand_mode;  /* QUADS_OPERANDS_W4A4 | QUADS_OPERANDS_BF16 */
+  int32_t epilogue;      /* QUADS_EPI_NONE | QUADS_EPI_SWIGLU */
+  int32_t y_dtype;       /* QUADS_F32 | QUADS_BF16 (EPI_NONE); SWIGLU writes BF16 */
+  int32_t num_experts;   /* E */
+  int32_t n_seg;         /* weight tensor scales per expert along N (1 or 2) */
+  int64_t num_rows;      /* R: routed rows = output rows */
+  int64_t act_rows;      /* rows of the activation tensors */
+  int64_t N, K;
+  /* W4A4 activation operand: codes [act_rows, K/2], scales [act_rows, K/16], gscale [1] */
+  const uint8_t *x_codes;
+  const uint8_t *x_scales;
+  const float *x_gscale;
+  /* RAC residual (NULL r_codes => plain W4A4): codes [act_rows, kpad/2],
+     scales [act_rows, kpad/16], gscale [1], sel_idx [kpad] ascending */
+  const uint8_t *r_codes;
+  const uint8_t *r_scales;
+  const float *r_gscale;
+  const int32_t *sel_idx;
+  int64_t kpad;
+  /* W4A4 weights: codes [E, N, K/2], scales [E, N, K/16], gscale [E * n_seg] */
+  const uint8_t *w_codes;
+  const uint8_t *w_scales;
+  const float *w_gscale;
+  /* BF16 operands (operand_mode == QUADS_OPERANDS_BF16) */
+  const void *x_bf16; /* [act_rows, K] */
+  const void *w_bf16; /* [E, N, K] */
+  const int32_t *row_token;      /* [num_rows] or NULL (identity) */
+  const int32_t *expert_offsets; /* [E + 1], device */
+  void *y;
+  void *ws;
+  size_t ws_bytes;
+} quads_moe_gemm_args;
+
+size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a);
+quads_status_t quads_moe_w4a4_gemm(const quads_moe_gemm_args *a, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * quads_weight_qdq -- trainer-side fake quantization [Gist 2.1, 2.2-A]: each
+ * of `batch` BF16 master matrices [rows, cols] is NVFP4-quantized with its own
+ * tensor scale and dequantized back to BF16 (nearest-even of the FP32 value
+ * fl32(e2m1 * fl32(dec(s) * g))), written to w_out.  If q_out is not NULL its
+ * codes/scales/gscale also receive the NVFP4 tensor -- identical to
+ * quads_quantize_nvfp4 on the same input (the shared path that aligns trainer
+ * and rollout weights).  flags: QUADS_GSCALE_GIVEN reads the tensor scales
+ * from q_out->gscale (q_out required).
+ * ------------------------------------------------------------------------- */
+size_t quads_weight_qdq_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
+quads_status_t quads_weight_qdq(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                void *w_out_bf16, const quads_nvfp4_t *q_out, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * MoE support steps around the expert GEMM (the pages name expert routing
+ * but not its mechanics; this is standard top-k softmax routing).
+ *
+ * quads_moe_route: logits [T, E] FP32 -> top-`top` experts per token by
+ * logit (ties to the lower expert index), combine weights = softmax
+ * probabilities of the chosen experts (no renormalization), and the
+ * permutation that groups routed rows by (expert, token): expert_offsets
+ * [E+1], row_token [T*top] (token of each routed row), inverse [T, top]
+ * (routed row of each (token, slot)).  E <= 1024, 1 <= top <= min(E, 16).
+ * ------------------------------------------------------------------------- */
+size_t quads_moe_route_workspace_bytes(int64_t T, int32_t E);
+quads_status_t quads_moe_route(const float *logits, int64_t T, int32_t E, int32_t top,
+                               int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                               int32_t *row_token, int32_t *inverse, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/* quads_moe_combine: out[t, :] = sum over slots j (in order) of
+ * topk_w[t, j] * y[inverse[t, j], :], FP32 ([T, N]; y is [T*top, N] FP32). */
+quads_status_t quads_moe_combine(const float *y, int64_t T, int32_t top, int64_t N,
+                                 const int32_t *inverse, const float *topk_w, float *out,
+                                 void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QUADS_H */

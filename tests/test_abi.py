@@ -1,0 +1,109 @@
+"""The C-ABI library loads on the CPU host and exports every entry point
+include/quads.h declares; argument validation happens on the host and returns
+the documented status codes without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_quantized_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "quads.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(quads_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libquads.so is not built (python -m fp4_quantized_moe_amd.build)")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_version_and_sizes(L):
+    assert L.quads_version().startswith(b"quads")
+    assert L.quads_rac_nsel(2048, 50) == 1024
+    assert L.quads_rac_nsel(256, 33) == 84
+    assert L.quads_rac_nsel(10, 101) == -1
+    assert L.quads_rac_nsel(-1, 10) == -1
+    assert L.quads_rac_kpad(84) == 96 and L.quads_rac_kpad(0) == 0 and L.quads_rac_kpad(-3) == -1
+    assert L.quads_quantize_workspace_bytes(1, 4096, 2048) >= 4
+    assert L.quads_moe_route_workspace_bytes(16384, 64) >= 64 * 64 * 4
+
+
+def _nv(rows, cols, batch=1, ptr=1):
+    return _lib._NVFP4(ptr, ptr, ptr, batch, rows, cols)
+
+
+def test_quantize_validation(L):
+    dummy = ctypes.c_void_p(16)
+    st = L.quads_quantize_nvfp4(dummy, 0, _nv(4, 10), 0, None, dummy, 1 << 20, None)
+    assert st == -2 and b"multiple of 16" in L.quads_last_error()
+    assert L.quads_quantize_nvfp4(dummy, 7, _nv(4, 16), 0, None, dummy, 1 << 20, None) == -1
+    assert L.quads_quantize_nvfp4(None, 0, _nv(4, 16), 0, None, dummy, 1 << 20, None) == -1
+    assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16), 0, None, None, 0, None) == -3
+    # scores need batch == 1
+    assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16, batch=2), 2, dummy, dummy, 1 << 20, None) == -1
+    assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16), 1 << 7, None, dummy, 1 << 20, None) == -1
+    # zero rows: valid no-op
+    assert L.quads_quantize_nvfp4(dummy, 0, _nv(0, 16), 0, None, dummy, 1 << 20, None) == 0
+
+
+def test_rac_select_validation(L):
+    dummy = ctypes.c_void_p(16)
+    xq = _nv(8, 256)
+    assert L.quads_rac_select(dummy, 0, ctypes.byref(xq), dummy, 101, dummy, _nv(8, 0), None, 0, None) == -1
+    assert L.quads_rac_select(dummy, 0, ctypes.byref(xq), dummy, 50, dummy, _nv(8, 64), None, 0, None) == -2
+    big = _nv(8, 32768)
+    assert L.quads_rac_select(dummy, 0, ctypes.byref(big), dummy, 50, dummy, _nv(8, 16384), None, 0, None) == -2
+    assert L.quads_rac_select(dummy, 0, None, dummy, 50, dummy, _nv(8, 128), None, 0, None) == -1
+
+
+def _gemm_args(**kw):
+    a = _lib._GemmArgs()
+    a.struct_size = ctypes.sizeof(_lib._GemmArgs)
+    a.num_experts, a.n_seg, a.num_rows, a.act_rows, a.N, a.K = 1, 1, 64, 64, 128, 256
+    for p in ("x_codes", "x_scales", "x_gscale", "w_codes", "w_scales", "w_gscale", "expert_offsets", "y"):
+        setattr(a, p, 16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_gemm_validation(L):
+    ok = _gemm_args()
+    assert L.quads_moe_gemm_workspace_bytes(ctypes.byref(ok)) > 0
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(ok), None) == -3  # no workspace
+    cases = [
+        (dict(struct_size=8), -1), (dict(operand_mode=5), -1), (dict(epilogue=3), -1),
+        (dict(K=100), -2), (dict(N=96), -2), (dict(num_experts=0), -2), (dict(n_seg=3), -2),
+        (dict(epilogue=1, n_seg=1), -2), (dict(y=None), -1), (dict(w_codes=None), -1),
+        (dict(act_rows=8, row_token=None), -2), (dict(r_codes=16, kpad=40), -2),
+    ]
+    for kw, want in cases:
+        a = _gemm_args(**kw)
+        assert L.quads_moe_w4a4_gemm(ctypes.byref(a), None) == want, kw
+        assert L.quads_last_error() != b""
+
+
+def test_qdq_route_combine_validation(L):
+    dummy = ctypes.c_void_p(16)
+    assert L.quads_weight_qdq(dummy, 1, 4, 24, dummy, None, 0, dummy, 1 << 20, None) == -2
+    assert L.quads_weight_qdq(dummy, 1, 4, 32, dummy, None, 1, dummy, 1 << 20, None) == -1
+    assert L.quads_moe_route(dummy, 16, 2000, 8, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None) == -2
+    assert L.quads_moe_route(dummy, 16, 64, 17, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None) == -2
+    assert L.quads_moe_route(dummy, 16, 64, 8, dummy, dummy, dummy, dummy, dummy, None, 0, None) == -3
+    assert L.quads_moe_combine(dummy, 4, 8, 6, dummy, dummy, dummy, None) == -2
