@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the QUADS rollout hot path on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--k 50]
+
+Prints ONE JSON line.  A step is one pass of the hot path over one batch of
+synthetic, seeded input already resident in HBM:
+
+  expert_gemm (default): one expert-sized linear, X bf16 4096 x 2048 with 1%
+      outlier channels, W 1536 x 2048 NVFP4 (quantized once, outside the
+      step): quantize X + RAC channel scores -> top-k% mask + second-pass
+      residual quantization -> tile list + selected-column gather -> grouped
+      W4A4+RAC GEMM (FP32 out).  The plain W4A4 step (quantize + GEMM) is timed
+      beside it for the RAC overhead.
+  moe_prefill: 16384 tokens, hidden 2048, 64 experts, top-8 Zipf-skewed
+      routing, SwiGLU 2048->768->2048: route -> quantize+RAC(X) -> gate_up
+      (SwiGLU epilogue) -> quantize+RAC(h) -> down -> combine.
+  moe_decode: the same layer at 256 tokens, 128 experts, intermediate 1024.
+  trainer_qdq: per layer, NVFP4 QDQ of 128 experts x (gate, up, down) bf16
+      master weights, then the bf16 grouped forward on 8192 tokens.
+
+`value` is tokens per second of the whole step; `roofline` describes the
+dominant kernel (its average duration from HIP events recorded on the
+stream it runs on, inside the timed steps); `cpu_baseline` is the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE W4A4+RAC expert-GEMM tokens/s & TFLOPS; % of MFMA peak; RAC overhead %"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="expert_gemm",
+                    choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq"])
+    ap.add_argument("--k", type=int, default=50, help="RAC k percent")
+    ap.add_argument("--layers", type=int, default=48, help="trainer_qdq: layers per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain", action="store_true", help="skip the plain W4A4 comparison run")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns a dict with the step's stages and accounting
+# ---------------------------------------------------------------------------
+
+def _dev(a):
+    import torch
+    if a.bits is not None:
+        return torch.from_numpy(a.bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a.f32)).cuda()
+
+
+def _weights_nvfp4(Q, w_dev, n_seg):
+    E, N, K = w_dev.shape
+    q, _ = Q.quantize_nvfp4(w_dev.reshape(E * n_seg, N // n_seg, K))
+    return q.codes.reshape(E, N, K // 2), q.scales.reshape(E, N, K // 16), q.gscale
+
+
+def setup_expert_gemm(Q, S, k):
+    import torch
+    wl = S.expert_gemm()
+    x, w = _dev(wl.x), _dev(wl.w)
+    M, K = wl.x.f32.shape
+    N = wl.w.f32.shape[0]
+    wc, wsc, wg = _weights_nvfp4(Q, w[None], 1)
+    offs = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    qc = Q.QuantizeCall(x, want_scores=True)
+    q, scores = qc()
+    scall = Q.SelectCall(x, q, scores, k)
+    sel, res, nsel = scall()
+    gc = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M,
+                    x=q, res=res if nsel else None, sel_idx=sel)
+    flops = 2.0 * M * N * (K + nsel)
+    stages = [("quantize_scores", qc), ("rac_select_residual", scall), ("gemm_prepare", gc.prepare),
+              ("gemm", gc.run)]
+    qp = Q.QuantizeCall(x, want_scores=False)
+    qpl, _ = qp()
+    gp = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M, x=qpl)
+    plain = [("quantize", qp), ("gemm_prepare", gp.prepare), ("gemm", gp.run)]
+    cfg = {"workload": "expert_gemm", "tokens": M, "K": K, "N": N, "k_percent": k, "nsel": nsel,
+           "x": "bf16 N(0,1), 1% outlier channels x30", "w": "bf16 N(0,0.02) -> NVFP4 (offline)"}
+
+    def cpu_baseline(rows):
+        from oracle import quads_oracle as O
+        qw = O.quantize_nvfp4(wl.w.f32)
+        we = O.dequant_exact(qw.codes, qw.scales, qw.g)[None]
+        xs = wl.x.f32[:rows]
+        t0 = time.perf_counter()
+        O.rac_linear(xs, we, k)
+        return time.perf_counter() - t0, f"first {rows} of {M} tokens (full K, N), oracle quantize+RAC+fp64 GEMM"
+
+    return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
+                dominant_kernel="k_gemm<0,0,true>", config=cfg, cpu_baseline=cpu_baseline, cpu_rows=M)
+
+
+def setup_moe(Q, S, k, decode):
+    import torch
+    wl = S.moe_decode(k=k) if decode else S.moe_prefill(k=k)
+    T, H = wl.x.f32.shape
+    E, N2, _ = wl.w_gate_up.f32.shape
+    I = N2 // 2
+    x = _dev(wl.x)
+    logits = torch.from_numpy(wl.logits).cuda()
+    guc, gus, gug = _weights_nvfp4(Q, _dev(wl.w_gate_up), 2)
+    dnc, dns, dng = _weights_nvfp4(Q, _dev(wl.w_down), 1)
+    R = T * wl.top
+    rc = Q.RouteCall(logits, wl.top)
+    ids, w, offs, rt, inv = rc()
+    qx = Q.QuantizeCall(x, want_scores=True)
+    q, sc = qx()
+    sx = Q.SelectCall(x, q, sc, k)
+    sel, res, nsel_x = sx()
+    g1 = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
+                    x=q, res=res if nsel_x else None, sel_idx=sel, row_token=rt, epilogue=Q.EPI_SWIGLU)
+    h = g1.y
+    qh = Q.QuantizeCall(h, want_scores=True)
+    hq, hsc = qh()
+    sh = Q.SelectCall(h, hq, hsc, k)
+    hsel, hres, nsel_h = sh()
+    g2 = Q.GemmCall(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs, num_rows=R,
+                    x=hq, res=hres if nsel_h else None, sel_idx=hsel)
+    cc = Q.CombineCall(g2.y, inv, w)
+    stages = [("route", rc), ("quantize_x", qx), ("rac_x", sx), ("gate_up_prepare", g1.prepare),
+              ("gate_up", g1.run), ("quantize_h", qh), ("rac_h", sh), ("down_prepare", g2.prepare),
+              ("down", g2.run), ("combine", cc)]
+    f1 = 2.0 * R * N2 * (H + nsel_x)
+    f2 = 2.0 * R * H * (I + nsel_h)
+    # plain W4A4 layer
+    qxp = Q.QuantizeCall(x)
+    qp, _ = qxp()
+    g1p = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
+                     x=qp, row_token=rt, epilogue=Q.EPI_SWIGLU)
+    qhp = Q.QuantizeCall(g1p.y)
+    hqp, _ = qhp()
+    g2p = Q.GemmCall(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs, num_rows=R,
+                     x=hqp)
+    ccp = Q.CombineCall(g2p.y, inv, w)
+    plain = [("route", rc), ("quantize_x", qxp), ("gate_up_prepare", g1p.prepare), ("gate_up", g1p.run),
+             ("quantize_h", qhp), ("down_prepare", g2p.prepare), ("down", g2p.run), ("combine", ccp)]
+    cnt = np.diff(offs.cpu().numpy())
+    cfg = {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "top": wl.top, "intermediate": I,
+           "k_percent": k, "nsel_x": nsel_x, "nsel_h": nsel_h,
+           "rows_per_expert": {"min": int(cnt.min()), "max": int(cnt.max()), "mean": float(cnt.mean())}}
+    wdec = {"gate_up": E * N2 * H * 0.5625, "down": E * H * I * 0.5625}
+
+    return dict(stages=stages, plain=plain, tokens=T, flops=f1 + f2, dominant="gate_up", dominant_flops=f1,
+                dominant_kernel="k_gemm<0,1,true>", config=cfg, cpu_baseline=None, weight_bytes=wdec)
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def run_steps(stages, steps, warmup):
+    """Run warmup steps, then `steps` timed steps with HIP events between
+    stages (recorded on torch's current stream, which every library call
+    uses).  Returns (seconds, {stage: mean ms})."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = {}
+    for i, (name, _) in enumerate(stages):
+        per[name] = float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+    return t1 - t0, per
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.stderr.write("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
+                         "(no multi-GPU path); run it with --gpus 1.\n")
+        sys.exit(2)
+    import torch
+    from fp4_quantized_moe_amd import _lib as Q
+    from fp4_quantized_moe_amd import synthetic as S
+
+    torch.cuda.set_device(0)
+    Q.load()
+    if args.workload == "expert_gemm":
+        wl = setup_expert_gemm(Q, S, args.k)
+    elif args.workload in ("moe_prefill", "moe_decode"):
+        wl = setup_moe(Q, S, args.k, args.workload == "moe_decode")
+    else:
+        raise SystemExit("trainer_qdq: not wired into bench.py yet")
+    torch.cuda.synchronize()
+
+    secs, per = run_steps(wl["stages"], args.steps, args.warmup)
+    ms = secs * 1e3 / args.steps
+    tokens_per_s = wl["tokens"] * args.steps / secs
+    dom_ms = per[wl["dominant"]]
+    dom_tflops = wl["dominant_flops"] / (dom_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": wl["config"],
+        "tflops_step": wl["flops"] / (ms * 1e-3) / 1e12,
+        "gemm_tflops": dom_tflops,
+        "pct_mfma_peak_bf16": 100.0 * dom_tflops / PEAK_BF16_TFLOPS,
+        "stages_ms": per,
+        "roofline": {"bound": "mfma", "kernel": wl["dominant_kernel"], "achieved": dom_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "flops_per_launch": wl["dominant_flops"], "avg_launch_ms": dom_ms},
+    }
+    if not args.no_plain and wl.get("plain"):
+        psecs, pper = run_steps(wl["plain"], args.steps, args.warmup)
+        out["plain_w4a4_ms_per_step"] = psecs * 1e3 / args.steps
+        out["plain_stages_ms"] = pper
+        out["rac_overhead_pct"] = 100.0 * (secs / psecs - 1.0)
+    if not args.no_cpu_baseline and wl.get("cpu_baseline") is not None:
+        cpu_s, sample = wl["cpu_baseline"](wl["cpu_rows"])
+        out["cpu_baseline"] = {"value": wl["cpu_rows"] / cpu_s, "unit": "tokens/s", "cores": blas_threads(),
+                               "kind": "oracle", "sample": sample, "seconds": cpu_s,
+                               "host_cpus": os.cpu_count()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

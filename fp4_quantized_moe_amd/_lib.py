@@ -35,7 +35,7 @@ class _NVFP4(ctypes.Structure):
 
 class _GemmArgs(ctypes.Structure):
     _fields_ = [
-        ("struct_size", _c_u32), ("operand_mode", _c_i32), ("epilogue", _c_i32), ("y_dtype", _c_i32),
+        ("struct_size", _c_u32), ("flags", _c_u32), ("operand_mode", _c_i32), ("epilogue", _c_i32), ("y_dtype", _c_i32),
         ("num_experts", _c_i32), ("n_seg", _c_i32),
         ("num_rows", _c_i64), ("act_rows", _c_i64), ("N", _c_i64), ("K", _c_i64),
         ("x_codes", _vp), ("x_scales", _vp), ("x_gscale", _vp),
@@ -51,7 +51,7 @@ EXPORTS = [
     "quads_last_error", "quads_version", "quads_rac_nsel", "quads_rac_kpad",
     "quads_quantize_workspace_bytes", "quads_quantize_nvfp4",
     "quads_rac_select_workspace_bytes", "quads_rac_select",
-    "quads_moe_gemm_workspace_bytes", "quads_moe_w4a4_gemm",
+    "quads_moe_gemm_workspace_bytes", "quads_moe_w4a4_gemm", "quads_moe_gemm_prepare",
     "quads_weight_qdq_workspace_bytes", "quads_weight_qdq",
     "quads_moe_route_workspace_bytes", "quads_moe_route", "quads_moe_combine",
 ]
@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH):
     L.quads_moe_gemm_workspace_bytes.argtypes = [ctypes.POINTER(_GemmArgs)]
     L.quads_moe_w4a4_gemm.restype = ctypes.c_int
     L.quads_moe_w4a4_gemm.argtypes = [ctypes.POINTER(_GemmArgs), _vp]
+    L.quads_moe_gemm_prepare.restype = ctypes.c_int
+    L.quads_moe_gemm_prepare.argtypes = [ctypes.POINTER(_GemmArgs), _vp]
     L.quads_weight_qdq_workspace_bytes.restype = ctypes.c_size_t
     L.quads_weight_qdq_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
     L.quads_weight_qdq.restype = ctypes.c_int
@@ -164,93 +166,145 @@ def rac_kpad(nsel: int) -> int:
     return int(load().quads_rac_kpad(nsel))
 
 
+class QuantizeCall:
+    """quads_quantize_nvfp4 with output buffers and workspace allocated once.
+    x: [rows, cols] or [batch, rows, cols] (bf16/fp32)."""
+
+    def __init__(self, x: torch.Tensor, want_scores: bool = False, gscale: torch.Tensor | None = None,
+                 out: NVFP4Tensor | None = None):
+        L = load()
+        _require_cuda(x)
+        self.x = x
+        batch, rows, cols = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+        self.q = out if out is not None else empty_nvfp4(batch, rows, cols, x.device)
+        self.flags = 0
+        if gscale is not None:
+            self.q.gscale.copy_(gscale.reshape(-1))
+            self.flags |= GSCALE_GIVEN
+        self.scores = None
+        if want_scores:
+            self.scores = torch.empty(cols, dtype=torch.float32, device=x.device)
+            self.flags |= WANT_SCORES
+        self.ws = _workspace(L.quads_quantize_workspace_bytes(batch, rows, cols), x.device)
+        self._st = self.q.c_struct()
+        self._dt = _dtype_code(x)
+
+    def __call__(self):
+        _check(load().quads_quantize_nvfp4(_ptr(self.x), self._dt, self._st, self.flags, _ptr(self.scores),
+                                           _ptr(self.ws), self.ws.numel(), _stream()), "quads_quantize_nvfp4")
+        return self.q, self.scores
+
+
 def quantize_nvfp4(x: torch.Tensor, want_scores: bool = False, gscale: torch.Tensor | None = None,
                    out: NVFP4Tensor | None = None):
-    """x: [rows, cols] or [batch, rows, cols] (bf16/fp32) -> (NVFP4Tensor, scores or None)."""
-    L = load()
-    _require_cuda(x)
-    batch, rows, cols = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
-    q = out if out is not None else empty_nvfp4(batch, rows, cols, x.device)
-    flags = 0
-    if gscale is not None:
-        q.gscale.copy_(gscale.reshape(-1))
-        flags |= GSCALE_GIVEN
-    scores = None
-    if want_scores:
-        scores = torch.empty(cols, dtype=torch.float32, device=x.device)
-        flags |= WANT_SCORES
-    ws = _workspace(L.quads_quantize_workspace_bytes(batch, rows, cols), x.device)
-    _check(L.quads_quantize_nvfp4(_ptr(x), _dtype_code(x), q.c_struct(), flags, _ptr(scores), _ptr(ws),
-                                  ws.numel(), _stream()), "quads_quantize_nvfp4")
-    return q, scores
+    """-> (NVFP4Tensor, scores or None)."""
+    return QuantizeCall(x, want_scores, gscale, out)()
+
+
+class SelectCall:
+    """quads_rac_select with sel_idx and the residual tensor allocated once."""
+
+    def __init__(self, x: torch.Tensor, xq: NVFP4Tensor, scores: torch.Tensor, k_percent: int):
+        _require_cuda(x, scores)
+        rows, cols = xq.rows, xq.cols
+        self.nsel = rac_nsel(cols, k_percent)
+        if self.nsel < 0:
+            raise QuadsError(f"invalid k_percent {k_percent}")
+        kpad = rac_kpad(self.nsel)
+        dev = x.device
+        self.sel = torch.empty(max(kpad, 1), dtype=torch.int32, device=dev)
+        self.res = empty_nvfp4(1, rows, kpad, dev) if kpad else NVFP4Tensor(
+            torch.empty(rows, 0, dtype=torch.uint8, device=dev), torch.empty(rows, 0, dtype=torch.uint8, device=dev),
+            torch.empty(1, dtype=torch.float32, device=dev), 1, rows, 0)
+        self.x, self.xq, self.scores, self.k = x, xq, scores, k_percent
+        self._xs = xq.c_struct()
+        self._rs = self.res.c_struct()
+        self._dt = _dtype_code(x)
+        self.kpad = kpad
+
+    def __call__(self):
+        _check(load().quads_rac_select(_ptr(self.x), self._dt, ctypes.byref(self._xs), _ptr(self.scores), self.k,
+                                       _ptr(self.sel), self._rs, None, 0, _stream()), "quads_rac_select")
+        return self.sel[:self.kpad], self.res, self.nsel
 
 
 def rac_select(x: torch.Tensor, xq: NVFP4Tensor, scores: torch.Tensor, k_percent: int):
     """-> (sel_idx int32 [kpad], residual NVFP4Tensor [rows, kpad], nsel)."""
-    L = load()
-    _require_cuda(x, scores)
-    rows, cols = xq.rows, xq.cols
-    nsel = rac_nsel(cols, k_percent)
-    if nsel < 0:
-        raise QuadsError(f"invalid k_percent {k_percent}")
-    kpad = rac_kpad(nsel)
-    sel = torch.empty(max(kpad, 1), dtype=torch.int32, device=x.device)
-    res = empty_nvfp4(1, rows, kpad, x.device) if kpad else NVFP4Tensor(
-        torch.empty(rows, 0, dtype=torch.uint8, device=x.device),
-        torch.empty(rows, 0, dtype=torch.uint8, device=x.device),
-        torch.empty(1, dtype=torch.float32, device=x.device), 1, rows, 0)
-    xs = xq.c_struct()
-    _check(L.quads_rac_select(_ptr(x), _dtype_code(x), ctypes.byref(xs), _ptr(scores), k_percent, _ptr(sel),
-                              res.c_struct(), None, 0, _stream()), "quads_rac_select")
-    return sel[:kpad], res, nsel
+    return SelectCall(x, xq, scores, k_percent)()
 
 
-def moe_w4a4_gemm(*, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
-                  expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
-                  sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
-                  x_bf16=None, w_bf16=None, y=None):
-    """Grouped expert GEMM (see quads.h).  W4A4 mode when `x` is given,
-    bf16-operand (trainer W4A16) mode when `x_bf16`/`w_bf16` are given."""
-    L = load()
-    E = int(expert_offsets.numel()) - 1
-    bf16_mode = x_bf16 is not None
-    dev = expert_offsets.device
-    if y is None:
-        if epilogue == EPI_SWIGLU:
-            y = torch.empty(num_rows, N // 2, dtype=torch.bfloat16, device=dev)
+class GemmCall:
+    """One grouped-GEMM call with its arguments and workspace built once.
+
+    W4A4 mode when `x` is given, bf16-operand (trainer W4A16) mode when
+    `x_bf16`/`w_bf16` are given.  ``prepare()`` + ``run()`` is the split form
+    (tile list and residual weight-column gather, then the GEMM kernel);
+    calling the object does both."""
+
+    def __init__(self, *, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
+                 expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
+                 sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
+                 x_bf16=None, w_bf16=None, y=None):
+        L = load()
+        E = int(expert_offsets.numel()) - 1
+        bf16_mode = x_bf16 is not None
+        dev = expert_offsets.device
+        if y is None:
+            if epilogue == EPI_SWIGLU:
+                y = torch.empty(num_rows, N // 2, dtype=torch.bfloat16, device=dev)
+            else:
+                y = torch.empty(num_rows, N, dtype=y_dtype, device=dev)
+        self.y = y
+        self._keep = [w_codes, w_scales, w_gscale, expert_offsets, x, res, sel_idx, row_token, x_bf16, w_bf16]
+        a = _GemmArgs()
+        a.struct_size = ctypes.sizeof(_GemmArgs)
+        a.operand_mode = OPERANDS_BF16 if bf16_mode else OPERANDS_W4A4
+        a.epilogue = epilogue
+        a.y_dtype = BF16 if y.dtype == torch.bfloat16 else F32
+        a.num_experts = E
+        a.n_seg = n_seg
+        a.num_rows = num_rows
+        a.N, a.K = N, K
+        if bf16_mode:
+            _require_cuda(x_bf16, w_bf16)
+            a.act_rows = x_bf16.shape[0]
+            a.x_bf16, a.w_bf16 = x_bf16.data_ptr(), w_bf16.data_ptr()
         else:
-            y = torch.empty(num_rows, N, dtype=y_dtype, device=dev)
-    a = _GemmArgs()
-    a.struct_size = ctypes.sizeof(_GemmArgs)
-    a.operand_mode = OPERANDS_BF16 if bf16_mode else OPERANDS_W4A4
-    a.epilogue = epilogue
-    a.y_dtype = BF16 if y.dtype == torch.bfloat16 else F32
-    a.num_experts = E
-    a.n_seg = n_seg
-    a.num_rows = num_rows
-    a.N, a.K = N, K
-    if bf16_mode:
-        _require_cuda(x_bf16, w_bf16)
-        a.act_rows = x_bf16.shape[0]
-        a.x_bf16, a.w_bf16 = x_bf16.data_ptr(), w_bf16.data_ptr()
-    else:
-        a.act_rows = x.rows
-        a.x_codes, a.x_scales, a.x_gscale = x.codes.data_ptr(), x.scales.data_ptr(), x.gscale.data_ptr()
-        a.w_codes, a.w_scales, a.w_gscale = w_codes.data_ptr(), w_scales.data_ptr(), w_gscale.data_ptr()
-        if res is not None and res.cols > 0:
-            a.r_codes, a.r_scales, a.r_gscale = res.codes.data_ptr(), res.scales.data_ptr(), res.gscale.data_ptr()
-            a.sel_idx = sel_idx.data_ptr()
-            a.kpad = res.cols
-    a.row_token = None if row_token is None else row_token.data_ptr()
-    a.expert_offsets = expert_offsets.data_ptr()
-    a.y = y.data_ptr()
-    nbytes = L.quads_moe_gemm_workspace_bytes(ctypes.byref(a))
-    if nbytes == 0:
-        _check(L.quads_moe_w4a4_gemm(ctypes.byref(a), _stream()), "quads_moe_w4a4_gemm")
-    ws = _workspace(nbytes, dev)
-    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
-    _check(L.quads_moe_w4a4_gemm(ctypes.byref(a), _stream()), "quads_moe_w4a4_gemm")
-    return y
+            a.act_rows = x.rows
+            a.x_codes, a.x_scales, a.x_gscale = x.codes.data_ptr(), x.scales.data_ptr(), x.gscale.data_ptr()
+            a.w_codes, a.w_scales, a.w_gscale = w_codes.data_ptr(), w_scales.data_ptr(), w_gscale.data_ptr()
+            if res is not None and res.cols > 0:
+                a.r_codes, a.r_scales, a.r_gscale = res.codes.data_ptr(), res.scales.data_ptr(), res.gscale.data_ptr()
+                a.sel_idx = sel_idx.data_ptr()
+                a.kpad = res.cols
+        a.row_token = None if row_token is None else row_token.data_ptr()
+        a.expert_offsets = expert_offsets.data_ptr()
+        a.y = y.data_ptr()
+        nbytes = L.quads_moe_gemm_workspace_bytes(ctypes.byref(a))
+        if nbytes == 0:  # invalid arguments: let the library report why
+            _check(L.quads_moe_w4a4_gemm(ctypes.byref(a), None), "quads_moe_w4a4_gemm")
+        self.ws = _workspace(nbytes, dev)
+        a.ws, a.ws_bytes = self.ws.data_ptr(), self.ws.numel()
+        self.args = a
+        self.flops_k = K + (a.kpad if a.r_codes else 0)
+
+    def prepare(self):
+        _check(load().quads_moe_gemm_prepare(ctypes.byref(self.args), _stream()), "quads_moe_gemm_prepare")
+
+    def run(self):
+        """Main GEMM kernel only (after prepare())."""
+        self.args.flags = 1
+        _check(load().quads_moe_w4a4_gemm(ctypes.byref(self.args), _stream()), "quads_moe_w4a4_gemm")
+
+    def __call__(self):
+        self.args.flags = 0
+        _check(load().quads_moe_w4a4_gemm(ctypes.byref(self.args), _stream()), "quads_moe_w4a4_gemm")
+        return self.y
+
+
+def moe_w4a4_gemm(**kw):
+    """Grouped expert GEMM (see quads.h); returns y."""
+    return GemmCall(**kw)()
 
 
 def weight_qdq(w: torch.Tensor, export: bool = False):
@@ -267,6 +321,45 @@ def weight_qdq(w: torch.Tensor, export: bool = False):
     _check(L.quads_weight_qdq(_ptr(w), batch, rows, cols, _ptr(out), ctypes.byref(qs) if qs is not None else None,
                               0, _ptr(ws), ws.numel(), _stream()), "quads_weight_qdq")
     return out, q
+
+
+class RouteCall:
+    """quads_moe_route with its outputs and workspace allocated once."""
+
+    def __init__(self, logits: torch.Tensor, top: int):
+        L = load()
+        _require_cuda(logits)
+        T, E = logits.shape
+        dev = logits.device
+        self.logits, self.T, self.E, self.top = logits, T, E, top
+        self.ids = torch.empty(T, top, dtype=torch.int32, device=dev)
+        self.w = torch.empty(T, top, dtype=torch.float32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.row_token = torch.empty(max(T * top, 1), dtype=torch.int32, device=dev)
+        self.inverse = torch.empty(T, top, dtype=torch.int32, device=dev)
+        self.ws = _workspace(L.quads_moe_route_workspace_bytes(T, E), dev)
+
+    def __call__(self):
+        _check(load().quads_moe_route(_ptr(self.logits), self.T, self.E, self.top, _ptr(self.ids), _ptr(self.w),
+                                      _ptr(self.offsets), _ptr(self.row_token), _ptr(self.inverse), _ptr(self.ws),
+                                      self.ws.numel(), _stream()), "quads_moe_route")
+        return self.ids, self.w, self.offsets, self.row_token[:self.T * self.top], self.inverse
+
+
+class CombineCall:
+    """quads_moe_combine with its output allocated once."""
+
+    def __init__(self, y: torch.Tensor, inverse: torch.Tensor, topk_w: torch.Tensor):
+        _require_cuda(y, inverse, topk_w)
+        self.y, self.inverse, self.w = y, inverse, topk_w
+        self.T, self.top = inverse.shape
+        self.N = y.shape[1]
+        self.out = torch.empty(self.T, self.N, dtype=torch.float32, device=y.device)
+
+    def __call__(self):
+        _check(load().quads_moe_combine(_ptr(self.y), self.T, self.top, self.N, _ptr(self.inverse), _ptr(self.w),
+                                        _ptr(self.out), _stream()), "quads_moe_combine")
+        return self.out
 
 
 def moe_route(logits: torch.Tensor, top: int):

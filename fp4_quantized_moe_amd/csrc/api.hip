@@ -142,6 +142,7 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
   if (!a) return fail(QUADS_ERR_ARG, "gemm: null args");
   if (a->struct_size != sizeof(quads_moe_gemm_args))
     return fail(QUADS_ERR_ARG, "gemm: struct_size %u != %zu", a->struct_size, sizeof(quads_moe_gemm_args));
+  if (a->flags & ~QUADS_GEMM_PREPARED) return fail(QUADS_ERR_ARG, "gemm: unknown flags");
   if (a->operand_mode != QUADS_OPERANDS_W4A4 && a->operand_mode != QUADS_OPERANDS_BF16)
     return fail(QUADS_ERR_ARG, "gemm: bad operand_mode");
   if (a->epilogue != QUADS_EPI_NONE && a->epilogue != QUADS_EPI_SWIGLU) return fail(QUADS_ERR_ARG, "gemm: bad epilogue");
@@ -205,13 +206,27 @@ size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a) {
   return quads::gemm_ws_bytes(g);
 }
 
+quads_status_t quads_moe_gemm_prepare(const quads_moe_gemm_args *a, void *stream) {
+  quads::GemmLaunch g;
+  const quads_status_t st = gemm_fill(a, g);
+  if (st != QUADS_OK) return st;
+  if (a->ws == nullptr || a->ws_bytes < quads::gemm_ws_bytes(g))
+    return fail(QUADS_ERR_WORKSPACE, "gemm: workspace too small (need %zu)", quads::gemm_ws_bytes(g));
+  return device_status(quads::launch_gemm_prepare(g, static_cast<hipStream_t>(stream)), "gemm_prepare");
+}
+
 quads_status_t quads_moe_w4a4_gemm(const quads_moe_gemm_args *a, void *stream) {
   quads::GemmLaunch g;
   const quads_status_t st = gemm_fill(a, g);
   if (st != QUADS_OK) return st;
   if (a->ws == nullptr || a->ws_bytes < quads::gemm_ws_bytes(g))
     return fail(QUADS_ERR_WORKSPACE, "gemm: workspace too small (need %zu)", quads::gemm_ws_bytes(g));
-  return device_status(quads::launch_gemm(g, static_cast<hipStream_t>(stream)), "gemm");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(a->flags & QUADS_GEMM_PREPARED)) {
+    const hipError_t e = quads::launch_gemm_prepare(g, s);
+    if (e != hipSuccess) return device_status(e, "gemm_prepare");
+  }
+  return device_status(quads::launch_gemm_main(g, s), "gemm");
 }
 
 size_t quads_weight_qdq_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {

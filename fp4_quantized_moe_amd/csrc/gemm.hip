@@ -11,93 +11,94 @@
 //                           + gr * sum_j W[e,n,sel_j] R[t(i),j] )
 //
 // Operand decode.  An NVFP4 value e2m1 * e4m3 has at most 2 + 4 significant
-// bits and lies in [2^-10, 2688], so it is exact in bf16; bf16 x bf16 products
-// are exact in FP32, so a bf16 MFMA with FP32 accumulation computes the
-// W4A4 sum with only accumulation rounding.  The block scales are 16-element
-// E4M3, which the gfx950 scaled f8f6f4 MFMA (32-element power-of-two scales)
-// cannot express exactly, so operands are decoded to bf16 on the way from
-// global memory to LDS, once per workgroup tile:
-//   - a 128-entry LDS table maps each E4M3 scale byte to the low and high
-//     bytes of the bf16 values level_i * scale for the eight E2M1 levels;
-//   - v_perm_b32 looks four 3-bit level indices up at once in that table, the
-//     sign bits are OR-ed in, and two more v_perm_b32 interleave low/high
-//     bytes into bf16 pairs: about 1.75 VALU operations per element.
-//   The decode emits each 8-element group in the order 0,2,4,6,1,3,5,7.  A
-//   contraction does not depend on the order of k, and both operands of a
-//   W4A4 product use the same order; the gathered bf16 residual weights are
-//   written in that order too.
+// bits and lies in [2^-10, 2688]: it is exact in fp16 (normal range
+// [2^-14, 65504]), and fp16 x fp16 products are exact in FP32, so an fp16 MFMA
+// with FP32 accumulation computes the W4A4 sum with only accumulation
+// rounding.  The block scales are 16-element E4M3, which the gfx950 scaled
+// f8f6f4 MFMA (32-element power-of-two scales) cannot express exactly, so
+// operands are decoded on the way from global memory to LDS, once per
+// workgroup tile: v_cvt_scalef32_pk_f16_fp4 (unit scale) turns two codes into
+// two fp16 levels, and one v_pk_mul_f16 by the block scale (v_cvt of the E4M3
+// byte, exact) gives the exact products -- two VALU operations per two
+// elements.  The bf16-operand (trainer) mode feeds bf16 MFMAs directly.
 //
-// Tiling: 128x128 output tile, K step 64, 256 threads = 4 waves each owning a
-// 64x64 sub-tile of 2x2 v_mfma_f32_32x32x16_bf16.  LDS holds double-buffered
-// bf16 tiles [128][64] whose 16-byte chunks are XOR-swizzled by (row & 7) so
-// that both the decode writes and the MFMA operand reads are conflict-free.
-// Global loads for step k+1 are issued before the MFMAs of step k.
+// Tiling: templated BM x BN workgroup tiles of WGM x WGN waves, K step 64,
+// v_mfma_f32_32x32x16_{f16,bf16}.  LDS holds two [rows][64] tiles per operand
+// whose 16-byte chunks are XOR-swizzled by (row & 7) so that both the decode
+// writes and the MFMA operand reads are conflict-free.  Global data is
+// fetched two K steps ahead into alternating register stages; the loop body
+// (fetch step k+2, MFMAs on step k, decode+store step k+1, barrier) has no
+// branches, so the next step's decode can be interleaved with this step's
+// MFMAs.
 //
-// Scheduling: a tile list over (expert, m-tile) is built on the device from
+// Scheduling: a per-expert tile list is built on the device from
 // expert_offsets (no host sync); the grid is an upper bound and surplus
 // workgroups exit.  Workgroup ids are remapped so that each of the 8 XCDs
 // (dispatched round-robin) owns a contiguous range of tiles, keeping an
 // expert's weights and an m-tile's activations in one L2.
 //
-// RAC segment: the selected weight columns are gathered once per call into a
-// bf16 [E, N, kpad] buffer (k_gather_wcols), after which the residual is a
+// RAC segment: the selected weight columns are gathered once per call into an
+// fp16 [E, N, kpad] buffer (k_gather_wcols), after which the residual is a
 // plain extended-K loop; the FP32 accumulator is rescaled by gx/gr between the
 // two segments so a single accumulator serves both.
+#include <stdlib.h>
+#include <string.h>
+
 #include "launch.hpp"
 #include "quads_device.hpp"
 
 namespace quads {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kThreads = 256;
+constexpr int BK = 64;  // K step: 4 NVFP4 blocks = 8 chunks of 8 16-bit values per row
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+// Workgroup tile BM x BN, WGM x WGN waves, each wave owning a (BM/WGM) x
+// (BN/WGN) sub-tile of 32x32 MFMA tiles.
+template <int BM_, int BN_, int WGM_, int WGN_, int MINB_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int MINB = MINB_;  // workgroups per CU the register budget must allow
+  static constexpr int THREADS = 64 * WGM * WGN;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;
+  static constexpr int MI = TM / 32, NI = TN / 32;
+  static constexpr int FA = BM * 4 / THREADS, FB = BN * 4 / THREADS;  // NVFP4 block loads / thread
+  static constexpr int HA = BM * 8 / THREADS, HB = BN * 8 / THREADS;  // 16-byte raw loads / thread
+  static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "wave tile must be 32-aligned");
+  static_assert(FA * THREADS == BM * 4 && FB * THREADS == BN * 4, "fp4 staging must divide");
+  static_assert(HA * THREADS == BM * 8 && HB * THREADS == BN * 8, "raw staging must divide");
+};
+
+// (dec(s), dec(s)) as fp16 for an E4M3 scale byte s: exact conversion.
+__device__ __forceinline__ h2 scale_h2(uint32_t s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s | (s << 8), 1.0f, false);
 }
 
-// Decode 8 E2M1 codes (one 32-bit word, element i in nibble i) with the
-// per-scale table entry L = (lo bytes of levels 0-3, 4-7, hi bytes 0-3, 4-7)
-// into 8 bf16 in the order 0,2,4,6,1,3,5,7.
-__device__ __forceinline__ uint4 decode8(uint32_t w, uint4 L) {
-  const uint32_t sel_e = w & 0x07070707u;
-  const uint32_t sel_o = (w >> 4) & 0x07070707u;
-  const uint32_t lo_e = perm(L.y, L.x, sel_e);
-  const uint32_t hi_e = perm(L.w, L.z, sel_e) | ((w << 4) & 0x80808080u);
-  const uint32_t lo_o = perm(L.y, L.x, sel_o);
-  const uint32_t hi_o = perm(L.w, L.z, sel_o) | (w & 0x80808080u);
-  uint4 o;
-  o.x = perm(hi_e, lo_e, 0x05010400u);
-  o.y = perm(hi_e, lo_e, 0x07030602u);
-  o.z = perm(hi_o, lo_o, 0x05010400u);
-  o.w = perm(hi_o, lo_o, 0x07030602u);
-  return o;
+// 8 E2M1 codes (element i in nibble i) times the block scale -> 8 fp16.
+__device__ __forceinline__ uint4 decode8_f16(uint32_t w, h2 sc) {
+  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
-// Table entry for E4M3 scale byte s: bf16 of level_i * dec(s), split into
-// low and high bytes.  Product of <= 2 and <= 4 significant bits: exact.
-__device__ __forceinline__ uint4 make_lut_entry(uint32_t s) {
-  uint32_t lo[2] = {0, 0}, hi[2] = {0, 0};
-  if (s < 0x7Fu) {
-    const float sc = e4m3_to_f32(s);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b = __float_as_uint(e2m1_level(i) * sc) >> 16;
-      lo[i >> 2] |= (b & 0xFFu) << (8 * (i & 3));
-      hi[i >> 2] |= (b >> 8) << (8 * (i & 3));
-    }
-  }
-  return make_uint4(lo[0], lo[1], hi[0], hi[1]);
-}
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// LDS tiles are [rows][8 chunks of 16 bytes]; chunk c of row r lives at
+// c ^ ((r >> 1) & 7).  gfx950's LDS has 64 four-byte banks, so one bank row
+// spans two 128-byte tile rows and 16 lanes of a 16-byte access are serviced
+// together: with this swizzle the 16 consecutive rows read at one logical
+// chunk (MFMA fragments) and the 2-4 rows x 4-8 chunks written by a
+// decode/store instruction all land in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 struct Params {
   const int32_t *expert_offsets;
-  const int32_t *tile_offsets;
+  const int32_t *tile_offsets;  // per-expert prefix of BM-row m-tiles
   int E, n_seg, n_tiles, grid_per_xcd;
   int64_t N, K, kpad;
   const int32_t *row_token;
@@ -107,258 +108,246 @@ struct Params {
   const float *r_g;
   const uint8_t *w_codes, *w_scales;
   const float *w_g;
-  const uint16_t *x_bf16, *w_bf16, *wg_bf16;
+  const uint16_t *x_bf16, *w_bf16, *wg_f16;
   void *y;
   int y_bf16;
 };
 
 // ---- operand stagers -------------------------------------------------------
-// NVFP4 rows: 128 rows x 4 blocks per K step; thread t stages blocks
-// (row t/4 + 64p, block t%4), p = 0,1.
+// NVFP4 rows: 4 blocks per row per K step; thread t stages blocks
+// (row fp4_row(t) + p*THREADS/4, block t%4).  `base[p]` is the row's first block
+// index.  Loads are unconditional: a block past the end of K re-reads block 0
+// of its row (in bounds) and is zeroed when decoded, so no branch or early
+// wait sits between a fetch and its use two steps later.
+template <int P>
 struct Fp4Stage {
-  uint2 w[2];
-  uint32_t s[2];
+  uint2 w[P];
+  uint32_t s[P];
+  bool ok;
 };
 
-__device__ __forceinline__ void fp4_fetch(Fp4Stage &st, const uint8_t *codes, const uint8_t *scales,
-                                          const int64_t (&row)[2], int64_t nblk, int kt) {
-  const int64_t blk = static_cast<int64_t>(kt) * 4 + (threadIdx.x & 3);
+template <int P>
+__device__ __forceinline__ void fp4_fetch(Fp4Stage<P> &st, const uint8_t *codes, const uint8_t *scales,
+                                          const int64_t (&base)[P], int nblk, int kt) {
+  const int blk = kt * 4 + (threadIdx.x & 3);
+  st.ok = blk < nblk;
+  const int off = st.ok ? blk : 0;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    if (blk < nblk) {
-      st.w[p] = *reinterpret_cast<const uint2 *>(codes + (row[p] * nblk + blk) * 8);
-      st.s[p] = scales[row[p] * nblk + blk];
-    } else {
-      st.w[p] = make_uint2(0, 0);
-      st.s[p] = 0;
-    }
+  for (int p = 0; p < P; ++p) {
+    st.w[p] = *reinterpret_cast<const uint2 *>(codes + (base[p] + off) * 8);
+    st.s[p] = scales[base[p] + off];
   }
 }
 
-__device__ __forceinline__ void fp4_store(const Fp4Stage &st, uint4 *tile, const uint4 *lut) {
+// Decode and store the blocks p of the stage with p % 4 == part (the store is
+// split in four parts so each can follow one MFMA sub-step).
+// Row staged by thread t's lane quad: bits 0 and 1 of the quad index t/4 are
+// swapped, so each group of 8 lanes (the granularity at which a 16-byte LDS
+// write is serviced) covers two rows whose swizzle keys differ in bit 0 and
+// the chunk sets {0,2,4,6} and {1,3,5,7} it writes do not collide.
+__device__ __forceinline__ int fp4_row(int t) {
+  const int q = t >> 2;
+  return (q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1);
+}
+
+template <int P, int THREADS>
+__device__ __forceinline__ void fp4_store(const Fp4Stage<P> &st, uint4 *tile, int part) {
   const int c = (threadIdx.x & 3) * 2;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int r = (threadIdx.x >> 2) + 64 * p;
-    const uint4 L = lut[st.s[p] & 0x7Fu];
-    tile[swz(r, c)] = decode8(st.w[p].x, L);
-    tile[swz(r, c + 1)] = decode8(st.w[p].y, L);
+  for (int p = 0; p < P; ++p) {
+    if (p % 4 != part) continue;
+    const int r = fp4_row(threadIdx.x) + p * (THREADS / 4);
+    const h2 sc = scale_h2(st.ok ? st.s[p] : 0u);
+    tile[swz(r, c)] = decode8_f16(st.w[p].x, sc);
+    tile[swz(r, c + 1)] = decode8_f16(st.w[p].y, sc);
   }
 }
 
-// bf16 rows: 128 rows x 8 chunks of 8 elements; thread t stages chunk t%8 of
-// rows t/8 + 32q, q = 0..3.
-struct Bf16Stage {
-  uint4 v[4];
+// 16-bit rows (bf16 or pre-decoded fp16): 8 chunks of 8 values per row per K
+// step; thread t stages chunk t%8 of rows t/8 + q*THREADS/8.  `base[q]` is the
+// row's first element; same unconditional-load rule as above.
+template <int P>
+struct RawStage {
+  uint4 v[P];
+  bool ok;
 };
 
-__device__ __forceinline__ void bf16_fetch(Bf16Stage &st, const uint16_t *base,
-                                           const int64_t (&row)[4], int64_t ld, int64_t kdim,
-                                           int kt) {
-  const int64_t k = static_cast<int64_t>(kt) * BK + (threadIdx.x & 7) * 8;
+template <int P>
+__device__ __forceinline__ void raw_fetch(RawStage<P> &st, const uint16_t *src, const int64_t (&base)[P],
+                                          int kdim, int kt) {
+  const int k = kt * BK + (threadIdx.x & 7) * 8;
+  st.ok = k < kdim;
+  const int off = st.ok ? k : 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (k < kdim)
-      st.v[q] = *reinterpret_cast<const uint4 *>(base + row[q] * ld + k);
-    else
-      st.v[q] = make_uint4(0, 0, 0, 0);
-  }
+  for (int q = 0; q < P; ++q) st.v[q] = *reinterpret_cast<const uint4 *>(src + base[q] + off);
 }
 
-__device__ __forceinline__ void bf16_store(const Bf16Stage &st, uint4 *tile) {
+template <int P, int THREADS>
+__device__ __forceinline__ void raw_store(const RawStage<P> &st, uint4 *tile, int part) {
   const int c = threadIdx.x & 7;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) tile[swz((threadIdx.x >> 3) + 32 * q, c)] = st.v[q];
+  for (int q = 0; q < P; ++q)
+    if (q % 4 == part)
+      tile[swz((threadIdx.x >> 3) + q * (THREADS / 8), c)] = st.ok ? st.v[q] : make_uint4(0, 0, 0, 0);
 }
 
-// One K step of MFMAs on the staged tiles.
-__device__ __forceinline__ void mfma_step(const uint4 *As, const uint4 *Bs, f32x16 (&acc)[2][2],
-                                          int wm, int wn, int lane) {
+// Operand fragments of one 16-wide K sub-step for this wave.
+template <class C>
+struct Frags {
+  uint4 a[C::MI], b[C::NI];
+};
+
+template <class C>
+__device__ __forceinline__ void load_frags(Frags<C> &f, const uint4 *As, const uint4 *Bs, int ks, int wm, int wn,
+                                           int lane) {
+  const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) f.a[mi] = As[swz(wm * C::TM + mi * 32 + (lane & 31), chunk)];
+#pragma unroll
+  for (int ni = 0; ni < C::NI; ++ni) f.b[ni] = Bs[swz(wn * C::TN + ni * 32 + (lane & 31), chunk)];
+}
+
+template <class C, bool F16>
+__device__ __forceinline__ void mfmas(const Frags<C> &f, f32x16 (&acc)[C::MI][C::NI]) {
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni) {
+      if constexpr (F16)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, f.a[mi]),
+                                                             __builtin_bit_cast(h8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+      else
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, f.a[mi]), __builtin_bit_cast(bf16x8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+    }
+}
+
+// One K step: four 16-wide sub-steps.  The fragments of sub-step ks+1 are
+// read from LDS before the MFMAs of sub-step ks are issued, and part ks of the
+// next step's decode/store follows them, so LDS latency and the decode VALU
+// overlap the MFMAs; scheduling fences keep the compiler from regrouping the
+// sub-steps (which would hoist every load and exhaust the register file).
+template <class C, bool F16, class Store>
+__device__ __forceinline__ void mfma_step(const uint4 *As, const uint4 *Bs, f32x16 (&acc)[C::MI][C::NI], int wm,
+                                          int wn, int lane, Store store_part) {
+  Frags<C> f0, f1;
+  load_frags<C>(f0, As, Bs, 0, wm, wn, lane);
 #pragma unroll
   for (int ks = 0; ks < BK / 16; ++ks) {
-    const int chunk = 2 * ks + (lane >> 5);
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-      a[mi] = __builtin_bit_cast(bf16x8, As[swz(wm * 64 + mi * 32 + (lane & 31), chunk)]);
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-      b[ni] = __builtin_bit_cast(bf16x8, Bs[swz(wn * 64 + ni * 32 + (lane & 31), chunk)]);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    Frags<C> &cur = (ks & 1) ? f1 : f0;
+    Frags<C> &nxt = (ks & 1) ? f0 : f1;
+    if (ks + 1 < BK / 16) load_frags<C>(nxt, As, Bs, ks + 1, wm, wn, lane);
+    mfmas<C, F16>(cur, acc);
+    store_part(ks);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Weight row of tile row tr.  SWIGLU tiles interleave 32-row gate and up
-// slices so each wave's 64 columns are 32 gate + the matching 32 up columns.
-template <int EPI>
+// Weight row of tile row tr.  For SWIGLU each wave's TN columns are TN/2
+// gate columns followed by the matching TN/2 up columns, so both halves of
+// an output element land in the same lane and register.
+template <class C, int EPI>
 __device__ __forceinline__ int64_t w_row_of(int tr, int nt, int64_t N) {
   if constexpr (EPI == 0) {
-    return static_cast<int64_t>(nt) * BN + tr;
+    return static_cast<int64_t>(nt) * C::BN + tr;
   } else {
-    const int64_t I = N / 2;
-    return ((tr & 63) >> 5) * I + static_cast<int64_t>(nt) * 64 + (tr >> 6) * 32 + (tr & 31);
+    constexpr int half = C::TN / 2;
+    const int wn = tr / C::TN, c = tr % C::TN;
+    const int64_t hc = static_cast<int64_t>(nt) * (C::BN / 2) + wn * half + (c % half);
+    return (c / half) * (N / 2) + hc;
   }
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// MODE 0: NVFP4 operands (+ residual segment if HAS_RES); MODE 1: bf16 operands.
-template <int MODE, int EPI, bool HAS_RES>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(Params p) {
-  __shared__ uint4 As[2][BM * BK / 8];
-  __shared__ uint4 Bs[2][BN * BK / 8];
-  __shared__ uint4 lut[128];
-  __shared__ int s_e, s_m0, s_mend;
+// Branch-free two-buffer pipeline.  Before half h of an iteration, LDS buffer
+// h holds step kt+h and register stage 1-h holds step kt+h+1 (fetched one
+// step earlier); half h fetches step kt+h+2 into stage h, runs the MFMAs on
+// buffer h, decodes+stores stage 1-h into buffer 1-h, then synchronizes.
+// Fetch indices are clamped to the last step, so the tail re-reads (in
+// bounds) data it never uses.
+template <class C, bool F16, class SA, class SB, class FetchA, class FetchB, class StoreA, class StoreB>
+__device__ __forceinline__ void k_loop(int nk, uint4 (*As)[C::BM * 8], uint4 (*Bs)[C::BN * 8],
+                                       f32x16 (&acc)[C::MI][C::NI], int wm, int wn, int lane, FetchA fa,
+                                       FetchB fb, StoreA sta, StoreB stb) {
+  // Steps are processed in pairs; an odd count gets one all-zero step (its
+  // blocks are past the end of K), so the loop body has no exit in between.
+  SA s0, s1;
+  SB t0, t1;
+  fa(s0, 0);
+  fb(t0, 0);
+  fa(s1, 1);
+  fb(t1, 1);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) {
+    sta(s0, As[0], part);
+    stb(t0, Bs[0], part);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    fa(s0, kt + 2);
+    fb(t0, kt + 2);
+    mfma_step<C, F16>(As[0], Bs[0], acc, wm, wn, lane, [&](int part) {
+      sta(s1, As[1], part);
+      stb(t1, Bs[1], part);
+    });
+    __syncthreads();
+    fa(s1, kt + 3);
+    fb(t1, kt + 3);
+    mfma_step<C, F16>(As[1], Bs[1], acc, wm, wn, lane, [&](int part) {
+      sta(s0, As[0], part);
+      stb(t0, Bs[0], part);
+    });
+    __syncthreads();
+  }
+}
 
-  // XCD-aware remap: XCD x (= blockIdx % 8) gets logical tiles
-  // [x * grid_per_xcd, (x + 1) * grid_per_xcd).
+// Map this workgroup to (expert e, rows [m0, min(m0+BM, mend)), n-tile nt).
+// XCD-aware remap: XCD x (= blockIdx % 8) gets logical tiles
+// [x * grid_per_xcd, (x + 1) * grid_per_xcd).  Returns false for surplus
+// workgroups (uniformly for the whole workgroup).
+template <class C>
+__device__ __forceinline__ bool tile_setup(const Params &p, int &nt, int &e, int &m0, int &mend, int &s_e, int &s_m0,
+                                           int &s_mend) {
   const int logical = (blockIdx.x & 7) * p.grid_per_xcd + (blockIdx.x >> 3);
-  const int mt = logical / p.n_tiles, nt = logical % p.n_tiles;
-  if (mt >= p.tile_offsets[p.E]) return;
+  const int mt = logical / p.n_tiles;
+  nt = logical % p.n_tiles;
+  if (mt >= p.tile_offsets[p.E]) return false;
   if (threadIdx.x == 0) {
-    int lo = 0, hi = p.E;  // largest e with tile_offsets[e] <= mt
+    int lo = 0, hi = p.E;  // largest e with tile_offsets[e] <= mt (skips empty experts)
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (p.tile_offsets[mid] <= mt) lo = mid; else hi = mid;
     }
     s_e = lo;
-    s_m0 = p.expert_offsets[lo] + (mt - p.tile_offsets[lo]) * BM;
+    s_m0 = p.expert_offsets[lo] + (mt - p.tile_offsets[lo]) * C::BM;
     s_mend = p.expert_offsets[lo + 1];
   }
-  if constexpr (MODE == 0) {
-    for (int s = threadIdx.x; s < 128; s += kThreads) lut[s] = make_lut_entry(s);
-  }
   __syncthreads();
-  const int e = s_e, m0 = s_m0, mend = s_mend;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  e = s_e;
+  m0 = s_m0;
+  mend = s_mend;
+  return true;
+}
 
-  auto act_row = [&](int r) -> int64_t {
-    int i = m0 + r;
-    if (i >= mend) i = mend - 1;  // padding rows re-read a valid row; never stored
-    return p.row_token ? static_cast<int64_t>(p.row_token[i]) : static_cast<int64_t>(i);
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  const int64_t wbase = static_cast<int64_t>(e) * p.N;  // expert's first weight row
-
-  if constexpr (MODE == 0) {
-    int64_t arow[2], brow[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      arow[q] = act_row((threadIdx.x >> 2) + 64 * q);
-      brow[q] = wbase + w_row_of<EPI>((threadIdx.x >> 2) + 64 * q, nt, p.N);
-    }
-    const int64_t nblk = p.K / 16;
-    const int nk = static_cast<int>((p.K + BK - 1) / BK);
-    Fp4Stage sa, sb;
-    fp4_fetch(sa, p.x_codes, p.x_scales, arow, nblk, 0);
-    fp4_fetch(sb, p.w_codes, p.w_scales, brow, nblk, 0);
-    fp4_store(sa, As[0], lut);
-    fp4_store(sb, Bs[0], lut);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        fp4_fetch(sa, p.x_codes, p.x_scales, arow, nblk, kt + 1);
-        fp4_fetch(sb, p.w_codes, p.w_scales, brow, nblk, kt + 1);
-      }
-      mfma_step(As[cur], Bs[cur], acc, wm, wn, lane);
-      if (kt + 1 < nk) {
-        fp4_store(sa, As[cur ^ 1], lut);
-        fp4_store(sb, Bs[cur ^ 1], lut);
-      }
-      __syncthreads();
-    }
-    if constexpr (HAS_RES) {
-      const float ratio = *p.x_g / *p.r_g;
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= ratio;
-      int64_t growb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) growb[q] = wbase + w_row_of<EPI>((threadIdx.x >> 3) + 32 * q, nt, p.N);
-      const int64_t rblk = p.kpad / 16;
-      const int nr = static_cast<int>((p.kpad + BK - 1) / BK);
-      Fp4Stage sr;
-      Bf16Stage sg;
-      fp4_fetch(sr, p.r_codes, p.r_scales, arow, rblk, 0);
-      bf16_fetch(sg, p.wg_bf16, growb, p.kpad, p.kpad, 0);
-      fp4_store(sr, As[0], lut);
-      bf16_store(sg, Bs[0]);
-      __syncthreads();
-      for (int kt = 0; kt < nr; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nr) {
-          fp4_fetch(sr, p.r_codes, p.r_scales, arow, rblk, kt + 1);
-          bf16_fetch(sg, p.wg_bf16, growb, p.kpad, p.kpad, kt + 1);
-        }
-        mfma_step(As[cur], Bs[cur], acc, wm, wn, lane);
-        if (kt + 1 < nr) {
-          fp4_store(sr, As[cur ^ 1], lut);
-          bf16_store(sg, Bs[cur ^ 1]);
-        }
-        __syncthreads();
-      }
-    }
-  } else {
-    int64_t arow[4], brow[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      arow[q] = act_row((threadIdx.x >> 3) + 32 * q);
-      brow[q] = wbase + w_row_of<EPI>((threadIdx.x >> 3) + 32 * q, nt, p.N);
-    }
-    const int nk = static_cast<int>((p.K + BK - 1) / BK);
-    Bf16Stage sa, sb;
-    bf16_fetch(sa, p.x_bf16, arow, p.K, p.K, 0);
-    bf16_fetch(sb, p.w_bf16, brow, p.K, p.K, 0);
-    bf16_store(sa, As[0]);
-    bf16_store(sb, Bs[0]);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) {
-        bf16_fetch(sa, p.x_bf16, arow, p.K, p.K, kt + 1);
-        bf16_fetch(sb, p.w_bf16, brow, p.K, p.K, kt + 1);
-      }
-      mfma_step(As[cur], Bs[cur], acc, wm, wn, lane);
-      if (kt + 1 < nk) {
-        bf16_store(sa, As[cur ^ 1]);
-        bf16_store(sb, Bs[cur ^ 1]);
-      }
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue ----
+// Scale, optional SwiGLU, and store one wave's accumulators.
+template <class C, int MODE, int EPI, bool HAS_RES>
+__device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C::NI], int e, int m0, int mend,
+                                         int nt, int wm, int wn, int lane) {
   float ascale = 1.0f;
   if constexpr (MODE == 0) ascale = HAS_RES ? *p.r_g : *p.x_g;
   if constexpr (EPI == 0) {
     const int64_t seg_len = p.N / p.n_seg;
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int64_t col = static_cast<int64_t>(nt) * BN + wn * 64 + ni * 32 + (lane & 31);
+    for (int ni = 0; ni < C::NI; ++ni) {
+      const int64_t col = static_cast<int64_t>(nt) * C::BN + wn * C::TN + ni * 32 + (lane & 31);
       float sc = ascale;
       if constexpr (MODE == 0) sc = p.w_g[e * p.n_seg + col / seg_len] * ascale;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int i = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int i = m0 + wm * C::TM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (i < mend) {
             const float v = acc[mi][ni][r] * sc;
             if (p.y_bf16)
@@ -370,86 +359,444 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(Params p) {
         }
     }
   } else {
+    static_assert(EPI == 0 || C::NI % 2 == 0, "SWIGLU needs an even number of 32-column tiles per wave");
     const int64_t I = p.N / 2;
-    const int64_t col = static_cast<int64_t>(nt) * 64 + wn * 32 + (lane & 31);
     float sg = ascale, su = ascale;
     if constexpr (MODE == 0) {
       sg = p.w_g[e * 2] * ascale;
       su = p.w_g[e * 2 + 1] * ascale;
     }
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int ni = 0; ni < C::NI / 2; ++ni) {
+      const int64_t col = static_cast<int64_t>(nt) * (C::BN / 2) + wn * (C::TN / 2) + ni * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (i < mend) {
-          const float g = acc[mi][0][r] * sg;
-          const float u = acc[mi][1][r] * su;
-          static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * I + col] =
-              static_cast<uint16_t>(f32_to_bf16_bits(silu(g) * u));
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = m0 + wm * C::TM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (i < mend) {
+            const float g = acc[mi][ni][r] * sg;
+            const float u = acc[mi][ni + C::NI / 2][r] * su;
+            static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * I + col] =
+                static_cast<uint16_t>(f32_to_bf16_bits(silu(g) * u));
+          }
         }
-      }
+    }
   }
 }
 
-// Exclusive scan of per-expert m-tile counts -> tile_offsets[E + 1].
-__global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *offsets, int E, int32_t *tile_offsets) {
-  __shared__ int32_t sums[1025];
-  const int t = threadIdx.x;
-  int32_t v = 0;
-  if (t < E) v = (offsets[t + 1] - offsets[t] + BM - 1) / BM;
-  sums[t + 1] = v;
-  if (t == 0) sums[0] = 0;
+// MODE 0: NVFP4 operands (+ residual segment if HAS_RES), fp16 MFMA;
+// MODE 1: bf16 operands, bf16 MFMA.
+template <class C, int MODE, int EPI, bool HAS_RES>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
+  __shared__ uint4 As[2][C::BM * 8];
+  __shared__ uint4 Bs[2][C::BN * 8];
+  __shared__ int s_e, s_m0, s_mend;
+
+  int nt, e, m0, mend;
+  if (!tile_setup<C>(p, nt, e, m0, mend, s_e, s_m0, s_mend)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+
+  auto act_row = [&](int r) -> int64_t {
+    int i = m0 + r;
+    if (i >= mend) i = mend - 1;  // padding rows re-read a valid row; never stored
+    return p.row_token ? static_cast<int64_t>(p.row_token[i]) : static_cast<int64_t>(i);
+  };
+
+  f32x16 acc[C::MI][C::NI];
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  const int64_t wbase = static_cast<int64_t>(e) * p.N;  // expert's first weight row
+  constexpr int T = C::THREADS;
+
+  if constexpr (MODE == 0) {
+    const int nblk = static_cast<int>(p.K / 16);
+    int64_t arow[C::FA], abase[C::FA], bbase[C::FB];
+#pragma unroll
+    for (int q = 0; q < C::FA; ++q) {
+      arow[q] = act_row(fp4_row(threadIdx.x) + q * (T / 4));
+      abase[q] = arow[q] * nblk;
+    }
+#pragma unroll
+    for (int q = 0; q < C::FB; ++q)
+      bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
+    k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](Fp4Stage<C::FA> &st, int kt) { fp4_fetch(st, p.x_codes, p.x_scales, abase, nblk, kt); },
+        [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
+        [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
+        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    if constexpr (HAS_RES) {
+      const float ratio = *p.x_g / *p.r_g;
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= ratio;
+      const int rblk = static_cast<int>(p.kpad / 16);
+      int64_t rbase[C::FA], gbase[C::HB];
+#pragma unroll
+      for (int q = 0; q < C::FA; ++q) rbase[q] = arow[q] * rblk;
+#pragma unroll
+      for (int q = 0; q < C::HB; ++q)
+        gbase[q] = (wbase + w_row_of<C, EPI>((threadIdx.x >> 3) + q * (T / 8), nt, p.N)) * p.kpad;
+      k_loop<C, true, Fp4Stage<C::FA>, RawStage<C::HB>>(
+          static_cast<int>((p.kpad + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+          [&](Fp4Stage<C::FA> &st, int kt) { fp4_fetch(st, p.r_codes, p.r_scales, rbase, rblk, kt); },
+          [&](RawStage<C::HB> &st, int kt) { raw_fetch(st, p.wg_f16, gbase, static_cast<int>(p.kpad), kt); },
+          [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
+          [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
+    }
+  } else {
+    int64_t abase[C::HA], bbase[C::HB];
+#pragma unroll
+    for (int q = 0; q < C::HA; ++q) abase[q] = act_row((threadIdx.x >> 3) + q * (T / 8)) * p.K;
+#pragma unroll
+    for (int q = 0; q < C::HB; ++q) bbase[q] = (wbase + w_row_of<C, EPI>((threadIdx.x >> 3) + q * (T / 8), nt, p.N)) * p.K;
+    k_loop<C, false, RawStage<C::HA>, RawStage<C::HB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt); },
+        [&](RawStage<C::HB> &st, int kt) { raw_fetch(st, p.w_bf16, bbase, static_cast<int>(p.K), kt); },
+        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
+        [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
+  }
+
+  epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+}
+
+// ---- 8-wave ping-pong kernel for 256x256 tiles ------------------------------
+// The eight waves form two groups of four (one wave of each group per SIMD):
+// group g owns output rows [128g, 128g+128) and stages rows [128g, 128g+128)
+// of both the A and the B tile.  The groups run a phase apart: while one group
+// issues MFMAs on the current LDS buffer, the other decodes and stores its half
+// of the next K step and issues the global loads for the step after, so the
+// matrix core of every SIMD always has one wave feeding it.  Each K step is
+// two phases separated by barriers:
+//   phase 1: group 0 computes step k | group 1 stores its half of step k+1
+//   phase 2: group 0 stores its half of step k+1 | group 1 computes step k
+// Two LDS buffers suffice: buffer (k+1)%2 was last read by group 0 in phase 1
+// and by group 1 in phase 2 of step k-1, both before either group writes it in
+// step k, and both halves of step k+1 are written before phase 1 of step k+1.
+using CfgPP = Cfg<256, 256, 2, 4, 1>;
+
+template <int P>
+__device__ __forceinline__ void fp4_store_rows(const Fp4Stage<P> &st, uint4 *tile, const int (&rows)[P]) {
+  const int c = (threadIdx.x & 3) * 2;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const h2 sc = scale_h2(st.ok ? st.s[p] : 0u);
+    tile[swz(rows[p], c)] = decode8_f16(st.w[p].x, sc);
+    tile[swz(rows[p], c + 1)] = decode8_f16(st.w[p].y, sc);
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void raw_store_rows(const RawStage<P> &st, uint4 *tile, const int (&rows)[P]) {
+  const int c = threadIdx.x & 7;
+#pragma unroll
+  for (int q = 0; q < P; ++q) tile[swz(rows[q], c)] = st.ok ? st.v[q] : make_uint4(0, 0, 0, 0);
+}
+
+template <bool F16>
+__device__ __forceinline__ void pp_compute(const uint4 *As, const uint4 *Bs, f32x16 (&acc)[CfgPP::MI][CfgPP::NI],
+                                           int wm, int wn, int lane) {
+  __builtin_amdgcn_s_setprio(1);
+  mfma_step<CfgPP, F16>(As, Bs, acc, wm, wn, lane, [](int) {});
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// init(): fetch step 0, store it into buffer 0, fetch step 1.
+// mem(k, buf): store this thread's part of step k+1 into buffer buf, fetch step k+2.
+template <bool F16, class Init, class Mem>
+__device__ __forceinline__ void pp_loop(int nk, uint4 (*As)[CfgPP::BM * 8], uint4 (*Bs)[CfgPP::BN * 8],
+                                        f32x16 (&acc)[CfgPP::MI][CfgPP::NI], int g, int wm, int wn, int lane,
+                                        Init init, Mem mem) {
+  init();
+  __syncthreads();
+  for (int k = 0; k < nk; ++k) {
+    const int cur = k & 1;
+    if (g == 0)
+      pp_compute<F16>(As[cur], Bs[cur], acc, wm, wn, lane);
+    else
+      mem(k, cur ^ 1);
+    __syncthreads();
+    if (g == 0)
+      mem(k, cur ^ 1);
+    else
+      pp_compute<F16>(As[cur], Bs[cur], acc, wm, wn, lane);
+    __syncthreads();
+  }
+}
+
+template <int MODE, int EPI, bool HAS_RES>
+__global__ __launch_bounds__(CfgPP::THREADS, 1) void k_gemm_pp(Params p) {
+  using C = CfgPP;
+  __shared__ uint4 As[2][C::BM * 8];
+  __shared__ uint4 Bs[2][C::BN * 8];
+  __shared__ int s_e, s_m0, s_mend;
+  int nt, e, m0, mend;
+  if (!tile_setup<C>(p, nt, e, m0, mend, s_e, s_m0, s_mend)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = wave >> 2, wm = g, wn = wave & 3;
+  const int tg = threadIdx.x & 255;
+
+  auto act_row = [&](int r) -> int64_t {
+    int i = m0 + r;
+    if (i >= mend) i = mend - 1;  // padding rows re-read a valid row; never stored
+    return p.row_token ? static_cast<int64_t>(p.row_token[i]) : static_cast<int64_t>(i);
+  };
+
+  f32x16 acc[C::MI][C::NI];
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  const int64_t wbase = static_cast<int64_t>(e) * p.N;
+
+  if constexpr (MODE == 0) {
+    const int nblk = static_cast<int>(p.K / 16);
+    int arows[2];
+    int64_t arow[2], abase[2], bbase[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      arows[q] = g * 128 + fp4_row(tg) + q * 64;
+      arow[q] = act_row(arows[q]);
+      abase[q] = arow[q] * nblk;
+      bbase[q] = (wbase + w_row_of<C, EPI>(arows[q], nt, p.N)) * nblk;
+    }
+    Fp4Stage<2> sa, sb;
+    auto fetch = [&](int kt) {
+      fp4_fetch(sa, p.x_codes, p.x_scales, abase, nblk, kt);
+      fp4_fetch(sb, p.w_codes, p.w_scales, bbase, nblk, kt);
+    };
+    auto store = [&](int buf) {
+      fp4_store_rows(sa, As[buf], arows);
+      fp4_store_rows(sb, Bs[buf], arows);
+    };
+    pp_loop<true>(static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, g, wm, wn, lane,
+                  [&] { fetch(0); store(0); fetch(1); },
+                  [&](int k, int buf) { store(buf); fetch(k + 2); });
+    if constexpr (HAS_RES) {
+      const float ratio = *p.x_g / *p.r_g;
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= ratio;
+      const int rblk = static_cast<int>(p.kpad / 16);
+      const int kpad = static_cast<int>(p.kpad);
+      int64_t rbase[2], gbase[4];
+      int grows[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) rbase[q] = arow[q] * rblk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        grows[q] = g * 128 + (tg >> 3) + q * 32;
+        gbase[q] = (wbase + w_row_of<C, EPI>(grows[q], nt, p.N)) * p.kpad;
+      }
+      Fp4Stage<2> sr;
+      RawStage<4> sg;
+      auto rfetch = [&](int kt) {
+        fp4_fetch(sr, p.r_codes, p.r_scales, rbase, rblk, kt);
+        raw_fetch(sg, p.wg_f16, gbase, kpad, kt);
+      };
+      auto rstore = [&](int buf) {
+        fp4_store_rows(sr, As[buf], arows);
+        raw_store_rows(sg, Bs[buf], grows);
+      };
+      pp_loop<true>((kpad + BK - 1) / BK, As, Bs, acc, g, wm, wn, lane,
+                    [&] { rfetch(0); rstore(0); rfetch(1); },
+                    [&](int k, int buf) { rstore(buf); rfetch(k + 2); });
+    }
+  } else {
+    const int K = static_cast<int>(p.K);
+    int arows[4];
+    int64_t abase[4], bbase[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      arows[q] = g * 128 + (tg >> 3) + q * 32;
+      abase[q] = act_row(arows[q]) * p.K;
+      bbase[q] = (wbase + w_row_of<C, EPI>(arows[q], nt, p.N)) * p.K;
+    }
+    RawStage<4> sa, sb;
+    auto fetch = [&](int kt) {
+      raw_fetch(sa, p.x_bf16, abase, K, kt);
+      raw_fetch(sb, p.w_bf16, bbase, K, kt);
+    };
+    auto store = [&](int buf) {
+      raw_store_rows(sa, As[buf], arows);
+      raw_store_rows(sb, Bs[buf], arows);
+    };
+    pp_loop<false>((K + BK - 1) / BK, As, Bs, acc, g, wm, wn, lane, [&] { fetch(0); store(0); fetch(1); },
+                   [&](int k, int buf) { store(buf); fetch(k + 2); });
+  }
+  epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+}
+
+// Exclusive scan of per-expert m-tile counts ceil(rows_e / bm) ->
+// tile_offsets[E + 1] (E <= 1024: one thread per expert, wave scans).
+__global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *offsets, int E, int bm, int32_t *tile_offsets) {
+  __shared__ int32_t wsum[17];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int32_t v = t < E ? (offsets[t + 1] - offsets[t] + bm - 1) / bm : 0;
+  int32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   if (t == 0) {
-    for (int i = 1; i <= E; ++i) sums[i] += sums[i - 1];
+    int32_t run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int32_t x = wsum[w];
+      wsum[w] = run;
+      run += x;
+    }
+    wsum[16] = run;
   }
   __syncthreads();
-  if (t < E) tile_offsets[t] = sums[t];
-  if (t == 0) tile_offsets[E] = sums[E];
+  if (t < E) tile_offsets[t] = wsum[wave] + incl - v;
+  if (t == 0) tile_offsets[E] = wsum[16];
 }
 
-// Gather the selected weight columns of every expert row into bf16
-// [E*N, kpad] (exact values e2m1 * e4m3, no tensor scale), each 8-element
-// group in the decode order 0,2,4,6,1,3,5,7.  Two rows per workgroup.
+// Gather the selected weight columns of every expert row into fp16
+// [E*N, kpad] (exact values e2m1 * e4m3, no tensor scale).  One row per
+// 64-thread quarter of the workgroup: the row's codes and scales are staged in
+// LDS, then each thread emits 8 consecutive outputs (one 16-byte store).
 __global__ __launch_bounds__(256) void k_gather_wcols(const uint8_t *w_codes, const uint8_t *w_scales,
                                                       int64_t rows_total, int K, const int32_t *sel,
                                                       int kpad, uint16_t *out) {
-  extern __shared__ uint8_t lds[];
-  const int half = threadIdx.x >> 7, t = threadIdx.x & 127;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 2 + half;
-  const int rb = K / 2 + K / 16;
-  uint8_t *mine = lds + half * ((rb + 15) / 16 * 16);
+  extern __shared__ uint4 gather_lds[];
+  const int q = threadIdx.x >> 6, t = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + q;
+  const int stride = (K / 2 + K / 16 + 15) / 16 * 16;
+  uint8_t *mine = reinterpret_cast<uint8_t *>(gather_lds) + q * stride;
   if (row < rows_total) {
-    const uint8_t *c = w_codes + row * (K / 2);
-    for (int i = t; i < K / 8; i += 128)
-      reinterpret_cast<uint32_t *>(mine)[i] = reinterpret_cast<const uint32_t *>(c)[i];
+    const uint2 *c = reinterpret_cast<const uint2 *>(w_codes + row * (K / 2));
+    for (int i = t; i < K / 16; i += 64) reinterpret_cast<uint2 *>(mine)[i] = c[i];
     const uint8_t *s = w_scales + row * (K / 16);
-    for (int i = t; i < K / 16; i += 128) mine[K / 2 + i] = s[i];
+    for (int i = t; i < K / 16; i += 64) mine[K / 2 + i] = s[i];
   }
   __syncthreads();
   if (row >= rows_total) return;
-  constexpr int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-  for (int g = t; g < kpad / 8; g += 128) {
+  for (int g = t; g < kpad / 8; g += 64) {
+    const int4 i0 = reinterpret_cast<const int4 *>(sel)[2 * g];
+    const int4 i1 = reinterpret_cast<const int4 *>(sel)[2 * g + 1];
+    const int idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
     uint32_t h[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int c = sel[g * 8 + order[q]];
+    for (int k = 0; k < 8; ++k) {
+      const int c = idx[k];
       const uint32_t code = (mine[c >> 1] >> ((c & 1) * 4)) & 0xFu;
-      const float v = e2m1_level(code & 7u) * e4m3_to_f32(mine[K / 2 + (c >> 4)]);
-      h[q] = (__float_as_uint(v) >> 16) | ((code & 8u) << 12);
+      const float v = dequant_code(code, e4m3_to_f32(mine[K / 2 + (c >> 4)]));
+      h[k] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
     }
     reinterpret_cast<uint4 *>(out + row * kpad)[g] =
         make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
   }
 }
 
-template <int MODE, int EPI, bool RES>
-void launch_k(const Params &p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<MODE, EPI, RES>), dim3(grid), dim3(kThreads), 0, s, p);
-}
+using CfgS = Cfg<128, 128, 2, 2, 2>;  // general / ragged shapes: 256 threads, 2 workgroups per CU
+using CfgM = Cfg<128, 192, 2, 2, 1>;  // N % 192 == 0 dense shapes: 64x96 wave tiles
+using CfgL = Cfg<256, 256, 2, 4, 1>;  // large grouped shapes: 512 threads, 128x64 wave tiles
+using CfgW = Cfg<256, 256, 2, 2, 1>;  // large grouped shapes: 256 threads, 128x128 wave tiles
+
+enum TileCfg { kS = 0, kM = 1, kL = 2, kW = 3, kP = 4 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Pick the tile shape from host-known sizes only (per-expert row counts live
+// on the device): estimated CU occupancy x expected per-workgroup efficiency
+// x fraction of tile rows that are real rows.
+TileCfg pick_cfg(const GemmLaunch &a) {
+  // Optional override for tuning: QUADS_GEMM_TILE=128x128 | 128x192 | 256x256.
+  static const char *force = getenv("QUADS_GEMM_TILE");
+  if (force != nullptr) {
+    if (strcmp(force, "256x256") == 0 && a.N % 256 == 0) return kL;
+    if (strcmp(force, "128x192") == 0 && a.N % 192 == 0 && a.epilogue == 0) return kM;
+    if (strcmp(force, "128x128") == 0) return kS;
+    if (strcmp(force, "256x256w4") == 0 && a.N % 256 == 0) return kW;
+    if (strcmp(force, "256x256pp") == 0 && a.N % 256 == 0) return kP;
+  }
+  struct Cand {
+    TileCfg c;
+    int bm, bn, slots;
+    double eff;
+  } cands[2] = {{kS, 128, 128, 512, 0.6}, {kL, 256, 256, 256, 1.0}};
+  TileCfg best = kS;
+  double best_score = -1.0;
+  // Large tiles: the ping-pong kernel wins for bf16 operands, the plain
+  // 8-wave kernel for NVFP4 operands (whose decode already overlaps the MFMAs).
+  const TileCfg large = a.mode == 1 ? kP : kL;
+  for (const Cand &c : cands) {
+    if (a.N % c.bn) continue;
+    if (c.c == kM && a.epilogue != 0) continue;  // SWIGLU pairs need an even tile count per wave
+    const double m_est = static_cast<double>((a.num_rows + c.bm - 1) / c.bm) + (a.E > 1 ? a.E / 2.0 : 0.0);
+    const double wgs = m_est * static_cast<double>(a.N / c.bn);
+    const double rounds = wgs > 0 ? static_cast<double>(static_cast<int64_t>((wgs + c.slots - 1) / c.slots)) : 1.0;
+    const double util = wgs / (rounds * c.slots);
+    const double pad = m_est > 0 ? static_cast<double>(a.num_rows) / (m_est * c.bm) : 0.0;
+    const double score = util * c.eff * (pad > 1.0 ? 1.0 : pad);
+    if (score > best_score) {
+      best_score = score;
+      best = c.c == kL ? large : c.c;
+    }
+  }
+  return best;
+}
+
+int cfg_bm(TileCfg c) { return (c == kL || c == kW || c == kP) ? 256 : 128; }
+int cfg_bn(TileCfg c) { return (c == kL || c == kW || c == kP) ? 256 : (c == kM ? CfgM::BN : CfgS::BN); }
+
+template <class C, int MODE, int EPI, bool RES>
+void launch_k(const Params &p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm<C, MODE, EPI, RES>), dim3(grid), dim3(C::THREADS), 0, s, p);
+}
+
+template <int MODE, int EPI, bool RES>
+void launch_pp(const Params &p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_pp<MODE, EPI, RES>), dim3(grid), dim3(CfgPP::THREADS), 0, s, p);
+}
+
+void launch_pp_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t stream) {
+  if (a.mode == 1) {
+    if (a.epilogue == 0) launch_pp<1, 0, false>(p, g, stream);
+    else launch_pp<1, 1, false>(p, g, stream);
+  } else if (res) {
+    if (a.epilogue == 0) launch_pp<0, 0, true>(p, g, stream);
+    else launch_pp<0, 1, true>(p, g, stream);
+  } else {
+    if (a.epilogue == 0) launch_pp<0, 0, false>(p, g, stream);
+    else launch_pp<0, 1, false>(p, g, stream);
+  }
+}
+
+template <class C>
+void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t stream) {
+  if (a.mode == 1) {
+    if (a.epilogue == 0) launch_k<C, 1, 0, false>(p, g, stream);
+    else if constexpr (C::NI % 2 == 0) launch_k<C, 1, 1, false>(p, g, stream);
+  } else if (res) {
+    if (a.epilogue == 0) launch_k<C, 0, 0, true>(p, g, stream);
+    else if constexpr (C::NI % 2 == 0) launch_k<C, 0, 1, true>(p, g, stream);
+  } else {
+    if (a.epilogue == 0) launch_k<C, 0, 0, false>(p, g, stream);
+    else if constexpr (C::NI % 2 == 0) launch_k<C, 0, 1, false>(p, g, stream);
+  }
+}
 
 }  // namespace
 
@@ -460,19 +807,30 @@ size_t gemm_ws_bytes(const GemmLaunch &a) {
   return b;
 }
 
-hipError_t launch_gemm(const GemmLaunch &a, hipStream_t stream) {
+hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
+  uint8_t *ws = static_cast<uint8_t *>(a.ws);
+  int32_t *tile_offsets = reinterpret_cast<int32_t *>(ws);
+  const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
+  const TileCfg c = pick_cfg(a);
+  hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
+  if (res) {
+    uint16_t *wg = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
+    const int64_t rows_total = static_cast<int64_t>(a.E) * a.N;
+    const int K = static_cast<int>(a.K);
+    const size_t lds = 4 * ((K / 2 + K / 16 + 15) / 16 * 16);
+    hipLaunchKernelGGL(k_gather_wcols, dim3((rows_total + 3) / 4), dim3(256), lds, stream, a.w_codes,
+                       a.w_scales, rows_total, K, a.sel_idx, static_cast<int>(a.kpad), wg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   uint8_t *ws = static_cast<uint8_t *>(a.ws);
   int32_t *tile_offsets = reinterpret_cast<int32_t *>(ws);
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
   uint16_t *wg = res ? reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t))) : nullptr;
-  hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, tile_offsets);
-  if (res) {
-    const int64_t rows_total = static_cast<int64_t>(a.E) * a.N;
-    const int K = static_cast<int>(a.K);
-    const size_t lds = 2 * ((K / 2 + K / 16 + 15) / 16 * 16);
-    hipLaunchKernelGGL(k_gather_wcols, dim3((rows_total + 1) / 2), dim3(256), lds, stream, a.w_codes,
-                       a.w_scales, rows_total, K, a.sel_idx, static_cast<int>(a.kpad), wg);
-  }
+  const TileCfg c = pick_cfg(a);
+  const int bm = cfg_bm(c), bn = cfg_bn(c);
   Params p{};
   p.expert_offsets = a.expert_offsets;
   p.tile_offsets = tile_offsets;
@@ -493,25 +851,20 @@ hipError_t launch_gemm(const GemmLaunch &a, hipStream_t stream) {
   p.w_g = a.w_g;
   p.x_bf16 = a.x_bf16;
   p.w_bf16 = a.w_bf16;
-  p.wg_bf16 = wg;
+  p.wg_f16 = wg;
   p.y = a.y;
   p.y_bf16 = a.y_bf16 ? 1 : 0;
-  p.n_tiles = static_cast<int>(a.epilogue == 0 ? a.N / BN : a.N / 128);
-  const int64_t m_tiles = (a.num_rows + BM - 1) / BM + a.E;
+  p.n_tiles = static_cast<int>(a.N / bn);
+  const int64_t m_tiles = (a.num_rows + bm - 1) / bm + a.E;
   int64_t grid = m_tiles * p.n_tiles;
   grid = (grid + 7) / 8 * 8;
   p.grid_per_xcd = static_cast<int>(grid / 8);
   const int g = static_cast<int>(grid);
-  if (a.mode == 1) {
-    if (a.epilogue == 0) launch_k<1, 0, false>(p, g, stream);
-    else launch_k<1, 1, false>(p, g, stream);
-  } else if (res) {
-    if (a.epilogue == 0) launch_k<0, 0, true>(p, g, stream);
-    else launch_k<0, 1, true>(p, g, stream);
-  } else {
-    if (a.epilogue == 0) launch_k<0, 0, false>(p, g, stream);
-    else launch_k<0, 1, false>(p, g, stream);
-  }
+  if (c == kP) launch_pp_cfg(a, p, g, res, stream);
+  else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream);
+  else if (c == kL) launch_cfg<CfgL>(a, p, g, res, stream);
+  else if (c == kM) launch_cfg<CfgM>(a, p, g, res, stream);
+  else launch_cfg<CfgS>(a, p, g, res, stream);
   return hipGetLastError();
 }
 

@@ -61,7 +61,9 @@ struct GemmLaunch {
   void *ws;
 };
 size_t gemm_ws_bytes(const GemmLaunch &a);
-hipError_t launch_gemm(const GemmLaunch &a, hipStream_t stream);
+// prepare: tile list + residual weight-column gather; main: the GEMM kernel.
+hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream);
+hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream);
 
 // ---- route.hip -------------------------------------------------------------
 size_t route_ws_bytes(int64_t T, int E);

@@ -76,15 +76,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // One 16-element block quantized: packed codes (element i in nibble i of the
-// 64-bit word), E4M3 scale byte, and the FP32 dequantized values / residuals
-// on request.
+// 64-bit word lo | hi << 32) and the E4M3 scale byte.
 struct BlockQ {
   uint32_t lo, hi;  // codes of elements 0..7 and 8..15
   uint32_t scale;
 };
 
-// Quantize 16 values with tensor scale g.  If `dq_out` is non-null, writes
-// dq = sign * fl32(level * d) for each element.
+// RN(a / d) for finite a >= 0 and normal d > 0, given r = RN(1 / d):
+// q = RN(a r) is within one ulp of a/d, the remainder a - d q is exact in one
+// FMA, and RN(q + (a - d q) r) is the correctly rounded quotient (Markstein's
+// theorem for round-to-nearest).  Quotients small enough to underflow are far
+// below the first E2M1 rounding threshold (0.25), so they cannot change a code.
+__device__ __forceinline__ float div_rn_with_rcp(float a, float d, float r) {
+  const float q = a * r;
+  const float e = __builtin_fmaf(-d, q, a);
+  return __builtin_fmaf(e, r, q);
+}
+
+// Quantize 16 values with tensor scale g.  The E2M1 rounding (nearest, ties
+// to even, saturating at 6, sign kept for zeros) and the nibble packing are
+// done by v_cvt_scalef32_pk_fp4_f32 with a unit scale on the exact quotient
+// fl32(x / d); its rounding equals the threshold rule of e2m1_index on every
+// FP32 input (checked exhaustively over the rounding-relevant range).  If
+// `dq_out` is non-null, writes dq = sign * fl32(level * d), decoding the codes
+// back with v_cvt_scalef32_pk_f32_fp4.
 __device__ __forceinline__ BlockQ quantize_block16(const float (&x)[16], float g, float *dq_out) {
   float amax = 0.0f;
 #pragma unroll
@@ -92,23 +107,47 @@ __device__ __forceinline__ BlockQ quantize_block16(const float (&x)[16], float g
   const float s_real = (amax / 6.0f) / g;
   const uint32_t s = f32_to_e4m3(s_real);
   const float d = e4m3_to_f32(s) * g;
+  float v[16];
+  if (d >= 0x1p-125f) {
+    const float r = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(div_rn_with_rcp(fabsf(x[i]), d, r), x[i]);
+  } else if (d > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = x[i] / d;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(0.0f, x[i]);
+  }
   BlockQ q;
   q.scale = s;
-  q.lo = q.hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float ax = fabsf(x[i]);
-    const uint32_t mag = d > 0.0f ? e2m1_index(ax / d) : 0u;
-    const uint32_t sgn = __float_as_uint(x[i]) >> 31;
-    const uint32_t code = (sgn << 3) | mag;
-    if (i < 8)
-      q.lo |= code << (4 * i);
-    else
-      q.hi |= code << (4 * (i - 8));
-    if (dq_out) {
-      const float m = e2m1_level(mag) * d;
-      dq_out[i] = sgn ? -m : m;
-    }
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0], v[1], 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2], v[3], 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4], v[5], 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6], v[7], 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8], v[9], 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10], v[11], 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12], v[13], 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14], v[15], 1.0f, 3);
+  q.lo = lo;
+  q.hi = hi;
+  if (dq_out) {
+#define QUADS_DQ_BYTE(word, byte, base)                                            \
+  {                                                                                \
+    const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, byte);     \
+    dq_out[(base)] = e[0] * d;                                                     \
+    dq_out[(base) + 1] = e[1] * d;                                                 \
+  }
+    QUADS_DQ_BYTE(lo, 0, 0)
+    QUADS_DQ_BYTE(lo, 1, 2)
+    QUADS_DQ_BYTE(lo, 2, 4)
+    QUADS_DQ_BYTE(lo, 3, 6)
+    QUADS_DQ_BYTE(hi, 0, 8)
+    QUADS_DQ_BYTE(hi, 1, 10)
+    QUADS_DQ_BYTE(hi, 2, 12)
+    QUADS_DQ_BYTE(hi, 3, 14)
+#undef QUADS_DQ_BYTE
   }
   return q;
 }

@@ -149,28 +149,39 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
 
   if (active) {
     const int64_t r_end = min(static_cast<int64_t>(rc + 1) * p.RW, p.rows);
-    for (int64_t r = static_cast<int64_t>(rc) * p.RW + rg; r < r_end; r += p.RG) {
-      const int64_t row = static_cast<int64_t>(b) * p.rows + r;
-      float v[16];
-      load16<BF16>(p.x, row * p.cols + gbc * 16, v);
-      float dq[16];
-      const BlockQ q = quantize_block16(v, g, (SCORES || QDQ) ? dq : nullptr);
-      if constexpr (CODES) {
-        reinterpret_cast<uint2 *>(p.codes)[row * p.cb + gbc] = make_uint2(q.lo, q.hi);
-        p.scales[row * p.cb + gbc] = static_cast<uint8_t>(q.scale);
-      }
-      if constexpr (QDQ) {
-        uint32_t w[8];
+    // Two row steps per iteration: both loads are in flight before either
+    // block is quantized.
+    for (int64_t r = static_cast<int64_t>(rc) * p.RW + rg; r < r_end; r += 2 * p.RG) {
+      const bool two = r + p.RG < r_end;
+      const int64_t row0 = static_cast<int64_t>(b) * p.rows + r;
+      const int64_t row1 = row0 + (two ? p.RG : 0);
+      float v0[16], v1[16];
+      load16<BF16>(p.x, row0 * p.cols + gbc * 16, v0);
+      load16<BF16>(p.x, row1 * p.cols + gbc * 16, v1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          w[i] = f32_to_bf16_bits(dq[2 * i]) | (f32_to_bf16_bits(dq[2 * i + 1]) << 16);
-        uint4 *o = reinterpret_cast<uint4 *>(p.qdq + row * p.cols + gbc * 16);
-        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      }
-      if constexpr (SCORES) {
+      for (int u = 0; u < 2; ++u) {
+        if (u == 1 && !two) break;
+        const int64_t row = u ? row1 : row0;
+        const float(&v)[16] = u ? v1 : v0;
+        float dq[16];
+        const BlockQ q = quantize_block16(v, g, (SCORES || QDQ) ? dq : nullptr);
+        if constexpr (CODES) {
+          reinterpret_cast<uint2 *>(p.codes)[row * p.cb + gbc] = make_uint2(q.lo, q.hi);
+          p.scales[row * p.cb + gbc] = static_cast<uint8_t>(q.scale);
+        }
+        if constexpr (QDQ) {
+          uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) smax[i] = fmaxf(smax[i], fabsf(v[i] - dq[i]));
+          for (int i = 0; i < 8; ++i)
+            w[i] = f32_to_bf16_bits(dq[2 * i]) | (f32_to_bf16_bits(dq[2 * i + 1]) << 16);
+          uint4 *o = reinterpret_cast<uint4 *>(p.qdq + row * p.cols + gbc * 16);
+          o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+        if constexpr (SCORES) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) smax[i] = fmaxf(smax[i], fabsf(v[i] - dq[i]));
+        }
       }
     }
   }
@@ -200,7 +211,7 @@ void launch_q(const QParams &qp, int grid, size_t lds, hipStream_t s) {
 }  // namespace
 
 int amax_partials_per_tensor(int64_t n_elem) {
-  int64_t p = (n_elem + 65535) / 65536;
+  int64_t p = (n_elem + 16383) / 16384;
   if (p < 1) p = 1;
   if (p > 1024) p = 1024;
   return static_cast<int>(p);
@@ -233,13 +244,17 @@ hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
   qp.rows = a.rows;
   qp.cols = a.cols;
   qp.cb = a.cols / 16;
-  qp.BC = static_cast<int>(qp.cb < 64 ? qp.cb : 64);
+  // With channel scores, narrow-and-tall tiles (4 blocks = 64 channels wide,
+  // 64 rows per step, 128-byte row segments) keep the per-workgroup column
+  // max to 64 atomics and the workgroup count near 1024.
+  const int64_t bc_max = a.scores != nullptr ? 4 : 64;
+  qp.BC = static_cast<int>(qp.cb < bc_max ? qp.cb : bc_max);
   qp.RG = kThreads / qp.BC;
   qp.col_chunks = static_cast<int>((qp.cb + qp.BC - 1) / qp.BC);
   const int64_t steps = a.batch * ((a.rows + qp.RG - 1) / qp.RG) * qp.col_chunks;
-  int64_t iters = steps / 2048;
+  int64_t iters = steps / 1024;
   if (iters < 1) iters = 1;
-  if (iters > 16) iters = 16;
+  if (iters > 64) iters = 64;
   qp.RW = static_cast<int>(qp.RG * iters);
   qp.row_chunks = static_cast<int>((a.rows + qp.RW - 1) / qp.RW);
   qp.P = P;

@@ -162,8 +162,9 @@ __global__ __launch_bounds__(kSelThreads) void k_rac_select(const uint32_t *scor
 }
 
 // Residual quantization.  One workgroup handles `rb` rows at a time: x, codes
-// and scales of those rows are staged in LDS, then each thread quantizes
-// 16-element residual blocks (row, j-block) from LDS.
+// and scales of those rows are staged in LDS with 16-byte loads, then each
+// thread quantizes 16-element residual blocks (row, j-block) from LDS.
+// row_bytes = x bytes + cols/2 + cols/16, rounded up to 16.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_rac_residual(const void *x, int64_t rows, int cols,
                                                       const uint8_t *x_codes,
@@ -172,8 +173,11 @@ __global__ __launch_bounds__(256) void k_rac_residual(const void *x, int64_t row
                                                       const float *r_g, uint8_t *r_codes,
                                                       uint8_t *r_scales, int rb, int rows_per_wg,
                                                       int row_bytes) {
-  extern __shared__ uint8_t lds[];
-  const int xbytes = cols * (BF16 ? 2 : 4);  // row_bytes: xbytes + cols/2 + cols/16, rounded to 16
+  extern __shared__ uint4 lds_u4[];
+  uint8_t *lds = reinterpret_cast<uint8_t *>(lds_u4);
+  const int xbytes = cols * (BF16 ? 2 : 4);  // multiple of 32
+  const int cbytes = cols / 2;                // multiple of 8
+  const int sbytes = cols / 16;
   int32_t *sel_l = reinterpret_cast<int32_t *>(lds);
   uint8_t *rows_l = lds + static_cast<size_t>(kpad) * 4;
   for (int j = threadIdx.x; j < kpad; j += 256) sel_l[j] = j < nsel ? sel[j] : -1;
@@ -184,17 +188,29 @@ __global__ __launch_bounds__(256) void k_rac_residual(const void *x, int64_t row
   for (int64_t r0 = r_begin; r0 < r_stop; r0 += rb) {
     const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
     __syncthreads();
-    // Stage rows: 4-byte words, coalesced.
-    for (int rr = 0; rr < nr; ++rr) {
-      uint8_t *dst = rows_l + static_cast<size_t>(rr) * row_bytes;
-      const uint32_t *sx =
-          reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(x) + (r0 + rr) * xbytes);
-      for (int i = threadIdx.x; i < xbytes / 4; i += 256) reinterpret_cast<uint32_t *>(dst)[i] = sx[i];
-      const uint32_t *sc = reinterpret_cast<const uint32_t *>(x_codes + (r0 + rr) * (cols / 2));
-      for (int i = threadIdx.x; i < cols / 8; i += 256)
-        reinterpret_cast<uint32_t *>(dst + xbytes)[i] = sc[i];
-      const uint8_t *ss = x_scales + (r0 + rr) * (cols / 16);
-      for (int i = threadIdx.x; i < cols / 16; i += 256) dst[xbytes + cols / 2 + i] = ss[i];
+    // x rows are contiguous in global memory: one flat 16-byte copy per row set.
+    {
+      const int xv = xbytes / 16;
+      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + r0 * xbytes);
+      for (int i = threadIdx.x; i < nr * xv; i += 256) {
+        const int rr = i / xv, c = i % xv;
+        reinterpret_cast<uint4 *>(rows_l + static_cast<size_t>(rr) * row_bytes)[c] = src[i];
+      }
+    }
+    {
+      const int cv = cbytes / 8;
+      const uint2 *src = reinterpret_cast<const uint2 *>(x_codes + r0 * cbytes);
+      for (int i = threadIdx.x; i < nr * cv; i += 256) {
+        const int rr = i / cv, c = i % cv;
+        reinterpret_cast<uint2 *>(rows_l + static_cast<size_t>(rr) * row_bytes + xbytes)[c] = src[i];
+      }
+    }
+    {
+      const uint8_t *src = x_scales + r0 * sbytes;
+      for (int i = threadIdx.x; i < nr * sbytes; i += 256) {
+        const int rr = i / sbytes, c = i % sbytes;
+        rows_l[static_cast<size_t>(rr) * row_bytes + xbytes + cbytes + c] = src[i];
+      }
     }
     __syncthreads();
     for (int t = threadIdx.x; t < nr * nblk; t += 256) {
@@ -212,7 +228,7 @@ __global__ __launch_bounds__(256) void k_rac_residual(const void *x, int64_t row
           else
             xv = reinterpret_cast<const float *>(rowp)[c];
           const uint32_t code = (rowp[xbytes + (c >> 1)] >> ((c & 1) * 4)) & 0xFu;
-          const float d = e4m3_to_f32(rowp[xbytes + cols / 2 + (c >> 4)]) * gx;
+          const float d = e4m3_to_f32(rowp[xbytes + cbytes + (c >> 4)]) * gx;
           dx = xv - dequant_code(code, d);
         }
         d16[i] = dx;
@@ -235,14 +251,13 @@ hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
   const int cols = static_cast<int>(a.cols);
   const int row_bytes = (cols * (a.x_bf16 ? 2 : 4) + cols / 2 + cols / 16 + 15) / 16 * 16;
   const int budget = 64 * 1024 - static_cast<int>(a.kpad) * 4;
-  int rb = static_cast<int>(256 / (a.kpad / 16));
-  if (rb < 1) rb = 1;
-  if (rb > budget / row_bytes) rb = budget / row_bytes;
+  int rb = budget / row_bytes;
+  if (rb > 16) rb = 16;
   if (rb < 1) rb = 1;
   int64_t n_wg = (a.rows + rb - 1) / rb;
   int rows_per_wg = rb;
-  if (n_wg > 2048) {
-    const int64_t iters = (n_wg + 2047) / 2048;
+  if (n_wg > 1024) {
+    const int64_t iters = (n_wg + 1023) / 1024;
     rows_per_wg = static_cast<int>(rb * iters);
     n_wg = (a.rows + rows_per_wg - 1) / rows_per_wg;
   }

@@ -163,8 +163,13 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
 #define QUADS_EPI_NONE 0
 #define QUADS_EPI_SWIGLU 1
 
+/* quads_moe_gemm_args.flags */
+#define QUADS_GEMM_PREPARED 1u /* workspace already filled by quads_moe_gemm_prepare for
+                                  these args: launch only the main GEMM kernel */
+
 typedef struct {
   uint32_t struct_size;  /* sizeof(quads_moe_gemm_args) (ABI versioning) */
+  uint32_t flags;        /* 0 or QUADS_GEMM_PREPARED */
   int32_t operand_mode;  /* QUADS_OPERANDS_W4A4 | QUADS_OPERANDS_BF16 */
   int32_t epilogue;      /* QUADS_EPI_NONE | QUADS_EPI_SWIGLU */
   int32_t y_dtype;       /* QUADS_F32 | QUADS_BF16 (EPI_NONE); SWIGLU writes BF16 */
@@ -200,6 +205,14 @@ typedef struct {
 
 size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a);
 quads_status_t quads_moe_w4a4_gemm(const quads_moe_gemm_args *a, void *stream);
+
+/* quads_moe_gemm_prepare -- the first half of quads_moe_w4a4_gemm, split out
+ * so callers can time or reuse it: builds the (expert, m-tile) list from
+ * expert_offsets and, with a RAC residual, gathers the selected weight columns
+ * sel_idx of every expert row into the workspace (bf16, exact e2m1 * e4m3
+ * values).  A following quads_moe_w4a4_gemm with flags |= QUADS_GEMM_PREPARED,
+ * the same arguments and the same workspace launches only the GEMM kernel. */
+quads_status_t quads_moe_gemm_prepare(const quads_moe_gemm_args *a, void *stream);
 
 /* ---------------------------------------------------------------------------
  * quads_weight_qdq -- trainer-side fake quantization [Gist 2.1, 2.2-A]: each
