@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/quads.h"
@@ -30,6 +32,13 @@ quads_status_t ok() {
 quads_status_t device_status(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(QUADS_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// Kernels read and write arrays with 8- and 16-byte vector accesses.
+bool misaligned(std::initializer_list<const void *> ptrs) {
+  for (const void *p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 16) return true;
+  return false;
 }
 
 bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a >= 0 && b >= 0 && (a == 0 || b <= lim / a); }
@@ -73,6 +82,7 @@ quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4
     return fail(QUADS_ERR_ARG, "quantize: QUADS_WANT_SCORES needs batch == 1 and a scores buffer");
   if (out.rows == 0) return ok();
   if (!x || !out.codes || !out.scales || !out.gscale) return fail(QUADS_ERR_ARG, "quantize: null pointer");
+  if (misaligned({x, out.codes, out.scales})) return fail(QUADS_ERR_ARG, "quantize: arrays must be 16-byte aligned");
   const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
   if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(out.batch, out.rows, out.cols)))
     return fail(QUADS_ERR_WORKSPACE, "quantize: workspace too small (need %zu)",
@@ -113,13 +123,14 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
   const int64_t nsel = quads_rac_nsel(xq->cols, k_percent), kpad = quads_rac_kpad(nsel);
   if (res.cols != kpad || res.rows != xq->rows || res.batch != 1)
     return fail(QUADS_ERR_SHAPE, "rac_select: res must be [rows=%lld, kpad=%lld]", (long long)xq->rows, (long long)kpad);
-  const int64_t row_bytes = ((xq->cols * (dt == QUADS_BF16 ? 2 : 4) + xq->cols / 2 + xq->cols / 16) + 15) / 16 * 16;
-  if (kpad * 4 + row_bytes > 64 * 1024)
-    return fail(QUADS_ERR_SHAPE, "rac_select: cols too large for the residual kernel's LDS staging");
+  if (quads::rac_rows_per_group(xq->cols, kpad) < 1)
+    return fail(QUADS_ERR_SHAPE, "rac_select: cols/kpad too large for the kernel's LDS staging (cols*4 + kpad*4 <= ~63 KiB)");
   if (!scores || !res.gscale || (kpad > 0 && !sel_idx))
     return fail(QUADS_ERR_ARG, "rac_select: null pointer");
   if (kpad > 0 && xq->rows > 0 && (!x || !xq->codes || !xq->scales || !xq->gscale || !res.codes || !res.scales))
     return fail(QUADS_ERR_ARG, "rac_select: null pointer");
+  if (misaligned({x, xq->codes, xq->scales, res.codes, res.scales, scores}))
+    return fail(QUADS_ERR_ARG, "rac_select: arrays must be 16-byte aligned");
   quads::RacLaunch a{};
   a.x = x;
   a.x_bf16 = dt == QUADS_BF16;
@@ -158,6 +169,9 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
   if (!mul_ok(a->num_rows, a->N, kMaxElems) || !mul_ok(int64_t(a->num_experts) * a->N, a->K, kMaxElems))
     return fail(QUADS_ERR_SHAPE, "gemm: size overflow");
   if (!a->expert_offsets || !a->y) return fail(QUADS_ERR_ARG, "gemm: null expert_offsets or y");
+  if (misaligned({a->y, a->ws, a->x_codes, a->x_scales, a->r_codes, a->r_scales, a->w_codes, a->w_scales, a->x_bf16,
+                  a->w_bf16}))
+    return fail(QUADS_ERR_ARG, "gemm: arrays must be 16-byte aligned");
   if (a->row_token == nullptr && a->act_rows < a->num_rows)
     return fail(QUADS_ERR_SHAPE, "gemm: identity rows need act_rows >= num_rows");
   g = quads::GemmLaunch{};
@@ -248,6 +262,8 @@ quads_status_t quads_weight_qdq(const void *w_bf16, int64_t batch, int64_t rows,
     return fail(QUADS_ERR_SHAPE, "weight_qdq: q_out shape mismatch");
   if (rows == 0) return ok();
   if (!w_bf16 || !w_out_bf16) return fail(QUADS_ERR_ARG, "weight_qdq: null pointer");
+  if (misaligned({w_bf16, w_out_bf16}) || (q_out && misaligned({q_out->codes, q_out->scales})))
+    return fail(QUADS_ERR_ARG, "weight_qdq: arrays must be 16-byte aligned");
   if (q_out && (!q_out->codes || !q_out->scales || !q_out->gscale)) return fail(QUADS_ERR_ARG, "weight_qdq: null q_out member");
   if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(batch, rows, cols)))
     return fail(QUADS_ERR_WORKSPACE, "weight_qdq: workspace too small (need %zu)", quads::quantize_ws_bytes(batch, rows, cols));

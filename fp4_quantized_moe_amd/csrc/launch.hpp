@@ -39,6 +39,8 @@ struct RacLaunch {
   uint8_t *r_codes, *r_scales;
   float *r_gscale;
 };
+// Rows of dx staged per pass by the RAC kernel (< 1: the shape does not fit in LDS).
+int rac_rows_per_group(int64_t cols, int64_t kpad);
 hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream);
 
 // ---- gemm.hip --------------------------------------------------------------

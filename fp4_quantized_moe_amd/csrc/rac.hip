@@ -1,5 +1,5 @@
 // Residual Activation Compensation (RAC) on gfx950: channel mask and
-// second-pass residual quantization.
+// second-pass residual quantization, in one kernel.
 //
 // QUADS technical summary, section 2.2-B: channels whose first-pass FP4
 // residual is largest get a binary mask (the top k% of channels, 50% being the
@@ -7,271 +7,369 @@
 // correction is added to the quantized path, so the native W4A4 GEMM still
 // does most of the work.
 //
-//   k_rac_select    one 1024-thread workgroup: radix select (4 passes of 8
-//                   bits over the FP32 score bit patterns, which order like
-//                   the non-negative floats they encode) finds the nsel-th
-//                   largest score T; channels above T plus the lowest-index
-//                   channels equal to T are kept; a block-wide prefix sum
-//                   writes them in ascending order.  Also writes the residual
-//                   tensor scale from the largest score.
-//   k_rac_residual  stages rows of x, their codes and scales in LDS, recomputes
-//                   dx = x - dq at the selected channels (same FP32 operations
-//                   as the quantizer) and NVFP4-quantizes the gathered
-//                   residual in 16-element blocks along the selected order.
+// k_rac, per workgroup:
+//   1. every workgroup finds the mask itself (redundant across workgroups, but
+//      in parallel and without a second launch): the nsel-th largest score T
+//      is built one bit at a time from the top, each step a workgroup count of
+//      the FP32 score bit patterns (which order like the non-negative floats
+//      they encode) at or above a candidate; channels above T plus the
+//      lowest-index channels equal to T are kept and written in ascending
+//      order with prefix sums over per-thread channel runs.  Workgroup 0 also
+//      publishes the mask and the residual tensor scale, taken from the
+//      largest score;
+//   2. for a group of rows, dx = x - dq is recomputed for every channel with
+//      16-element vector loads of x, codes and scales (the same FP32
+//      operations as the quantizer) into LDS;
+//   3. the selected channels are gathered from LDS in ascending order and
+//      NVFP4-quantized in 16-element blocks with the residual tensor scale.
 #include "launch.hpp"
 #include "quads_device.hpp"
 
 namespace quads {
 namespace {
 
-constexpr int kSelThreads = 1024;
-constexpr int kMaxSelCols = 16384;
+constexpr int kThreads = 256;
 
-// Exclusive prefix sum over the 1024 threads of the block; returns the
-// exclusive prefix of `v` and stores the block total in *total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wave_sums,
-                                                         uint32_t *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
+    const uint32_t t = __shfl_up(v, off);
+    if (lane >= off) v += t;
   }
-  __syncthreads();
-  if (lane == 63) wave_sums[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      const uint32_t s = wave_sums[w];
-      wave_sums[w] = run;
-      run += s;
-    }
-    wave_sums[kSelThreads / 64] = run;
-  }
-  __syncthreads();
-  *total = wave_sums[kSelThreads / 64];
-  return wave_sums[wave] + incl - v;
+  return v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_rac_select(const uint32_t *scores, int K, int nsel,
-                                                            int kpad, int32_t *sel, float *res_g) {
-  __shared__ uint32_t keys[kMaxSelCols];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_sums[kSelThreads / 64 + 1];
-  __shared__ uint32_t s_prefix, s_remaining, s_max;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_max = 0;
-  __syncthreads();
-  uint32_t mymax = 0;
-  for (int c = tid; c < K; c += kSelThreads) {
-    const uint32_t k = scores[c];
-    keys[c] = k;
-    mymax = max(mymax, k);
-  }
-  atomicMax(&s_max, mymax);  // LDS atomic
-  __syncthreads();
-  if (tid == 0) *res_g = tensor_scale_from_amax(nsel > 0 ? __uint_as_float(s_max) : 0.0f);
-  for (int j = nsel + tid; j < kpad; j += kSelThreads) sel[j] = 0;
-  if (nsel == 0) return;
+// Per-thread channel runs of the mask search: thread t owns channels
+// [t*PER, t*PER + PER), so the selected indices come out in ascending order
+// from prefix sums over threads.
+template <int PER>
+struct Keys {
+  uint32_t k[PER];
+};
 
-  // Radix select of the nsel-th largest key.
-  if (tid == 0) {
-    s_prefix = 0;
-    s_remaining = static_cast<uint32_t>(nsel);
+// Sum of `v` over the workgroup, and the exclusive prefix of `w` over threads,
+// with one barrier; `slot` holds 2 * kThreads / 64 words of LDS.
+__device__ __forceinline__ void block_sum_and_scan(uint32_t v, uint32_t w, uint32_t *slot, uint32_t &v_total,
+                                                   uint32_t &w_before) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int W = kThreads / 64;
+  const uint32_t w_incl = wave_incl_scan(w, lane);
+  uint32_t vs = v;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) vs += static_cast<uint32_t>(__shfl_xor(static_cast<int>(vs), off));
+  if (lane == 63) {
+    slot[wave] = vs;
+    slot[W + wave] = w_incl;
   }
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
-    for (int c = tid; c < K; c += kSelThreads) {
-      const uint32_t k = keys[c];
-      const bool match = shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0;
-      if (match) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // Suffix counts over bins, 4 bins per lane, highest bins first.
-      const int lane = tid;
-      uint32_t c4[4];
-      uint32_t sum = 0;
+  __syncthreads();
+  v_total = 0;
+  w_before = w_incl - w;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c4[q] = hist[255 - (lane * 4 + q)];
-        sum += c4[q];
-      }
-      uint32_t incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
-      uint32_t before = incl - sum;  // keys in bins above this lane's first bin
-      const uint32_t need = s_remaining;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (before < need && before + c4[q] >= need) {
-          const uint32_t bin = 255u - static_cast<uint32_t>(lane * 4 + q);
-          s_prefix = prefix | (bin << shift);
-          s_remaining = need - before;
-        }
-        before += c4[q];
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < W; ++i) {
+    v_total += slot[i];
+    if (i < wave) w_before += slot[W + i];
   }
-  const uint32_t T = s_prefix;
-  const uint32_t need_eq = s_remaining;  // how many keys equal to T are kept
+}
 
-  // Each thread owns a contiguous run of channels (keeps ascending order).
-  const int per = (K + kSelThreads - 1) / kSelThreads;
-  const int c0 = tid * per, c1 = min(c0 + per, K);
-  uint32_t n_eq = 0;
-  for (int c = c0; c < c1; ++c) n_eq += keys[c] == T;
-  uint32_t tot;
-  uint32_t eq_before = block_exclusive_scan(n_eq, wave_sums, &tot);
+// Number of keys >= cand over the workgroup (one barrier; `slot` alternates
+// between two buffers of kThreads / 64 words so consecutive calls need no
+// second barrier).
+template <int PER>
+__device__ __forceinline__ uint32_t block_count_ge(const Keys<PER> &ks, uint32_t cand, uint32_t *slot) {
+  const int wave = threadIdx.x >> 6;
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) n += ks.k[i] >= cand;
+  // Wave sum of n in [0, PER] from one ballot per bit of n (scalar popcounts,
+  // no cross-lane data movement).
+  constexpr int kBits = PER < 8 ? 3 : PER < 16 ? 4 : PER < 32 ? 5 : PER < 64 ? 6 : 7;
+  uint32_t wsum = 0;
+#pragma unroll
+  for (int b = 0; b < kBits; ++b) wsum += static_cast<uint32_t>(__popcll(__ballot((n >> b) & 1u))) << b;
+  if ((threadIdx.x & 63) == 0) slot[wave] = wsum;
+  __syncthreads();
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) total += slot[i];
+  return total;
+}
+
+// Writes the nsel selected channel indices (largest scores first by value,
+// ties to the lower index) in ascending order to sel[0..nsel).  Keys are the
+// FP32 score bit patterns: non-negative, so below 2^31 and ordered like the
+// scores.  The nsel-th largest key T is built bit by bit from the top: a bit
+// stays set when at least nsel keys are >= the candidate.
+template <int PER>
+__device__ void block_select(const Keys<PER> &ks, int nsel, uint32_t *slots, int32_t *sel) {
+  const int c0 = threadIdx.x * PER;
+  uint32_t T = 0;
+  int buf = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (block_count_ge(ks, cand, slots + buf * (kThreads / 64)) >= static_cast<uint32_t>(nsel)) T = cand;
+    buf ^= 1;
+  }
+  // Keys beyond K (padding) are 0 and come after every real channel: they are
+  // never above T, and when T == 0 they only follow the real zeros among the
+  // ties, of which there are at least need_eq, so no padding channel is kept.
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    n_gt += ks.k[i] > T;
+    n_eq += ks.k[i] == T;
+  }
+  uint32_t gt_total, eq_before;
+  block_sum_and_scan(n_gt, n_eq, slots + 2 * (kThreads / 64), gt_total, eq_before);
+  const uint32_t need_eq = static_cast<uint32_t>(nsel) - gt_total;
+  // Branch-free keep flags: a channel is kept if its key is above T, or equal
+  // to T and among the first need_eq such channels.
   uint32_t n_keep = 0;
   {
     uint32_t e = eq_before;
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t k = keys[c];
-      if (k > T) {
-        ++n_keep;
-      } else if (k == T) {
-        n_keep += e < need_eq;
-        ++e;
-      }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool eq = ks.k[i] == T;
+      n_keep += ks.k[i] > T || (eq && e < need_eq);
+      e += eq;
     }
   }
-  uint32_t pos = block_exclusive_scan(n_keep, wave_sums, &tot);
+  uint32_t unused, pos;
+  block_sum_and_scan(0, n_keep, slots + 4 * (kThreads / 64), unused, pos);
   {
+    __shared__ int32_t trash;
     uint32_t e = eq_before;
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t k = keys[c];
-      bool keep = false;
-      if (k > T) {
-        keep = true;
-      } else if (k == T) {
-        keep = e < need_eq;
-        ++e;
-      }
-      if (keep) sel[pos++] = c;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool eq = ks.k[i] == T;
+      const bool kk = ks.k[i] > T || (eq && e < need_eq);
+      e += eq;
+      int32_t *dst = kk ? sel + pos : &trash;
+      *dst = c0 + i;
+      pos += kk;
     }
   }
 }
 
-// Residual quantization.  One workgroup handles `rb` rows at a time: x, codes
-// and scales of those rows are staged in LDS with 16-byte loads, then each
-// thread quantizes 16-element residual blocks (row, j-block) from LDS.
-// row_bytes = x bytes + cols/2 + cols/16, rounded up to 16.
+// One 16-element block of x with its FP4 codes and E4M3 scale, as loaded.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_rac_residual(const void *x, int64_t rows, int cols,
-                                                      const uint8_t *x_codes,
-                                                      const uint8_t *x_scales, const float *x_g,
-                                                      const int32_t *sel, int nsel, int kpad,
-                                                      const float *r_g, uint8_t *r_codes,
-                                                      uint8_t *r_scales, int rb, int rows_per_wg,
-                                                      int row_bytes) {
+struct RawBlock {
+  uint4 x[BF16 ? 2 : 4];
+  uint2 codes;
+  uint32_t scale;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_raw(RawBlock<BF16> &r, const void *x, const uint8_t *codes,
+                                         const uint8_t *scales, int64_t blk_global) {
+  constexpr int n = BF16 ? 2 : 4;
+  const uint4 *p = reinterpret_cast<const uint4 *>(x) + blk_global * n;
+#pragma unroll
+  for (int i = 0; i < n; ++i) r.x[i] = p[i];
+  r.codes = reinterpret_cast<const uint2 *>(codes)[blk_global];
+  r.scale = scales[blk_global];
+}
+
+// dx = x - dq for one block (the quantizer's FP32 operations: dq = level * d
+// with d = dec(scale) * g), stored to LDS.
+template <bool BF16>
+__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *dst) {
+  float v[16];
+  if constexpr (BF16) {
+    const uint32_t w[8] = {r.x[0].x, r.x[0].y, r.x[0].z, r.x[0].w, r.x[1].x, r.x[1].y, r.x[1].z, r.x[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = __uint_as_float(r.x[i].x);
+      v[4 * i + 1] = __uint_as_float(r.x[i].y);
+      v[4 * i + 2] = __uint_as_float(r.x[i].z);
+      v[4 * i + 3] = __uint_as_float(r.x[i].w);
+    }
+  }
+  const float d = e4m3_to_f32(r.scale) * gx;
+  float dx[16];
+#define QUADS_DX(word, byte, i0)                                               \
+  {                                                                            \
+    const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, byte); \
+    dx[i0] = v[i0] - e[0] * d;                                                 \
+    dx[i0 + 1] = v[i0 + 1] - e[1] * d;                                         \
+  }
+  QUADS_DX(r.codes.x, 0, 0)
+  QUADS_DX(r.codes.x, 1, 2)
+  QUADS_DX(r.codes.x, 2, 4)
+  QUADS_DX(r.codes.x, 3, 6)
+  QUADS_DX(r.codes.y, 0, 8)
+  QUADS_DX(r.codes.y, 1, 10)
+  QUADS_DX(r.codes.y, 2, 12)
+  QUADS_DX(r.codes.y, 3, 14)
+#undef QUADS_DX
+  float4 *o = reinterpret_cast<float4 *>(dst);
+  o[0] = make_float4(dx[0], dx[1], dx[2], dx[3]);
+  o[1] = make_float4(dx[4], dx[5], dx[6], dx[7]);
+  o[2] = make_float4(dx[8], dx[9], dx[10], dx[11]);
+  o[3] = make_float4(dx[12], dx[13], dx[14], dx[15]);
+}
+
+// Blocks of one row group held in registers per thread: block tid + j*kThreads.
+constexpr int kGroupSlots = 4;
+
+// LDS: sel[kpad] int32 | dx rows [rb][K] fp32.  A row group has at most
+// kGroupSlots * kThreads blocks.
+//
+// Schedule per workgroup: the loads of the first row group are issued before
+// the mask search so that their latency overlaps it; afterwards, while group
+// g is gathered and quantized, the loads of group g+1 are in flight.
+template <bool BF16, int PER>
+__global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, int K, const uint8_t *x_codes,
+                                                  const uint8_t *x_scales, const float *x_g,
+                                                  const uint32_t *scores, int nsel, int kpad, int32_t *sel_out,
+                                                  float *r_g_out, uint8_t *r_codes, uint8_t *r_scales, int rb,
+                                                  int rows_per_wg) {
   extern __shared__ uint4 lds_u4[];
-  uint8_t *lds = reinterpret_cast<uint8_t *>(lds_u4);
-  const int xbytes = cols * (BF16 ? 2 : 4);  // multiple of 32
-  const int cbytes = cols / 2;                // multiple of 8
-  const int sbytes = cols / 16;
-  int32_t *sel_l = reinterpret_cast<int32_t *>(lds);
-  uint8_t *rows_l = lds + static_cast<size_t>(kpad) * 4;
-  for (int j = threadIdx.x; j < kpad; j += 256) sel_l[j] = j < nsel ? sel[j] : -1;
-  const float gx = *x_g, gr = *r_g;
-  const int nblk = kpad / 16;
+  int32_t *sel = reinterpret_cast<int32_t *>(lds_u4);
+  float *region = reinterpret_cast<float *>(lds_u4) + kpad;
+  __shared__ uint32_t slots[6 * (kThreads / 64)];
+  const int tid = threadIdx.x;
+  const int cb = K / 16, nblk = kpad / 16;
   const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
   const int64_t r_stop = min(r_begin + rows_per_wg, rows);
+
+  // Loads of a row group starting at row r0 (nb blocks; clamped addresses,
+  // slots past nb are skipped with a uniform test).
+  RawBlock<BF16> raw[kGroupSlots];
+  auto issue = [&](int64_t r0) {
+    const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
+    const int nb = nr * cb;
+#pragma unroll
+    for (int j = 0; j < kGroupSlots; ++j)
+      if (j * kThreads < nb) load_raw<BF16>(raw[j], x, x_codes, x_scales, r0 * cb + min(tid + j * kThreads, nb - 1));
+  };
+  const bool has_rows = kpad > 0 && r_begin < r_stop;
+  if (has_rows) issue(r_begin);
+
+  // 1. Mask.
+  Keys<PER> ks;
+  const int c0 = tid * PER;
+  const int n_real = min(max(K - c0, 0), PER);  // multiple of 4 (K % 16 == 0)
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    // Clamped unconditional load; channels beyond K become key 0 via an
+    // arithmetic mask (all ones while i < n_real).
+    const uint4 v = *reinterpret_cast<const uint4 *>(scores + min(c0 + i, K - 4));
+    const uint32_t m = static_cast<uint32_t>((i - n_real) >> 31);
+    ks.k[i] = v.x & m;
+    ks.k[i + 1] = v.y & m;
+    ks.k[i + 2] = v.z & m;
+    ks.k[i + 3] = v.w & m;
+  }
+  for (int j = nsel + tid; j < kpad; j += kThreads) sel[j] = -1;
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mx = max(mx, ks.k[i]);
+  if (nsel > 0) block_select(ks, nsel, slots, sel);
+  // The largest score is always selected (nsel >= 1): it sets the residual
+  // tensor scale.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
+  __syncthreads();
+  if ((tid & 63) == 0) slots[tid >> 6] = mx;
+  __syncthreads();
+  uint32_t mx_total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) mx_total = max(mx_total, slots[i]);
+  const float gr = tensor_scale_from_amax(nsel > 0 ? __uint_as_float(mx_total) : 0.0f);
+  if (blockIdx.x == 0) {
+    for (int j = tid; j < kpad; j += kThreads) sel_out[j] = max(sel[j], 0);
+    if (tid == 0) *r_g_out = gr;
+  }
+  if (!has_rows) return;
+
+  // 2-3. Residual rows.
+  const float gx = *x_g;
   for (int64_t r0 = r_begin; r0 < r_stop; r0 += rb) {
     const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
+    const int nb = nr * cb;
+#pragma unroll
+    for (int j = 0; j < kGroupSlots; ++j) {
+      const int b = tid + j * kThreads;
+      if (j * kThreads < nb && b < nb) store_dx<BF16>(raw[j], gx, region + b * 16);
+    }
+    if (r0 + rb < r_stop) issue(r0 + rb);
     __syncthreads();
-    // x rows are contiguous in global memory: one flat 16-byte copy per row set.
-    {
-      const int xv = xbytes / 16;
-      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + r0 * xbytes);
-      for (int i = threadIdx.x; i < nr * xv; i += 256) {
-        const int rr = i / xv, c = i % xv;
-        reinterpret_cast<uint4 *>(rows_l + static_cast<size_t>(rr) * row_bytes)[c] = src[i];
-      }
-    }
-    {
-      const int cv = cbytes / 8;
-      const uint2 *src = reinterpret_cast<const uint2 *>(x_codes + r0 * cbytes);
-      for (int i = threadIdx.x; i < nr * cv; i += 256) {
-        const int rr = i / cv, c = i % cv;
-        reinterpret_cast<uint2 *>(rows_l + static_cast<size_t>(rr) * row_bytes + xbytes)[c] = src[i];
-      }
-    }
-    {
-      const uint8_t *src = x_scales + r0 * sbytes;
-      for (int i = threadIdx.x; i < nr * sbytes; i += 256) {
-        const int rr = i / sbytes, c = i % sbytes;
-        rows_l[static_cast<size_t>(rr) * row_bytes + xbytes + cbytes + c] = src[i];
-      }
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < nr * nblk; t += 256) {
-      const int rr = t / nblk, jb = t % nblk;
-      const uint8_t *rowp = rows_l + static_cast<size_t>(rr) * row_bytes;
-      float d16[16];
+    for (int t = tid; t < nr * nblk; t += kThreads) {
+      const int rr = t / nblk, jb = t - rr * nblk;
+      const float *src = region + rr * K;
+      float g16[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int c = sel_l[jb * 16 + i];
-        float dx = 0.0f;
-        if (c >= 0) {
-          float xv;
-          if constexpr (BF16)
-            xv = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(rowp)[c]);
-          else
-            xv = reinterpret_cast<const float *>(rowp)[c];
-          const uint32_t code = (rowp[xbytes + (c >> 1)] >> ((c & 1) * 4)) & 0xFu;
-          const float d = e4m3_to_f32(rowp[xbytes + cbytes + (c >> 4)]) * gx;
-          dx = xv - dequant_code(code, d);
-        }
-        d16[i] = dx;
+        const int c = sel[jb * 16 + i];
+        g16[i] = c >= 0 ? src[c] : 0.0f;
       }
-      const BlockQ q = quantize_block16(d16, gr, nullptr);
+      const BlockQ q = quantize_block16(g16, gr, nullptr);
       const int64_t row = r0 + rr;
       reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
       r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);
     }
+    __syncthreads();  // dx region is rewritten by the next group
   }
 }
 
 }  // namespace
 
+int rac_rows_per_group(int64_t cols, int64_t kpad) {
+  const int64_t budget = 64 * 1024 - kpad * 4 - 64;
+  int64_t rb = budget / (cols * 4);
+  if (rb > 4) rb = 4;  // ~40 KiB per workgroup at cols 2048: four workgroups per CU
+  const int64_t by_slots = static_cast<int64_t>(kGroupSlots) * kThreads / (cols / 16);
+  if (rb > by_slots) rb = by_slots;  // a row group's blocks fit the per-thread load slots
+  return static_cast<int>(rb);
+}
+
+namespace {
+template <bool BF16, int PER>
+void launch_rac_t(const RacLaunch &a, int64_t n_wg, int rb, int rows_per_wg, size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((k_rac<BF16, PER>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
+                     static_cast<int>(a.cols), a.x_codes, a.x_scales, a.x_gscale,
+                     reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.nsel),
+                     static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg);
+}
+
+template <bool BF16>
+void launch_rac_per(const RacLaunch &a, int64_t n_wg, int rb, int rows_per_wg, size_t lds, hipStream_t stream) {
+  const int64_t per = (a.cols + kThreads - 1) / kThreads;
+  if (per <= 4)
+    launch_rac_t<BF16, 4>(a, n_wg, rb, rows_per_wg, lds, stream);
+  else if (per <= 8)
+    launch_rac_t<BF16, 8>(a, n_wg, rb, rows_per_wg, lds, stream);
+  else if (per <= 16)
+    launch_rac_t<BF16, 16>(a, n_wg, rb, rows_per_wg, lds, stream);
+  else if (per <= 32)
+    launch_rac_t<BF16, 32>(a, n_wg, rb, rows_per_wg, lds, stream);
+  else
+    launch_rac_t<BF16, 64>(a, n_wg, rb, rows_per_wg, lds, stream);
+}
+}  // namespace
+
 hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(kSelThreads), 0, stream,
-                     reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.cols),
-                     static_cast<int>(a.nsel), static_cast<int>(a.kpad), a.sel_idx, a.r_gscale);
-  if (a.kpad == 0 || a.rows == 0) return hipGetLastError();
-  const int cols = static_cast<int>(a.cols);
-  const int row_bytes = (cols * (a.x_bf16 ? 2 : 4) + cols / 2 + cols / 16 + 15) / 16 * 16;
-  const int budget = 64 * 1024 - static_cast<int>(a.kpad) * 4;
-  int rb = budget / row_bytes;
-  if (rb > 16) rb = 16;
-  if (rb < 1) rb = 1;
-  int64_t n_wg = (a.rows + rb - 1) / rb;
+  if (a.cols > 64 * kThreads) return hipErrorInvalidValue;  // the API bounds cols first
+  int rb = rac_rows_per_group(a.cols, a.kpad);
+  if (rb < 1) return hipErrorInvalidValue;
+  int64_t n_wg = a.kpad == 0 || a.rows == 0 ? 1 : (a.rows + rb - 1) / rb;
   int rows_per_wg = rb;
   if (n_wg > 1024) {
     const int64_t iters = (n_wg + 1023) / 1024;
     rows_per_wg = static_cast<int>(rb * iters);
     n_wg = (a.rows + rows_per_wg - 1) / rows_per_wg;
   }
-  const size_t lds = static_cast<size_t>(a.kpad) * 4 + static_cast<size_t>(rb) * row_bytes;
+  const size_t lds = static_cast<size_t>(a.kpad) * 4 + static_cast<size_t>(rb) * a.cols * 4;
   if (a.x_bf16)
-    hipLaunchKernelGGL(k_rac_residual<true>, dim3(n_wg), dim3(256), lds, stream, a.x, a.rows, cols,
-                       a.x_codes, a.x_scales, a.x_gscale, a.sel_idx, static_cast<int>(a.nsel),
-                       static_cast<int>(a.kpad), a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg,
-                       row_bytes);
+    launch_rac_per<true>(a, n_wg, rb, rows_per_wg, lds, stream);
   else
-    hipLaunchKernelGGL(k_rac_residual<false>, dim3(n_wg), dim3(256), lds, stream, a.x, a.rows, cols,
-                       a.x_codes, a.x_scales, a.x_gscale, a.sel_idx, static_cast<int>(a.nsel),
-                       static_cast<int>(a.kpad), a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg,
-                       row_bytes);
+    launch_rac_per<false>(a, n_wg, rb, rows_per_wg, lds, stream);
   return hipGetLastError();
 }
 

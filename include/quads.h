@@ -39,6 +39,8 @@
  *   - Return value: QUADS_OK or a negative quads_status_t; on error nothing is
  *     enqueued and quads_last_error() (thread-local) describes the problem.
  *     Nothing throws or aborts across the ABI.
+ *   - Array pointers must be 16-byte aligned (QUADS_ERR_ARG otherwise); fresh
+ *     torch allocations are.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified (but memory-safe)
  *     results.
  */

@@ -44,7 +44,7 @@ def test_version_and_sizes(L):
     assert L.quads_moe_route_workspace_bytes(16384, 64) >= 64 * 64 * 4
 
 
-def _nv(rows, cols, batch=1, ptr=1):
+def _nv(rows, cols, batch=1, ptr=16):
     return _lib._NVFP4(ptr, ptr, ptr, batch, rows, cols)
 
 
@@ -60,6 +60,10 @@ def test_quantize_validation(L):
     assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16), 1 << 7, None, dummy, 1 << 20, None) == -1
     # zero rows: valid no-op
     assert L.quads_quantize_nvfp4(dummy, 0, _nv(0, 16), 0, None, dummy, 1 << 20, None) == 0
+    # misaligned arrays are rejected before anything is enqueued
+    st = L.quads_quantize_nvfp4(ctypes.c_void_p(24), 0, _nv(4, 16), 0, None, dummy, 1 << 20, None)
+    assert st == -1 and b"aligned" in L.quads_last_error()
+    assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16, ptr=8), 0, None, dummy, 1 << 20, None) == -1
 
 
 def test_rac_select_validation(L):
@@ -70,6 +74,11 @@ def test_rac_select_validation(L):
     big = _nv(8, 32768)
     assert L.quads_rac_select(dummy, 0, ctypes.byref(big), dummy, 50, dummy, _nv(8, 16384), None, 0, None) == -2
     assert L.quads_rac_select(dummy, 0, None, dummy, 50, dummy, _nv(8, 128), None, 0, None) == -1
+    st = L.quads_rac_select(ctypes.c_void_p(40), 0, ctypes.byref(xq), dummy, 50, dummy, _nv(8, 128), None, 0, None)
+    assert st == -1 and b"aligned" in L.quads_last_error()
+    # the LDS budget: cols * 4 + kpad * 4 must stay under ~63 KiB
+    wide = _nv(8, 16384)
+    assert L.quads_rac_select(dummy, 0, ctypes.byref(wide), dummy, 0, dummy, _nv(8, 0), None, 0, None) == -2
 
 
 def _gemm_args(**kw):
