@@ -38,8 +38,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE W4A4+RAC expert-GEMM tokens/s & TFLOPS; % of MFMA peak; RAC overhead %"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+CPU_BASELINE_MIN_S = 10.0  # repeat the oracle sample until at least this much CPU time
 
 
 def parse():
@@ -97,17 +98,25 @@ def setup_expert_gemm(Q, S, k):
     cfg = {"workload": "expert_gemm", "tokens": M, "K": K, "N": N, "k_percent": k, "nsel": nsel,
            "x": "bf16 N(0,1), 1% outlier channels x30", "w": "bf16 N(0,0.02) -> NVFP4 (offline)"}
 
-    def cpu_baseline(rows):
+    def cpu_baseline():
+        """The oracle's quantize + RAC + fp64 GEMM over all M tokens (the same
+        step), repeated until CPU_BASELINE_MIN_S have passed."""
         from oracle import quads_oracle as O
         qw = O.quantize_nvfp4(wl.w.f32)
         we = O.dequant_exact(qw.codes, qw.scales, qw.g)[None]
-        xs = wl.x.f32[:rows]
-        t0 = time.perf_counter()
-        O.rac_linear(xs, we, k)
-        return time.perf_counter() - t0, f"first {rows} of {M} tokens (full K, N), oracle quantize+RAC+fp64 GEMM"
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            O.rac_linear(wl.x.f32, we, k)
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= CPU_BASELINE_MIN_S:
+                break
+        return M * reps / secs, secs, (f"the whole step ({M} tokens, K={K}, N={N}, k={k}%) x {reps} repetitions: "
+                                       "oracle quantize + RAC + fp64 GEMM (weights quantized beforehand)")
 
     return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
-                dominant_kernel="k_gemm<0,0,true>", config=cfg, cpu_baseline=cpu_baseline, cpu_rows=M)
+                dominant_kernel="k_gemm<...,0,0,true> (W4A4 + RAC segment)", config=cfg, cpu_baseline=cpu_baseline,
+                traffic_summary=os.path.join(ROOT, "profiles", f"k_gemm_expert_gemm_k{k}_traffic.txt"))
 
 
 def setup_moe(Q, S, k, decode):
@@ -168,29 +177,83 @@ def setup_moe(Q, S, k, decode):
 # timing
 # ---------------------------------------------------------------------------
 
-def run_steps(stages, steps, warmup):
-    """Run warmup steps, then `steps` timed steps with HIP events between
-    stages (recorded on torch's current stream, which every library call
-    uses).  Returns (seconds, {stage: mean ms})."""
+def capture(fns, reps=1):
+    """One HIP graph holding `reps` passes over fns (every library call enqueues
+    on torch's current stream, which is the capture stream here)."""
     import torch
-    for _ in range(warmup):
-        for _, fn in stages:
-            fn()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            for fn in fns:
+                fn()
+    return g
+
+
+def run_steps(stages, steps, warmup, dominant=None):
+    """One step = a HIP graph of the stages before `dominant`, the dominant
+    stage launched directly between two HIP events, then a graph of the stages
+    after it.  The host enqueues the dominant launch while the first graph is
+    still running, so the events bracket the kernel itself (no launch gap);
+    they are recorded on the stream every call uses.  `warmup` untimed steps,
+    then `steps` timed steps bracketed by device synchronisation.
+    Returns (wall seconds, event ms over all steps, dominant-stage ms per step)."""
+    import torch
+    for _, fn in stages:  # eager pass: lazy allocations happen outside the capture
+        fn()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    names = [n for n, _ in stages]
+    i = names.index(dominant) if dominant in names else len(names)
+    pre, dom, post = stages[:i], stages[i:i + 1], stages[i + 1:]
+    g_pre = capture([fn for _, fn in pre]) if pre else None
+    g_post = capture([fn for _, fn in post]) if post else None
+
+    def step(ev=None):
+        if g_pre:
+            g_pre.replay()
+        if ev:
+            ev[0].record()
+        for _, fn in dom:
+            fn()
+        if ev:
+            ev[1].record()
+        if g_post:
+            g_post.replay()
+
+    for _ in range(warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for s in range(steps):
-        ev[s][0].record()
-        for i, (_, fn) in enumerate(stages):
-            fn()
-            ev[s][i + 1].record()
+        step(evs[s])
+    e1.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    per = {}
-    for i, (name, _) in enumerate(stages):
-        per[name] = float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
-    return t1 - t0, per
+    secs = time.perf_counter() - t0
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) if dom else None
+    return secs, e0.elapsed_time(e1), dom_ms
+
+
+def stage_times(stages, reps=20, iters=3):
+    """Mean device time of each stage per call: a graph of `reps` back-to-back
+    calls of that stage alone, replayed `iters` times between HIP events on the
+    stream the graph runs on.  Stages are pure functions of buffers set up
+    beforehand, so repeating one in isolation recomputes the same outputs."""
+    import torch
+    out = {}
+    for name, fn in stages:
+        g = capture([fn], reps)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / (reps * iters)
+    return out
 
 
 def blas_threads():
@@ -222,11 +285,15 @@ def main():
         raise SystemExit("trainer_qdq: not wired into bench.py yet")
     torch.cuda.synchronize()
 
-    secs, per = run_steps(wl["stages"], args.steps, args.warmup)
+    secs, ev_ms, dom_ms = run_steps(wl["stages"], args.steps, args.warmup, wl["dominant"])
+    per = stage_times(wl["stages"])
     ms = secs * 1e3 / args.steps
     tokens_per_s = wl["tokens"] * args.steps / secs
-    dom_ms = per[wl["dominant"]]
     dom_tflops = wl["dominant_flops"] / (dom_ms * 1e-3) / 1e12
+    from fp4_quantized_moe_amd.profiling import read_traffic
+    traffic, tinfo = (None, "no traffic summary for this workload")
+    if wl.get("traffic_summary"):
+        traffic, tinfo = read_traffic(wl["traffic_summary"])
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -235,30 +302,38 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_events": ev_ms / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": wl["config"],
         "tflops_step": wl["flops"] / (ms * 1e-3) / 1e12,
         "gemm_tflops": dom_tflops,
-        "pct_mfma_peak_bf16": 100.0 * dom_tflops / PEAK_BF16_TFLOPS,
+        "pct_mfma_peak_f16": 100.0 * dom_tflops / PEAK_F16_TFLOPS,
         "stages_ms": per,
+        "timing": "step = HIP graph of the stages before the dominant one, the dominant kernel launched "
+                  "between two HIP events (roofline.avg_launch_ms, every timed step), graph of the rest; "
+                  "stages_ms from graphs of 20 back-to-back calls of one stage",
         "roofline": {"bound": "mfma", "kernel": wl["dominant_kernel"], "achieved": dom_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None, "flops_per_launch": wl["dominant_flops"], "avg_launch_ms": dom_ms},
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_F16_TFLOPS,
+                     "traffic": traffic, "flops_per_launch": wl["dominant_flops"], "avg_launch_ms": dom_ms,
+                     "traffic_note": tinfo if traffic is None else
+                     f"HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain copy), "
+                     f"{os.path.relpath(wl['traffic_summary'], ROOT)}"},
     }
     if not args.no_plain and wl.get("plain"):
-        psecs, pper = run_steps(wl["plain"], args.steps, args.warmup)
+        psecs, _, _ = run_steps(wl["plain"], args.steps, args.warmup)
         out["plain_w4a4_ms_per_step"] = psecs * 1e3 / args.steps
-        out["plain_stages_ms"] = pper
+        out["plain_stages_ms"] = stage_times(wl["plain"])
         out["rac_overhead_pct"] = 100.0 * (secs / psecs - 1.0)
     if not args.no_cpu_baseline and wl.get("cpu_baseline") is not None:
-        cpu_s, sample = wl["cpu_baseline"](wl["cpu_rows"])
-        out["cpu_baseline"] = {"value": wl["cpu_rows"] / cpu_s, "unit": "tokens/s", "cores": blas_threads(),
+        rate, cpu_s, sample = wl["cpu_baseline"]()
+        out["cpu_baseline"] = {"value": rate, "unit": "tokens/s", "cores": blas_threads(),
                                "kind": "oracle", "sample": sample, "seconds": cpu_s,
-                               "host_cpus": os.cpu_count()}
+                               "host_cpus": os.cpu_count(),
+                               "cores_note": "fp64 GEMM on the BLAS threads; quantize and RAC single-threaded NumPy"}
     print(json.dumps(out), flush=True)
 
 

@@ -24,8 +24,8 @@
 //
 // Tiling: templated BM x BN workgroup tiles of WGM x WGN waves, K step 64,
 // v_mfma_f32_32x32x16_{f16,bf16}.  LDS holds two [rows][64] tiles per operand
-// whose 16-byte chunks are XOR-swizzled by (row & 7) so that both the decode
-// writes and the MFMA operand reads are conflict-free.  Global data is
+// whose 16-byte chunks are XOR-swizzled by ((row >> 1) & 7) so that both the
+// decode writes and the MFMA operand reads are conflict-free.  Global data is
 // fetched two K steps ahead into alternating register stages; the loop body
 // (fetch step k+2, MFMAs on step k, decode+store step k+1, barrier) has no
 // branches, so the next step's decode can be interleaved with this step's
