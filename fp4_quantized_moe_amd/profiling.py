@@ -37,11 +37,20 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank space, so that editing a comment
+    does not mark a profile as stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_sha256(kernel_family: str) -> str:
+    """Hash of the code (comments and spacing removed) of a kernel's sources."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel_family]:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        with open(os.path.join(PKG, rel)) as f:
+            h.update(rel.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 
