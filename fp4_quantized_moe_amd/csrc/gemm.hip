@@ -44,6 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "fp4_mfma.hpp"
 #include "launch.hpp"
 #include "quads_device.hpp"
 
@@ -51,11 +52,6 @@ namespace quads {
 namespace {
 
 constexpr int BK = 64;  // K step: 4 NVFP4 blocks = 8 chunks of 8 16-bit values per row
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Workgroup tile BM x BN, WGM x WGN waves, each wave owning a (BM/WGM) x
 // (BN/WGN) sub-tile of 32x32 MFMA tiles.
@@ -72,21 +68,6 @@ struct Cfg {
   static_assert(FA * THREADS == BM * 4 && FB * THREADS == BN * 4, "fp4 staging must divide");
   static_assert(HA * THREADS == BM * 8 && HB * THREADS == BN * 8, "raw staging must divide");
 };
-
-// (dec(s), dec(s)) as fp16 for an E4M3 scale byte s: exact conversion.
-__device__ __forceinline__ h2 scale_h2(uint32_t s) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s | (s << 8), 1.0f, false);
-}
-
-// 8 E2M1 codes (element i in nibble i) times the block scale -> 8 fp16.
-__device__ __forceinline__ uint4 decode8_f16(uint32_t w, h2 sc) {
-  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
-  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
-  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
-  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
-  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
-}
 
 // LDS tiles are [rows][8 chunks of 16 bytes]; chunk c of row r lives at
 // c ^ ((r >> 1) & 7).  gfx950's LDS has 64 four-byte banks, so one bank row
@@ -803,7 +784,8 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
 size_t gemm_ws_bytes(const GemmLaunch &a) {
   size_t b = align256(static_cast<size_t>(a.E + 1) * sizeof(int32_t));
   if (a.mode == 0 && a.r_codes != nullptr && a.kpad > 0)
-    b += align256(static_cast<size_t>(a.E) * a.N * a.kpad * sizeof(uint16_t));
+    b += gemm_use_small(a) ? align256(gemm_small_res_bytes(a))
+                           : align256(static_cast<size_t>(a.E) * a.N * a.kpad * sizeof(uint16_t));
   return b;
 }
 
@@ -811,6 +793,10 @@ hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
   uint8_t *ws = static_cast<uint8_t *>(a.ws);
   int32_t *tile_offsets = reinterpret_cast<int32_t *>(ws);
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
+  if (gemm_use_small(a)) {
+    uint16_t *rd = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
+    return res ? launch_gemm_small_prepare(a, rd, stream) : hipSuccess;
+  }
   const TileCfg c = pick_cfg(a);
   hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
   if (res) {
@@ -829,6 +815,7 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   int32_t *tile_offsets = reinterpret_cast<int32_t *>(ws);
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
   uint16_t *wg = res ? reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t))) : nullptr;
+  if (gemm_use_small(a)) return launch_gemm_small(a, wg, stream);
   const TileCfg c = pick_cfg(a);
   const int bm = cfg_bm(c), bn = cfg_bn(c);
   Params p{};

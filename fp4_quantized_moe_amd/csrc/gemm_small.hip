@@ -1,0 +1,356 @@
+// Grouped W4A4 (+RAC) expert GEMM for few rows per expert (decode-shaped
+// rollout batches), gfx950.
+//
+// With ~16 rows per expert the GEMM is bound by reading the NVFP4 weights
+// once from HBM (0.5625 B per weight), not by the MFMAs.  So each weight
+// element must be read exactly once per call, including for the RAC segment:
+// QUADS technical summary section 2.2-B adds the second-pass residual of the
+// selected channels to the quantized activation, and with the selected
+// channels scattered back to their positions in K (zero elsewhere) the
+// correction is one more MFMA on the weight fragment already in registers:
+//
+//   Y[i,n] = gw * ( gx * sum_k W'[n,k] X'[t(i),k] + gr * sum_k W'[n,k] Rd[t(i),k] )
+//
+// where Rd is the residual scattered to dense K in fp16 (exact values
+// e2m1 * e4m3, no tensor scale) by k_scatter_residual.
+//
+// k_gemm_small: a workgroup of 4 waves per (expert, 128 output columns); wave
+// w owns 32 weight rows (output columns) and runs v_mfma_f32_32x32x16_f16 with
+// the expert's rows (32 per pass) as the A operand.  A K step is 256 elements:
+// one 128-byte line of codes per weight row.  Operands go from global memory
+// straight to LDS (global_load_lds_dwordx4) with every load instruction
+// covering whole 128-byte lines (8 lanes per line) -- on MI355X a wave load
+// spread over 32 rows at 32 bytes per row streams at a quarter of the HBM rate
+// that whole lines reach.  Each wave stages its own weight rows; the
+// activation rows, their scales and the scattered residual are staged once
+// per workgroup, a quarter by each wave.  16-byte chunks are XOR-swizzled per
+// row (by choosing which chunk each lane fetches) so that the MFMA fragment
+// reads are bank-conflict-free.  Two LDS stages: step k+1 is in flight while
+// step k is decoded (cvt + pk_mul, exact) and multiplied.  The contraction
+// order inside a step is permuted identically for both operands (lane half h
+// takes elements [128h, 128h+128), 8 per MFMA).
+#include <stdlib.h>
+#include <string.h>
+
+#include "fp4_mfma.hpp"
+#include "launch.hpp"
+#include "quads_device.hpp"
+
+namespace quads {
+namespace {
+
+constexpr int kSK = 256;   // K per step
+constexpr int kSBN = 128;  // output columns per workgroup: 4 waves x 32
+constexpr int kSM = 32;    // rows per pass
+
+struct SmallParams {
+  const int32_t *expert_offsets, *row_token;
+  int E, n_tiles, n_seg;
+  int64_t N, K;
+  const uint8_t *x_codes, *x_scales;
+  const float *x_g;
+  const uint16_t *r_dense;  // [act_rows, K] fp16 residual scattered to K, or null
+  const float *r_g;
+  const uint8_t *w_codes, *w_scales;
+  const float *w_g;
+  void *y;
+  int y_bf16;
+};
+
+// One LDS stage.  Rows of 128 bytes hold 8 chunks; chunk c of row r sits in
+// slot c ^ ((r >> 1) & 7) (32 residual chunks per row: slot c ^ (r & 15)).
+template <bool RES>
+struct StageLds {
+  uint4 w[4 * 32 * 8];          // [wave][row][slot] weight codes
+  uint32_t ws[4 * 32 * 4];      // [wave][row][4 words] weight block scales
+  uint4 x[32 * 8];              // [row][slot] activation codes
+  uint32_t xs[32 * 4];          // [row][4 words] activation block scales
+  uint4 r[RES ? 32 * 32 : 1];   // [row][slot] residual, fp16
+};
+
+typedef __attribute__((address_space(3))) void lds_t;
+
+// One DMA instruction: lane l's `bytes` bytes land at lds_base + l * bytes.
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_t *)(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_t *)(lds_base), 4, 0, 0);
+}
+
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// Per-lane row bookkeeping for the staging loads of one pass.
+struct SmallRows {
+  int64_t wrow[4];  // weight rows of this wave's 4 code loads (rows 8q + lane/8)
+  int64_t wsrow[2]; // weight rows of the 2 scale loads (rows (64i + lane)/4)
+  int64_t xrow;     // activation row of the code load (pass row 8*wave + lane/8)
+  int64_t xsrow;    // activation row of the scale load (pass row (64*wave + lane)/4, waves 0-1)
+  int64_t rrow[4];  // activation rows of the residual loads (pass row 2*(4*wave + q) + lane/32)
+};
+
+template <bool RES>
+__device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, const SmallRows &rw, int kt,
+                                      int wave, int lane) {
+  const int64_t K = p.K;
+  const int slot = lane & 7;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * q + (lane >> 3);
+    const int chunk = slot ^ swz8(r);
+    dma16(p.w_codes + rw.wrow[q] * (K / 2) + kt * 128 + chunk * 16, &st.w[(wave * 32 + 8 * q) * 8]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    dma4(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i]);
+  {
+    const int r = 8 * wave + (lane >> 3);
+    const int chunk = slot ^ swz8(r);
+    dma16(p.x_codes + rw.xrow * (K / 2) + kt * 128 + chunk * 16, &st.x[8 * wave * 8]);
+  }
+  if (wave < 2) dma4(p.x_scales + rw.xsrow * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * wave]);
+  if constexpr (RES) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = 4 * wave + q;
+      const int r = 2 * b + (lane >> 5);
+      const int chunk = (lane & 31) ^ (r & 15);
+      dma16(p.r_dense + rw.rrow[q] * K + kt * 256 + chunk * 8, &st.r[2 * b * 32]);
+    }
+  }
+}
+
+template <bool RES>
+__device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int lane, f32x16 &acc_x, f32x16 &acc_r) {
+  const int r = lane & 31, h = lane >> 5;
+  const uint32_t ws0 = st.ws[wave * 128 + r * 4 + 2 * h], ws1 = st.ws[wave * 128 + r * 4 + 2 * h + 1];
+  const uint32_t xs0 = st.xs[r * 4 + 2 * h], xs1 = st.xs[r * 4 + 2 * h + 1];
+#pragma unroll
+  for (int cq = 0; cq < 4; ++cq) {
+    const int c = 4 * h + cq;
+    const uint4 wc = st.w[(wave * 32 + r) * 8 + (c ^ swz8(r))];
+    const uint4 xc = st.x[r * 8 + (c ^ swz8(r))];
+    const uint32_t wv[4] = {wc.x, wc.y, wc.z, wc.w};
+    const uint32_t xv[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+    for (int sq = 0; sq < 4; ++sq) {
+      const int s = 4 * cq + sq;                 // sub-step: elements [128h + 8s, +8)
+      const int blk = s >> 1;                    // block among the lane's 8
+      const uint32_t wsw = blk < 4 ? ws0 : ws1, xsw = blk < 4 ? xs0 : xs1;
+      const uint4 bw = decode8_f16(wv[sq], scale_h2((wsw >> (8 * (blk & 3))) & 0xFFu));
+      const uint4 ax = decode8_f16(xv[sq], scale_h2((xsw >> (8 * (blk & 3))) & 0xFFu));
+      acc_x = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw), acc_x,
+                                                     0, 0, 0);
+      if constexpr (RES) {
+        const uint4 rv = st.r[r * 32 + ((16 * h + s) ^ (r & 15))];
+        acc_r = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, rv), __builtin_bit_cast(h8, bw),
+                                                       acc_r, 0, 0, 0);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store_out(const SmallParams &p, int64_t row, int64_t col, int64_t ld, float v) {
+  if (p.y_bf16)
+    static_cast<uint16_t *>(p.y)[row * ld + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+  else
+    static_cast<float *>(p.y)[row * ld + col] = v;
+}
+
+// EPI 0: Y fp32/bf16 [rows, N].  EPI 1 (SwiGLU): waves 0-1 own gate columns
+// and waves 2-3 the matching up columns; h = silu(gate) * up -> bf16 [rows, N/2].
+template <int EPI, bool RES>
+__global__ __launch_bounds__(256) void k_gemm_small(SmallParams p) {
+  __shared__ StageLds<RES> st0;
+  __shared__ StageLds<RES> st1;
+  const int e = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+  const int m0 = p.expert_offsets[e], mend = p.expert_offsets[e + 1];
+  if (m0 >= mend) return;
+
+  // First weight row (output column) of this wave.
+  int64_t col0, wcol0;
+  if constexpr (EPI == 0) {
+    col0 = static_cast<int64_t>(nt) * kSBN + 32 * wave;
+    wcol0 = col0;
+  } else {
+    col0 = static_cast<int64_t>(nt) * (kSBN / 2) + 32 * (wave & 1);
+    wcol0 = (wave >> 1) * (p.N / 2) + col0;
+  }
+  const int64_t wrow0 = static_cast<int64_t>(e) * p.N + wcol0;
+  const float gw = p.w_g[e * p.n_seg + static_cast<int>(wcol0) / static_cast<int>(p.N / p.n_seg)];
+  const float gx = *p.x_g;
+  const float gr = RES ? *p.r_g : 0.0f;
+  const int nk = static_cast<int>(p.K / kSK);  // even
+
+  auto act_row = [&](int pm, int r) -> int64_t {
+    const int i = min(pm + r, mend - 1);  // rows past the expert re-read a valid row, never stored
+    return p.row_token ? static_cast<int64_t>(p.row_token[i]) : static_cast<int64_t>(i);
+  };
+
+  for (int pm = m0; pm < mend; pm += kSM) {
+    SmallRows rw;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rw.wrow[q] = wrow0 + 8 * q + (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rw.wsrow[i] = wrow0 + (64 * i + lane) / 4;
+    rw.xrow = act_row(pm, 8 * wave + (lane >> 3));
+    rw.xsrow = act_row(pm, (64 * (wave & 1) + lane) / 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rw.rrow[q] = RES ? act_row(pm, 2 * (4 * wave + q) + (lane >> 5)) : 0;
+
+    f32x16 acc_x, acc_r;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc_x[r] = 0.0f;
+      acc_r[r] = 0.0f;
+    }
+    __syncthreads();  // the previous pass (or its epilogue) no longer reads the stages
+    issue<RES>(st0, p, rw, 0, wave, lane);
+    for (int kt = 0; kt < nk; kt += 2) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of step kt has landed in LDS
+      __syncthreads();                // ... and every wave's; step kt-1 is no longer read
+      issue<RES>(st1, p, rw, kt + 1, wave, lane);
+      compute<RES>(st0, wave, lane, acc_x, acc_r);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 2 < nk) issue<RES>(st0, p, rw, kt + 2, wave, lane);
+      compute<RES>(st1, wave, lane, acc_x, acc_r);
+    }
+
+    // Element r of the accumulator is row 8*(r/4) + 4*h + r%4 of the pass,
+    // column lane%32 of the wave's 32.
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = RES ? (acc_x[r] * gx + acc_r[r] * gr) * gw : acc_x[r] * (gw * gx);
+    const int64_t col = col0 + (lane & 31);
+    if constexpr (EPI == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = pm + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < mend) store_out(p, row, col, p.N, v[r]);
+      }
+    } else {
+      float *up = reinterpret_cast<float *>(st0.w);  // 8 KB of stage 0, free after the K loop
+      __syncthreads();
+      if (wave >= 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) up[((wave - 2) * 16 + r) * 64 + lane] = v[r];
+      }
+      __syncthreads();
+      if (wave < 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = pm + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float u = up[(wave * 16 + r) * 64 + lane];
+          const float g = v[r];
+          if (row < mend)
+            static_cast<uint16_t *>(p.y)[static_cast<int64_t>(row) * (p.N / 2) + col] =
+                static_cast<uint16_t>(f32_to_bf16_bits(g / (1.0f + expf(-g)) * u));
+        }
+      }
+    }
+  }
+}
+
+// Residual codes [rows, kpad] in selected order -> fp16 [rows, K] with each
+// selected channel's exact value at its own position and zeros elsewhere.
+// The inverse of sel_idx is built in LDS first.  sel_idx is strictly
+// ascending over the nsel real entries and padded with index 0 (zero
+// residual): an entry j > 0 that points at channel 0 is padding and skipped.
+__global__ __launch_bounds__(256) void k_scatter_residual(const uint8_t *r_codes, const uint8_t *r_scales,
+                                                          int64_t rows, int K, int kpad, const int32_t *sel,
+                                                          uint16_t *out, int rows_per_wg) {
+  extern __shared__ int16_t inv[];
+  for (int k = threadIdx.x; k < K; k += 256) inv[k] = -1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < kpad; j += 256) {
+    const int c = sel[j];
+    if (j == 0 || c != 0) inv[c] = static_cast<int16_t>(j);
+  }
+  __syncthreads();
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int64_t r1 = min(r0 + rows_per_wg, rows);
+  const int chunks = K / 8;
+  for (int64_t t = threadIdx.x; t < (r1 - r0) * chunks; t += 256) {
+    const int64_t row = r0 + t / chunks;
+    const int k0 = static_cast<int>(t % chunks) * 8;
+    const uint8_t *rc = r_codes + row * (kpad / 2);
+    const uint8_t *rs = r_scales + row * (kpad / 16);
+    uint32_t hv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = inv[k0 + q];
+      float v = 0.0f;
+      if (j >= 0) {
+        const uint32_t code = (rc[j >> 1] >> ((j & 1) * 4)) & 0xFu;
+        v = dequant_code(code, e4m3_to_f32(rs[j >> 4]));
+      }
+      hv[q] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+    }
+    reinterpret_cast<uint4 *>(out + row * K)[k0 / 8] =
+        make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+  }
+}
+
+
+}  // namespace
+
+bool gemm_use_small(const GemmLaunch &a) {
+  // K in whole pairs of 256-element steps (the K loop is unrolled by two)
+  if (a.mode != 0 || a.K % (2 * kSK) != 0 || a.K > 16384 || a.N % kSBN != 0) return false;
+  if (const char *f = getenv("QUADS_GEMM_TILE")) {
+    if (strcmp(f, "small") == 0) return true;
+    if (strcmp(f, "128x128") == 0 || strncmp(f, "256x256", 7) == 0 || strcmp(f, "128x192") == 0) return false;
+  }
+  return a.num_rows <= static_cast<int64_t>(kSM) * a.E;  // about one pass of rows per expert
+}
+
+size_t gemm_small_res_bytes(const GemmLaunch &a) {
+  return static_cast<size_t>(a.act_rows) * static_cast<size_t>(a.K) * sizeof(uint16_t);
+}
+
+hipError_t launch_gemm_small_prepare(const GemmLaunch &a, uint16_t *r_dense, hipStream_t stream) {
+  if (a.r_codes == nullptr || a.kpad == 0 || a.act_rows == 0) return hipSuccess;
+  // One row per workgroup up to 4096 rows (the inverse map is rebuilt by every
+  // workgroup: K/256 + kpad/256 LDS stores per thread), more rows beyond.
+  const int rows_per_wg = static_cast<int>((a.act_rows + 4095) / 4096);
+  const int64_t grid = (a.act_rows + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(k_scatter_residual, dim3(grid), dim3(256), a.K * sizeof(int16_t), stream, a.r_codes,
+                     a.r_scales, a.act_rows, static_cast<int>(a.K), static_cast<int>(a.kpad), a.sel_idx, r_dense,
+                     rows_per_wg);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_small(const GemmLaunch &a, const uint16_t *r_dense, hipStream_t stream) {
+  SmallParams p{};
+  p.expert_offsets = a.expert_offsets;
+  p.row_token = a.row_token;
+  p.E = a.E;
+  p.n_seg = a.n_seg;
+  p.N = a.N;
+  p.K = a.K;
+  p.n_tiles = static_cast<int>(a.N / kSBN);
+  p.x_codes = a.x_codes;
+  p.x_scales = a.x_scales;
+  p.x_g = a.x_g;
+  p.r_dense = r_dense;
+  p.r_g = a.r_g;
+  p.w_codes = a.w_codes;
+  p.w_scales = a.w_scales;
+  p.w_g = a.w_g;
+  p.y = a.y;
+  p.y_bf16 = a.y_bf16 ? 1 : 0;
+  const bool res = r_dense != nullptr;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.E) * p.n_tiles));
+  if (a.epilogue == 0) {
+    if (res) hipLaunchKernelGGL((k_gemm_small<0, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((k_gemm_small<0, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (res) hipLaunchKernelGGL((k_gemm_small<1, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((k_gemm_small<1, false>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace quads

@@ -66,6 +66,12 @@ size_t gemm_ws_bytes(const GemmLaunch &a);
 // prepare: tile list + residual weight-column gather; main: the GEMM kernel.
 hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream);
 hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream);
+// Few rows per expert (decode-shaped calls): weights read once, the RAC
+// residual scattered to dense K (gemm_small.hip).
+bool gemm_use_small(const GemmLaunch &a);
+size_t gemm_small_res_bytes(const GemmLaunch &a);
+hipError_t launch_gemm_small_prepare(const GemmLaunch &a, uint16_t *r_dense, hipStream_t stream);
+hipError_t launch_gemm_small(const GemmLaunch &a, const uint16_t *r_dense, hipStream_t stream);
 
 // ---- route.hip -------------------------------------------------------------
 size_t route_ws_bytes(int64_t T, int E);

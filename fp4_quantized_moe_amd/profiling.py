@@ -31,7 +31,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 # Sources that determine each kernel's memory traffic.
 KERNEL_SOURCES = {
-    "k_gemm": ["csrc/gemm.hip", "csrc/quads_device.hpp", "csrc/launch.hpp"],
+    "k_gemm": ["csrc/gemm.hip", "csrc/fp4_mfma.hpp", "csrc/quads_device.hpp", "csrc/launch.hpp"],
+    "k_gemm_small": ["csrc/gemm_small.hip", "csrc/fp4_mfma.hpp", "csrc/quads_device.hpp", "csrc/launch.hpp"],
     "k_rac": ["csrc/rac.hip", "csrc/quads_device.hpp", "csrc/launch.hpp"],
     "k_quantize": ["csrc/quantize.hip", "csrc/quads_device.hpp", "csrc/launch.hpp"],
 }
