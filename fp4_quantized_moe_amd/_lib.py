@@ -307,6 +307,29 @@ def moe_w4a4_gemm(**kw):
     return GemmCall(**kw)()
 
 
+class QdqCall:
+    """quads_weight_qdq with its output and workspace allocated once (or the
+    output given): w bf16 [rows, cols] or [batch, rows, cols]."""
+
+    def __init__(self, w: torch.Tensor, out: torch.Tensor | None = None, export: bool = False):
+        L = load()
+        _require_cuda(w, out)
+        if w.dtype != torch.bfloat16 or (out is not None and (out.dtype != torch.bfloat16 or out.shape != w.shape)):
+            raise QuadsError("weight_qdq expects bf16 master weights and a bf16 output of the same shape")
+        self.w = w
+        self.batch, self.rows, self.cols = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+        self.out = torch.empty_like(w) if out is None else out
+        self.q = empty_nvfp4(self.batch, self.rows, self.cols, w.device) if export else None
+        self._qs = self.q.c_struct() if self.q is not None else None
+        self.ws = _workspace(L.quads_weight_qdq_workspace_bytes(self.batch, self.rows, self.cols), w.device)
+
+    def __call__(self):
+        _check(load().quads_weight_qdq(_ptr(self.w), self.batch, self.rows, self.cols, _ptr(self.out),
+                                       ctypes.byref(self._qs) if self._qs is not None else None, 0, _ptr(self.ws),
+                                       self.ws.numel(), _stream()), "quads_weight_qdq")
+        return self.out, self.q
+
+
 def weight_qdq(w: torch.Tensor, export: bool = False):
     """w: bf16 [rows, cols] or [batch, rows, cols] -> (bf16 QDQ tensor, NVFP4Tensor or None)."""
     L = load()

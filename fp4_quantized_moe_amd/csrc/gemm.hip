@@ -694,8 +694,10 @@ using CfgS = Cfg<128, 128, 2, 2, 2>;  // general / ragged shapes: 256 threads, 2
 using CfgM = Cfg<128, 192, 2, 2, 1>;  // N % 192 == 0 dense shapes: 64x96 wave tiles
 using CfgL = Cfg<256, 256, 2, 4, 1>;  // large grouped shapes: 512 threads, 128x64 wave tiles
 using CfgW = Cfg<256, 256, 2, 2, 1>;  // large grouped shapes: 256 threads, 128x128 wave tiles
+using CfgS8a = Cfg<128, 128, 4, 2, 2>;  // 512 threads, 32x64 wave tiles
+using CfgS8b = Cfg<128, 128, 2, 4, 2>;  // 512 threads, 64x32 wave tiles
 
-enum TileCfg { kS = 0, kM = 1, kL = 2, kW = 3, kP = 4 };
+enum TileCfg { kS = 0, kM = 1, kL = 2, kW = 3, kP = 4, kS8a = 5, kS8b = 6 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -711,6 +713,8 @@ TileCfg pick_cfg(const GemmLaunch &a) {
     if (strcmp(force, "128x128") == 0) return kS;
     if (strcmp(force, "256x256w4") == 0 && a.N % 256 == 0) return kW;
     if (strcmp(force, "256x256pp") == 0 && a.N % 256 == 0) return kP;
+    if (strcmp(force, "128x128w8a") == 0) return kS8a;
+    if (strcmp(force, "128x128w8b") == 0 && a.epilogue == 0) return kS8b;  // SwiGLU needs 2 tiles per wave
   }
   struct Cand {
     TileCfg c;
@@ -849,6 +853,8 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   const int g = static_cast<int>(grid);
   if (c == kP) launch_pp_cfg(a, p, g, res, stream);
   else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream);
+  else if (c == kS8a) launch_cfg<CfgS8a>(a, p, g, res, stream);
+  else if (c == kS8b) launch_cfg<CfgS8b>(a, p, g, res, stream);
   else if (c == kL) launch_cfg<CfgL>(a, p, g, res, stream);
   else if (c == kM) launch_cfg<CfgM>(a, p, g, res, stream);
   else launch_cfg<CfgS>(a, p, g, res, stream);
