@@ -112,3 +112,73 @@ def test_moe_layer_end_to_end_small():
     ref = O.moe_layer(xa.f32, logits, gue, dne, k, top)
     assert rel_err(host(h.float()), ref["h"]) <= 1e-2
     assert rel_err(host(out), ref["out"]) <= 2e-2
+
+
+def test_prefill_layer_full_size_sampled_experts():
+    """The prefill-shaped layer at full size (16384 tokens, hidden 2048, 64
+    experts with Zipf-skewed top-8 routing, intermediate 768, k=50) as the
+    benchmark launches it; the oracle recomputes the rows of the largest,
+    smallest and one random non-empty expert of the gate_up GEMM (FP32 and
+    SwiGLU outputs) and of the down GEMM on a seeded h."""
+    wl = S.moe_prefill()
+    T, H = wl.x.f32.shape
+    E, N2, _ = wl.w_gate_up.f32.shape
+    I = N2 // 2
+    k = wl.k_percent
+    log(f"[moe] prefill full size T={T} E={E} H={H} I={I} k={k}")
+    ids, w, offs, rt, inv = Q.moe_route(torch.from_numpy(wl.logits).cuda(), wl.top)
+    _, _, roffs, rrt, _ = O.route(wl.logits, wl.top)
+    assert np.array_equal(host(offs), roffs) and np.array_equal(host(rt), rrt)
+    R = int(roffs[-1])
+    x = dev_act(wl.x)
+    guc, gus, gug = quantize_weights_gpu(dev_act(wl.w_gate_up), 2)
+    q, sc = Q.quantize_nvfp4(x, want_scores=True)
+    sel, res, nsel = Q.rac_select(x, q, sc, k)
+    args = dict(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
+                x=q, res=res, sel_idx=sel, row_token=rt)
+    y = host(Q.moe_w4a4_gemm(**args))
+    h = host(Q.moe_w4a4_gemm(epilogue=Q.EPI_SWIGLU, **args).float())
+    xq = O.quantize_nvfp4(wl.x.f32)
+    xsel, xn = O.rac_select(O.rac_scores(wl.x.f32, xq), k)
+    xr = O.rac_quantize_residual(wl.x.f32, xq, xsel, xn)
+    assert np.array_equal(host(q.codes), xq.codes) and np.array_equal(host(sel), xsel)
+    assert np.array_equal(host(res.codes), xr.codes)
+    xe = O.dequant_exact(xq.codes, xq.scales, xq.g)
+    re = O.dequant_exact(xr.codes, xr.scales, xr.g)
+    cnt = np.diff(roffs)
+    nz = np.flatnonzero(cnt)
+    pick = sorted({int(nz[np.argmax(cnt[nz])]), int(nz[np.argmin(cnt[nz])]),
+                   int(np.random.default_rng(97).choice(nz))})
+    for e in pick:
+        a, b = int(roffs[e]), int(roffs[e + 1])
+        _, _, _, we = O.quantize_weights(wl.w_gate_up.f32[e:e + 1], 2)
+        yr = O.gemm_ref(xe[rrt[a:b]], we[0], re[rrt[a:b]], xsel)
+        err = rel_err(y[a:b], yr)
+        log(f"  gate_up expert {e} rows {b - a}: rel err {err:.2e}")
+        assert err <= 1e-3, e
+        hr = O.swiglu(yr[:, :I], yr[:, I:])
+        ymax = np.abs(yr).max()
+        tol = 2.0 ** -8 * np.abs(hr) + 2e-3 * ymax * (np.abs(yr[:, I:]) + np.abs(yr[:, :I]) + 1)
+        assert (np.abs(h[a:b] - hr) <= tol).all(), e
+
+    rng = np.random.default_rng(98)
+    ha = S.activation(rng, R, I, 2, 8.0, bf16=True)
+    hd = dev_act(ha)
+    dnc, dns, dng = quantize_weights_gpu(dev_act(wl.w_down), 1)
+    hq, hsc = Q.quantize_nvfp4(hd, want_scores=True)
+    hsel, hres, _ = Q.rac_select(hd, hq, hsc, k)
+    yd = host(Q.moe_w4a4_gemm(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs,
+                              num_rows=R, x=hq, res=hres, sel_idx=hsel))
+    oq = O.quantize_nvfp4(ha.f32)
+    osel, on = O.rac_select(O.rac_scores(ha.f32, oq), k)
+    orr = O.rac_quantize_residual(ha.f32, oq, osel, on)
+    assert np.array_equal(host(hsel), osel) and np.array_equal(host(hres.codes), orr.codes)
+    he = O.dequant_exact(oq.codes, oq.scales, oq.g)
+    hre = O.dequant_exact(orr.codes, orr.scales, orr.g)
+    for e in pick:
+        a, b = int(roffs[e]), int(roffs[e + 1])
+        _, _, _, we = O.quantize_weights(wl.w_down.f32[e:e + 1], 1)
+        yr = O.gemm_ref(he[a:b], we[0], hre[a:b], osel)
+        err = rel_err(yd[a:b], yr)
+        log(f"  down expert {e} rows {b - a}: rel err {err:.2e}")
+        assert err <= 1e-3, e
