@@ -626,12 +626,19 @@ __global__ __launch_bounds__(CfgPP::THREADS, 1) void k_gemm_pp(Params p) {
 }
 
 // Exclusive scan of per-expert m-tile counts ceil(rows_e / bm) ->
-// tile_offsets[E + 1] (E <= 1024: one thread per expert, wave scans).
-__global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *offsets, int E, int bm, int32_t *tile_offsets) {
-  __shared__ int32_t wsum[17];
+// tile_offsets[E + 1] by one 256-thread workgroup (E <= 1024: thread t owns
+// experts [4t, 4t + 4)).
+__device__ void tile_prefix_256(const int32_t *offsets, int E, int bm, int32_t *tile_offsets) {
+  __shared__ int32_t wsum[5];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int32_t v = t < E ? (offsets[t + 1] - offsets[t] + bm - 1) / bm : 0;
-  int32_t incl = v;
+  int32_t c[4], own = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    c[q] = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+    own += c[q];
+  }
+  int32_t incl = own;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int32_t o = __shfl_up(incl, off);
@@ -641,26 +648,43 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t *offsets, in
   __syncthreads();
   if (t == 0) {
     int32_t run = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < 4; ++w) {
       const int32_t x = wsum[w];
       wsum[w] = run;
       run += x;
     }
-    wsum[16] = run;
+    wsum[4] = run;
   }
   __syncthreads();
-  if (t < E) tile_offsets[t] = wsum[wave] + incl - v;
-  if (t == 0) tile_offsets[E] = wsum[16];
+  int32_t run = wsum[wave] + incl - own;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    if (e < E) tile_offsets[e] = run;
+    run += c[q];
+  }
+  if (t == 0) tile_offsets[E] = wsum[4];
+}
+
+__global__ __launch_bounds__(256) void k_tile_prefix(const int32_t *offsets, int E, int bm, int32_t *tile_offsets) {
+  tile_prefix_256(offsets, E, bm, tile_offsets);
 }
 
 // Gather the selected weight columns of every expert row into fp16
 // [E*N, kpad] (exact values e2m1 * e4m3, no tensor scale).  One row per
 // 64-thread quarter of the workgroup: the row's codes and scales are staged in
 // LDS, then each thread emits 8 consecutive outputs (one 16-byte store).
+// The launch has one workgroup more than the gather needs; the last one
+// builds the per-expert tile prefix instead (one launch for both).
 __global__ __launch_bounds__(256) void k_gather_wcols(const uint8_t *w_codes, const uint8_t *w_scales,
                                                       int64_t rows_total, int K, const int32_t *sel,
-                                                      int kpad, uint16_t *out) {
+                                                      int kpad, uint16_t *out, const int32_t *offsets, int E,
+                                                      int bm, int32_t *tile_offsets) {
   extern __shared__ uint4 gather_lds[];
+  if (blockIdx.x == gridDim.x - 1) {
+    tile_prefix_256(offsets, E, bm, tile_offsets);
+    return;
+  }
   const int q = threadIdx.x >> 6, t = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + q;
   const int stride = (K / 2 + K / 16 + 15) / 16 * 16;
@@ -802,14 +826,16 @@ hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
     return res ? launch_gemm_small_prepare(a, rd, stream) : hipSuccess;
   }
   const TileCfg c = pick_cfg(a);
-  hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(1024), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
   if (res) {
     uint16_t *wg = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
     const int64_t rows_total = static_cast<int64_t>(a.E) * a.N;
     const int K = static_cast<int>(a.K);
     const size_t lds = 4 * ((K / 2 + K / 16 + 15) / 16 * 16);
-    hipLaunchKernelGGL(k_gather_wcols, dim3((rows_total + 3) / 4), dim3(256), lds, stream, a.w_codes,
-                       a.w_scales, rows_total, K, a.sel_idx, static_cast<int>(a.kpad), wg);
+    hipLaunchKernelGGL(k_gather_wcols, dim3((rows_total + 3) / 4 + 1), dim3(256), lds, stream, a.w_codes,
+                       a.w_scales, rows_total, K, a.sel_idx, static_cast<int>(a.kpad), wg, a.expert_offsets, a.E,
+                       cfg_bm(c), tile_offsets);
+  } else {
+    hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(256), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
   }
   return hipGetLastError();
 }

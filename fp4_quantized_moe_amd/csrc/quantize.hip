@@ -24,27 +24,42 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// 16 elements as loaded (bf16: 2 x 16 bytes, fp32: 4 x 16 bytes); converted
+// to FP32 only where they are used, so a load can be issued early.
 template <bool BF16>
-__device__ __forceinline__ void load16(const void *base, int64_t elem, float (&v)[16]) {
+struct Raw16 {
+  uint4 u[BF16 ? 2 : 4];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_raw16(const void *base, int64_t elem, Raw16<BF16> &r) {
   if constexpr (BF16) {
     const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
-    const uint4 a = load_nt16(p);
-    const uint4 b = load_nt16(p + 1);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    r.u[0] = load_nt16(p);
+    r.u[1] = load_nt16(p + 1);
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.u[i] = load_nt16(p + i);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void to_f32(const Raw16<BF16> &r, float (&v)[16]) {
+  if constexpr (BF16) {
+    const uint32_t w[8] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w, r.u[1].x, r.u[1].y, r.u[1].z, r.u[1].w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 f = load_nt16(p + i);
-      v[4 * i] = __uint_as_float(f.x);
-      v[4 * i + 1] = __uint_as_float(f.y);
-      v[4 * i + 2] = __uint_as_float(f.z);
-      v[4 * i + 3] = __uint_as_float(f.w);
+      v[4 * i] = __uint_as_float(r.u[i].x);
+      v[4 * i + 1] = __uint_as_float(r.u[i].y);
+      v[4 * i + 2] = __uint_as_float(r.u[i].z);
+      v[4 * i + 3] = __uint_as_float(r.u[i].w);
     }
   }
 }
@@ -79,10 +94,10 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const void *x, int64_
   const int64_t base = static_cast<int64_t>(b) * n_per_tensor;
   float m = 0.0f;
   constexpr int kVec = BF16 ? 8 : 4;  // elements per 16-byte load
-  for (int64_t i = start + static_cast<int64_t>(threadIdx.x) * kVec; i < end;
-       i += static_cast<int64_t>(kThreads) * kVec) {
+  constexpr int kUnroll = 4;          // loads in flight per thread
+  const int64_t stride = static_cast<int64_t>(kThreads) * kVec;
+  auto fold = [&](const uint4 &u) {
     if constexpr (BF16) {
-      const uint4 u = load_nt16(static_cast<const uint16_t *>(x) + base + i);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -90,11 +105,23 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const void *x, int64_
         m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xFFFF0000u)));
       }
     } else {
-      const uint4 u = load_nt16(static_cast<const float *>(x) + base + i);
       m = fmaxf(fmaxf(fabsf(__uint_as_float(u.x)), fabsf(__uint_as_float(u.y))),
                 fmaxf(fmaxf(fabsf(__uint_as_float(u.z)), fabsf(__uint_as_float(u.w))), m));
     }
+  };
+  auto addr = [&](int64_t i) -> const void * {
+    if constexpr (BF16) return static_cast<const uint16_t *>(x) + base + i;
+    else return static_cast<const float *>(x) + base + i;
+  };
+  int64_t i = start + static_cast<int64_t>(threadIdx.x) * kVec;
+  for (; i + (kUnroll - 1) * stride < end; i += kUnroll * stride) {
+    uint4 u[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) u[k] = load_nt16(addr(i + k * stride));
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) fold(u[k]);
   }
+  for (; i < end; i += stride) fold(load_nt16(addr(i)));
   m = block_max(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
   if (scores != nullptr && blockIdx.x == 0) {
@@ -143,26 +170,35 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
   const int bcol = threadIdx.x % p.BC, rg = threadIdx.x / p.BC;
   const int64_t gbc = static_cast<int64_t>(cc) * p.BC + bcol;
   const bool active = rg < p.RG && gbc < p.cb;
+  const int64_t r_end = min(static_cast<int64_t>(rc + 1) * p.RW, p.rows);
+  int64_t r = static_cast<int64_t>(rc) * p.RW + rg;
+
+  Raw16<BF16> x0, x1;
+  bool two = false;
+  int64_t row0 = 0, row1 = 0;
+  auto issue = [&]() {
+    two = r + p.RG < r_end;
+    row0 = static_cast<int64_t>(b) * p.rows + r;
+    row1 = row0 + (two ? p.RG : 0);
+    load_raw16<BF16>(p.x, row0 * p.cols + gbc * 16, x0);
+    load_raw16<BF16>(p.x, row1 * p.cols + gbc * 16, x1);
+  };
+  if (active && r < r_end) issue();
+
   float smax[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) smax[i] = 0.0f;
 
   if (active) {
-    const int64_t r_end = min(static_cast<int64_t>(rc + 1) * p.RW, p.rows);
     // Two row steps per iteration: both loads are in flight before either
     // block is quantized.
-    for (int64_t r = static_cast<int64_t>(rc) * p.RW + rg; r < r_end; r += 2 * p.RG) {
-      const bool two = r + p.RG < r_end;
-      const int64_t row0 = static_cast<int64_t>(b) * p.rows + r;
-      const int64_t row1 = row0 + (two ? p.RG : 0);
-      float v0[16], v1[16];
-      load16<BF16>(p.x, row0 * p.cols + gbc * 16, v0);
-      load16<BF16>(p.x, row1 * p.cols + gbc * 16, v1);
+    while (r < r_end) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (u == 1 && !two) break;
         const int64_t row = u ? row1 : row0;
-        const float(&v)[16] = u ? v1 : v0;
+        float v[16];
+        to_f32<BF16>(u ? x1 : x0, v);
         float dq[16];
         const BlockQ q = quantize_block16(v, g, (SCORES || QDQ) ? dq : nullptr);
         if constexpr (CODES) {
@@ -183,6 +219,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
           for (int i = 0; i < 16; ++i) smax[i] = fmaxf(smax[i], fabsf(v[i] - dq[i]));
         }
       }
+      r += 2 * p.RG;
+      if (r < r_end) issue();
     }
   }
 
