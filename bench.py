@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=48, help="trainer_qdq: layers per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true", help="skip the plain W4A4 comparison run")
+    ap.add_argument("--graph", action="store_true", help="replay the non-dominant stages as HIP graphs")
     return ap.parse_args()
 
 
@@ -227,35 +228,43 @@ def capture(fns, reps=1):
     return g
 
 
-def run_steps(stages, steps, warmup, dominant=None):
-    """One step = a HIP graph of the stages before `dominant`, the dominant
-    stage launched directly between two HIP events, then a graph of the stages
-    after it.  The host enqueues the dominant launch while the first graph is
-    still running, so the events bracket the kernel itself (no launch gap);
-    they are recorded on the stream every call uses.  `warmup` untimed steps,
-    then `steps` timed steps bracketed by device synchronisation.
+def run_steps(stages, steps, warmup, dominant=None, graph=False):
+    """Run `warmup` untimed steps, then `steps` timed steps bracketed by device
+    synchronisation.  Every library call only enqueues work, so the host runs
+    ahead of the device and the kernels of consecutive steps execute back to
+    back; HIP events recorded on the stream every call uses, around the
+    dominant stage of each timed step, give that kernel's duration inside the
+    timed region.  With graph=True the stages before and after the dominant
+    one are replayed as HIP graphs instead (on this stack a graph launch costs
+    more host time than the few direct launches it replaces).
     Returns (wall seconds, event ms over all steps, dominant-stage ms per step)."""
     import torch
-    for _, fn in stages:  # eager pass: lazy allocations happen outside the capture
+    for _, fn in stages:  # eager pass: lazy allocations happen outside any capture
         fn()
     torch.cuda.synchronize()
     names = [n for n, _ in stages]
     i = names.index(dominant) if dominant in names else len(names)
     pre, dom, post = stages[:i], stages[i:i + 1], stages[i + 1:]
-    g_pre = capture([fn for _, fn in pre]) if pre else None
-    g_post = capture([fn for _, fn in post]) if post else None
+    if graph:
+        g_pre = capture([fn for _, fn in pre]) if pre else None
+        g_post = capture([fn for _, fn in post]) if post else None
+        run_pre = [g_pre.replay] if g_pre else []
+        run_post = [g_post.replay] if g_post else []
+    else:
+        run_pre = [fn for _, fn in pre]
+        run_post = [fn for _, fn in post]
 
     def step(ev=None):
-        if g_pre:
-            g_pre.replay()
+        for fn in run_pre:
+            fn()
         if ev:
             ev[0].record()
         for _, fn in dom:
             fn()
         if ev:
             ev[1].record()
-        if g_post:
-            g_post.replay()
+        for fn in run_post:
+            fn()
 
     for _ in range(warmup):
         step()
@@ -323,7 +332,7 @@ def main():
         wl = setup_trainer(Q, S, args.layers)
     torch.cuda.synchronize()
 
-    secs, ev_ms, dom_ms = run_steps(wl["stages"], args.steps, args.warmup, wl["dominant"])
+    secs, ev_ms, dom_ms = run_steps(wl["stages"], args.steps, args.warmup, wl["dominant"], args.graph)
     per = stage_times(wl.get("layer0_stages", wl["stages"]))
     if dom_ms is None:  # no directly launched dominant stage: its graph-of-20 time
         dom_ms = per[wl["dominant_stage_for_roofline"]]
@@ -353,8 +362,9 @@ def main():
         "gemm_tflops": dom_tflops,
         "pct_mfma_peak_f16": 100.0 * dom_tflops / PEAK_F16_TFLOPS,
         "stages_ms": per,
-        "timing": "step = HIP graph of the stages before the dominant one, the dominant kernel launched "
-                  "between two HIP events (roofline.avg_launch_ms, every timed step), graph of the rest; "
+        "timing": ("stages launched directly (host runs ahead of the device)" if not args.graph else
+                   "stages before/after the dominant one replayed as HIP graphs") +
+                  "; roofline.avg_launch_ms from HIP events around the dominant kernel in every timed step; "
                   "stages_ms from graphs of 20 back-to-back calls of one stage",
         "roofline": {"bound": "mfma", "kernel": wl["dominant_kernel"], "achieved": dom_tflops,
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_F16_TFLOPS,
@@ -368,7 +378,7 @@ def main():
         out["qdq"] = {"bytes_per_layer": wl["qdq_bytes_layer"], "ms_per_layer": qdq_ms,
                       "achieved_GBps": wl["qdq_bytes_layer"] / (qdq_ms * 1e-3) / 1e9, "peak_GBps": PEAK_HBM_GBS}
     if not args.no_plain and wl.get("plain"):
-        psecs, _, _ = run_steps(wl["plain"], args.steps, args.warmup)
+        psecs, _, _ = run_steps(wl["plain"], args.steps, args.warmup, None, args.graph)
         out["plain_w4a4_ms_per_step"] = psecs * 1e3 / args.steps
         out["plain_stages_ms"] = stage_times(wl["plain"])
         out["rac_overhead_pct"] = 100.0 * (secs / psecs - 1.0)
