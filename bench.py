@@ -116,7 +116,7 @@ def setup_expert_gemm(Q, S, k):
                                        "oracle quantize + RAC + fp64 GEMM (weights quantized beforehand)")
 
     return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
-                dominant_kernel="k_gemm<...,0,0,true> (W4A4 + RAC segment)", config=cfg, cpu_baseline=cpu_baseline,
+                dominant_kernel="k_gemm_dma<0,true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)", config=cfg, cpu_baseline=cpu_baseline,
                 traffic_summary=os.path.join(ROOT, "profiles", f"k_gemm_expert_gemm_k{k}_traffic.txt"))
 
 
@@ -171,7 +171,9 @@ def setup_moe(Q, S, k, decode):
     wdec = {"gate_up": E * N2 * H * 0.5625, "down": E * H * I * 0.5625}
 
     return dict(stages=stages, plain=plain, tokens=T, flops=f1 + f2, dominant="gate_up", dominant_flops=f1,
-                dominant_kernel="k_gemm<0,1,true>", config=cfg, cpu_baseline=None, weight_bytes=wdec)
+                dominant_kernel=("k_gemm_small<1,true> (gate_up, SwiGLU, few rows per expert)" if decode else
+                                 "k_gemm<256x256 tiles,0,1,true> (gate_up, SwiGLU)"),
+                config=cfg, cpu_baseline=None, weight_bytes=wdec)
 
 
 def setup_trainer(Q, S, layers):
