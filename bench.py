@@ -117,7 +117,7 @@ def setup_expert_gemm(Q, S, k):
 
     return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
                 dominant_kernel="k_gemm_dma<0,true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)", config=cfg, cpu_baseline=cpu_baseline,
-                traffic_summary=os.path.join(ROOT, "profiles", f"k_gemm_expert_gemm_k{k}_traffic.txt"))
+                traffic_summary=os.path.join(ROOT, "profiles", f"k_gemm_dma_expert_gemm_k{k}_traffic.txt"))
 
 
 def setup_moe(Q, S, k, decode):
