@@ -17,7 +17,7 @@ def test_code_hash_ignores_comments_only():
 
 
 def test_read_traffic_checks_source_hash(tmp_path):
-    src = os.path.join(ROOT, "profiles", "k_gemm_expert_gemm_k50_traffic.txt")
+    src = os.path.join(ROOT, "profiles", "k_gemm_dma_expert_gemm_k50_traffic.txt")
     text = open(src).read()
     good = tmp_path / "good.txt"
     good.write_text(re.sub(r"source_sha256: \w+", "source_sha256: " + P.sources_sha256("k_gemm"), text))
