@@ -193,6 +193,23 @@ def read_traffic(path: str):
     return float(fields["traffic_bytes_per_launch"]), fields
 
 
+def cmd_counters(a):
+    """Mean per dispatch of every counter recorded for one kernel in the
+    --pmc databases under each directory."""
+    lines = [f"# rocprofv3 counters per launch: {a.title}", "",
+             "commands (`cd /tmp && export TMPDIR=/tmp` first; $REPO is the repository root):", ""]
+    lines += [f"    {c}" for c in a.cmd]
+    lines += ["", f"{'counter':<32} {'per launch':>14} {'dispatches':>10}"]
+    name = None
+    for d in a.dirs:
+        n, cs = _match(kernel_counters(d), a.kernel)
+        name = name or n
+        for c, vals in sorted(cs.items()):
+            lines.append(f"{c:<32} {statistics.mean(vals):>14.5g} {len(vals):>10}")
+    lines.insert(1, f"kernel: {name}")
+    _write(a.out, lines)
+
+
 def cmd_copy(a):
     import torch
     n = a.mib * 2 ** 20
@@ -237,8 +254,14 @@ def main(argv=None):
     r.add_argument("--algorithmic-bytes", type=float, default=None)
     r.add_argument("--cmd", action="append", required=True)
     r.add_argument("--out", required=True)
+    n = sub.add_parser("counters")
+    n.add_argument("dirs", nargs="+")
+    n.add_argument("--kernel", required=True, help="regex selecting one kernel")
+    n.add_argument("--title", default="")
+    n.add_argument("--cmd", action="append", required=True)
+    n.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"trace": cmd_trace, "copy": cmd_copy, "traffic": cmd_traffic}[a.what](a)
+    {"trace": cmd_trace, "copy": cmd_copy, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
