@@ -89,9 +89,11 @@ struct SmallRows {
   int64_t rrow[4];  // activation rows of the residual loads (pass row 2*(4*wave + q) + lane/32)
 };
 
+// `rows16`: a 16-row pass, which reads activation and residual rows 0-15 only
+// (staged by waves 0-1; wave 0 the scales).
 template <bool RES>
 __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, const SmallRows &rw, int kt,
-                                      int wave, int lane) {
+                                      int wave, int lane, bool rows16 = false) {
   const int64_t K = p.K;
   const int slot = lane & 7;
 #pragma unroll
@@ -103,19 +105,21 @@ __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, c
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     dma4(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i]);
-  {
+  if (!rows16 || wave < 2) {
     const int r = 8 * wave + (lane >> 3);
     const int chunk = slot ^ swz8(r);
     dma16(p.x_codes + rw.xrow * (K / 2) + kt * 128 + chunk * 16, &st.x[8 * wave * 8]);
   }
-  if (wave < 2) dma4(p.x_scales + rw.xsrow * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * wave]);
+  if (wave < (rows16 ? 1 : 2)) dma4(p.x_scales + rw.xsrow * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * wave]);
   if constexpr (RES) {
+    if (!rows16 || wave < 2) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int b = 4 * wave + q;
-      const int r = 2 * b + (lane >> 5);
-      const int chunk = (lane & 31) ^ (r & 15);
-      dma16(p.r_dense + rw.rrow[q] * K + kt * 256 + chunk * 8, &st.r[2 * b * 32]);
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * wave + q;
+        const int r = 2 * b + (lane >> 5);
+        const int chunk = (lane & 31) ^ (r & 15);
+        dma16(p.r_dense + rw.rrow[q] * K + kt * 256 + chunk * 8, &st.r[2 * b * 32]);
+      }
     }
   }
 }
@@ -150,6 +154,51 @@ __device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int l
   }
 }
 
+// 16-row pass (v_mfma_f32_16x16x32_f16): lane quarter q takes chunks 2q
+// and 2q+1 of each 256-element step, 8 elements per MFMA; the wave's 32
+// weight rows are two 16-column blocks.  Same contraction-order permutation
+// for both operands (and the scattered residual).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool RES>
+__device__ __forceinline__ void compute16(const StageLds<RES> &st, int wave, int lane, f32x4 (&acc_x)[2],
+                                          f32x4 (&acc_r)[2]) {
+  const int r = lane & 15, q = lane >> 4;
+  const uint32_t xsw = st.xs[r * 4 + q];  // blocks 4q..4q+3 of the step
+  uint32_t wsw[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) wsw[cb] = st.ws[wave * 128 + (16 * cb + r) * 4 + q];
+#pragma unroll
+  for (int cq = 0; cq < 2; ++cq) {
+    const int c = 2 * q + cq;
+    const uint4 xc = st.x[r * 8 + (c ^ swz8(r))];
+    uint4 wc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int wr = 16 * cb + r;
+      wc[cb] = st.w[(wave * 32 + wr) * 8 + (c ^ swz8(wr))];
+    }
+    const uint32_t xv[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+    for (int sq = 0; sq < 4; ++sq) {
+      const int blk = 2 * cq + (sq >> 1);  // block among the lane's 4
+      const uint4 ax = decode8_f16(xv[sq], scale_h2((xsw >> (8 * blk)) & 0xFFu));
+      uint4 rv = make_uint4(0, 0, 0, 0);
+      if constexpr (RES) rv = st.r[r * 32 + ((8 * q + 4 * cq + sq) ^ r)];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t wv[4] = {wc[cb].x, wc[cb].y, wc[cb].z, wc[cb].w};
+        const uint4 bw = decode8_f16(wv[sq], scale_h2((wsw[cb] >> (8 * blk)) & 0xFFu));
+        acc_x[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
+                                                           acc_x[cb], 0, 0, 0);
+        if constexpr (RES)
+          acc_r[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, rv), __builtin_bit_cast(h8, bw),
+                                                             acc_r[cb], 0, 0, 0);
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ void store_out(const SmallParams &p, int64_t row, int64_t col, int64_t ld, float v) {
   if (p.y_bf16)
     static_cast<uint16_t *>(p.y)[row * ld + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
@@ -160,7 +209,7 @@ __device__ __forceinline__ void store_out(const SmallParams &p, int64_t row, int
 // EPI 0: Y fp32/bf16 [rows, N].  EPI 1 (SwiGLU): waves 0-1 own gate columns
 // and waves 2-3 the matching up columns; h = silu(gate) * up -> bf16 [rows, N/2].
 template <int EPI, bool RES>
-__global__ __launch_bounds__(256) void k_gemm_small(SmallParams p) {
+__global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
   __shared__ StageLds<RES> st0;
   __shared__ StageLds<RES> st1;
   const int e = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
@@ -199,13 +248,77 @@ __global__ __launch_bounds__(256) void k_gemm_small(SmallParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) rw.rrow[q] = RES ? act_row(pm, 2 * (4 * wave + q) + (lane >> 5)) : 0;
 
+    __syncthreads();  // the previous pass (or its epilogue) no longer reads the stages
+    if (mend - pm <= 16) {  // last pass of at most 16 rows: 16-row MFMAs, half the work
+      f32x4 ax[2], ar[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          ax[cb][v] = 0.0f;
+          ar[cb][v] = 0.0f;
+        }
+      issue<RES>(st0, p, rw, 0, wave, lane, true);
+      for (int kt = 0; kt < nk; kt += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        issue<RES>(st1, p, rw, kt + 1, wave, lane, true);
+        compute16<RES>(st0, wave, lane, ax, ar);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 2 < nk) issue<RES>(st0, p, rw, kt + 2, wave, lane, true);
+        compute16<RES>(st1, wave, lane, ax, ar);
+      }
+      // Element v of accumulator cb is row 4*(lane/16) + v of the pass,
+      // column 16*cb + lane%16 of the wave's 32.
+      const int q = lane >> 4;
+      float v16[2][4];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          v16[cb][v] = RES ? (ax[cb][v] * gx + ar[cb][v] * gr) * gw : ax[cb][v] * (gw * gx);
+      if constexpr (EPI == 0) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = pm + 4 * q + v;
+            if (row < mend) store_out(p, row, col0 + 16 * cb + (lane & 15), p.N, v16[cb][v]);
+          }
+      } else {
+        float *up = reinterpret_cast<float *>(st0.w);  // free after the K loop
+        __syncthreads();
+        if (wave >= 2) {
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) up[(((wave - 2) * 2 + cb) * 4 + v) * 64 + lane] = v16[cb][v];
+        }
+        __syncthreads();
+        if (wave < 2) {
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int row = pm + 4 * q + v;
+              const float u = up[((wave * 2 + cb) * 4 + v) * 64 + lane];
+              const float g = v16[cb][v];
+              if (row < mend)
+                static_cast<uint16_t *>(p.y)[static_cast<int64_t>(row) * (p.N / 2) + col0 + 16 * cb + (lane & 15)] =
+                    static_cast<uint16_t>(f32_to_bf16_bits(g / (1.0f + expf(-g)) * u));
+            }
+        }
+      }
+      continue;
+    }
+
     f32x16 acc_x, acc_r;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc_x[r] = 0.0f;
       acc_r[r] = 0.0f;
     }
-    __syncthreads();  // the previous pass (or its epilogue) no longer reads the stages
     issue<RES>(st0, p, rw, 0, wave, lane);
     for (int kt = 0; kt < nk; kt += 2) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's part of step kt has landed in LDS
