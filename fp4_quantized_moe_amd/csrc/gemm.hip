@@ -625,16 +625,17 @@ __global__ __launch_bounds__(CfgPP::THREADS, 1) void k_gemm_pp(Params p) {
   epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
 }
 
-// ---- DMA-staged NVFP4 kernel (128x128 tiles, 8 waves) -----------------------
+// ---- DMA-staged NVFP4 kernel (128 x 64NI tiles, 8 waves) ---------------------
 // Operands travel from global memory to LDS as raw codes and scales
 // (global_load_lds, no registers on the way), so an LDS stage is a quarter of
-// the size of a decoded fp16 tile and three stages fit beside a second
-// workgroup on the CU.  Each wave decodes its own MFMA fragments from LDS.
+// the size of a decoded fp16 tile.  Each wave decodes its own MFMA fragments
+// from LDS (cvt + pk_mul, exact).
 //
 // The eight waves form two groups of four; both groups cover the whole
-// 128x128 output tile (64x64 per wave) and split every K step between them,
-// so a tile keeps two waves per SIMD busy.  The two partial accumulators are
-// summed through LDS at the end.
+// output tile (64 x 32NI per wave) and split every K step between them, so a
+// tile keeps two waves per SIMD busy.  The two partial accumulators are
+// summed through LDS at the end.  NI = 2 (128x128, two workgroups per CU) or
+// NI = 3 (128x192, one per CU).
 //
 // A main-segment K step is 128 elements: 64 code bytes (four 16-byte chunks)
 // and 8 scale bytes per row.  The contraction order inside a step is
@@ -645,20 +646,29 @@ __global__ __launch_bounds__(CfgPP::THREADS, 1) void k_gemm_pp(Params p) {
 // per residual row, 128 bytes of gathered fp16 weight columns per weight row;
 // in group g, lane half h takes the 16 residual codes [32h + 16g, +16).
 // Stage k+2 is in flight while step k is computed; one barrier per step.
-// Every thread issues three DMA instructions per step in both segments, so
-// "all but the newest three" is the wait for the step about to be computed.
+// Every wave issues the same number of DMA instructions (P) per step in both
+// segments (a few duplicate loads write identical bytes to the same LDS words
+// to even the count), so "all but the newest P" is the wait for the step
+// about to be computed.
 namespace dmak {
 
-using C = Cfg<128, 128, 2, 2, 2>;  // per-group wave layout and epilogue mapping
 constexpr int kThreads = 512;
 constexpr int kStages = 3;
 constexpr int kStepM = 128;  // main-segment K step
 constexpr int kStepR = 64;   // residual-segment K step
-// Main stage layout (bytes): A codes [128][64], B codes [128][64], A scales [128][8], B scales [128][8].
-constexpr int kMA = 0, kMB = 8192, kMAS = 16384, kMBS = 17408;
-// Residual stage layout: R codes [128][32], R scales [128][4], gathered W [128][128 B].
-constexpr int kRA = 0, kRAS = 4096, kRB = 4608;
-constexpr int kStage = 20992;
+
+template <int NI_>
+struct Lay {
+  static constexpr int NI = NI_;
+  static constexpr int BM = 128, BN = 64 * NI;
+  using C = Cfg<BM, BN, 2, 2, NI == 2 ? 2 : 1>;  // per-group wave layout: tile_setup, w_row_of, epilogue
+  static constexpr int P = NI == 2 ? 3 : 4;  // DMA instructions per wave per step
+  // Main stage (bytes): A codes [128][64], B codes [BN][64], A scales [128][8], B scales [BN][8].
+  static constexpr int MA = 0, MB = 8192, MAS = MB + BN * 64, MBS = MAS + 1024, MEND = MBS + BN * 8;
+  // Residual stage: R codes [128][32], R scales [128][4], gathered W [BN][128 B].
+  static constexpr int RA = 0, RAS = 4096, RB = 4608, REND = RB + BN * 128;
+  static constexpr int STAGE = MEND > REND ? MEND : REND;
+};
 
 typedef __attribute__((address_space(3))) void lds_t;
 
@@ -680,10 +690,14 @@ __device__ __forceinline__ void dma(const void *g, uint8_t *lds_base, int bytes)
 }
 #pragma clang diagnostic pop
 
-// Wait until at most the newest 3 (resp. 0) vector-memory operations of this
-// wave are outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-__device__ __forceinline__ void wait_all_but_one_step() { __builtin_amdgcn_s_waitcnt(0x0F73); }
+// Wait until at most the newest P (resp. 0) vector-memory operations of this
+// wave are outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int P>
+__device__ __forceinline__ void wait_all_but_one_step() {
+  static_assert(P >= 0 && P < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | P);
+}
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier without a memory fence: __syncthreads() would also wait
@@ -710,78 +724,100 @@ __device__ __forceinline__ void scales2(uint32_t w, uint32_t sel, h2 (&s)[2]) {
   s[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, 1.0f, true);
 }
 
-__device__ __forceinline__ void mfma4(const uint4 (&a)[2], const uint4 (&b)[2], f32x16 (&acc)[2][2]) {
+template <int NI>
+__device__ __forceinline__ void mfmas(const uint4 (&a)[2], const uint4 (&b)[NI], f32x16 (&acc)[2][NI]) {
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, a[mi]), __builtin_bit_cast(h8, b[ni]),
                                                            acc[mi][ni], 0, 0, 0);
 }
 
-// Group g's half of one main step from stage `st`: 4 sub-steps of 4 MFMAs.
-__device__ __forceinline__ void compute_main(const uint8_t *st, f32x16 (&acc)[2][2], int wm, int wn, int g,
+// Group g's half of one main step from stage `st`: 4 sub-steps of 2*NI MFMAs.
+template <int NI>
+__device__ __forceinline__ void compute_main(const uint8_t *st, f32x16 (&acc)[2][NI], int wm, int wn, int g,
                                              int lane) {
+  using L = Lay<NI>;
   const int r = lane & 31, h = lane >> 5, c = 2 * g + h;
   const uint32_t sel = h ? 0x03030202u : 0x01010000u;  // blocks 4g+2h, 4g+2h+1 of the row's 8
-  uint4 ca[2], cb[2];
-  h2 sa[2][2], sb[2][2];
+  uint4 ca[2], cb[NI];
+  h2 sa[2][2], sb[NI][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int arow = wm * 64 + i * 32 + r, brow = wn * 64 + i * 32 + r;
-    scales2(*reinterpret_cast<const uint32_t *>(st + kMAS + arow * 8 + 4 * g), sel, sa[i]);
-    scales2(*reinterpret_cast<const uint32_t *>(st + kMBS + brow * 8 + 4 * g), sel, sb[i]);
-    ca[i] = *reinterpret_cast<const uint4 *>(st + kMA + arow * 64 + slot64(arow, c) * 16);
-    cb[i] = *reinterpret_cast<const uint4 *>(st + kMB + brow * 64 + slot64(brow, c) * 16);
+    const int row = wm * 64 + i * 32 + r;
+    scales2(*reinterpret_cast<const uint32_t *>(st + L::MAS + row * 8 + 4 * g), sel, sa[i]);
+    ca[i] = *reinterpret_cast<const uint4 *>(st + L::MA + row * 64 + slot64(row, c) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = wn * 32 * NI + i * 32 + r;
+    scales2(*reinterpret_cast<const uint32_t *>(st + L::MBS + row * 8 + 4 * g), sel, sb[i]);
+    cb[i] = *reinterpret_cast<const uint4 *>(st + L::MB + row * 64 + slot64(row, c) * 16);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint4 a[2], b[2];
+    uint4 a[2], b[NI];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t wa[4] = {ca[i].x, ca[i].y, ca[i].z, ca[i].w};
-      const uint32_t wb[4] = {cb[i].x, cb[i].y, cb[i].z, cb[i].w};
       a[i] = decode8_f16(wa[j], sa[i][j >> 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t wb[4] = {cb[i].x, cb[i].y, cb[i].z, cb[i].w};
       b[i] = decode8_f16(wb[j], sb[i][j >> 1]);
     }
-    mfma4(a, b, acc);
+    mfmas<NI>(a, b, acc);
   }
 }
 
 // Group g's half of one residual step: 2 sub-steps; A = residual codes, B =
 // gathered fp16 weight columns.
-__device__ __forceinline__ void compute_res(const uint8_t *st, f32x16 (&acc)[2][2], int wm, int wn, int g,
+template <int NI>
+__device__ __forceinline__ void compute_res(const uint8_t *st, f32x16 (&acc)[2][NI], int wm, int wn, int g,
                                             int lane) {
+  using L = Lay<NI>;
   const int r = lane & 31, h = lane >> 5;
   uint2 ca[2];
   h2 sa[2];
-  int brow[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + r;
-    brow[i] = wn * 64 + i * 32 + r;
-    ca[i] = *reinterpret_cast<const uint2 *>(st + kRA + row * 32 + slot32(row, h) * 16 + 8 * g);
-    sa[i] = scale_h2(st[kRAS + row * 4 + 2 * h + g]);
+    ca[i] = *reinterpret_cast<const uint2 *>(st + L::RA + row * 32 + slot32(row, h) * 16 + 8 * g);
+    sa[i] = scale_h2(st[L::RAS + row * 4 + 2 * h + g]);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    uint4 a[2], b[2];
+    uint4 a[2], b[NI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = decode8_f16(j ? ca[i].y : ca[i].x, sa[i]);
-      b[i] = *reinterpret_cast<const uint4 *>(st + kRB + brow[i] * 128 + slot128(brow[i], 4 * h + 2 * g + j) * 16);
+    for (int i = 0; i < 2; ++i) a[i] = decode8_f16(j ? ca[i].y : ca[i].x, sa[i]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = wn * 32 * NI + i * 32 + r;
+      b[i] = *reinterpret_cast<const uint4 *>(st + L::RB + row * 128 + slot128(row, 4 * h + 2 * g + j) * 16);
     }
-    mfma4(a, b, acc);
+    mfmas<NI>(a, b, acc);
   }
 }
+
+// One DMA instruction of a thread: source at step 0, bytes per step, LDS
+// offset inside a stage, bytes per lane.
+struct Dma {
+  const uint8_t *g;
+  int stride, lds, bytes;
+};
 
 }  // namespace dmak
 
 // K % 128 == 0 and (residual) kpad % 64 == 0 (host-checked).
-template <int EPI, bool HAS_RES>
-__global__ __launch_bounds__(dmak::kThreads, 2) void k_gemm_dma(Params p) {
+template <int NI, int EPI, bool HAS_RES>
+__global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Params p) {
   using namespace dmak;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
+  using L = Lay<NI>;
+  using C = typename L::C;
+  constexpr int P = L::P;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * L::STAGE];
   __shared__ int s_e, s_m0, s_mend;
   int nt, e, m0, mend;
   if (!tile_setup<C>(p, nt, e, m0, mend, s_e, s_m0, s_mend)) return;
@@ -797,112 +833,112 @@ __global__ __launch_bounds__(dmak::kThreads, 2) void k_gemm_dma(Params p) {
   auto w_row = [&](int r) -> int64_t { return static_cast<int64_t>(e) * p.N + w_row_of<C, EPI>(r, nt, p.N); };
   const int64_t K = p.K;
 
-  // Main-segment DMA sources (byte pointers at step 0).  Code loads: wave w
-  // fills 16-byte slots [64w, 64w+64), row slot/4.  Scale loads: waves 0-3
-  // the activation rows, waves 4-7 the weight rows, 2 lanes per row.
-  const uint8_t *ga, *gb, *gs;
-  {
-    const int pos = 64 * wave + lane, row = pos >> 2, c = slot64(row, pos & 3);
-    ga = p.x_codes + act_row(row) * (K / 2) + c * 16;
-    gb = p.w_codes + w_row(row) * (K / 2) + c * 16;
-    const int spos = 64 * wq + lane, srow = spos >> 1, half = spos & 1;
-    gs = (g == 0 ? p.x_scales + act_row(srow) * (K / 16) : p.w_scales + w_row(srow) * (K / 16)) + half * 4;
-  }
-  const int s_lds = (g == 0 ? kMAS : kMBS) + 256 * wq;
-  auto issue_main = [&](int kt, uint8_t *st) {
-    dma(ga + kt * 64, st + kMA + 1024 * wave, 16);
-    dma(gb + kt * 64, st + kMB + 1024 * wave, 16);
-    dma(gs + kt * 8, st + s_lds, 4);
+  // Wave-instructions of a segment are numbered 0..8P-1; wave w issues its P
+  // of them.  Code loads fill 64 16-byte slots per instruction (row = slot/4
+  // for 64-byte rows); scale loads fill 64 words (2 per 8-byte row).
+  auto code_a = [&](int n) -> Dma {  // activation codes, instruction n (0..7)
+    const int pos = 64 * n + lane, row = pos >> 2, c = slot64(row, pos & 3);
+    return {p.x_codes + act_row(row) * (K / 2) + c * 16, 64, L::MA + 1024 * n, 16};
   };
-
-  // Residual-segment DMA sources: waves 0-3 the residual codes (2 lanes per
-  // row), waves 4-5 the 4 residual scale bytes per row (waves 6-7 fetch the
-  // same rows into the same LDS words, identical bytes, which keeps three
-  // DMAs per thread), every wave 2 of the 16 loads of gathered weights.
-  const uint8_t *gr = nullptr;
-  const uint8_t *gw[2] = {nullptr, nullptr};
-  int r_lds = 0;
+  auto code_b = [&](int n) -> Dma {  // weight codes, instruction n (0..BN/16-1)
+    const int pos = 64 * n + lane, row = pos >> 2, c = slot64(row, pos & 3);
+    return {p.w_codes + w_row(row) * (K / 2) + c * 16, 64, L::MB + 1024 * n, 16};
+  };
+  auto scale_a = [&](int n) -> Dma {  // activation scales, instruction n (0..3)
+    const int pos = 64 * n + lane, row = pos >> 1, half = pos & 1;
+    return {p.x_scales + act_row(row) * (K / 16) + half * 4, 8, L::MAS + 256 * n, 4};
+  };
+  auto scale_b = [&](int n) -> Dma {  // weight scales, instruction n (0..BN/32-1)
+    const int pos = 64 * n + lane, row = pos >> 1, half = pos & 1;
+    return {p.w_scales + w_row(row) * (K / 16) + half * 4, 8, L::MBS + 256 * n, 4};
+  };
+  Dma dm[P];
+  dm[0] = code_a(wave);
+  dm[1] = code_b(wave);
+  if constexpr (NI == 2) {
+    dm[2] = g == 0 ? scale_a(wq) : scale_b(wq);
+  } else {  // 30 loads: waves 6-7 repeat two of the weight-scale loads
+    dm[2] = g == 0 ? code_b(8 + wq) : scale_b(wq);
+    dm[3] = g == 0 ? scale_a(wq) : scale_b(4 + (wq & 1));
+  }
+  Dma dr[P];
   if constexpr (HAS_RES) {
     const int64_t kp = p.kpad;
-    if (g == 0) {
-      const int pos = 64 * wq + lane, row = pos >> 1, c = slot32(row, pos & 1);
-      gr = p.r_codes + act_row(row) * (kp / 2) + c * 16;
-      r_lds = kRA + 1024 * wq;
-    } else {
-      gr = p.r_scales + act_row(64 * (wq & 1) + lane) * (kp / 16);
-      r_lds = kRAS + 256 * (wq & 1);
-    }
+    auto wcols = [&](int n) -> Dma {  // gathered fp16 weight columns, instruction n (0..BN/8-1)
+      const int pos = 64 * n + lane, row = pos >> 3, c = slot128(row, pos & 7);
+      return {reinterpret_cast<const uint8_t *>(p.wg_f16 + w_row(row) * kp) + c * 16, 128, L::RB + 1024 * n, 16};
+    };
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int pos = 64 * (8 * i + wave) + lane, row = pos >> 3, c = slot128(row, pos & 7);
-      gw[i] = reinterpret_cast<const uint8_t *>(p.wg_f16 + w_row(row) * kp) + c * 16;
+    for (int q = 0; q < P - 1; ++q) dr[q] = wcols(wave + 8 * q);
+    if (g == 0) {  // residual codes, 2 slots per 32-byte row
+      const int pos = 64 * wq + lane, row = pos >> 1, c = slot32(row, pos & 1);
+      dr[P - 1] = {p.r_codes + act_row(row) * (kp / 2) + c * 16, 32, L::RA + 1024 * wq, 16};
+    } else {  // residual scales, 4 bytes per row (waves 6-7 repeat waves 4-5)
+      dr[P - 1] = {p.r_scales + act_row(64 * (wq & 1) + lane) * (kp / 16), 4, L::RAS + 256 * (wq & 1), 4};
     }
   }
-  auto issue_res = [&](int kt, uint8_t *st) {
-    if (g == 0) dma(gr + kt * 32, st + r_lds, 16);
-    else dma(gr + kt * 4, st + r_lds, 4);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma(gw[i] + kt * 128, st + kRB + 1024 * (8 * i + wave), 16);
-  };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][NI];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
   const int nm = static_cast<int>(K / kStepM);
   const int nr = HAS_RES ? static_cast<int>(p.kpad / kStepR) : 0;
   const int total = nm + nr;
+  auto stage = [&](int k) { return lds + (k % kStages) * L::STAGE; };
   auto issue = [&](int k) {
-    uint8_t *st = lds + (k % kStages) * kStage;
-    if (k < nm) issue_main(k, st);
-    else issue_res(k - nm, st);
+    uint8_t *st = stage(k);
+    const Dma *d = k < nm ? dm : dr;
+    const int kk = k < nm ? k : k - nm;
+#pragma unroll
+    for (int q = 0; q < P; ++q) dma(d[q].g + static_cast<int64_t>(kk) * d[q].stride, st + d[q].lds, d[q].bytes);
   };
   issue(0);
   if (total > 1) issue(1);
   for (int k = 0; k < nm; ++k) {
-    if (k + 1 < total) wait_all_but_one_step(); else wait_all();
+    if (k + 1 < total) wait_all_but_one_step<P>(); else wait_all();
     barrier_no_fence();
     if (k + 2 < total) issue(k + 2);
-    compute_main(lds + (k % kStages) * kStage, acc, wm, wn, g, lane);
+    compute_main<NI>(stage(k), acc, wm, wn, g, lane);
   }
   if constexpr (HAS_RES) {
-    const float ratio = *p.x_g / *p.r_g;
+    const float ratio = *p.x_g / *p.r_g;  // the residual segment accumulates in units of g_r
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= ratio;
     for (int k = nm; k < total; ++k) {
-      if (k + 1 < total) wait_all_but_one_step(); else wait_all();
+      if (k + 1 < total) wait_all_but_one_step<P>(); else wait_all();
       barrier_no_fence();
       if (k + 2 < total) issue(k + 2);
-      compute_res(lds + (k % kStages) * kStage, acc, wm, wn, g, lane);
+      compute_res<NI>(stage(k), acc, wm, wn, g, lane);
     }
   }
 
   // Sum the groups' partial tiles: group 1 hands its accumulators to group 0
-  // through LDS, one 32 KiB half (mi) at a time, laid out [wave][ni][r][lane].
+  // through LDS, one half (mi) at a time, laid out [wave][ni][r][lane].
   float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
     __syncthreads();
     if (g == 1) {
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[((wq * 2 + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
+        for (int r = 0; r < 16; ++r) red[((wq * NI + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
     }
     __syncthreads();
     if (g == 0) {
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][ni][r] += red[((wq * 2 + ni) * 16 + r) * 64 + lane];
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] += red[((wq * NI + ni) * 16 + r) * 64 + lane];
     }
   }
   if (g == 0) epilogue<C, 0, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
@@ -1004,7 +1040,7 @@ using CfgW = Cfg<256, 256, 2, 2, 1>;  // large grouped shapes: 256 threads, 128x
 using CfgS8a = Cfg<128, 128, 4, 2, 2>;  // 512 threads, 32x64 wave tiles
 using CfgS8b = Cfg<128, 128, 2, 4, 2>;  // 512 threads, 64x32 wave tiles
 
-enum TileCfg { kS = 0, kM = 1, kL = 2, kW = 3, kP = 4, kS8a = 5, kS8b = 6, kD = 7 };
+enum TileCfg { kS = 0, kM = 1, kL = 2, kW = 3, kP = 4, kS8a = 5, kS8b = 6, kD = 7, kD3 = 8 };
 
 // The DMA-staged kernel's shape limits: NVFP4 operands, 128-element main
 // steps, 64-element residual steps.
@@ -1030,6 +1066,7 @@ TileCfg pick_cfg(const GemmLaunch &a) {
     if (strcmp(force, "128x128w8a") == 0) return kS8a;
     if (strcmp(force, "128x128w8b") == 0 && a.epilogue == 0) return kS8b;  // SwiGLU needs 2 tiles per wave
     if (strcmp(force, "128x128dma") == 0 && dma_fits(a)) return kD;
+    if (strcmp(force, "128x192dma") == 0 && dma_fits(a) && a.N % 192 == 0 && a.epilogue == 0) return kD3;
   }
   struct Cand {
     TileCfg c;
@@ -1063,7 +1100,9 @@ TileCfg pick_cfg(const GemmLaunch &a) {
 }
 
 int cfg_bm(TileCfg c) { return (c == kL || c == kW || c == kP) ? 256 : 128; }
-int cfg_bn(TileCfg c) { return (c == kL || c == kW || c == kP) ? 256 : (c == kM ? CfgM::BN : CfgS::BN); }
+int cfg_bn(TileCfg c) {
+  return (c == kL || c == kW || c == kP) ? 256 : ((c == kM || c == kD3) ? CfgM::BN : CfgS::BN);
+}
 
 template <class C, int MODE, int EPI, bool RES>
 void launch_k(const Params &p, int grid, hipStream_t s) {
@@ -1088,14 +1127,15 @@ void launch_pp_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStr
   }
 }
 
+template <int NI>
 void launch_dma(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t s) {
   const dim3 grid(g), block(dmak::kThreads);
   if (res) {
-    if (a.epilogue == 0) hipLaunchKernelGGL((k_gemm_dma<0, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_dma<1, true>), grid, block, 0, s, p);
+    if (a.epilogue == 0) hipLaunchKernelGGL((k_gemm_dma<NI, 0, true>), grid, block, 0, s, p);
+    else if constexpr (NI % 2 == 0) hipLaunchKernelGGL((k_gemm_dma<NI, 1, true>), grid, block, 0, s, p);
   } else {
-    if (a.epilogue == 0) hipLaunchKernelGGL((k_gemm_dma<0, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_dma<1, false>), grid, block, 0, s, p);
+    if (a.epilogue == 0) hipLaunchKernelGGL((k_gemm_dma<NI, 0, false>), grid, block, 0, s, p);
+    else if constexpr (NI % 2 == 0) hipLaunchKernelGGL((k_gemm_dma<NI, 1, false>), grid, block, 0, s, p);
   }
 }
 
@@ -1183,7 +1223,8 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   grid = (grid + 7) / 8 * 8;
   p.grid_per_xcd = static_cast<int>(grid / 8);
   const int g = static_cast<int>(grid);
-  if (c == kD) launch_dma(a, p, g, res, stream);
+  if (c == kD) launch_dma<2>(a, p, g, res, stream);
+  else if (c == kD3) launch_dma<3>(a, p, g, res, stream);
   else if (c == kP) launch_pp_cfg(a, p, g, res, stream);
   else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream);
   else if (c == kS8a) launch_cfg<CfgS8a>(a, p, g, res, stream);
