@@ -132,7 +132,7 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
 
 /* ---------------------------------------------------------------------------
  * quads_moe_w4a4_gemm -- token-permuted grouped expert GEMM with the RAC
- * segment (extended K), on bf16 MFMA with exact NVFP4 -> bf16 operand decode:
+ * segment (extended K), on fp16 MFMA with exact NVFP4 -> fp16 operand decode:
  *
  *   Y[i, n] = gw[e, seg(n)] * ( gx * sum_k W[e,n,k] X[t(i),k]
  *                             + gr * sum_j W[e,n,sel_j] R[t(i),j] )
