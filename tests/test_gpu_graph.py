@@ -70,3 +70,63 @@ def test_graph_replay_matches_eager(k):
         # eager work between replays: the same calls on other data, then back
         Q.quantize_nvfp4(other, want_scores=True)
         torch.cuda.synchronize()
+
+
+def test_graph_replay_decode_layer():
+    """The decode-shaped RAC layer (route, quantize + RAC of x, few-rows gate_up
+    with SwiGLU and its dense-residual prepare, quantize + RAC of h, down,
+    combine) captured in one graph: every replay gives the eager output bit
+    for bit, with eager work between replays."""
+    wl = S.moe_decode()
+    T, H = wl.x.f32.shape
+    E, N2, _ = wl.w_gate_up.f32.shape
+    I = N2 // 2
+    k = wl.k_percent
+    log(f"[graph] decode layer T={T} E={E} H={H} I={I} k={k}")
+    x = dev_act(wl.x)
+    logits = torch.from_numpy(wl.logits).cuda()
+    guc, gus, gug = quantize_weights_gpu(dev_act(wl.w_gate_up), 2)
+    dnc, dns, dng = quantize_weights_gpu(dev_act(wl.w_down), 1)
+    rc = Q.RouteCall(logits, wl.top)
+    ids, w, offs, rt, inv = rc()
+    R = T * wl.top
+    qx = Q.QuantizeCall(x, want_scores=True)
+    xq, xs = qx()
+    sx = Q.SelectCall(x, xq, xs, k)
+    xsel, xres, _ = sx()
+    g1 = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
+                    x=xq, res=xres, sel_idx=xsel, row_token=rt, epilogue=Q.EPI_SWIGLU)
+    g1()
+    qh = Q.QuantizeCall(g1.y, want_scores=True)
+    hq, hs = qh()
+    sh = Q.SelectCall(g1.y, hq, hs, k)
+    hsel, hres, _ = sh()
+    g2 = Q.GemmCall(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs, num_rows=R,
+                    x=hq, res=hres, sel_idx=hsel)
+    g2()
+    cc = Q.CombineCall(g2.y, inv, w)
+    out = cc()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert torch.isfinite(eager).all()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rc()
+        qx()
+        sx()
+        g1()
+        qh()
+        sh()
+        g2()
+        cc()
+    other = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+    for rep in range(3):
+        for t in (g1.y, g2.y, cc.out):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cc.out.view(torch.int32), eager.view(torch.int32)), rep
+        Q.quantize_nvfp4(other, want_scores=True)
+        torch.cuda.synchronize()
