@@ -480,3 +480,49 @@ def moe_layer(x, logits, w_gu_exact, w_down_exact, k_percent, top=8):
     out = combine(dn["y"], inv, wts)
     return dict(ids=ids, weights=wts, offsets=offs, row_token=rt, inverse=inv,
                 gate_up=gu, h=h, h_bf16=h_bf16, down=dn, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Ablation variants ([Gist §2.1], [Gist §4] "Ablatie studies")
+# ---------------------------------------------------------------------------
+
+def fake_quant_activation(x):
+    """Symmetric W4A4 QAT's trainer-side activation: the same NVFP4
+    quantize-dequantize as the weights, applied to the activation tensor (one
+    tensor scale for the whole tensor), rounded to bf16.  [Gist §2.1] names
+    this scheme (weights and activations fake-quantized on the trainer) and
+    [Gist §4] compares it with the asymmetric W4A16 scheme.  Returns bf16 bits
+    [rows, cols]."""
+    return weight_qdq(x)[0]
+
+
+def rac_linear_per_expert(x, w_exact, k_percent, expert_offsets):
+    """RAC with one channel mask per expert instead of one per input tensor.
+
+    Rows of x are grouped by expert (row i belongs to expert e for
+    offsets[e] <= i < offsets[e+1]).  The activation is quantized once with
+    its tensor scale g; each expert then scores the channels over its own rows
+    only, selects its top k% and quantizes its own residual with its own
+    residual tensor scale.  Y rows are the expert's W4A4 + RAC product.
+    Returns dict(q=global NVFP4, experts=[per-expert dict or None], y)."""
+    x = np.asarray(x, dtype=np.float32)
+    offs = np.asarray(expert_offsets)
+    q = quantize_nvfp4(x)
+    E = w_exact.shape[0]
+    y = np.zeros((x.shape[0], w_exact.shape[1]), np.float64)
+    experts = []
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            experts.append(None)
+            continue
+        xe = x[a:b]
+        qe = quantize_nvfp4(xe, q.g)  # row blocks: the same codes as q's rows a..b
+        scores = rac_scores(xe, qe)
+        sel, nsel = rac_select(scores, k_percent)
+        r = rac_quantize_residual(xe, qe, sel, nsel)
+        xq = dequant_exact(qe.codes, qe.scales, qe.g)
+        rq = dequant_exact(r.codes, r.scales, r.g) if sel.size else None
+        y[a:b] = gemm_ref(xq, w_exact[e], rq, sel if nsel else None)
+        experts.append(dict(q=qe, scores=scores, sel=sel, nsel=nsel, r=r))
+    return dict(q=q, experts=experts, y=y)
