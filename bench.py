@@ -18,6 +18,12 @@ synthetic, seeded input already resident in HBM:
   moe_decode: the same layer at 256 tokens, 128 experts, intermediate 1024.
   trainer_qdq: per layer, NVFP4 QDQ of 128 experts x (gate, up, down) bf16
       master weights, then the bf16 grouped forward on 8192 tokens.
+  ablation: not a throughput run.  Output error of every trainer and rollout
+      variant (bf16, asymmetric W4A16, symmetric W4A4 QAT, W4A4, RAC with one
+      mask per tensor or per expert) against the float64 product of the
+      masters, and the trainer/rollout output mismatch with a drifted rollout
+      activation, on the expert-GEMM shape and on the decode-shaped down
+      projection (128 experts, routed rows of 256 tokens x top-8, 1024 -> 2048).
 
 `value` is tokens per second of the whole step; `roofline` describes the
 dominant kernel (its average duration from HIP events recorded on the
@@ -49,7 +55,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="expert_gemm",
-                    choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq"])
+                    choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq", "ablation"])
     ap.add_argument("--k", type=int, default=50, help="RAC k percent")
     ap.add_argument("--layers", type=int, default=48, help="trainer_qdq: layers per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -214,6 +220,39 @@ def setup_trainer(Q, S, layers):
                 qdq_bytes_layer=qdq_bytes_layer, layer0_stages=[st for st in stages if st[0].startswith(("route", "L0."))])
 
 
+def run_ablation(Q, S):
+    """The ablation report (one JSON line): errors vs float64 and
+    trainer/rollout mismatches for two seeded layers."""
+    import torch
+    from fp4_quantized_moe_amd import ablation as A
+    rng = np.random.default_rng(7)
+    layers = {}
+    wl = S.expert_gemm()
+    dense = (_dev(wl.x), _dev(wl.w)[None], [0, wl.x.f32.shape[0]], S.drifted(rng, wl.x))
+    dec = S.moe_decode()
+    _, _, offs, _, _ = Q.moe_route(torch.from_numpy(dec.logits).cuda(), dec.top)
+    offs = [int(v) for v in offs.cpu().numpy()]
+    R, I = offs[-1], dec.w_down.f32.shape[2]
+    h = S.activation(rng, R, I, I // 100, 30.0, bf16=True)
+    down = (_dev(h), _dev(dec.w_down), offs, S.drifted(rng, h))
+    pairs = [("w4a4", "w4a16"), ("rac25", "w4a16"), ("rac50", "w4a16"), ("rac100", "w4a16"),
+             ("rac50_pe", "w4a16"), ("w4a4", "w4a4_sym"), ("rac50", "w4a4_sym")]
+    for name, (x, w, o, xd) in (("expert_gemm", dense), ("decode_down", down)):
+        out = A.grouped_linear_variants(x, w, o)
+        err = A.errors(out, A.reference_fp64(x, w, o))
+        drift = A.grouped_linear_variants(x, w, o, x_rollout=_dev(xd))
+        layers[name] = {"rows": o[-1], "experts": len(o) - 1, "N": w.shape[1], "K": w.shape[2],
+                        "error_vs_fp64": err, "mismatch": A.mismatch(out, pairs),
+                        "mismatch_with_drift": A.mismatch(drift, pairs)}
+    print(json.dumps({
+        "metric": "QUADS ablation: relative output error vs the float64 master product (RAC k=50%, decode-shaped down projection)",
+        "value": layers["decode_down"]["error_vs_fp64"]["rac50"]["rel_fro"], "unit": "relative Frobenius error",
+        "higher_is_better": False, "n_gpus": 1, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "ablation", "drift": "rollout activation = bf16(x * (1 + e)), e ~ N(0, 2^-9)",
+                   "down_input": "bf16 N(0,1) rows with 1% outlier channels x30 over the decode routing"},
+        "layers": layers}), flush=True)
+
+
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
@@ -326,6 +365,9 @@ def main():
 
     torch.cuda.set_device(0)
     Q.load()
+    if args.workload == "ablation":
+        run_ablation(Q, S)
+        return
     if args.workload == "expert_gemm":
         wl = setup_expert_gemm(Q, S, args.k)
     elif args.workload in ("moe_prefill", "moe_decode"):

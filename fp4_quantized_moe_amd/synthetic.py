@@ -75,6 +75,16 @@ def weights(rng, shape, std=0.02, bf16=True):
     return Activation(w, None)
 
 
+def drifted(rng, act, rel_std=2.0 ** -9):
+    """A second copy of a bf16 activation that differs from it by engine
+    drift: each element is multiplied by (1 + e) with e ~ N(0, rel_std) and
+    rounded to bf16 again (about one bf16 rounding step of noise at the
+    default)."""
+    e = _normal(rng, act.f32.shape, rel_std)
+    bits, vals = to_bf16(act.f32 * (np.float32(1.0) + e))
+    return Activation(vals, bits)
+
+
 def zipf_logits(rng, tokens, experts, s=1.1):
     """Logits log p_Zipf(s)[rank(e)] + Gumbel(0,1) noise; ranks are a seeded
     permutation of the experts.  Top-k of these is sampling without
