@@ -526,3 +526,42 @@ def rac_linear_per_expert(x, w_exact, k_percent, expert_offsets):
         y[a:b] = gemm_ref(xq, w_exact[e], rq, sel if nsel else None)
         experts.append(dict(q=qe, scores=scores, sel=sel, nsel=nsel, r=r))
     return dict(q=q, experts=experts, y=y)
+
+
+# ---------------------------------------------------------------------------
+# W4A16 QAT backward of a grouped linear ([Gist §2.2-A])
+# ---------------------------------------------------------------------------
+
+def qat_linear_backward(x, w_master, dy, row_token=None, expert_offsets=None):
+    """Backward of y[i] = W_qdq[e(i)] · x[t(i)] with the straight-through
+    estimator through the weight QDQ.
+
+    [Gist §2.2-A]: every forward sees the discretized weights while the
+    optimizer updates the bf16 masters; the gradient reaches the masters
+    unchanged through the QDQ (the straight-through reading).
+    - dX: per routed row i, dxr[i] = dy[i] · W_qdq[e(i)]; each token sums
+      the rows that read it: dx[t] = sum over {i : t(i) = t} of dxr[i].
+    - dW: dW_master[e] = dW_qdq[e] = sum over the expert's rows i of
+      dy[i]^T x[t(i)].
+    x [A, K], w_master [E, N, K] float32 (bf16 values), dy [R, N]; float64
+    products.  Returns dict(w_qdq float64 [E,N,K], dxr [R,K], dx [A,K],
+    dw [E,N,K])."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    w_master = np.asarray(w_master, dtype=np.float32)
+    E, N, K = w_master.shape
+    R = dy.shape[0]
+    rt = np.arange(R) if row_token is None else np.asarray(row_token)
+    offs = np.array([0, R]) if expert_offsets is None else np.asarray(expert_offsets)
+    w_qdq = np.stack([f32_from_bf16_bits(weight_qdq(w_master[e])[0]) for e in range(E)]).astype(np.float64)
+    dxr = np.zeros((R, K), np.float64)
+    dw = np.zeros((E, N, K), np.float64)
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        dxr[a:b] = dy[a:b] @ w_qdq[e]
+        dw[e] = dy[a:b].T @ x[rt[a:b]]
+    dx = np.zeros_like(x)
+    np.add.at(dx, rt, dxr)
+    return dict(w_qdq=w_qdq, dxr=dxr, dx=dx, dw=dw)
