@@ -18,6 +18,10 @@ synthetic, seeded input already resident in HBM:
   moe_decode: the same layer at 256 tokens, 128 experts, intermediate 1024.
   trainer_qdq: per layer, NVFP4 QDQ of 128 experts x (gate, up, down) bf16
       master weights, then the bf16 grouped forward on 8192 tokens.
+  trainer_bwd: one layer's W4A16 QAT backward at the trainer shape (8192
+      tokens, 128 experts, top-8, gate_up 2048 -> 2048, down 1024 -> 2048):
+      per projection, transpose of W_qdq, dX grouped GEMM (+ per-token sum for
+      gate_up) and the dW grouped GEMM (FP32), from synthetic output gradients.
   ablation: not a throughput run.  Output error of every trainer and rollout
       variant (bf16, asymmetric W4A16, symmetric W4A4 QAT, W4A4, RAC with one
       mask per tensor or per expert) against the float64 product of the
@@ -55,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="expert_gemm",
-                    choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq", "ablation"])
+                    choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq", "trainer_bwd", "ablation"])
     ap.add_argument("--k", type=int, default=50, help="RAC k percent")
     ap.add_argument("--layers", type=int, default=48, help="trainer_qdq: layers per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -220,6 +224,58 @@ def setup_trainer(Q, S, layers):
                 qdq_bytes_layer=qdq_bytes_layer, layer0_stages=[st for st in stages if st[0].startswith(("route", "L0."))])
 
 
+def setup_trainer_bwd(Q, S):
+    """Backward of one trainer layer's two grouped projections (W4A16 QAT,
+    straight-through QDQ), with seeded synthetic upstream gradients."""
+    import torch
+    T, H, E, I, top = 8192, 2048, 128, 1024, 8
+    rng = np.random.default_rng(6)
+    x = _dev(S.activation(rng, T, H, 0, 1.0, bf16=True))
+    logits = torch.from_numpy(S.gaussian_logits(rng, T, E)).cuda()
+    gu_m, dn_m = S.trainer_layer_weights_device(6, 0, E, H, I)
+    wq_gu, _ = Q.QdqCall(gu_m)()
+    wq_dn, _ = Q.QdqCall(dn_m)()
+    _, _, offs, rt, inv = Q.moe_route(logits, top)
+    R = T * top
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    dy_gu = torch.randn((R, 2 * I), generator=gen, device="cuda").to(torch.bfloat16)
+    dy_dn = torch.randn((R, H), generator=gen, device="cuda").to(torch.bfloat16)
+    h = torch.randn((R, I), generator=gen, device="cuda").to(torch.bfloat16)
+    bgu = Q.QatBackward(wq_gu.view(E, 2 * I, H), dy_gu, x, offs, rt, inv)
+    bdn = Q.QatBackward(wq_dn, dy_dn, h, offs)
+    stages = [(f"gate_up.{n}", f) for n, f in bgu.stages()] + [(f"down.{n}", f) for n, f in bdn.stages()]
+    flops = 2.0 * 2.0 * R * (2 * I) * H + 2.0 * 2.0 * R * H * I  # dX and dW of both projections
+    cfg = {"workload": "trainer_bwd", "tokens": T, "hidden": H, "experts": E, "top": top, "intermediate": I,
+           "note": "W4A16 QAT backward of gate_up and down (straight-through QDQ): dX and FP32 dW; synthetic dY"}
+
+    def cpu_baseline():
+        """The oracle's backward (QDQ of the expert's masters, dX, dW in
+        float64) of gate_up for whole experts, repeated until
+        CPU_BASELINE_MIN_S; converted to tokens/s of the full step by flops."""
+        from oracle import quads_oracle as O
+        ho, hrt = offs.cpu().numpy(), rt.cpu().numpy()
+        xs = x.float().cpu().numpy()
+        reps, fl, t0 = 0, 0.0, time.perf_counter()
+        while True:
+            e = reps % E
+            a, b = int(ho[e]), int(ho[e + 1])
+            w = gu_m[2 * e:2 * e + 2].float().cpu().numpy().reshape(1, 2 * I, H)
+            O.qat_linear_backward(xs, w, dy_gu[a:b].float().cpu().numpy(), hrt[a:b], np.array([0, b - a]))
+            fl += 2.0 * 2.0 * (b - a) * (2 * I) * H
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= CPU_BASELINE_MIN_S:
+                break
+        return T * (fl / flops) / secs, secs, (f"oracle gate_up backward of {reps} whole experts (weight QDQ, dX, dW "
+                                               "in float64), scaled to the full step by flops")
+
+    return dict(stages=stages, plain=None, tokens=T, flops=flops, dominant="gate_up.wgrad",
+                dominant_flops=2.0 * R * (2 * I) * H,
+                dominant_kernel="gate_up dW: k_pad_map + 2 gather-transposes + k_wgrad (bf16 MFMA, FP32 dW)",
+                config=cfg, cpu_baseline=cpu_baseline)
+
+
 def run_ablation(Q, S):
     """The ablation report (one JSON line): errors vs float64 and
     trainer/rollout mismatches for two seeded layers."""
@@ -370,6 +426,8 @@ def main():
         return
     if args.workload == "expert_gemm":
         wl = setup_expert_gemm(Q, S, args.k)
+    elif args.workload == "trainer_bwd":
+        wl = setup_trainer_bwd(Q, S)
     elif args.workload in ("moe_prefill", "moe_decode"):
         wl = setup_moe(Q, S, args.k, args.workload == "moe_decode")
     else:

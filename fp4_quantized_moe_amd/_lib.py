@@ -54,6 +54,7 @@ EXPORTS = [
     "quads_moe_gemm_workspace_bytes", "quads_moe_w4a4_gemm", "quads_moe_gemm_prepare",
     "quads_weight_qdq_workspace_bytes", "quads_weight_qdq",
     "quads_moe_route_workspace_bytes", "quads_moe_route", "quads_moe_combine",
+    "quads_moe_wgrad_workspace_bytes", "quads_moe_wgrad_bf16", "quads_transpose_bf16",
 ]
 
 _lib = None
@@ -99,6 +100,13 @@ def load(path: str = LIB_PATH):
     L.quads_moe_route.argtypes = [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.quads_moe_combine.restype = ctypes.c_int
     L.quads_moe_combine.argtypes = [_vp, _c_i64, _c_i32, _c_i64, _vp, _vp, _vp, _vp]
+    L.quads_moe_wgrad_workspace_bytes.restype = ctypes.c_size_t
+    L.quads_moe_wgrad_workspace_bytes.argtypes = [_c_i64, _c_i32, _c_i64, _c_i64]
+    L.quads_moe_wgrad_bf16.restype = ctypes.c_int
+    L.quads_moe_wgrad_bf16.argtypes = [_vp, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+    L.quads_transpose_bf16.restype = ctypes.c_int
+    L.quads_transpose_bf16.argtypes = [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp]
     _lib = L
     return L
 
@@ -412,3 +420,80 @@ def moe_combine(y: torch.Tensor, inverse: torch.Tensor, topk_w: torch.Tensor):
     _check(L.quads_moe_combine(_ptr(y), T, top, N, _ptr(inverse), _ptr(topk_w), _ptr(out), _stream()),
            "quads_moe_combine")
     return out
+
+
+def transpose_bf16(x: torch.Tensor, out: torch.Tensor | None = None):
+    """quads_transpose_bf16: bf16 [rows, cols] or [batch, rows, cols] -> the
+    transposed matrices [.., cols, rows]."""
+    _require_cuda(x)
+    if x.dtype != torch.bfloat16:
+        raise QuadsError("transpose_bf16 expects bf16")
+    batch, rows, cols = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+    if out is None:
+        out = torch.empty(*x.shape[:-2], cols, rows, dtype=torch.bfloat16, device=x.device)
+    _check(load().quads_transpose_bf16(_ptr(x), batch, rows, cols, _ptr(out), _stream()), "quads_transpose_bf16")
+    return out
+
+
+class WgradCall:
+    """quads_moe_wgrad_bf16 with dw and the workspace allocated once:
+    dw[e] = sum over the expert's routed rows i of dy[i]^T x[t(i)] (FP32)."""
+
+    def __init__(self, dy: torch.Tensor, x: torch.Tensor, expert_offsets: torch.Tensor,
+                 row_token: torch.Tensor | None = None, dw: torch.Tensor | None = None):
+        L = load()
+        _require_cuda(dy, x, expert_offsets, row_token, dw)
+        if dy.dtype != torch.bfloat16 or x.dtype != torch.bfloat16:
+            raise QuadsError("wgrad expects bf16 dy and x")
+        self.R, self.N = dy.shape
+        self.A, self.K = x.shape
+        self.E = int(expert_offsets.numel()) - 1
+        self.dy, self.x, self.offs, self.rt = dy, x, expert_offsets, row_token
+        self.dw = torch.empty(self.E, self.N, self.K, dtype=torch.float32, device=dy.device) if dw is None else dw
+        self.ws = _workspace(L.quads_moe_wgrad_workspace_bytes(self.R, self.E, self.N, self.K), dy.device)
+
+    def __call__(self):
+        _check(load().quads_moe_wgrad_bf16(_ptr(self.dy), _ptr(self.x), _ptr(self.rt), _ptr(self.offs), self.E,
+                                           self.R, self.A, self.N, self.K, _ptr(self.dw), _ptr(self.ws),
+                                           self.ws.numel(), _stream()), "quads_moe_wgrad_bf16")
+        return self.dw
+
+
+class QatBackward:
+    """W4A16 QAT backward of the grouped linear y[i] = W_qdq[e(i)] . x[t(i)]
+    (straight-through QDQ), composed of library calls:
+      transpose W_qdq [E, N, K] -> [E, K, N];
+      dxr = bf16-operand grouped GEMM of dy over W_qdq^T  (FP32 [R, K]);
+      dx  = per-token sum of its routed rows (combine with unit weights),
+            or dxr itself when rows are not gathered (row_token None);
+      dw  = quads_moe_wgrad_bf16 (FP32 [E, N, K]).
+    `inverse` [T, top] is the routed row of each (token, slot), needed with
+    row_token."""
+
+    def __init__(self, w_qdq: torch.Tensor, dy: torch.Tensor, x: torch.Tensor, expert_offsets: torch.Tensor,
+                 row_token: torch.Tensor | None = None, inverse: torch.Tensor | None = None):
+        E, N, K = w_qdq.shape
+        self.w_qdq = w_qdq
+        self.wt = torch.empty(E, K, N, dtype=torch.bfloat16, device=w_qdq.device)
+        R = dy.shape[0]
+        self.dxr_call = GemmCall(N=K, K=N, expert_offsets=expert_offsets, num_rows=R, x_bf16=dy, w_bf16=self.wt)
+        self.combine = None
+        if row_token is not None:
+            if inverse is None:
+                raise QuadsError("QatBackward: inverse is required with row_token")
+            ones = torch.ones(inverse.shape, dtype=torch.float32, device=dy.device)
+            self.combine = CombineCall(self.dxr_call.y, inverse, ones)
+        self.wgrad = WgradCall(dy, x, expert_offsets, row_token)
+
+    def stages(self):
+        st = [("transpose_w", lambda: transpose_bf16(self.w_qdq, self.wt)), ("dx_gemm", self.dxr_call)]
+        if self.combine is not None:
+            st.append(("dx_token_sum", self.combine))
+        st.append(("wgrad", self.wgrad))
+        return st
+
+    def __call__(self):
+        for _, fn in self.stages():
+            fn()
+        dx = self.combine.out if self.combine is not None else self.dxr_call.y
+        return dx, self.dxr_call.y, self.wgrad.dw

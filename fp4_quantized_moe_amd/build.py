@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libquads.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "quantize.hip", "rac.hip", "gemm.hip", "gemm_small.hip", "route.hip"]
+SOURCES = ["api.hip", "quantize.hip", "rac.hip", "gemm.hip", "gemm_small.hip", "route.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

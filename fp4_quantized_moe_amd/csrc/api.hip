@@ -312,4 +312,53 @@ quads_status_t quads_moe_combine(const float *y, int64_t T, int32_t top, int64_t
                        "combine");
 }
 
+size_t quads_moe_wgrad_workspace_bytes(int64_t num_rows, int32_t num_experts, int64_t N, int64_t K) {
+  if (num_rows < 0 || num_experts < 1 || num_experts > 1024 || N <= 0 || K <= 0) return 0;
+  return quads::wgrad_ws_bytes(num_rows, num_experts, N, K);
+}
+
+quads_status_t quads_moe_wgrad_bf16(const void *dy_bf16, const void *x_bf16, const int32_t *row_token,
+                                    const int32_t *expert_offsets, int32_t num_experts, int64_t num_rows,
+                                    int64_t act_rows, int64_t N, int64_t K, float *dw, void *ws, size_t ws_bytes,
+                                    void *stream) {
+  if (num_experts < 1 || num_experts > 1024) return fail(QUADS_ERR_SHAPE, "wgrad: num_experts outside [1,1024]");
+  if (N <= 0 || K <= 0 || N % 128 || K % 128) return fail(QUADS_ERR_SHAPE, "wgrad: N and K must be positive multiples of 128");
+  if (num_rows < 0 || act_rows < 0 || num_rows + 63 * int64_t(num_experts) > (int64_t(1) << 31) - 64)
+    return fail(QUADS_ERR_SHAPE, "wgrad: row counts out of range");
+  if (!mul_ok(int64_t(num_experts) * N, K, kMaxElems) || !mul_ok(num_rows + 64 * int64_t(num_experts), N + K, kMaxElems))
+    return fail(QUADS_ERR_SHAPE, "wgrad: size overflow");
+  if (row_token == nullptr && act_rows < num_rows)
+    return fail(QUADS_ERR_SHAPE, "wgrad: identity rows need act_rows >= num_rows");
+  if (!expert_offsets || !dw || (num_rows > 0 && (!dy_bf16 || !x_bf16))) return fail(QUADS_ERR_ARG, "wgrad: null pointer");
+  if (misaligned({dy_bf16, x_bf16, dw, ws})) return fail(QUADS_ERR_ARG, "wgrad: arrays must be 16-byte aligned");
+  const size_t need = quads::wgrad_ws_bytes(num_rows, num_experts, N, K);
+  if (ws == nullptr || ws_bytes < need) return fail(QUADS_ERR_WORKSPACE, "wgrad: workspace too small (need %zu)", need);
+  quads::WgradLaunch a{};
+  a.dy = static_cast<const uint16_t *>(dy_bf16);
+  a.x = static_cast<const uint16_t *>(x_bf16);
+  a.row_token = row_token;
+  a.expert_offsets = expert_offsets;
+  a.E = num_experts;
+  a.R = num_rows;
+  a.N = N;
+  a.K = K;
+  a.dw = dw;
+  a.ws = ws;
+  return device_status(quads::launch_wgrad(a, static_cast<hipStream_t>(stream)), "wgrad");
+}
+
+quads_status_t quads_transpose_bf16(const void *in_bf16, int64_t batch, int64_t rows, int64_t cols, void *out_bf16,
+                                    void *stream) {
+  if (batch < 0 || batch > 65535 || rows < 0 || cols < 0 || rows % 8 || cols % 8)
+    return fail(QUADS_ERR_SHAPE, "transpose: rows and cols must be multiples of 8, batch <= 65535");
+  if (!mul_ok(rows, cols, kMaxElems) || !mul_ok(batch, rows * cols, kMaxElems) || cols / 64 >= 65535)
+    return fail(QUADS_ERR_SHAPE, "transpose: size overflow");
+  if (batch * rows * cols == 0) return ok();
+  if (!in_bf16 || !out_bf16) return fail(QUADS_ERR_ARG, "transpose: null pointer");
+  if (misaligned({in_bf16, out_bf16})) return fail(QUADS_ERR_ARG, "transpose: arrays must be 16-byte aligned");
+  return device_status(quads::launch_transpose_bf16(static_cast<const uint16_t *>(in_bf16), batch, rows, cols,
+                                                    static_cast<uint16_t *>(out_bf16), static_cast<hipStream_t>(stream)),
+                       "transpose");
+}
+
 }  // extern "C"

@@ -81,4 +81,20 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t 
 hipError_t launch_combine(const float *y, int64_t T, int top, int64_t N, const int32_t *inverse,
                           const float *w, float *out, hipStream_t stream);
 
+// ---- backward.hip ----------------------------------------------------------
+struct WgradLaunch {
+  const uint16_t *dy;  // [R, N] bf16, routed rows grouped by expert
+  const uint16_t *x;   // [act_rows, K] bf16
+  const int32_t *row_token, *expert_offsets;
+  int E;
+  int64_t R, N, K;
+  float *dw;  // [E, N, K]
+  void *ws;
+};
+int64_t wgrad_padded_cols(int64_t R, int E);
+size_t wgrad_ws_bytes(int64_t R, int E, int64_t N, int64_t K);
+hipError_t launch_wgrad(const WgradLaunch &a, hipStream_t stream);
+hipError_t launch_transpose_bf16(const uint16_t *in, int64_t batch, int64_t rows, int64_t cols, uint16_t *out,
+                                 hipStream_t stream);
+
 }  // namespace quads

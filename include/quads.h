@@ -254,6 +254,38 @@ quads_status_t quads_moe_combine(const float *y, int64_t T, int32_t top, int64_t
                                  const int32_t *inverse, const float *topk_w, float *out,
                                  void *stream);
 
+/* ---------------------------------------------------------------------------
+ * W4A16 QAT backward of the grouped expert linear y[i] = W_qdq[e(i)] . x[t(i)]
+ * [Gist 2.2-A]: the trainer's forward sees the NVFP4 fake-quantized weights
+ * W_qdq (quads_weight_qdq) while the optimizer updates the bf16 masters, so
+ * the gradient passes the QDQ unchanged (straight-through reading).
+ *
+ * quads_moe_wgrad_bf16: dw[e, n, k] = sum over the expert's routed rows i of
+ * dy[i, n] * x[t(i), k], FP32 [E, N, K] (= the master gradient).  dy [R, N]
+ * bf16 with rows grouped by expert_offsets [E+1] (device; offsets[E] == R);
+ * x [act_rows, K] bf16 read at row_token[i] (NULL: row i).  An expert with no
+ * rows gets a zero gradient.  N and K are multiples of 128, E <= 1024.  The
+ * workspace (quads_moe_wgrad_workspace_bytes) holds dy and the gathered x
+ * transposed, each expert's rows padded to a multiple of 64: about
+ * 2 * (N + K) * (R + 63 E) bytes.  Arrays 16-byte aligned; errors as above.
+ *
+ * The input gradient dxr[i] = dy[i] . W_qdq[e(i)] is quads_moe_w4a4_gemm in
+ * bf16-operand mode over W_qdq^T: quads_transpose_bf16(W_qdq, E, N, K, WT)
+ * gives WT [E, K, N], and the GEMM with x_bf16 = dy (act_rows = R, identity
+ * rows), w_bf16 = WT, N' = K, K' = N writes dxr [R, K].  Tokens read by
+ * several routed rows sum theirs: quads_moe_combine with unit weights.
+ *
+ * quads_transpose_bf16: out[b] = in[b]^T for `batch` bf16 matrices
+ * [rows, cols] -> [cols, rows]; rows and cols multiples of 8.
+ * ------------------------------------------------------------------------- */
+size_t quads_moe_wgrad_workspace_bytes(int64_t num_rows, int32_t num_experts, int64_t N, int64_t K);
+quads_status_t quads_moe_wgrad_bf16(const void *dy_bf16, const void *x_bf16, const int32_t *row_token,
+                                    const int32_t *expert_offsets, int32_t num_experts, int64_t num_rows,
+                                    int64_t act_rows, int64_t N, int64_t K, float *dw, void *ws,
+                                    size_t ws_bytes, void *stream);
+quads_status_t quads_transpose_bf16(const void *in_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                    void *out_bf16, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
