@@ -97,16 +97,32 @@ __device__ __forceinline__ uint32_t block_count_ge(const Keys<PER> &ks, uint32_t
 // Writes the nsel selected channel indices (largest scores first by value,
 // ties to the lower index) in ascending order to sel[0..nsel).  Keys are the
 // FP32 score bit patterns: non-negative, so below 2^31 and ordered like the
-// scores.  The nsel-th largest key T is built bit by bit from the top: a bit
-// stays set when at least nsel keys are >= the candidate.
+// scores.  A threshold T is built bit by bit from the top: a bit stays set
+// when at least nsel keys are >= the candidate.  Two exact shortcuts:
+//  - every real key lies in [lo, hi], so the nsel-th largest does too, and it
+//    shares the bits above the highest bit in which lo and hi differ; the
+//    search starts below them;
+//  - once exactly nsel keys are >= T, the set {keys >= T} is the selection
+//    and the remaining bits cannot change it, so the search stops there.
+//    The tie handling below then keeps every key equal to T.
+// n_total is the number of keys >= any T <= lo: the K real keys, plus the
+// zero padding keys when T is 0.
 template <int PER>
-__device__ void block_select(const Keys<PER> &ks, int nsel, uint32_t *slots, int32_t *sel) {
+__device__ void block_select(const Keys<PER> &ks, int nsel, uint32_t lo, uint32_t hi, int K, uint32_t *slots,
+                             int32_t *sel) {
   const int c0 = threadIdx.x * PER;
-  uint32_t T = 0;
+  const uint32_t diff = lo ^ hi;
+  const int top = diff ? 31 - __builtin_clz(diff) : -1;  // keys < 2^31, so top <= 30
+  uint32_t T = top >= 0 ? hi & ~((2u << top) - 1u) : hi;
+  uint32_t cur = T > 0 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(kThreads * PER);
   int buf = 0;
-  for (int bit = 30; bit >= 0; --bit) {
+  for (int bit = top; bit >= 0 && cur != static_cast<uint32_t>(nsel); --bit) {
     const uint32_t cand = T | (1u << bit);
-    if (block_count_ge(ks, cand, slots + buf * (kThreads / 64)) >= static_cast<uint32_t>(nsel)) T = cand;
+    const uint32_t n = block_count_ge(ks, cand, slots + buf * (kThreads / 64));
+    if (n >= static_cast<uint32_t>(nsel)) {
+      T = cand;
+      cur = n;
+    }
     buf ^= 1;
   }
   // Keys beyond K (padding) are 0 and come after every real channel: they are
@@ -232,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
   extern __shared__ uint4 lds_u4[];
   int32_t *sel = reinterpret_cast<int32_t *>(lds_u4);
   float *region = reinterpret_cast<float *>(lds_u4) + kpad;
-  __shared__ uint32_t slots[6 * (kThreads / 64)];
+  __shared__ uint32_t slots[8 * (kThreads / 64)];
   const int tid = threadIdx.x;
   const int cb = K / 16, nblk = kpad / 16;
   const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
@@ -267,20 +283,34 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
     ks.k[i + 3] = v.w & m;
   }
   for (int j = nsel + tid; j < kpad; j += kThreads) sel[j] = -1;
-  uint32_t mx = 0;
+  // Largest and smallest real key over the workgroup (slots 24..31; the
+  // search uses slots 0..23).
+  uint32_t mx = 0, mn = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) mx = max(mx, ks.k[i]);
-  if (nsel > 0) block_select(ks, nsel, slots, sel);
+  for (int i = 0; i < PER; ++i) {
+    mx = max(mx, ks.k[i]);
+    if (i < n_real) mn = min(mn, ks.k[i]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
+    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), off)));
+  }
+  if ((tid & 63) == 0) {
+    slots[24 + (tid >> 6)] = mx;
+    slots[28 + (tid >> 6)] = mn;
+  }
+  __syncthreads();
+  uint32_t mx_total = 0, mn_total = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    mx_total = max(mx_total, slots[24 + i]);
+    mn_total = min(mn_total, slots[28 + i]);
+  }
   // The largest score is always selected (nsel >= 1): it sets the residual
   // tensor scale.
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
+  if (nsel > 0) block_select(ks, nsel, mn_total, mx_total, K, slots, sel);
   __syncthreads();
-  if ((tid & 63) == 0) slots[tid >> 6] = mx;
-  __syncthreads();
-  uint32_t mx_total = 0;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) mx_total = max(mx_total, slots[i]);
   const float gr = tensor_scale_from_amax(nsel > 0 ? __uint_as_float(mx_total) : 0.0f);
   if (blockIdx.x == 0) {
     for (int j = tid; j < kpad; j += kThreads) sel_out[j] = max(sel[j], 0);
