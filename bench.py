@@ -126,7 +126,7 @@ def setup_expert_gemm(Q, S, k):
                                        "oracle quantize + RAC + fp64 GEMM (weights quantized beforehand)")
 
     return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
-                dominant_kernel="k_gemm_dma<0,true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)", config=cfg, cpu_baseline=cpu_baseline,
+                dominant_kernel="k_gemm_dma<2, 0, true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)", config=cfg, cpu_baseline=cpu_baseline,
                 traffic_summary=os.path.join(ROOT, "profiles", f"k_gemm_dma_expert_gemm_k{k}_traffic.txt"))
 
 
@@ -273,7 +273,8 @@ def setup_trainer_bwd(Q, S):
     return dict(stages=stages, plain=None, tokens=T, flops=flops, dominant="gate_up.wgrad",
                 dominant_flops=2.0 * R * (2 * I) * H,
                 dominant_kernel="gate_up dW: k_pad_map + 2 gather-transposes + k_wgrad (bf16 MFMA, FP32 dW)",
-                config=cfg, cpu_baseline=cpu_baseline)
+                config=cfg, cpu_baseline=cpu_baseline,
+                cpu_cores_note="float64 products on the BLAS threads; the weight QDQ single-threaded NumPy")
 
 
 def run_ablation(Q, S):
@@ -489,7 +490,8 @@ def main():
         out["cpu_baseline"] = {"value": rate, "unit": "tokens/s", "cores": blas_threads(),
                                "kind": "oracle", "sample": sample, "seconds": cpu_s,
                                "host_cpus": os.cpu_count(),
-                               "cores_note": "fp64 GEMM on the BLAS threads; quantize and RAC single-threaded NumPy"}
+                               "cores_note": wl.get("cpu_cores_note",
+                                                    "fp64 GEMM on the BLAS threads; quantize and RAC single-threaded NumPy")}
     print(json.dumps(out), flush=True)
 
 
