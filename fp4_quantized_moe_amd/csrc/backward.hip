@@ -24,7 +24,9 @@
 namespace quads {
 namespace {
 
-constexpr int kPad = 64;  // contraction step of k_wgrad = per-expert row padding
+constexpr int kPad = 64;   // per-expert row padding (a 64-column transpose tile stays in one expert)
+constexpr int kStep = 64;  // contraction step of k_wgrad (divides kPad): one 128-byte line per row
+constexpr int kCh = kStep / 8;  // 16-byte chunks per tile row and step
 
 __device__ __forceinline__ int pad_up(int m) { return (m + kPad - 1) / kPad * kPad; }
 
@@ -118,104 +120,123 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t *in, int64_t C
 }
 
 // dW[e, n, k] = sum over j in [pad_off[e], pad_off[e+1]) of dyT[n, j] * xT[k, j].
-// Workgroup tile 128 (n) x 128 (k), 4 waves of 64 x 64; contraction steps of
-// 64 (one 128-byte line per tile row: 8 chunks, chunk c of row r in slot
-// c ^ ((r >> 1) & 7), which keeps the 16 rows a fragment read touches at
-// one chunk, and the 2 rows x 8 chunks a store instruction's 16 lanes write,
-// in distinct 16-byte bank groups).  Two LDS stages; the next step's loads
-// are in flight while a step is multiplied.  The workgroup order keeps all tiles of
-// an expert on one XCD (dispatch is round-robin over the 8 XCDs), so that
-// expert's dyT and xT blocks are read from one L2.  Each expert's operand
-// blocks are contiguous ([N, padded rows] and [K, padded rows]), so a tile's
-// rows lie in one region of memory.
+// Workgroup tile TN (n) x TK (k) of WN x WK waves (256 x 256 with 8 waves of
+// 128 x 64 where N and K allow, else 128 x 128 with 4 waves of 64 x 64): the
+// larger tile halves the operand re-reads, which (an expert's two transposed
+// blocks being larger than one XCD's L2) set this kernel's speed.
+// Contraction steps of 64: each staging load instruction reads whole
+// 128-byte lines (8 lanes per row; a load spread over 64 bytes of each of
+// 16 rows streams at about half that rate on MI355X).  LDS rows hold 8
+// chunks, chunk c of row r in slot c ^ ((r >> 1) & 7), which keeps the 16
+// rows a fragment read touches at one chunk, and the 2 rows x 8 chunks a store
+// instruction's 16 lanes write, in distinct 16-byte bank groups.  Two LDS stages; the next step's loads
+// are in flight while a step is multiplied.  The workgroup order keeps all
+// tiles of an expert on one XCD (dispatch is round-robin over the 8 XCDs).
+// Each expert's operand blocks are contiguous ([N, padded rows] and
+// [K, padded rows]), so a tile's rows lie in one region of memory.
+template <int TN, int TK>
 struct WgradLds {
-  uint4 a[128 * 8];
-  uint4 b[128 * 8];
+  uint4 a[TN * kCh];
+  uint4 b[TK * kCh];
 };
 
-__device__ __forceinline__ int wslot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+__device__ __forceinline__ int wslot(int row, int c) { return row * kCh + (c ^ ((row / (16 / kCh)) & (kCh - 1))); }
 
-// Step s of this thread's staging loads (4 chunks of each operand).
-__device__ __forceinline__ void wg_fetch(uint4 (&ra)[4], uint4 (&rb)[4], const uint16_t *ga, const uint16_t *gb,
-                                         int64_t ld, int s) {
-  const int64_t o = static_cast<int64_t>(s) * kPad;
+template <int TN, int TK, int WN, int WK>
+struct WgradCfg {
+  static constexpr int THREADS = 64 * WN * WK;
+  static constexpr int LA = TN * kCh / THREADS, LB = TK * kCh / THREADS;  // staging loads per thread
+  static constexpr int RS = THREADS / kCh;                               // tile rows between them
+  static constexpr int MI = TN / WN / 32, KI = TK / WK / 32;              // 32x32 MFMA tiles per wave
+  static_assert(LA >= 1 && LB >= 1 && TN * kCh % THREADS == 0 && TK * kCh % THREADS == 0, "staging split");
+};
+
+template <class C, int TN, int TK>
+__device__ __forceinline__ void wg_fetch(uint4 (&ra)[C::LA], uint4 (&rb)[C::LB], const uint16_t *ga,
+                                         const uint16_t *gb, int64_t ld, int s) {
+  const int64_t o = static_cast<int64_t>(s) * kStep;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ra[q] = *reinterpret_cast<const uint4 *>(ga + 32 * q * ld + o);
-    rb[q] = *reinterpret_cast<const uint4 *>(gb + 32 * q * ld + o);
-  }
+  for (int q = 0; q < C::LA; ++q) ra[q] = *reinterpret_cast<const uint4 *>(ga + C::RS * q * ld + o);
+#pragma unroll
+  for (int q = 0; q < C::LB; ++q) rb[q] = *reinterpret_cast<const uint4 *>(gb + C::RS * q * ld + o);
 }
 
-__device__ __forceinline__ void wg_store(WgradLds &l, const uint4 (&ra)[4], const uint4 (&rb)[4], int srow, int sch) {
+template <class C, int TN, int TK>
+__device__ __forceinline__ void wg_store(WgradLds<TN, TK> &l, const uint4 (&ra)[C::LA], const uint4 (&rb)[C::LB],
+                                         int srow, int sch) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    l.a[wslot(srow + 32 * q, sch)] = ra[q];
-    l.b[wslot(srow + 32 * q, sch)] = rb[q];
-  }
+  for (int q = 0; q < C::LA; ++q) l.a[wslot(srow + C::RS * q, sch)] = ra[q];
+#pragma unroll
+  for (int q = 0; q < C::LB; ++q) l.b[wslot(srow + C::RS * q, sch)] = rb[q];
 }
 
-// One 64-element contraction step of this wave's 64 x 64 sub-tile.
-__device__ __forceinline__ void wg_compute(const WgradLds &l, f32x16 (&acc)[2][2], int wn, int wk, int fr, int fh) {
+// One contraction step of this wave's (32 MI) x (32 KI) sub-tile.
+template <class C, int TN, int TK>
+__device__ __forceinline__ void wg_compute(const WgradLds<TN, TK> &l, f32x16 (&acc)[C::MI][C::KI], int an0,
+                                           int bk0, int fr, int fh) {
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
+  for (int sub = 0; sub < kCh / 2; ++sub) {
     const int c = 2 * sub + fh;
-    uint4 a[2], b[2];
+    uint4 a[C::MI], b[C::KI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = l.a[wslot(wn * 64 + i * 32 + fr, c)];
-      b[i] = l.b[wslot(wk * 64 + i * 32 + fr, c)];
-    }
+    for (int i = 0; i < C::MI; ++i) a[i] = l.a[wslot(an0 + i * 32 + fr, c)];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int i = 0; i < C::KI; ++i) b[i] = l.b[wslot(bk0 + i * 32 + fr, c)];
 #pragma unroll
-      for (int ki = 0; ki < 2; ++ki)
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int ki = 0; ki < C::KI; ++ki)
         acc[mi][ki] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[mi]),
                                                               __builtin_bit_cast(bf16x8, b[ki]), acc[mi][ki], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(256, 2) void k_wgrad(const uint16_t *dyT, const uint16_t *xT, const int32_t *pad_off,
-                                                  int64_t N, int64_t K, float *dw) {
-  __shared__ WgradLds st[2];
-  const int nN = static_cast<int>(N / 128), nK = static_cast<int>(K / 128);
+template <int TN, int TK, int WN, int WK>
+__global__ __launch_bounds__(64 * WN * WK) void k_wgrad(const uint16_t *dyT, const uint16_t *xT,
+                                                        const int32_t *pad_off, int64_t N, int64_t K, float *dw) {
+  using C = WgradCfg<TN, TK, WN, WK>;
+  __shared__ WgradLds<TN, TK> st[2];
+  const int nN = static_cast<int>(N / TN), nK = static_cast<int>(K / TK);
   const int G = gridDim.x;
   const int bid = G % 8 == 0 ? static_cast<int>((blockIdx.x % 8) * (G / 8) + blockIdx.x / 8)
                              : static_cast<int>(blockIdx.x);
   const int e = bid / (nN * nK), nb = (bid / nK) % nN, kb = bid % nK;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wn = wave >> 1, wk = wave & 1;
-  const int64_t n0 = static_cast<int64_t>(nb) * 128, k0 = static_cast<int64_t>(kb) * 128;
+  const int wn = wave / WK, wk = wave % WK;
+  const int64_t n0 = static_cast<int64_t>(nb) * TN, k0 = static_cast<int64_t>(kb) * TK;
   const int j_begin = pad_off[e], j_end = pad_off[e + 1];
   const int64_t ld = j_end - j_begin;  // the expert's block: [N, ld] of dyT, [K, ld] of xT
-  const int ns = static_cast<int>(ld / kPad);
+  const int ns = static_cast<int>(ld / kStep);
 
-  // Thread t stages chunk t % 8 of rows t / 8 + 32 q (q = 0..3) of both operands.
-  const int srow = t >> 3, sch = t & 7;
+  // Thread t stages chunk t % kCh of rows t / kCh + RS * q of both operands.
+  const int srow = t / kCh, sch = t % kCh;
   const uint16_t *ga = dyT + N * j_begin + (n0 + srow) * ld + sch * 8;
   const uint16_t *gb = xT + K * j_begin + (k0 + srow) * ld + sch * 8;
   const int fr = lane & 31, fh = lane >> 5;
+  const int an0 = wn * (TN / WN), bk0 = wk * (TK / WK);
 
-  f32x16 acc[2][2];
+  f32x16 acc[C::MI][C::KI];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-    for (int ki = 0; ki < 2; ++ki)
+    for (int ki = 0; ki < C::KI; ++ki)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ki][r] = 0.0f;
 
   // Step s+1 loads into registers while step s is multiplied from its LDS
   // stage; the registers then go to the other stage.  The last step's
   // prefetch re-reads that step (in bounds) into a stage no one reads again,
-  // so the loop body has no branches.
+  // so the loop body has no branches (with a branch the compiler kept the
+  // staging registers in scratch memory).
   if (ns > 0) {
-    uint4 ra[4], rb[4];
-    wg_fetch(ra, rb, ga, gb, ld, 0);
-    wg_store(st[0], ra, rb, srow, sch);
+    uint4 ra[C::LA], rb[C::LB];
+    wg_fetch<C, TN, TK>(ra, rb, ga, gb, ld, 0);
+    wg_store<C, TN, TK>(st[0], ra, rb, srow, sch);
     __syncthreads();
     for (int s = 0; s < ns; ++s) {
-      wg_fetch(ra, rb, ga, gb, ld, min(s + 1, ns - 1));
-      wg_compute(st[s & 1], acc, wn, wk, fr, fh);
-      wg_store(st[(s + 1) & 1], ra, rb, srow, sch);
+      wg_fetch<C, TN, TK>(ra, rb, ga, gb, ld, min(s + 1, ns - 1));
+      wg_compute<C, TN, TK>(st[s & 1], acc, an0, bk0, fr, fh);
+      wg_store<C, TN, TK>(st[(s + 1) & 1], ra, rb, srow, sch);
       __syncthreads();
     }
   }
@@ -224,13 +245,13 @@ __global__ __launch_bounds__(256, 2) void k_wgrad(const uint16_t *dyT, const uin
   // column lane%32 (k).
   float *out = dw + static_cast<int64_t>(e) * N * K;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-    for (int ki = 0; ki < 2; ++ki)
+    for (int ki = 0; ki < C::KI; ++ki)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t n = n0 + wn * 64 + mi * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-        const int64_t k = k0 + wk * 64 + ki * 32 + fr;
+        const int64_t n = n0 + an0 + mi * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+        const int64_t k = k0 + bk0 + ki * 32 + fr;
         out[n * K + k] = acc[mi][ki][r];
       }
 }
@@ -272,9 +293,15 @@ hipError_t launch_wgrad(const WgradLaunch &a, hipStream_t stream) {
   hipLaunchKernelGGL((k_transpose<true>), dim3(jt, static_cast<unsigned>((a.K + 63) / 64), 1), dim3(256), 0,
                      stream, a.x, a.K, J, int64_t(0), colsrc, a.row_token, pad_off, colexp, a.E, xT, int64_t(0),
                      int64_t(0));
-  const int64_t grid = static_cast<int64_t>(a.E) * (a.N / 128) * (a.K / 128);
-  hipLaunchKernelGGL(k_wgrad, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, dyT, xT, pad_off, a.N, a.K,
-                     a.dw);
+  if (a.N % 256 == 0 && a.K % 256 == 0) {
+    const int64_t grid = static_cast<int64_t>(a.E) * (a.N / 256) * (a.K / 256);
+    hipLaunchKernelGGL((k_wgrad<256, 256, 2, 4>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, dyT, xT,
+                       pad_off, a.N, a.K, a.dw);
+  } else {
+    const int64_t grid = static_cast<int64_t>(a.E) * (a.N / 128) * (a.K / 128);
+    hipLaunchKernelGGL((k_wgrad<128, 128, 2, 2>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, dyT, xT,
+                       pad_off, a.N, a.K, a.dw);
+  }
   return hipGetLastError();
 }
 
