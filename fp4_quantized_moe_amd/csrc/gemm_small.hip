@@ -2,17 +2,24 @@
 // rollout batches), gfx950.
 //
 // With ~16 rows per expert the GEMM is bound by reading the NVFP4 weights
-// once from HBM (0.5625 B per weight), not by the MFMAs.  So each weight
-// element must be read exactly once per call, including for the RAC segment:
-// QUADS technical summary section 2.2-B adds the second-pass residual of the
-// selected channels to the quantized activation, and with the selected
-// channels scattered back to their positions in K (zero elsewhere) the
-// correction is one more MFMA on the weight fragment already in registers:
+// once from HBM (0.5625 B per weight), and by the MFMA and decode issue of
+// each weight fragment, not by the size of the contraction.  QUADS technical
+// summary section 2.2-B adds the second-pass residual of the selected
+// channels to the quantized activation before the GEMM
+// (Y = W_q (X_q + M * dX_q)).  Here that sum is formed once per activation
+// element (k_merge_residual), in units of the activation's tensor scale:
 //
-//   Y[i,n] = gw * ( gx * sum_k W'[n,k] X'[t(i),k] + gr * sum_k W'[n,k] Rd[t(i),k] )
+//   A[t, k] = fp16( X'[t, k] + (gr / gx) * R'[t, j] )   (k = sel_j; X' alone elsewhere)
+//   Y[i, n] = gw * gx * sum_k W'[n, k] A[t(i), k]
 //
-// where Rd is the residual scattered to dense K in fp16 (exact values
-// e2m1 * e4m3, no tensor scale) by k_scatter_residual.
+// X' and R' are the exact e2m1 * e4m3 values (no tensor scale).  The
+// rounding of the sum to fp16 is the only rounding besides the FP32
+// accumulation: at most 2^-11 of each corrected element, which measures
+// 2-3e-4 of max|Y| on the seeded workloads (the bar is 1e-3).  One MFMA per
+// weight fragment instead of two, and no separate activation-code staging,
+// makes this cheaper than carrying the residual as a second operand.  Plain
+// W4A4 (no residual) stages and decodes the activation codes instead and is
+// exact up to accumulation.
 //
 // k_gemm_small: a workgroup of 4 waves per (expert, 128 output columns); wave
 // w owns 32 weight rows (output columns) and runs v_mfma_f32_32x32x16_f16 with
@@ -22,13 +29,13 @@
 // covering whole 128-byte lines (8 lanes per line) -- on MI355X a wave load
 // spread over 32 rows at 32 bytes per row streams at a quarter of the HBM rate
 // that whole lines reach.  Each wave stages its own weight rows; the
-// activation rows, their scales and the scattered residual are staged once
-// per workgroup, a quarter by each wave.  16-byte chunks are XOR-swizzled per
-// row (by choosing which chunk each lane fetches) so that the MFMA fragment
-// reads are bank-conflict-free.  Two LDS stages: step k+1 is in flight while
-// step k is decoded (cvt + pk_mul, exact) and multiplied.  The contraction
-// order inside a step is permuted identically for both operands (lane half h
-// takes elements [128h, 128h+128), 8 per MFMA).
+// activation rows (codes and scales, or the merged fp16 operand) are staged
+// once per workgroup, a quarter by each wave.  16-byte chunks are XOR-swizzled
+// per row (by choosing which chunk each lane fetches) so that the MFMA
+// fragment reads are bank-conflict-free.  Two LDS stages: step k+1 is in
+// flight while step k is decoded (cvt + pk_mul, exact) and multiplied.  The
+// contraction order inside a step is permuted identically for both operands
+// (lane half h takes elements [128h, 128h+128), 8 per MFMA).
 #include <stdlib.h>
 #include <string.h>
 
@@ -49,7 +56,7 @@ struct SmallParams {
   int64_t N, K;
   const uint8_t *x_codes, *x_scales;
   const float *x_g;
-  const uint16_t *r_dense;  // [act_rows, K] fp16 residual scattered to K, or null
+  const uint16_t *r_dense;  // [act_rows, K] fp16 merged activation (RAC), or null
   const float *r_g;
   const uint8_t *w_codes, *w_scales;
   const float *w_g;
@@ -58,14 +65,14 @@ struct SmallParams {
 };
 
 // One LDS stage.  Rows of 128 bytes hold 8 chunks; chunk c of row r sits in
-// slot c ^ ((r >> 1) & 7) (32 residual chunks per row: slot c ^ (r & 15)).
+// slot c ^ ((r >> 1) & 7) (32 merged-operand chunks per row: slot c ^ (r & 15)).
 template <bool RES>
 struct StageLds {
-  uint4 w[4 * 32 * 8];          // [wave][row][slot] weight codes
-  uint32_t ws[4 * 32 * 4];      // [wave][row][4 words] weight block scales
-  uint4 x[32 * 8];              // [row][slot] activation codes
-  uint32_t xs[32 * 4];          // [row][4 words] activation block scales
-  uint4 r[RES ? 32 * 32 : 1];   // [row][slot] residual, fp16
+  uint4 w[4 * 32 * 8];             // [wave][row][slot] weight codes
+  uint32_t ws[4 * 32 * 4];         // [wave][row][4 words] weight block scales
+  uint4 x[RES ? 1 : 32 * 8];       // [row][slot] activation codes (plain W4A4)
+  uint32_t xs[RES ? 1 : 32 * 4];   // [row][4 words] activation block scales (plain W4A4)
+  uint4 r[RES ? 32 * 32 : 1];      // [row][slot] merged fp16 activation (RAC)
 };
 
 typedef __attribute__((address_space(3))) void lds_t;
@@ -105,13 +112,14 @@ __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, c
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     dma4(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i]);
-  if (!rows16 || wave < 2) {
-    const int r = 8 * wave + (lane >> 3);
-    const int chunk = slot ^ swz8(r);
-    dma16(p.x_codes + rw.xrow * (K / 2) + kt * 128 + chunk * 16, &st.x[8 * wave * 8]);
-  }
-  if (wave < (rows16 ? 1 : 2)) dma4(p.x_scales + rw.xsrow * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * wave]);
-  if constexpr (RES) {
+  if constexpr (!RES) {
+    if (!rows16 || wave < 2) {
+      const int r = 8 * wave + (lane >> 3);
+      const int chunk = slot ^ swz8(r);
+      dma16(p.x_codes + rw.xrow * (K / 2) + kt * 128 + chunk * 16, &st.x[8 * wave * 8]);
+    }
+    if (wave < (rows16 ? 1 : 2)) dma4(p.x_scales + rw.xsrow * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * wave]);
+  } else {
     if (!rows16 || wave < 2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -125,31 +133,40 @@ __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, c
 }
 
 template <bool RES>
-__device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int lane, f32x16 &acc_x, f32x16 &acc_r) {
+__device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int lane, f32x16 &acc) {
   const int r = lane & 31, h = lane >> 5;
   const uint32_t ws0 = st.ws[wave * 128 + r * 4 + 2 * h], ws1 = st.ws[wave * 128 + r * 4 + 2 * h + 1];
-  const uint32_t xs0 = st.xs[r * 4 + 2 * h], xs1 = st.xs[r * 4 + 2 * h + 1];
 #pragma unroll
   for (int cq = 0; cq < 4; ++cq) {
     const int c = 4 * h + cq;
     const uint4 wc = st.w[(wave * 32 + r) * 8 + (c ^ swz8(r))];
-    const uint4 xc = st.x[r * 8 + (c ^ swz8(r))];
     const uint32_t wv[4] = {wc.x, wc.y, wc.z, wc.w};
-    const uint32_t xv[4] = {xc.x, xc.y, xc.z, xc.w};
+    uint32_t xv[4] = {0, 0, 0, 0};
+    uint32_t xs0 = 0, xs1 = 0;
+    if constexpr (!RES) {
+      const uint4 xc = st.x[r * 8 + (c ^ swz8(r))];
+      xv[0] = xc.x;
+      xv[1] = xc.y;
+      xv[2] = xc.z;
+      xv[3] = xc.w;
+      xs0 = st.xs[r * 4 + 2 * h];
+      xs1 = st.xs[r * 4 + 2 * h + 1];
+    }
 #pragma unroll
     for (int sq = 0; sq < 4; ++sq) {
       const int s = 4 * cq + sq;                 // sub-step: elements [128h + 8s, +8)
       const int blk = s >> 1;                    // block among the lane's 8
-      const uint32_t wsw = blk < 4 ? ws0 : ws1, xsw = blk < 4 ? xs0 : xs1;
+      const uint32_t wsw = blk < 4 ? ws0 : ws1;
       const uint4 bw = decode8_f16(wv[sq], scale_h2((wsw >> (8 * (blk & 3))) & 0xFFu));
-      const uint4 ax = decode8_f16(xv[sq], scale_h2((xsw >> (8 * (blk & 3))) & 0xFFu));
-      acc_x = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw), acc_x,
-                                                     0, 0, 0);
+      uint4 ax;
       if constexpr (RES) {
-        const uint4 rv = st.r[r * 32 + ((16 * h + s) ^ (r & 15))];
-        acc_r = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, rv), __builtin_bit_cast(h8, bw),
-                                                       acc_r, 0, 0, 0);
+        ax = st.r[r * 32 + ((16 * h + s) ^ (r & 15))];
+      } else {
+        const uint32_t xsw = blk < 4 ? xs0 : xs1;
+        ax = decode8_f16(xv[sq], scale_h2((xsw >> (8 * (blk & 3))) & 0xFFu));
       }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw), acc, 0, 0,
+                                                   0);
     }
   }
 }
@@ -157,43 +174,48 @@ __device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int l
 // 16-row pass (v_mfma_f32_16x16x32_f16): lane quarter q takes chunks 2q
 // and 2q+1 of each 256-element step, 8 elements per MFMA; the wave's 32
 // weight rows are two 16-column blocks.  Same contraction-order permutation
-// for both operands (and the scattered residual).
+// for both operands (and the merged operand).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <bool RES>
-__device__ __forceinline__ void compute16(const StageLds<RES> &st, int wave, int lane, f32x4 (&acc_x)[2],
-                                          f32x4 (&acc_r)[2]) {
+__device__ __forceinline__ void compute16(const StageLds<RES> &st, int wave, int lane, f32x4 (&acc)[2]) {
   const int r = lane & 15, q = lane >> 4;
-  const uint32_t xsw = st.xs[r * 4 + q];  // blocks 4q..4q+3 of the step
   uint32_t wsw[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) wsw[cb] = st.ws[wave * 128 + (16 * cb + r) * 4 + q];
 #pragma unroll
   for (int cq = 0; cq < 2; ++cq) {
     const int c = 2 * q + cq;
-    const uint4 xc = st.x[r * 8 + (c ^ swz8(r))];
     uint4 wc[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int wr = 16 * cb + r;
       wc[cb] = st.w[(wave * 32 + wr) * 8 + (c ^ swz8(wr))];
     }
-    const uint32_t xv[4] = {xc.x, xc.y, xc.z, xc.w};
+    uint32_t xv[4] = {0, 0, 0, 0};
+    uint32_t xsw = 0;
+    if constexpr (!RES) {
+      const uint4 xc = st.x[r * 8 + (c ^ swz8(r))];
+      xv[0] = xc.x;
+      xv[1] = xc.y;
+      xv[2] = xc.z;
+      xv[3] = xc.w;
+      xsw = st.xs[r * 4 + q];  // blocks 4q..4q+3 of the step
+    }
 #pragma unroll
     for (int sq = 0; sq < 4; ++sq) {
       const int blk = 2 * cq + (sq >> 1);  // block among the lane's 4
-      const uint4 ax = decode8_f16(xv[sq], scale_h2((xsw >> (8 * blk)) & 0xFFu));
-      uint4 rv = make_uint4(0, 0, 0, 0);
-      if constexpr (RES) rv = st.r[r * 32 + ((8 * q + 4 * cq + sq) ^ r)];
+      uint4 ax;
+      if constexpr (RES)
+        ax = st.r[r * 32 + ((8 * q + 4 * cq + sq) ^ r)];
+      else
+        ax = decode8_f16(xv[sq], scale_h2((xsw >> (8 * blk)) & 0xFFu));
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const uint32_t wv[4] = {wc[cb].x, wc[cb].y, wc[cb].z, wc[cb].w};
         const uint4 bw = decode8_f16(wv[sq], scale_h2((wsw[cb] >> (8 * blk)) & 0xFFu));
-        acc_x[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
-                                                           acc_x[cb], 0, 0, 0);
-        if constexpr (RES)
-          acc_r[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, rv), __builtin_bit_cast(h8, bw),
-                                                             acc_r[cb], 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
+                                                         acc[cb], 0, 0, 0);
       }
     }
   }
@@ -229,7 +251,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
   const int64_t wrow0 = static_cast<int64_t>(e) * p.N + wcol0;
   const float gw = p.w_g[e * p.n_seg + static_cast<int>(wcol0) / static_cast<int>(p.N / p.n_seg)];
   const float gx = *p.x_g;
-  const float gr = RES ? *p.r_g : 0.0f;
   const int nk = static_cast<int>(p.K / kSK);  // even
 
   auto act_row = [&](int pm, int r) -> int64_t {
@@ -250,24 +271,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
 
     __syncthreads();  // the previous pass (or its epilogue) no longer reads the stages
     if (mend - pm <= 16) {  // last pass of at most 16 rows: 16-row MFMAs, half the work
-      f32x4 ax[2], ar[2];
+      f32x4 ax[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           ax[cb][v] = 0.0f;
-          ar[cb][v] = 0.0f;
         }
       issue<RES>(st0, p, rw, 0, wave, lane, true);
       for (int kt = 0; kt < nk; kt += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         issue<RES>(st1, p, rw, kt + 1, wave, lane, true);
-        compute16<RES>(st0, wave, lane, ax, ar);
+        compute16<RES>(st0, wave, lane, ax);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kt + 2 < nk) issue<RES>(st0, p, rw, kt + 2, wave, lane, true);
-        compute16<RES>(st1, wave, lane, ax, ar);
+        compute16<RES>(st1, wave, lane, ax);
       }
       // Element v of accumulator cb is row 4*(lane/16) + v of the pass,
       // column 16*cb + lane%16 of the wave's 32.
@@ -277,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          v16[cb][v] = RES ? (ax[cb][v] * gx + ar[cb][v] * gr) * gw : ax[cb][v] * (gw * gx);
+          v16[cb][v] = ax[cb][v] * (gw * gx);  // the merged operand is in units of gx too
       if constexpr (EPI == 0) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
@@ -313,29 +333,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
       continue;
     }
 
-    f32x16 acc_x, acc_r;
+    f32x16 acc_x;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc_x[r] = 0.0f;
-      acc_r[r] = 0.0f;
-    }
+    for (int r = 0; r < 16; ++r) acc_x[r] = 0.0f;
     issue<RES>(st0, p, rw, 0, wave, lane);
     for (int kt = 0; kt < nk; kt += 2) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's part of step kt has landed in LDS
       __syncthreads();                // ... and every wave's; step kt-1 is no longer read
       issue<RES>(st1, p, rw, kt + 1, wave, lane);
-      compute<RES>(st0, wave, lane, acc_x, acc_r);
+      compute<RES>(st0, wave, lane, acc_x);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kt + 2 < nk) issue<RES>(st0, p, rw, kt + 2, wave, lane);
-      compute<RES>(st1, wave, lane, acc_x, acc_r);
+      compute<RES>(st1, wave, lane, acc_x);
     }
 
     // Element r of the accumulator is row 8*(r/4) + 4*h + r%4 of the pass,
     // column lane%32 of the wave's 32.
     float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = RES ? (acc_x[r] * gx + acc_r[r] * gr) * gw : acc_x[r] * (gw * gx);
+    for (int r = 0; r < 16; ++r) v[r] = acc_x[r] * (gw * gx);  // merged operand: units of gx too
     const int64_t col = col0 + (lane & 31);
     if constexpr (EPI == 0) {
 #pragma unroll
@@ -366,14 +383,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
   }
 }
 
-// Residual codes [rows, kpad] in selected order -> fp16 [rows, K] with each
-// selected channel's exact value at its own position and zeros elsewhere.
-// The inverse of sel_idx is built in LDS first.  sel_idx is strictly
-// ascending over the nsel real entries and padded with index 0 (zero
-// residual): an entry j > 0 that points at channel 0 is padding and skipped.
-__global__ __launch_bounds__(256) void k_scatter_residual(const uint8_t *r_codes, const uint8_t *r_scales,
-                                                          int64_t rows, int K, int kpad, const int32_t *sel,
-                                                          uint16_t *out, int rows_per_wg) {
+// The RAC-corrected activation as one fp16 operand [rows, K], in units of
+// the activation's tensor scale gx: A[t, k] = fp16(X'[t, k] + (gr / gx) *
+// R'[t, j]) for a selected channel k = sel_j, X'[t, k] elsewhere, with the
+// exact e2m1 * e4m3 values X' and R' (fp32 sum, one rounding to fp16).  The
+// inverse of sel_idx is built in LDS first.  sel_idx is strictly ascending
+// over the nsel real entries and padded with index 0 (zero residual): an entry
+// j > 0 that points at channel 0 is padding and skipped.
+__global__ __launch_bounds__(256) void k_merge_residual(const uint8_t *x_codes, const uint8_t *x_scales,
+                                                        const float *x_g, const uint8_t *r_codes,
+                                                        const uint8_t *r_scales, const float *r_g, int64_t rows,
+                                                        int K, int kpad, const int32_t *sel, uint16_t *out,
+                                                        int rows_per_wg) {
   extern __shared__ int16_t inv[];
   for (int k = threadIdx.x; k < K; k += 256) inv[k] = -1;
   __syncthreads();
@@ -382,22 +403,25 @@ __global__ __launch_bounds__(256) void k_scatter_residual(const uint8_t *r_codes
     if (j == 0 || c != 0) inv[c] = static_cast<int16_t>(j);
   }
   __syncthreads();
+  const float ratio = *r_g / *x_g;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
   const int64_t r1 = min(r0 + rows_per_wg, rows);
   const int chunks = K / 8;
   for (int64_t t = threadIdx.x; t < (r1 - r0) * chunks; t += 256) {
     const int64_t row = r0 + t / chunks;
     const int k0 = static_cast<int>(t % chunks) * 8;
+    const uint32_t xw = reinterpret_cast<const uint32_t *>(x_codes + row * (K / 2))[k0 / 8];
+    const float xs = e4m3_to_f32(x_scales[row * (K / 16) + k0 / 16]);
     const uint8_t *rc = r_codes + row * (kpad / 2);
     const uint8_t *rs = r_scales + row * (kpad / 16);
     uint32_t hv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
+      float v = dequant_code((xw >> (4 * q)) & 0xFu, xs);
       const int j = inv[k0 + q];
-      float v = 0.0f;
       if (j >= 0) {
         const uint32_t code = (rc[j >> 1] >> ((j & 1) * 4)) & 0xFu;
-        v = dequant_code(code, e4m3_to_f32(rs[j >> 4]));
+        v += dequant_code(code, e4m3_to_f32(rs[j >> 4])) * ratio;
       }
       hv[q] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
     }
@@ -405,7 +429,6 @@ __global__ __launch_bounds__(256) void k_scatter_residual(const uint8_t *r_codes
         make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
   }
 }
-
 
 }  // namespace
 
@@ -429,9 +452,9 @@ hipError_t launch_gemm_small_prepare(const GemmLaunch &a, uint16_t *r_dense, hip
   // workgroup: K/256 + kpad/256 LDS stores per thread), more rows beyond.
   const int rows_per_wg = static_cast<int>((a.act_rows + 4095) / 4096);
   const int64_t grid = (a.act_rows + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(k_scatter_residual, dim3(grid), dim3(256), a.K * sizeof(int16_t), stream, a.r_codes,
-                     a.r_scales, a.act_rows, static_cast<int>(a.K), static_cast<int>(a.kpad), a.sel_idx, r_dense,
-                     rows_per_wg);
+  hipLaunchKernelGGL(k_merge_residual, dim3(grid), dim3(256), a.K * sizeof(int16_t), stream, a.x_codes,
+                     a.x_scales, a.x_g, a.r_codes, a.r_scales, a.r_g, a.act_rows, static_cast<int>(a.K),
+                     static_cast<int>(a.kpad), a.sel_idx, r_dense, rows_per_wg);
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ size_t gemm_ws_bytes(const GemmLaunch &a);
 hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream);
 hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream);
 // Few rows per expert (decode-shaped calls): weights read once, the RAC
-// residual scattered to dense K (gemm_small.hip).
+// correction merged into one fp16 activation operand (gemm_small.hip).
 bool gemm_use_small(const GemmLaunch &a);
 size_t gemm_small_res_bytes(const GemmLaunch &a);
 hipError_t launch_gemm_small_prepare(const GemmLaunch &a, uint16_t *r_dense, hipStream_t stream);

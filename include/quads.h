@@ -144,6 +144,13 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
  * quantized output: the same sum.  With r_codes == NULL (or kpad == 0) it is
  * plain W4A4.
  *
+ * Rounding: the contraction accumulates exact operand values in FP32, except
+ * that calls with few rows per expert (num_rows <= 32 * num_experts, the
+ * decode shape) add the correction to the activation before the GEMM as one
+ * fp16 operand per element, X + (gr/gx) R, in units of gx: each corrected
+ * element is rounded once more (relative 2^-11).  Both stay within
+ * max|Y - Y_exact| <= 1e-3 max|Y_exact| on the seeded workloads.
+ *
  * operand_mode QUADS_OPERANDS_BF16 is the trainer's W4A16 forward [Gist
  * 2.2-A]: x_bf16 [act_rows, K] times w_bf16 [E, N, K] (QDQ'd weights),
  * no scales, no residual.
@@ -211,8 +218,9 @@ quads_status_t quads_moe_w4a4_gemm(const quads_moe_gemm_args *a, void *stream);
 /* quads_moe_gemm_prepare -- the first half of quads_moe_w4a4_gemm, split out
  * so callers can time or reuse it: builds the (expert, m-tile) list from
  * expert_offsets and, with a RAC residual, gathers the selected weight columns
- * sel_idx of every expert row into the workspace (bf16, exact e2m1 * e4m3
- * values).  A following quads_moe_w4a4_gemm with flags |= QUADS_GEMM_PREPARED,
+ * sel_idx of every expert row into the workspace (fp16, exact e2m1 * e4m3
+ * values), or for few rows per expert writes the corrected fp16 activation
+ * operand there.  A following quads_moe_w4a4_gemm with flags |= QUADS_GEMM_PREPARED,
  * the same arguments and the same workspace launches only the GEMM kernel. */
 quads_status_t quads_moe_gemm_prepare(const quads_moe_gemm_args *a, void *stream);
 
