@@ -90,6 +90,7 @@ struct Params {
   const uint8_t *w_codes, *w_scales;
   const float *w_g;
   const uint16_t *x_bf16, *w_bf16, *wg_f16;
+  const uint16_t *x_f16;  // MODE 2: RAC-merged fp16 activation [act_rows, K], units of x_g
   void *y;
   int y_bf16;
 };
@@ -317,13 +318,14 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
                                          int nt, int wm, int wn, int lane) {
   float ascale = 1.0f;
   if constexpr (MODE == 0) ascale = HAS_RES ? *p.r_g : *p.x_g;
+  if constexpr (MODE == 2) ascale = *p.x_g;
   if constexpr (EPI == 0) {
     const int64_t seg_len = p.N / p.n_seg;
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni) {
       const int64_t col = static_cast<int64_t>(nt) * C::BN + wn * C::TN + ni * 32 + (lane & 31);
       float sc = ascale;
-      if constexpr (MODE == 0) sc = p.w_g[e * p.n_seg + col / seg_len] * ascale;
+      if constexpr (MODE != 1) sc = p.w_g[e * p.n_seg + col / seg_len] * ascale;
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -343,7 +345,7 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
     static_assert(EPI == 0 || C::NI % 2 == 0, "SWIGLU needs an even number of 32-column tiles per wave");
     const int64_t I = p.N / 2;
     float sg = ascale, su = ascale;
-    if constexpr (MODE == 0) {
+    if constexpr (MODE != 1) {
       sg = p.w_g[e * 2] * ascale;
       su = p.w_g[e * 2 + 1] * ascale;
     }
@@ -367,7 +369,9 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
 }
 
 // MODE 0: NVFP4 operands (+ residual segment if HAS_RES), fp16 MFMA;
-// MODE 1: bf16 operands, bf16 MFMA.
+// MODE 1: bf16 operands, bf16 MFMA;
+// MODE 2: the RAC-merged fp16 activation (X' + (gr/gx) R', built by the GEMM
+// prepare step) times NVFP4 weights, fp16 MFMA over K alone.
 template <class C, int MODE, int EPI, bool HAS_RES>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
   __shared__ uint4 As[2][C::BM * 8];
@@ -435,6 +439,20 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
           [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
           [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
     }
+  } else if constexpr (MODE == 2) {
+    const int nblk = static_cast<int>(p.K / 16);
+    int64_t abase[C::HA], bbase[C::FB];
+#pragma unroll
+    for (int q = 0; q < C::HA; ++q) abase[q] = act_row((threadIdx.x >> 3) + q * (T / 8)) * p.K;
+#pragma unroll
+    for (int q = 0; q < C::FB; ++q)
+      bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
+    k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt); },
+        [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
+        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
+        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
   } else {
     int64_t abase[C::HA], bbase[C::HB];
 #pragma unroll
@@ -1140,8 +1158,11 @@ void launch_dma(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
 }
 
 template <class C>
-void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t stream) {
-  if (a.mode == 1) {
+void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t stream, bool merged = false) {
+  if (merged) {
+    if (a.epilogue == 0) launch_k<C, 2, 0, false>(p, g, stream);
+    else if constexpr (C::NI % 2 == 0) launch_k<C, 2, 1, false>(p, g, stream);
+  } else if (a.mode == 1) {
     if (a.epilogue == 0) launch_k<C, 1, 0, false>(p, g, stream);
     else if constexpr (C::NI % 2 == 0) launch_k<C, 1, 1, false>(p, g, stream);
   } else if (res) {
@@ -1153,13 +1174,40 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
   }
 }
 
+// RAC calls with many rows per expert: which formulation of the correction.
+// The merged fp16 activation operand (MODE 2: one MFMA pass over K, after a
+// merge pass) wins where the extended-K GEMM would run on the large
+// register-staged tiles (measured on the 16384-token prefill layer: 0.94 vs
+// 1.30 ms gate_up, 0.64 vs 0.83 ms down, merge passes included); on the
+// 128x128 DMA-staged shapes the merge pass costs what the shorter GEMM saves
+// (4096 x 1536 x 2048: 18 + 48 vs 5 + 62 us), so the exact extended-K kernel
+// stays.  QUADS_RAC_GEMM=extended | merged overrides the choice; it is read on
+// every call, so one process can compare the two.
+bool use_merged(const GemmLaunch &a) {
+  if (a.mode != 0 || a.r_codes == nullptr || a.kpad == 0 || gemm_use_small(a)) return false;
+  if (const char *f = getenv("QUADS_RAC_GEMM")) {
+    if (strcmp(f, "extended") == 0) return false;
+    if (strcmp(f, "merged") == 0) return true;
+  }
+  const TileCfg c = pick_cfg(a);
+  return c == kL || c == kW || c == kP;
+}
+
+TileCfg pick_cfg_for(const GemmLaunch &a) {
+  TileCfg c = pick_cfg(a);
+  if (use_merged(a)) {
+    if (c == kD || c == kD3 || c == kP) c = c == kD3 ? kM : (c == kP ? kL : kS);
+  }
+  return c;
+}
+
 }  // namespace
 
 size_t gemm_ws_bytes(const GemmLaunch &a) {
   size_t b = align256(static_cast<size_t>(a.E + 1) * sizeof(int32_t));
   if (a.mode == 0 && a.r_codes != nullptr && a.kpad > 0)
-    b += gemm_use_small(a) ? align256(gemm_small_res_bytes(a))
-                           : align256(static_cast<size_t>(a.E) * a.N * a.kpad * sizeof(uint16_t));
+    b += (gemm_use_small(a) || use_merged(a)) ? align256(gemm_small_res_bytes(a))
+                                              : align256(static_cast<size_t>(a.E) * a.N * a.kpad * sizeof(uint16_t));
   return b;
 }
 
@@ -1171,8 +1219,13 @@ hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
     uint16_t *rd = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
     return res ? launch_gemm_small_prepare(a, rd, stream) : hipSuccess;
   }
-  const TileCfg c = pick_cfg(a);
-  if (res) {
+  const TileCfg c = pick_cfg_for(a);
+  if (use_merged(a)) {
+    uint16_t *xm = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
+    const hipError_t e = launch_gemm_small_prepare(a, xm, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(256), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
+  } else if (res) {
     uint16_t *wg = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
     const int64_t rows_total = static_cast<int64_t>(a.E) * a.N;
     const int K = static_cast<int>(a.K);
@@ -1192,7 +1245,8 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
   uint16_t *wg = res ? reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t))) : nullptr;
   if (gemm_use_small(a)) return launch_gemm_small(a, wg, stream);
-  const TileCfg c = pick_cfg(a);
+  const bool merged = use_merged(a);
+  const TileCfg c = pick_cfg_for(a);
   const int bm = cfg_bm(c), bn = cfg_bn(c);
   Params p{};
   p.expert_offsets = a.expert_offsets;
@@ -1214,7 +1268,8 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   p.w_g = a.w_g;
   p.x_bf16 = a.x_bf16;
   p.w_bf16 = a.w_bf16;
-  p.wg_f16 = wg;
+  p.wg_f16 = merged ? nullptr : wg;
+  p.x_f16 = merged ? wg : nullptr;
   p.y = a.y;
   p.y_bf16 = a.y_bf16 ? 1 : 0;
   p.n_tiles = static_cast<int>(a.N / bn);
@@ -1226,12 +1281,12 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   if (c == kD) launch_dma<2>(a, p, g, res, stream);
   else if (c == kD3) launch_dma<3>(a, p, g, res, stream);
   else if (c == kP) launch_pp_cfg(a, p, g, res, stream);
-  else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream);
-  else if (c == kS8a) launch_cfg<CfgS8a>(a, p, g, res, stream);
-  else if (c == kS8b) launch_cfg<CfgS8b>(a, p, g, res, stream);
-  else if (c == kL) launch_cfg<CfgL>(a, p, g, res, stream);
-  else if (c == kM) launch_cfg<CfgM>(a, p, g, res, stream);
-  else launch_cfg<CfgS>(a, p, g, res, stream);
+  else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream, merged);
+  else if (c == kS8a) launch_cfg<CfgS8a>(a, p, g, res, stream, merged);
+  else if (c == kS8b) launch_cfg<CfgS8b>(a, p, g, res, stream, merged);
+  else if (c == kL) launch_cfg<CfgL>(a, p, g, res, stream, merged);
+  else if (c == kM) launch_cfg<CfgM>(a, p, g, res, stream, merged);
+  else launch_cfg<CfgS>(a, p, g, res, stream, merged);
   return hipGetLastError();
 }
 

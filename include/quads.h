@@ -144,11 +144,14 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
  * quantized output: the same sum.  With r_codes == NULL (or kpad == 0) it is
  * plain W4A4.
  *
- * Rounding: the contraction accumulates exact operand values in FP32, except
- * that calls with few rows per expert (num_rows <= 32 * num_experts, the
- * decode shape) add the correction to the activation before the GEMM as one
- * fp16 operand per element, X + (gr/gx) R, in units of gx: each corrected
- * element is rounded once more (relative 2^-11).  Both stay within
+ * Rounding: with the correction as an extended contraction the GEMM
+ * accumulates exact operand values in FP32.  Where that is slower -- few rows
+ * per expert (num_rows <= 32 * num_experts, the decode shape) and large
+ * grouped shapes that run on 256 x 256 tiles -- the correction is instead
+ * added to the activation before the GEMM, as one fp16 operand per element
+ * X + (gr/gx) R in units of gx, so each corrected element is rounded once
+ * more (relative 2^-11).  The environment variable QUADS_RAC_GEMM=extended |
+ * merged forces either form for many-rows calls.  Both stay within
  * max|Y - Y_exact| <= 1e-3 max|Y_exact| on the seeded workloads.
  *
  * operand_mode QUADS_OPERANDS_BF16 is the trainer's W4A16 forward [Gist

@@ -1,0 +1,103 @@
+"""GPU parity of both formulations of the RAC correction in the many-rows
+grouped GEMM, selected per call with QUADS_RAC_GEMM:
+- extended: the correction as an extended contraction, exact up to FP32
+  accumulation;
+- merged: the correction added to the activation as one fp16 operand, with
+  one more rounding per corrected element.
+Both are checked against the oracle's float64 extended-K reference at the
+1e-3 bar: dense and grouped shapes, ragged rows, a gathered row order, and
+the SwiGLU epilogue."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quads_oracle as O
+from fp4_quantized_moe_amd import _lib as Q
+from fp4_quantized_moe_amd import synthetic as S
+from tests.gpu_util import dev_act, host, log, quantize_weights_gpu, rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+@pytest.fixture
+def rac_mode():
+    old = os.environ.get("QUADS_RAC_GEMM")
+
+    def set_mode(m):
+        os.environ["QUADS_RAC_GEMM"] = m
+
+    yield set_mode
+    if old is None:
+        os.environ.pop("QUADS_RAC_GEMM", None)
+    else:
+        os.environ["QUADS_RAC_GEMM"] = old
+
+
+def _grouped(seed, counts, T, K, N, n_seg=1):
+    rng = np.random.default_rng(seed)
+    xa = S.activation(rng, T, K, max(1, K // 100), 30.0, bf16=True)
+    wa = S.weights(rng, (len(counts), N, K))
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rt = rng.integers(0, T, int(offs[-1])).astype(np.int32)
+    return xa, wa, offs, rt
+
+
+def _run(xa, wa, offs, rt, k, n_seg=1, epilogue=Q.EPI_NONE):
+    x = dev_act(xa)
+    E, N, K = wa.f32.shape
+    wc, ws_, wg = quantize_weights_gpu(dev_act(wa), n_seg)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    sel, res, nsel = Q.rac_select(x, q, scores, k)
+    R = int(offs[-1])
+    return Q.moe_w4a4_gemm(w_codes=wc, w_scales=ws_, w_gscale=wg, n_seg=n_seg, N=N, K=K,
+                           expert_offsets=torch.from_numpy(offs).cuda(), num_rows=R, x=q,
+                           res=res if nsel else None, sel_idx=sel,
+                           row_token=None if rt is None else torch.from_numpy(rt).cuda(), epilogue=epilogue)
+
+
+@pytest.mark.parametrize("mode", ["extended", "merged"])
+@pytest.mark.parametrize("k", [25, 50, 100])
+def test_dense_both_formulations(rac_mode, mode, k):
+    rac_mode(mode)
+    wl = S.expert_gemm(M=1024)
+    log(f"[gemm-rac] dense 1024x2048x1536 k={k} {mode}")
+    offs = np.array([0, 1024], np.int32)
+    y = host(_run(wl.x, S.Activation(wl.w.f32[None], wl.w.bits[None]), offs, None, k))
+    _, _, _, we = O.quantize_weights(wl.w.f32[None], 1)
+    ref = O.rac_linear(wl.x.f32, we, k)["y"]
+    err = rel_err(y, ref)
+    log(f"  rel err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("mode", ["extended", "merged"])
+def test_grouped_gathered_both_formulations(rac_mode, mode):
+    rac_mode(mode)
+    counts = [300, 0, 257, 511, 64, 1, 200, 129]
+    xa, wa, offs, rt = _grouped(601, counts, 700, 768, 512)
+    log(f"[gemm-rac] grouped experts {counts} K=768 N=512 k=50 {mode}")
+    y = host(_run(xa, wa, offs, rt, 50))
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    ref = O.rac_linear(xa.f32, we, 50, rt, offs)["y"]
+    err = rel_err(y, ref)
+    log(f"  rel err {err:.2e}")
+    assert err <= TOL
+
+
+def test_grouped_swiglu_merged(rac_mode):
+    """gate/up stacked along N with two tensor scales, SwiGLU epilogue, merged
+    operand: h against silu(gate) * up of the oracle's float64 product."""
+    rac_mode("merged")
+    counts = [400, 333, 0, 291]
+    xa, wa, offs, rt = _grouped(602, counts, 600, 512, 512)
+    log(f"[gemm-rac] grouped SwiGLU experts {counts} K=512 N=512 merged")
+    h = host(_run(xa, wa, offs, rt, 50, n_seg=2, epilogue=Q.EPI_SWIGLU).float())
+    _, _, _, we = O.quantize_weights(wa.f32, 2)
+    y = O.rac_linear(xa.f32, we, 50, rt, offs)["y"]
+    I = y.shape[1] // 2
+    h_ref = O.swiglu(y[:, :I], y[:, I:])
+    tol = 2.0 ** -8 * np.abs(h_ref) + 2e-3 * np.abs(y).max() * (np.abs(y[:, I:]) + np.abs(y[:, :I]) + 1)
+    assert (np.abs(h - h_ref) <= tol).all()
