@@ -160,8 +160,12 @@ def setup_moe(Q, S, k, decode):
     stages = [("route", rc), ("quantize_x", qx), ("rac_x", sx), ("gate_up_prepare", g1.prepare),
               ("gate_up", g1.run), ("quantize_h", qh), ("rac_h", sh), ("down_prepare", g2.prepare),
               ("down", g2.run), ("combine", cc)]
-    f1 = 2.0 * R * N2 * (H + nsel_x)
-    f2 = 2.0 * R * H * (I + nsel_h)
+    # MFMA work the RAC GEMMs execute: both shapes add the correction to the
+    # activation operand (one contraction over K), unless QUADS_RAC_GEMM=extended
+    # forces the extended contraction (K + nsel) on the prefill's 256x256 tiles.
+    merged = decode or os.environ.get("QUADS_RAC_GEMM") != "extended"
+    f1 = 2.0 * R * N2 * (H + (0 if merged else nsel_x))
+    f2 = 2.0 * R * H * (I + (0 if merged else nsel_h))
     # plain W4A4 layer
     qxp = Q.QuantizeCall(x)
     qp, _ = qxp()
@@ -177,12 +181,15 @@ def setup_moe(Q, S, k, decode):
     cnt = np.diff(offs.cpu().numpy())
     cfg = {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "top": wl.top, "intermediate": I,
            "k_percent": k, "nsel_x": nsel_x, "nsel_h": nsel_h,
+           "rac_gemm": "merged fp16 operand (flops 2*R*N*K)" if merged else "extended K (flops 2*R*N*(K+nsel))",
            "rows_per_expert": {"min": int(cnt.min()), "max": int(cnt.max()), "mean": float(cnt.mean())}}
     wdec = {"gate_up": E * N2 * H * 0.5625, "down": E * H * I * 0.5625}
 
     return dict(stages=stages, plain=plain, tokens=T, flops=f1 + f2, dominant="gate_up", dominant_flops=f1,
-                dominant_kernel=("k_gemm_small<1,true> (gate_up, SwiGLU, few rows per expert)" if decode else
-                                 "k_gemm<256x256 tiles,0,1,true> (gate_up, SwiGLU)"),
+                dominant_kernel=("k_gemm_small<1, true> (gate_up, SwiGLU, merged RAC operand, few rows per expert)"
+                                 if decode else
+                                 ("k_gemm<Cfg<256, 256, 2, 4, 1>, 2, 1, false> (gate_up, SwiGLU, merged RAC operand)"
+                                  if merged else "k_gemm<Cfg<256, 256, 2, 4, 1>, 0, 1, true> (gate_up, SwiGLU, extended K)")),
                 config=cfg, cpu_baseline=None, weight_bytes=wdec)
 
 
