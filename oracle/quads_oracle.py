@@ -565,3 +565,21 @@ def qat_linear_backward(x, w_master, dy, row_token=None, expert_offsets=None):
     dx = np.zeros_like(x)
     np.add.at(dx, rt, dxr)
     return dict(w_qdq=w_qdq, dxr=dxr, dx=dx, dw=dw)
+
+
+def rac_merged_operand(q, r, sel_idx, nsel):
+    """The RAC-corrected activation as one fp16 operand, in units of the
+    activation's tensor scale: for a selected channel c = sel_j,
+    A[t, c] = fp16(X'[t, c] + fl32(R'[t, j] * fl32(g_r / g_x))), and X'[t, c]
+    elsewhere.  X' and R' are the exact e2m1 * e4m3 values (no tensor scale);
+    the sum is one fp32 addition, then one rounding to fp16 ([Gist §2.2-B]:
+    the correction is added to the quantized activation before the GEMM).
+    Returns float16 [rows, cols]."""
+    xs = dequant_exact(q.codes, q.scales, np.float32(1.0)).astype(np.float32)
+    out = xs.copy()
+    if nsel:
+        rs = dequant_exact(r.codes, r.scales, np.float32(1.0)).astype(np.float32)
+        ratio = np.float32(np.float32(r.g) / np.float32(q.g))
+        cols = sel_idx[:nsel]
+        out[:, cols] = (xs[:, cols] + (rs[:, :nsel] * ratio).astype(np.float32)).astype(np.float32)
+    return out.astype(np.float16)

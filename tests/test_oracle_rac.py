@@ -136,3 +136,23 @@ def test_residual_pad_columns_are_zero():
     assert (code[:, n:] == 0).all()
     # the last block holds 4 real + 12 pad entries: the scale comes from the real ones
     assert O.dequant_exact(r.codes, r.scales, r.g)[:, n:].max() == 0
+
+
+def test_merged_operand_definition():
+    """The merged operand equals the compensated activation divided by g_x,
+    up to the fp16 rounding: unselected channels carry X' exactly (NVFP4
+    values fit fp16), selected ones are within one fp16 rounding of the fp64
+    value X' + R' g_r / g_x."""
+    x = _dense(48, 64, 256)
+    q = O.quantize_nvfp4(x)
+    for k in (0, 50, 100):
+        sel, n = O.rac_select(O.rac_scores(x, q), k)
+        r = O.rac_quantize_residual(x, q, sel, n)
+        a = O.rac_merged_operand(q, r, sel, n).astype(np.float64)
+        xe = O.dequant_exact(q.codes, q.scales, np.float32(1.0))
+        unsel = np.setdiff1d(np.arange(256), sel[:n])
+        assert np.array_equal(a[:, unsel], xe[:, unsel])
+        if n:
+            re = O.dequant_exact(r.codes, r.scales, np.float32(1.0))
+            exact = xe[:, sel[:n]] + re[:, :n] * (np.float64(np.float32(r.g)) / np.float64(np.float32(q.g)))
+            assert (np.abs(a[:, sel[:n]] - exact) <= 2.0 ** -10 * np.abs(exact) + 2.0 ** -24).all()
