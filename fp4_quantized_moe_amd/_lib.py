@@ -43,14 +43,14 @@ class _GemmArgs(ctypes.Structure):
         ("w_codes", _vp), ("w_scales", _vp), ("w_gscale", _vp),
         ("x_bf16", _vp), ("w_bf16", _vp),
         ("row_token", _vp), ("expert_offsets", _vp),
-        ("y", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
+        ("y", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t), ("x_merged", _vp),
     ]
 
 
 EXPORTS = [
     "quads_last_error", "quads_version", "quads_rac_nsel", "quads_rac_kpad",
     "quads_quantize_workspace_bytes", "quads_quantize_nvfp4",
-    "quads_rac_select_workspace_bytes", "quads_rac_select",
+    "quads_rac_select_workspace_bytes", "quads_rac_select", "quads_rac_select_merged",
     "quads_moe_gemm_workspace_bytes", "quads_moe_w4a4_gemm", "quads_moe_gemm_prepare",
     "quads_weight_qdq_workspace_bytes", "quads_weight_qdq",
     "quads_moe_route_workspace_bytes", "quads_moe_route", "quads_moe_combine",
@@ -83,6 +83,9 @@ def load(path: str = LIB_PATH):
     L.quads_rac_select.restype = ctypes.c_int
     L.quads_rac_select.argtypes = [_vp, ctypes.c_int, ctypes.POINTER(_NVFP4), _vp, _c_i32, _vp, _NVFP4,
                                    _vp, ctypes.c_size_t, _vp]
+    L.quads_rac_select_merged.restype = ctypes.c_int
+    L.quads_rac_select_merged.argtypes = [_vp, ctypes.c_int, ctypes.POINTER(_NVFP4), _vp, _c_i32, _vp, _NVFP4, _vp,
+                                          _vp, ctypes.c_size_t, _vp]
     L.quads_moe_gemm_workspace_bytes.restype = ctypes.c_size_t
     L.quads_moe_gemm_workspace_bytes.argtypes = [ctypes.POINTER(_GemmArgs)]
     L.quads_moe_w4a4_gemm.restype = ctypes.c_int
@@ -210,9 +213,12 @@ def quantize_nvfp4(x: torch.Tensor, want_scores: bool = False, gscale: torch.Ten
 
 
 class SelectCall:
-    """quads_rac_select with sel_idx and the residual tensor allocated once."""
+    """quads_rac_select with sel_idx and the residual tensor allocated once;
+    with merged=True quads_rac_select_merged, which also writes the
+    RAC-merged fp16 activation `self.merged` [rows, cols]."""
 
-    def __init__(self, x: torch.Tensor, xq: NVFP4Tensor, scores: torch.Tensor, k_percent: int):
+    def __init__(self, x: torch.Tensor, xq: NVFP4Tensor, scores: torch.Tensor, k_percent: int,
+                 merged: bool = False):
         _require_cuda(x, scores)
         rows, cols = xq.rows, xq.cols
         self.nsel = rac_nsel(cols, k_percent)
@@ -229,10 +235,16 @@ class SelectCall:
         self._rs = self.res.c_struct()
         self._dt = _dtype_code(x)
         self.kpad = kpad
+        self.merged = torch.empty(rows, cols, dtype=torch.float16, device=dev) if merged else None
 
     def __call__(self):
-        _check(load().quads_rac_select(_ptr(self.x), self._dt, ctypes.byref(self._xs), _ptr(self.scores), self.k,
-                                       _ptr(self.sel), self._rs, None, 0, _stream()), "quads_rac_select")
+        if self.merged is not None:
+            _check(load().quads_rac_select_merged(_ptr(self.x), self._dt, ctypes.byref(self._xs), _ptr(self.scores),
+                                                  self.k, _ptr(self.sel), self._rs, _ptr(self.merged), None, 0,
+                                                  _stream()), "quads_rac_select_merged")
+        else:
+            _check(load().quads_rac_select(_ptr(self.x), self._dt, ctypes.byref(self._xs), _ptr(self.scores), self.k,
+                                           _ptr(self.sel), self._rs, None, 0, _stream()), "quads_rac_select")
         return self.sel[:self.kpad], self.res, self.nsel
 
 
@@ -252,7 +264,7 @@ class GemmCall:
     def __init__(self, *, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
                  expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
                  sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
-                 x_bf16=None, w_bf16=None, y=None):
+                 x_bf16=None, w_bf16=None, y=None, x_merged=None):
         L = load()
         E = int(expert_offsets.numel()) - 1
         bf16_mode = x_bf16 is not None
@@ -263,7 +275,7 @@ class GemmCall:
             else:
                 y = torch.empty(num_rows, N, dtype=y_dtype, device=dev)
         self.y = y
-        self._keep = [w_codes, w_scales, w_gscale, expert_offsets, x, res, sel_idx, row_token, x_bf16, w_bf16]
+        self._keep = [w_codes, w_scales, w_gscale, expert_offsets, x, res, sel_idx, row_token, x_bf16, w_bf16, x_merged]
         a = _GemmArgs()
         a.struct_size = ctypes.sizeof(_GemmArgs)
         a.operand_mode = OPERANDS_BF16 if bf16_mode else OPERANDS_W4A4
@@ -285,6 +297,9 @@ class GemmCall:
                 a.r_codes, a.r_scales, a.r_gscale = res.codes.data_ptr(), res.scales.data_ptr(), res.gscale.data_ptr()
                 a.sel_idx = sel_idx.data_ptr()
                 a.kpad = res.cols
+                if x_merged is not None:
+                    _require_cuda(x_merged)
+                    a.x_merged = x_merged.data_ptr()
         a.row_token = None if row_token is None else row_token.data_ptr()
         a.expert_offsets = expert_offsets.data_ptr()
         a.y = y.data_ptr()

@@ -109,28 +109,26 @@ size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols) {
   return 0;
 }
 
-quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq, const float *scores,
-                                int32_t k_percent, int32_t *sel_idx, quads_nvfp4_t res, void *ws,
-                                size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
-  if (dt != QUADS_F32 && dt != QUADS_BF16) return fail(QUADS_ERR_ARG, "rac_select: bad dtype");
-  if (!xq) return fail(QUADS_ERR_ARG, "rac_select: null xq");
-  if (k_percent < 0 || k_percent > 100) return fail(QUADS_ERR_ARG, "rac_select: k_percent %d outside [0,100]", k_percent);
+static quads_status_t rac_select_impl(const char *what, const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
+                                      const float *scores, int32_t k_percent, int32_t *sel_idx, quads_nvfp4_t res,
+                                      void *merged_f16, void *stream) {
+  if (dt != QUADS_F32 && dt != QUADS_BF16) return fail(QUADS_ERR_ARG, "%s: bad dtype", what);
+  if (!xq) return fail(QUADS_ERR_ARG, "%s: null xq", what);
+  if (k_percent < 0 || k_percent > 100) return fail(QUADS_ERR_ARG, "%s: k_percent %d outside [0,100]", what, k_percent);
   if (xq->batch != 1 || xq->cols <= 0 || xq->cols % 16 || xq->rows < 0)
-    return fail(QUADS_ERR_SHAPE, "rac_select: xq must be one [rows, cols] tensor with cols %% 16 == 0");
-  if (xq->cols > kMaxSelectCols) return fail(QUADS_ERR_SHAPE, "rac_select: cols > %lld", (long long)kMaxSelectCols);
+    return fail(QUADS_ERR_SHAPE, "%s: xq must be one [rows, cols] tensor with cols %% 16 == 0", what);
+  if (xq->cols > kMaxSelectCols) return fail(QUADS_ERR_SHAPE, "%s: cols > %lld", what, (long long)kMaxSelectCols);
   const int64_t nsel = quads_rac_nsel(xq->cols, k_percent), kpad = quads_rac_kpad(nsel);
   if (res.cols != kpad || res.rows != xq->rows || res.batch != 1)
-    return fail(QUADS_ERR_SHAPE, "rac_select: res must be [rows=%lld, kpad=%lld]", (long long)xq->rows, (long long)kpad);
-  if (quads::rac_rows_per_group(xq->cols, kpad) < 1)
-    return fail(QUADS_ERR_SHAPE, "rac_select: cols/kpad too large for the kernel's LDS staging (cols*4 + kpad*4 <= ~63 KiB)");
-  if (!scores || !res.gscale || (kpad > 0 && !sel_idx))
-    return fail(QUADS_ERR_ARG, "rac_select: null pointer");
+    return fail(QUADS_ERR_SHAPE, "%s: res must be [rows=%lld, kpad=%lld]", what, (long long)xq->rows, (long long)kpad);
+  const bool merged = merged_f16 != nullptr;
+  if (quads::rac_rows_per_group(xq->cols, kpad, merged && kpad > 0) < 1)
+    return fail(QUADS_ERR_SHAPE, "%s: cols/kpad too large for the kernel's LDS staging", what);
+  if (!scores || !res.gscale || (kpad > 0 && !sel_idx)) return fail(QUADS_ERR_ARG, "%s: null pointer", what);
   if (kpad > 0 && xq->rows > 0 && (!x || !xq->codes || !xq->scales || !xq->gscale || !res.codes || !res.scales))
-    return fail(QUADS_ERR_ARG, "rac_select: null pointer");
-  if (misaligned({x, xq->codes, xq->scales, res.codes, res.scales, scores}))
-    return fail(QUADS_ERR_ARG, "rac_select: arrays must be 16-byte aligned");
+    return fail(QUADS_ERR_ARG, "%s: null pointer", what);
+  if (misaligned({x, xq->codes, xq->scales, res.codes, res.scales, scores, merged_f16}))
+    return fail(QUADS_ERR_ARG, "%s: arrays must be 16-byte aligned", what);
   quads::RacLaunch a{};
   a.x = x;
   a.x_bf16 = dt == QUADS_BF16;
@@ -146,7 +144,25 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
   a.r_codes = res.codes;
   a.r_scales = res.scales;
   a.r_gscale = res.gscale;
-  return device_status(quads::launch_rac_select(a, static_cast<hipStream_t>(stream)), "rac_select");
+  a.merged = static_cast<uint16_t *>(merged_f16);
+  return device_status(quads::launch_rac_select(a, static_cast<hipStream_t>(stream)), what);
+}
+
+quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq, const float *scores,
+                                int32_t k_percent, int32_t *sel_idx, quads_nvfp4_t res, void *ws,
+                                size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return rac_select_impl("rac_select", x, dt, xq, scores, k_percent, sel_idx, res, nullptr, stream);
+}
+
+quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
+                                       const float *scores, int32_t k_percent, int32_t *sel_idx, quads_nvfp4_t res,
+                                       void *merged_f16, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!merged_f16) return fail(QUADS_ERR_ARG, "rac_select_merged: null merged_f16");
+  return rac_select_impl("rac_select_merged", x, dt, xq, scores, k_percent, sel_idx, res, merged_f16, stream);
 }
 
 static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch &g) {
@@ -170,7 +186,7 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
     return fail(QUADS_ERR_SHAPE, "gemm: size overflow");
   if (!a->expert_offsets || !a->y) return fail(QUADS_ERR_ARG, "gemm: null expert_offsets or y");
   if (misaligned({a->y, a->ws, a->x_codes, a->x_scales, a->r_codes, a->r_scales, a->w_codes, a->w_scales, a->x_bf16,
-                  a->w_bf16}))
+                  a->w_bf16, a->x_merged}))
     return fail(QUADS_ERR_ARG, "gemm: arrays must be 16-byte aligned");
   if (a->row_token == nullptr && a->act_rows < a->num_rows)
     return fail(QUADS_ERR_SHAPE, "gemm: identity rows need act_rows >= num_rows");
@@ -205,6 +221,7 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
       g.r_g = a->r_gscale;
       g.sel_idx = a->sel_idx;
       g.kpad = a->kpad;
+      g.x_merged = static_cast<const uint16_t *>(a->x_merged);
     }
   } else {
     if (!a->x_bf16 || !a->w_bf16) return fail(QUADS_ERR_ARG, "gemm: null bf16 operand");

@@ -1185,6 +1185,7 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
 // every call, so one process can compare the two.
 bool use_merged(const GemmLaunch &a) {
   if (a.mode != 0 || a.r_codes == nullptr || a.kpad == 0 || gemm_use_small(a)) return false;
+  if (a.x_merged != nullptr) return true;  // the caller built it: no merge pass to pay for
   if (const char *f = getenv("QUADS_RAC_GEMM")) {
     if (strcmp(f, "extended") == 0) return false;
     if (strcmp(f, "merged") == 0) return true;
@@ -1205,7 +1206,7 @@ TileCfg pick_cfg_for(const GemmLaunch &a) {
 
 size_t gemm_ws_bytes(const GemmLaunch &a) {
   size_t b = align256(static_cast<size_t>(a.E + 1) * sizeof(int32_t));
-  if (a.mode == 0 && a.r_codes != nullptr && a.kpad > 0)
+  if (a.mode == 0 && a.r_codes != nullptr && a.kpad > 0 && a.x_merged == nullptr)
     b += (gemm_use_small(a) || use_merged(a)) ? align256(gemm_small_res_bytes(a))
                                               : align256(static_cast<size_t>(a.E) * a.N * a.kpad * sizeof(uint16_t));
   return b;
@@ -1217,13 +1218,15 @@ hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
   if (gemm_use_small(a)) {
     uint16_t *rd = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
-    return res ? launch_gemm_small_prepare(a, rd, stream) : hipSuccess;
+    return res && a.x_merged == nullptr ? launch_gemm_small_prepare(a, rd, stream) : hipSuccess;
   }
   const TileCfg c = pick_cfg_for(a);
   if (use_merged(a)) {
-    uint16_t *xm = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
-    const hipError_t e = launch_gemm_small_prepare(a, xm, stream);
-    if (e != hipSuccess) return e;
+    if (a.x_merged == nullptr) {
+      uint16_t *xm = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
+      const hipError_t e = launch_gemm_small_prepare(a, xm, stream);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(256), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
   } else if (res) {
     uint16_t *wg = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
@@ -1244,6 +1247,7 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   int32_t *tile_offsets = reinterpret_cast<int32_t *>(ws);
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
   uint16_t *wg = res ? reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t))) : nullptr;
+  if (res && a.x_merged != nullptr) wg = const_cast<uint16_t *>(a.x_merged);  // read only
   if (gemm_use_small(a)) return launch_gemm_small(a, wg, stream);
   const bool merged = use_merged(a);
   const TileCfg c = pick_cfg_for(a);

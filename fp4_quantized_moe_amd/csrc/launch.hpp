@@ -38,9 +38,10 @@ struct RacLaunch {
   int32_t *sel_idx;
   uint8_t *r_codes, *r_scales;
   float *r_gscale;
+  uint16_t *merged;  // [rows, cols] fp16 RAC-merged activation, or null
 };
 // Rows of dx staged per pass by the RAC kernel (< 1: the shape does not fit in LDS).
-int rac_rows_per_group(int64_t cols, int64_t kpad);
+int rac_rows_per_group(int64_t cols, int64_t kpad, bool merged = false);
 hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream);
 
 // ---- gemm.hip --------------------------------------------------------------
@@ -61,6 +62,7 @@ struct GemmLaunch {
   const int32_t *row_token, *expert_offsets;
   void *y;
   void *ws;
+  const uint16_t *x_merged;  // caller's RAC-merged fp16 activation, or null
 };
 size_t gemm_ws_bytes(const GemmLaunch &a);
 // prepare: tile list + residual weight-column gather; main: the GEMM kernel.

@@ -186,9 +186,10 @@ __device__ __forceinline__ void load_raw(RawBlock<BF16> &r, const void *x, const
 }
 
 // dx = x - dq for one block (the quantizer's FP32 operations: dq = level * d
-// with d = dec(scale) * g), stored to LDS.
+// with d = dec(scale) * g), stored to LDS; with `xp` also the block's exact
+// values X' = level * dec(scale) (units of g, exact in fp16) as fp16.
 template <bool BF16>
-__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *dst) {
+__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *dst, uint16_t *xp = nullptr) {
   float v[16];
   if constexpr (BF16) {
     const uint32_t w[8] = {r.x[0].x, r.x[0].y, r.x[0].z, r.x[0].w, r.x[1].x, r.x[1].y, r.x[1].z, r.x[1].w};
@@ -206,8 +207,9 @@ __device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, floa
       v[4 * i + 3] = __uint_as_float(r.x[i].w);
     }
   }
-  const float d = e4m3_to_f32(r.scale) * gx;
-  float dx[16];
+  const float sd = e4m3_to_f32(r.scale);
+  const float d = sd * gx;
+  float dx[16], xv[16];
 #define QUADS_DX(word, byte, i0)                                               \
   {                                                                            \
     const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, byte); \
@@ -228,6 +230,24 @@ __device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, floa
   o[1] = make_float4(dx[4], dx[5], dx[6], dx[7]);
   o[2] = make_float4(dx[8], dx[9], dx[10], dx[11]);
   o[3] = make_float4(dx[12], dx[13], dx[14], dx[15]);
+  if (xp != nullptr) {
+    // X' from the code itself, so that a negative-zero code (0x8) gives -0
+    // like every other dequantization here (the hardware conversion gives
+    // +0 for it, which is immaterial for dx).
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = i < 8 ? r.codes.x : r.codes.y;
+      xv[i] = dequant_code((w >> (4 * (i & 7))) & 0xFu, sd);
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      h[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(xv[2 * i]))) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(xv[2 * i + 1]))) << 16);
+    uint4 *q = reinterpret_cast<uint4 *>(xp);
+    q[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    q[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  }
 }
 
 // Blocks of one row group held in registers per thread: block tid + j*kThreads.
@@ -239,15 +259,21 @@ constexpr int kGroupSlots = 4;
 // Schedule per workgroup: the loads of the first row group are issued before
 // the mask search so that their latency overlaps it; afterwards, while group
 // g is gathered and quantized, the loads of group g+1 are in flight.
-template <bool BF16, int PER>
+// MERGED: also write the RAC-corrected activation as one fp16 operand
+// merged[rows, K] = fp16(X' + (g_r/g_x) R') on the selected channels, X'
+// elsewhere (units of g_x): X' goes to a second LDS array when dx is
+// computed, each gathered block adds its dequantized residual to its
+// channels, and the row group is copied out with 16-byte stores.
+template <bool BF16, int PER, bool MERGED>
 __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, int K, const uint8_t *x_codes,
                                                   const uint8_t *x_scales, const float *x_g,
                                                   const uint32_t *scores, int nsel, int kpad, int32_t *sel_out,
                                                   float *r_g_out, uint8_t *r_codes, uint8_t *r_scales, int rb,
-                                                  int rows_per_wg) {
+                                                  int rows_per_wg, uint16_t *merged) {
   extern __shared__ uint4 lds_u4[];
   int32_t *sel = reinterpret_cast<int32_t *>(lds_u4);
   float *region = reinterpret_cast<float *>(lds_u4) + kpad;
+  uint16_t *xm = reinterpret_cast<uint16_t *>(region + static_cast<int64_t>(rb) * K);  // MERGED: [rb][K] fp16
   __shared__ uint32_t slots[8 * (kThreads / 64)];
   const int tid = threadIdx.x;
   const int cb = K / 16, nblk = kpad / 16;
@@ -326,7 +352,8 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
 #pragma unroll
     for (int j = 0; j < kGroupSlots; ++j) {
       const int b = tid + j * kThreads;
-      if (j * kThreads < nb && b < nb) store_dx<BF16>(raw[j], gx, region + b * 16);
+      if (j * kThreads < nb && b < nb)
+        store_dx<BF16>(raw[j], gx, region + b * 16, MERGED ? xm + b * 16 : nullptr);
     }
     if (r0 + rb < r_stop) issue(r0 + rb);
     __syncthreads();
@@ -343,6 +370,27 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
       const int64_t row = r0 + rr;
       reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
       r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);
+      if constexpr (MERGED) {
+        // Each selected channel of a row sits in exactly one gathered block.
+        const float ratio = gr / gx;
+        const float sr = e4m3_to_f32(q.scale);
+        uint16_t *xr = xm + rr * K;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = sel[jb * 16 + i];
+          if (c >= 0) {
+            const uint32_t code = ((i < 8 ? q.lo : q.hi) >> (4 * (i & 7))) & 0xFu;
+            const float xv = static_cast<float>(__builtin_bit_cast(_Float16, xr[c]));
+            xr[c] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(xv + dequant_code(code, sr) * ratio));
+          }
+        }
+      }
+    }
+    if constexpr (MERGED) {
+      __syncthreads();  // every block's residual is in xm
+      const int chunks = nr * K / 8;
+      for (int t = tid; t < chunks; t += kThreads)
+        reinterpret_cast<uint4 *>(merged + r0 * K)[t] = reinterpret_cast<const uint4 *>(xm)[t];
     }
     __syncthreads();  // dx region is rewritten by the next group
   }
@@ -350,9 +398,9 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
 
 }  // namespace
 
-int rac_rows_per_group(int64_t cols, int64_t kpad) {
+int rac_rows_per_group(int64_t cols, int64_t kpad, bool merged) {
   const int64_t budget = 64 * 1024 - kpad * 4 - 64;
-  int64_t rb = budget / (cols * 4);
+  int64_t rb = budget / (cols * (merged ? 6 : 4));
   if (rb > 4) rb = 4;  // ~40 KiB per workgroup at cols 2048: four workgroups per CU
   const int64_t by_slots = static_cast<int64_t>(kGroupSlots) * kThreads / (cols / 16);
   if (rb > by_slots) rb = by_slots;  // a row group's blocks fit the per-thread load slots
@@ -362,10 +410,18 @@ int rac_rows_per_group(int64_t cols, int64_t kpad) {
 namespace {
 template <bool BF16, int PER>
 void launch_rac_t(const RacLaunch &a, int64_t n_wg, int rb, int rows_per_wg, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((k_rac<BF16, PER>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
-                     static_cast<int>(a.cols), a.x_codes, a.x_scales, a.x_gscale,
-                     reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.nsel),
-                     static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg);
+  if (a.merged != nullptr)
+    hipLaunchKernelGGL((k_rac<BF16, PER, true>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
+                       static_cast<int>(a.cols), a.x_codes, a.x_scales, a.x_gscale,
+                       reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.nsel),
+                       static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg,
+                       a.merged);
+  else
+    hipLaunchKernelGGL((k_rac<BF16, PER, false>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
+                       static_cast<int>(a.cols), a.x_codes, a.x_scales, a.x_gscale,
+                       reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.nsel),
+                       static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg,
+                       static_cast<uint16_t *>(nullptr));
 }
 
 template <bool BF16>
@@ -384,9 +440,12 @@ void launch_rac_per(const RacLaunch &a, int64_t n_wg, int rb, int rows_per_wg, s
 }
 }  // namespace
 
-hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
-  if (a.cols > 64 * kThreads) return hipErrorInvalidValue;  // the API bounds cols first
-  int rb = rac_rows_per_group(a.cols, a.kpad);
+hipError_t launch_rac_select(const RacLaunch &a_in, hipStream_t stream) {
+  if (a_in.cols > 64 * kThreads) return hipErrorInvalidValue;  // the API bounds cols first
+  const bool merged = a_in.merged != nullptr && a_in.kpad > 0;
+  RacLaunch a = a_in;
+  if (!merged) a.merged = nullptr;  // nothing selected: the GEMM takes the plain path
+  int rb = rac_rows_per_group(a.cols, a.kpad, merged);
   if (rb < 1) return hipErrorInvalidValue;
   int64_t n_wg = a.kpad == 0 || a.rows == 0 ? 1 : (a.rows + rb - 1) / rb;
   int rows_per_wg = rb;
@@ -395,7 +454,7 @@ hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
     rows_per_wg = static_cast<int>(rb * iters);
     n_wg = (a.rows + rows_per_wg - 1) / rows_per_wg;
   }
-  const size_t lds = static_cast<size_t>(a.kpad) * 4 + static_cast<size_t>(rb) * a.cols * 4;
+  const size_t lds = static_cast<size_t>(a.kpad) * 4 + static_cast<size_t>(rb) * a.cols * (merged ? 6 : 4);
   if (a.x_bf16)
     launch_rac_per<true>(a, n_wg, rb, rows_per_wg, lds, stream);
   else

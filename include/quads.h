@@ -130,6 +130,22 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
                                 const float *scores, int32_t k_percent, int32_t *sel_idx,
                                 quads_nvfp4_t res, void *ws, size_t ws_bytes, void *stream);
 
+/* quads_rac_select_merged -- quads_rac_select that also writes the corrected
+ * activation as one fp16 operand [Gist 2.2-B: the correction is added to the
+ * quantized activation before the GEMM], merged_f16 [rows, cols] (device,
+ * 16-byte aligned, caller-owned), in units of xq's tensor scale g_x:
+ *   merged[r, c] = fp16( X'[r, c] + fl32(R'[r, j] * fl32(g_r / g_x)) )  for c = sel_j,
+ *   merged[r, c] = X'[r, c]                                              otherwise,
+ * with X' and R' the exact e2m1 * e4m3 values of xq and res (no tensor scale)
+ * and one fp32 addition before the rounding.  Passing it to
+ * quads_moe_w4a4_gemm (x_merged) lets the GEMM contract over K alone with no
+ * merge pass of its own.  With kpad == 0 nothing is written (there is no
+ * correction; the GEMM then takes the plain path). */
+quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
+                                       const float *scores, int32_t k_percent, int32_t *sel_idx,
+                                       quads_nvfp4_t res, void *merged_f16, void *ws, size_t ws_bytes,
+                                       void *stream);
+
 /* ---------------------------------------------------------------------------
  * quads_moe_w4a4_gemm -- token-permuted grouped expert GEMM with the RAC
  * segment (extended K), on fp16 MFMA with exact NVFP4 -> fp16 operand decode:
@@ -213,6 +229,11 @@ typedef struct {
   void *y;
   void *ws;
   size_t ws_bytes;
+  /* Optional [act_rows, K] fp16 RAC-merged activation from
+     quads_rac_select_merged (units of x_gscale), or NULL.  With a residual
+     present the GEMM then contracts it over K alone (the merged form below),
+     whatever the shape, and builds no merged operand of its own. */
+  const void *x_merged;
 } quads_moe_gemm_args;
 
 size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a);

@@ -101,3 +101,60 @@ def test_grouped_swiglu_merged(rac_mode):
     h_ref = O.swiglu(y[:, :I], y[:, I:])
     tol = 2.0 ** -8 * np.abs(h_ref) + 2e-3 * np.abs(y).max() * (np.abs(y[:, I:]) + np.abs(y[:, :I]) + 1)
     assert (np.abs(h - h_ref) <= tol).all()
+
+
+@pytest.mark.parametrize("case", [("bf16", 300, 2048, 50), ("bf16", 300, 2048, 100), ("bf16", 77, 768, 25),
+                                  ("f32", 64, 256, 50), ("bf16", 40, 512, 0)])
+def test_rac_select_merged_bit_exact(case):
+    """quads_rac_select_merged's fp16 operand equals the oracle's
+    rac_merged_operand bit for bit (same fp32 operations, one rounding); the
+    mask and residual match as for quads_rac_select."""
+    dt, M, K, k = case
+    log(f"[rac-merged] {dt} M={M} K={K} k={k}")
+    rng = np.random.default_rng(603 + M + k)
+    xa = S.activation(rng, M, K, max(1, K // 100), 30.0, bf16=(dt == "bf16"))
+    x = dev_act(xa)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    call = Q.SelectCall(x, q, scores, k, merged=True)
+    sel, res, nsel = call()
+    oq = O.quantize_nvfp4(xa.f32)
+    osel, on = O.rac_select(O.rac_scores(xa.f32, oq), k)
+    assert nsel == on and np.array_equal(host(sel), osel)
+    if on == 0:
+        return  # nothing selected: the merged operand is not written
+    orr = O.rac_quantize_residual(xa.f32, oq, osel, on)
+    assert np.array_equal(host(res.codes), orr.codes) and np.array_equal(host(res.scales), orr.scales)
+    want = O.rac_merged_operand(oq, orr, osel, on)
+    got = host(call.merged)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("shape", ["dense", "grouped", "decode"])
+def test_gemm_with_caller_merged_operand(shape):
+    """The GEMM reads the operand quads_rac_select_merged wrote (no merge pass
+    of its own) on the DMA-tile, large-tile and few-rows shapes."""
+    if shape == "dense":
+        wl = S.expert_gemm(M=512)
+        xa, wa = wl.x, S.Activation(wl.w.f32[None], wl.w.bits[None])
+        offs, rt = np.array([0, 512], np.int32), None
+    elif shape == "grouped":
+        xa, wa, offs, rt = _grouped(604, [300, 0, 257, 511, 64, 1, 200, 129], 700, 768, 512)
+    else:
+        counts = [16, 0, 9, 16, 31, 1, 16, 12, 16, 16, 3, 16, 20, 16, 16, 8]
+        xa, wa, offs, rt = _grouped(605, counts, 200, 512, 256)
+    log(f"[gemm-rac] caller-merged operand, {shape}")
+    x = dev_act(xa)
+    E, N, K = wa.f32.shape
+    wc, ws_, wg = quantize_weights_gpu(dev_act(wa), 1)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    call = Q.SelectCall(x, q, scores, 50, merged=True)
+    sel, res, nsel = call()
+    R = int(offs[-1])
+    y = Q.moe_w4a4_gemm(w_codes=wc, w_scales=ws_, w_gscale=wg, N=N, K=K, expert_offsets=torch.from_numpy(offs).cuda(),
+                        num_rows=R, x=q, res=res, sel_idx=sel, x_merged=call.merged,
+                        row_token=None if rt is None else torch.from_numpy(rt).cuda())
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    ref = O.rac_linear(xa.f32, we, 50, rt, offs)["y"]
+    err = rel_err(host(y), ref)
+    log(f"  rel err {err:.2e}")
+    assert err <= TOL
