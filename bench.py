@@ -51,6 +51,9 @@ METRIC = "MoE W4A4+RAC expert-GEMM tokens/s & TFLOPS; % of MFMA peak; RAC overhe
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 CPU_BASELINE_MIN_S = 10.0  # repeat the oracle sample until at least this much CPU time
+# RAC steps write the merged fp16 activation (quads_rac_select_merged) and the
+# GEMMs read it; QUADS_RAC_GEMM=extended times the extended-K formulation.
+MERGED_RAC = os.environ.get("QUADS_RAC_GEMM") != "extended"
 
 
 def parse():
@@ -95,11 +98,14 @@ def setup_expert_gemm(Q, S, k):
     offs = torch.tensor([0, M], dtype=torch.int32, device="cuda")
     qc = Q.QuantizeCall(x, want_scores=True)
     q, scores = qc()
-    scall = Q.SelectCall(x, q, scores, k)
+    merged = MERGED_RAC and k > 0
+    scall = Q.SelectCall(x, q, scores, k, merged=merged)
     sel, res, nsel = scall()
     gc = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M,
-                    x=q, res=res if nsel else None, sel_idx=sel)
-    flops = 2.0 * M * N * (K + nsel)
+                    x=q, res=res if nsel else None, sel_idx=sel, x_merged=scall.merged if merged else None)
+    # MFMA work the RAC GEMM executes: one contraction over K on the merged
+    # operand, K + nsel with the extended contraction.
+    flops = 2.0 * M * N * (K + (0 if merged else nsel))
     stages = [("quantize_scores", qc), ("rac_select_residual", scall), ("gemm_prepare", gc.prepare),
               ("gemm", gc.run)]
     qp = Q.QuantizeCall(x, want_scores=False)
@@ -107,7 +113,9 @@ def setup_expert_gemm(Q, S, k):
     gp = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M, x=qpl)
     plain = [("quantize", qp), ("gemm_prepare", gp.prepare), ("gemm", gp.run)]
     cfg = {"workload": "expert_gemm", "tokens": M, "K": K, "N": N, "k_percent": k, "nsel": nsel,
-           "x": "bf16 N(0,1), 1% outlier channels x30", "w": "bf16 N(0,0.02) -> NVFP4 (offline)"}
+           "x": "bf16 N(0,1), 1% outlier channels x30", "w": "bf16 N(0,0.02) -> NVFP4 (offline)",
+           "rac_gemm": ("merged fp16 operand from quads_rac_select_merged (flops 2*M*N*K)" if merged else
+                        "extended K (flops 2*M*N*(K+nsel))")}
 
     def cpu_baseline():
         """The oracle's quantize + RAC + fp64 GEMM over all M tokens (the same
@@ -125,9 +133,12 @@ def setup_expert_gemm(Q, S, k):
         return M * reps / secs, secs, (f"the whole step ({M} tokens, K={K}, N={N}, k={k}%) x {reps} repetitions: "
                                        "oracle quantize + RAC + fp64 GEMM (weights quantized beforehand)")
 
+    kern = ("k_gemm<Cfg<128, 128, 2, 2, 2>, 2, 0, false> (merged RAC operand x NVFP4 weights, 128x128 tiles)"
+            if merged else "k_gemm_dma<2, 0, true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)")
+    summary = (f"k_gemm_merged_expert_gemm_k{k}_traffic.txt" if merged else f"k_gemm_dma_expert_gemm_k{k}_traffic.txt")
     return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
-                dominant_kernel="k_gemm_dma<2, 0, true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)", config=cfg, cpu_baseline=cpu_baseline,
-                traffic_summary=os.path.join(ROOT, "profiles", f"k_gemm_dma_expert_gemm_k{k}_traffic.txt"))
+                dominant_kernel=kern, config=cfg, cpu_baseline=cpu_baseline,
+                traffic_summary=os.path.join(ROOT, "profiles", summary))
 
 
 def setup_moe(Q, S, k, decode):
@@ -145,17 +156,19 @@ def setup_moe(Q, S, k, decode):
     ids, w, offs, rt, inv = rc()
     qx = Q.QuantizeCall(x, want_scores=True)
     q, sc = qx()
-    sx = Q.SelectCall(x, q, sc, k)
+    mr = MERGED_RAC and k > 0
+    sx = Q.SelectCall(x, q, sc, k, merged=mr)
     sel, res, nsel_x = sx()
     g1 = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
-                    x=q, res=res if nsel_x else None, sel_idx=sel, row_token=rt, epilogue=Q.EPI_SWIGLU)
+                    x=q, res=res if nsel_x else None, sel_idx=sel, row_token=rt, epilogue=Q.EPI_SWIGLU,
+                    x_merged=sx.merged if mr else None)
     h = g1.y
     qh = Q.QuantizeCall(h, want_scores=True)
     hq, hsc = qh()
-    sh = Q.SelectCall(h, hq, hsc, k)
+    sh = Q.SelectCall(h, hq, hsc, k, merged=mr)
     hsel, hres, nsel_h = sh()
     g2 = Q.GemmCall(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs, num_rows=R,
-                    x=hq, res=hres if nsel_h else None, sel_idx=hsel)
+                    x=hq, res=hres if nsel_h else None, sel_idx=hsel, x_merged=sh.merged if mr else None)
     cc = Q.CombineCall(g2.y, inv, w)
     stages = [("route", rc), ("quantize_x", qx), ("rac_x", sx), ("gate_up_prepare", g1.prepare),
               ("gate_up", g1.run), ("quantize_h", qh), ("rac_h", sh), ("down_prepare", g2.prepare),
@@ -163,7 +176,7 @@ def setup_moe(Q, S, k, decode):
     # MFMA work the RAC GEMMs execute: both shapes add the correction to the
     # activation operand (one contraction over K), unless QUADS_RAC_GEMM=extended
     # forces the extended contraction (K + nsel) on the prefill's 256x256 tiles.
-    merged = decode or os.environ.get("QUADS_RAC_GEMM") != "extended"
+    merged = mr or decode
     f1 = 2.0 * R * N2 * (H + (0 if merged else nsel_x))
     f2 = 2.0 * R * H * (I + (0 if merged else nsel_h))
     # plain W4A4 layer
