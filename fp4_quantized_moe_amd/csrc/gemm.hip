@@ -685,7 +685,11 @@ struct Lay {
   static constexpr int MA = 0, MB = 8192, MAS = MB + BN * 64, MBS = MAS + 1024, MEND = MBS + BN * 8;
   // Residual stage: R codes [128][32], R scales [128][4], gathered W [BN][128 B].
   static constexpr int RA = 0, RAS = 4096, RB = 4608, REND = RB + BN * 128;
-  static constexpr int STAGE = MEND > REND ? MEND : REND;
+  // Merged stage (64-element steps): merged fp16 activation [128][128 B],
+  // W codes [BN][32], W scales [BN][4].
+  static constexpr int XA = 0, XB = 16384, XBS = XB + BN * 32, XEND = XBS + BN * 4;
+  static constexpr int STAGE0 = MEND > REND ? MEND : REND;
+  static constexpr int STAGE = STAGE0 > XEND ? STAGE0 : XEND;
 };
 
 typedef __attribute__((address_space(3))) void lds_t;
@@ -819,6 +823,37 @@ __device__ __forceinline__ void compute_res(const uint8_t *st, f32x16 (&acc)[2][
   }
 }
 
+// Group g's half of one merged step (64 elements): A = the merged fp16
+// activation rows, B = weight codes decoded with their block scales.  The
+// contraction order is the residual step's with the operands swapped: lane
+// half h of group g takes elements [32h + 16g, +16) of the step.
+template <int NI>
+__device__ __forceinline__ void compute_merged(const uint8_t *st, f32x16 (&acc)[2][NI], int wm, int wn, int g,
+                                               int lane) {
+  using L = Lay<NI>;
+  const int r = lane & 31, h = lane >> 5;
+  uint2 cb[NI];
+  h2 sb[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = wn * 32 * NI + i * 32 + r;
+    cb[i] = *reinterpret_cast<const uint2 *>(st + L::XB + row * 32 + slot32(row, h) * 16 + 8 * g);
+    sb[i] = scale_h2(st[L::XBS + row * 4 + 2 * h + g]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint4 a[2], b[NI];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + r;
+      a[i] = *reinterpret_cast<const uint4 *>(st + L::XA + row * 128 + slot128(row, 4 * h + 2 * g + j) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) b[i] = decode8_f16(j ? cb[i].y : cb[i].x, sb[i]);
+    mfmas<NI>(a, b, acc);
+  }
+}
+
 // One DMA instruction of a thread: source at step 0, bytes per step, LDS
 // offset inside a stage, bytes per lane.
 struct Dma {
@@ -828,9 +863,12 @@ struct Dma {
 
 }  // namespace dmak
 
-// K % 128 == 0 and (residual) kpad % 64 == 0 (host-checked).
-template <int NI, int EPI, bool HAS_RES>
+// K % 128 == 0 and (residual) kpad % 64 == 0 (host-checked).  MERGED
+// (NI == 2 only): A is the RAC-merged fp16 activation p.x_f16, contracted
+// over K alone in 64-element steps; no residual segment.
+template <int NI, int EPI, bool HAS_RES, bool MERGED = false>
 __global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Params p) {
+  static_assert(!MERGED || (NI == 2 && !HAS_RES), "merged DMA steps: 128x128 tiles, no residual segment");
   using namespace dmak;
   using L = Lay<NI>;
   using C = typename L::C;
@@ -904,6 +942,39 @@ __global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Pa
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
+  if constexpr (MERGED) {
+    // Merged fp16 rows: 16 instructions of 8 lanes per 128-byte row; weight
+    // codes: 4 of 2 lanes per 32-byte row; weight scales: 2 of 4 bytes per
+    // row (waves 6-7 repeat waves 4-5).
+    auto xrows = [&](int n) -> Dma {
+      const int pos = 64 * n + lane, row = pos >> 3, c = slot128(row, pos & 7);
+      return {reinterpret_cast<const uint8_t *>(p.x_f16 + act_row(row) * K) + c * 16, 128, L::XA + 1024 * n, 16};
+    };
+    Dma dx[P];
+#pragma unroll
+    for (int q = 0; q < P - 1; ++q) dx[q] = xrows(wave + 8 * q);
+    if (g == 0) {
+      const int pos = 64 * wq + lane, row = pos >> 1, c = slot32(row, pos & 1);
+      dx[P - 1] = {p.w_codes + w_row(row) * (K / 2) + c * 16, 32, L::XB + 1024 * wq, 16};
+    } else {
+      dx[P - 1] = {p.w_scales + w_row(64 * (wq & 1) + lane) * (K / 16), 4, L::XBS + 256 * (wq & 1), 4};
+    }
+    const int total = static_cast<int>(K / kStepR);
+    auto stage_m = [&](int k) { return lds + (k % kStages) * L::STAGE; };
+    auto issue_m = [&](int k) {
+      uint8_t *st = stage_m(k);
+#pragma unroll
+      for (int q = 0; q < P; ++q) dma(dx[q].g + static_cast<int64_t>(k) * dx[q].stride, st + dx[q].lds, dx[q].bytes);
+    };
+    issue_m(0);
+    if (total > 1) issue_m(1);
+    for (int k = 0; k < total; ++k) {
+      if (k + 1 < total) wait_all_but_one_step<P>(); else wait_all();
+      barrier_no_fence();
+      if (k + 2 < total) issue_m(k + 2);
+      compute_merged<NI>(stage_m(k), acc, wm, wn, g, lane);
+    }
+  } else {
   const int nm = static_cast<int>(K / kStepM);
   const int nr = HAS_RES ? static_cast<int>(p.kpad / kStepR) : 0;
   const int total = nm + nr;
@@ -938,6 +1009,7 @@ __global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Pa
       compute_res<NI>(stage(k), acc, wm, wn, g, lane);
     }
   }
+  }
 
   // Sum the groups' partial tiles: group 1 hands its accumulators to group 0
   // through LDS, one half (mi) at a time, laid out [wave][ni][r][lane].
@@ -959,7 +1031,7 @@ __global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Pa
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] += red[((wq * NI + ni) * 16 + r) * 64 + lane];
     }
   }
-  if (g == 0) epilogue<C, 0, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  if (g == 0) epilogue<C, MERGED ? 2 : 0, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
 }
 
 // Exclusive scan of per-expert m-tile counts ceil(rows_e / bm) ->
@@ -1146,8 +1218,15 @@ void launch_pp_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStr
 }
 
 template <int NI>
-void launch_dma(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t s) {
+void launch_dma(const GemmLaunch &a, const Params &p, int g, bool res, hipStream_t s, bool merged = false) {
   const dim3 grid(g), block(dmak::kThreads);
+  if constexpr (NI == 2) {
+    if (merged) {
+      if (a.epilogue == 0) hipLaunchKernelGGL((k_gemm_dma<2, 0, false, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((k_gemm_dma<2, 1, false, true>), grid, block, 0, s, p);
+      return;
+    }
+  }
   if (res) {
     if (a.epilogue == 0) hipLaunchKernelGGL((k_gemm_dma<NI, 0, true>), grid, block, 0, s, p);
     else if constexpr (NI % 2 == 0) hipLaunchKernelGGL((k_gemm_dma<NI, 1, true>), grid, block, 0, s, p);
@@ -1181,8 +1260,10 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
 // 1.30 ms gate_up, 0.64 vs 0.83 ms down, merge passes included); on the
 // 128x128 DMA-staged shapes the merge pass costs what the shorter GEMM saves
 // (4096 x 1536 x 2048: 18 + 48 vs 5 + 62 us), so the exact extended-K kernel
-// stays.  QUADS_RAC_GEMM=extended | merged overrides the choice; it is read on
-// every call, so one process can compare the two.
+// stays.  A merged operand the caller built (quads_rac_select_merged) is
+// always taken: the DMA-staged 128x128 kernel reads it as well.
+// QUADS_RAC_GEMM=extended | merged overrides the choice; it is read on every
+// call, so one process can compare the two.
 bool use_merged(const GemmLaunch &a) {
   if (a.mode != 0 || a.r_codes == nullptr || a.kpad == 0 || gemm_use_small(a)) return false;
   if (a.x_merged != nullptr) return true;  // the caller built it: no merge pass to pay for
@@ -1197,7 +1278,7 @@ bool use_merged(const GemmLaunch &a) {
 TileCfg pick_cfg_for(const GemmLaunch &a) {
   TileCfg c = pick_cfg(a);
   if (use_merged(a)) {
-    if (c == kD || c == kD3 || c == kP) c = c == kD3 ? kM : (c == kP ? kL : kS);
+    if (c == kD3 || c == kP) c = c == kD3 ? kM : kL;  // kD has a merged form
   }
   return c;
 }
@@ -1282,7 +1363,7 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   grid = (grid + 7) / 8 * 8;
   p.grid_per_xcd = static_cast<int>(grid / 8);
   const int g = static_cast<int>(grid);
-  if (c == kD) launch_dma<2>(a, p, g, res, stream);
+  if (c == kD) launch_dma<2>(a, p, g, res, stream, merged);
   else if (c == kD3) launch_dma<3>(a, p, g, res, stream);
   else if (c == kP) launch_pp_cfg(a, p, g, res, stream);
   else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream, merged);

@@ -186,10 +186,10 @@ __device__ __forceinline__ void load_raw(RawBlock<BF16> &r, const void *x, const
 }
 
 // dx = x - dq for one block (the quantizer's FP32 operations: dq = level * d
-// with d = dec(scale) * g), stored to LDS; with `xp` also the block's exact
-// values X' = level * dec(scale) (units of g, exact in fp16) as fp16.
+// with d = dec(scale) * g); with `xv` also the block's exact values
+// X' = level * dec(scale) (units of g).
 template <bool BF16>
-__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *dst, uint16_t *xp = nullptr) {
+__device__ __forceinline__ void block_dx(const RawBlock<BF16> &r, float gx, float (&dx)[16], float *xv = nullptr) {
   float v[16];
   if constexpr (BF16) {
     const uint32_t w[8] = {r.x[0].x, r.x[0].y, r.x[0].z, r.x[0].w, r.x[1].x, r.x[1].y, r.x[1].z, r.x[1].w};
@@ -209,7 +209,6 @@ __device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, floa
   }
   const float sd = e4m3_to_f32(r.scale);
   const float d = sd * gx;
-  float dx[16], xv[16];
 #define QUADS_DX(word, byte, i0)                                               \
   {                                                                            \
     const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, byte); \
@@ -225,12 +224,7 @@ __device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, floa
   QUADS_DX(r.codes.y, 2, 12)
   QUADS_DX(r.codes.y, 3, 14)
 #undef QUADS_DX
-  float4 *o = reinterpret_cast<float4 *>(dst);
-  o[0] = make_float4(dx[0], dx[1], dx[2], dx[3]);
-  o[1] = make_float4(dx[4], dx[5], dx[6], dx[7]);
-  o[2] = make_float4(dx[8], dx[9], dx[10], dx[11]);
-  o[3] = make_float4(dx[12], dx[13], dx[14], dx[15]);
-  if (xp != nullptr) {
+  if (xv != nullptr) {
     // X' from the code itself, so that a negative-zero code (0x8) gives -0
     // like every other dequantization here (the hardware conversion gives
     // +0 for it, which is immaterial for dx).
@@ -239,61 +233,30 @@ __device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, floa
       const uint32_t w = i < 8 ? r.codes.x : r.codes.y;
       xv[i] = dequant_code((w >> (4 * (i & 7))) & 0xFu, sd);
     }
-    uint32_t h[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      h[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(xv[2 * i]))) |
-             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(xv[2 * i + 1]))) << 16);
-    uint4 *q = reinterpret_cast<uint4 *>(xp);
-    q[0] = make_uint4(h[0], h[1], h[2], h[3]);
-    q[1] = make_uint4(h[4], h[5], h[6], h[7]);
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *dst) {
+  float dx[16];
+  block_dx<BF16>(r, gx, dx);
+  float4 *o = reinterpret_cast<float4 *>(dst);
+  o[0] = make_float4(dx[0], dx[1], dx[2], dx[3]);
+  o[1] = make_float4(dx[4], dx[5], dx[6], dx[7]);
+  o[2] = make_float4(dx[8], dx[9], dx[10], dx[11]);
+  o[3] = make_float4(dx[12], dx[13], dx[14], dx[15]);
 }
 
 // Blocks of one row group held in registers per thread: block tid + j*kThreads.
 constexpr int kGroupSlots = 4;
 
-// LDS: sel[kpad] int32 | dx rows [rb][K] fp32.  A row group has at most
-// kGroupSlots * kThreads blocks.
-//
-// Schedule per workgroup: the loads of the first row group are issued before
-// the mask search so that their latency overlaps it; afterwards, while group
-// g is gathered and quantized, the loads of group g+1 are in flight.
-// MERGED: also write the RAC-corrected activation as one fp16 operand
-// merged[rows, K] = fp16(X' + (g_r/g_x) R') on the selected channels, X'
-// elsewhere (units of g_x): X' goes to a second LDS array when dx is
-// computed, each gathered block adds its dequantized residual to its
-// channels, and the row group is copied out with 16-byte stores.
-template <bool BF16, int PER, bool MERGED>
-__global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, int K, const uint8_t *x_codes,
-                                                  const uint8_t *x_scales, const float *x_g,
-                                                  const uint32_t *scores, int nsel, int kpad, int32_t *sel_out,
-                                                  float *r_g_out, uint8_t *r_codes, uint8_t *r_scales, int rb,
-                                                  int rows_per_wg, uint16_t *merged) {
-  extern __shared__ uint4 lds_u4[];
-  int32_t *sel = reinterpret_cast<int32_t *>(lds_u4);
-  float *region = reinterpret_cast<float *>(lds_u4) + kpad;
-  uint16_t *xm = reinterpret_cast<uint16_t *>(region + static_cast<int64_t>(rb) * K);  // MERGED: [rb][K] fp16
-  __shared__ uint32_t slots[8 * (kThreads / 64)];
+// Phase 1 of both kernels: the mask, written ascending to sel[0..nsel) with
+// sel[nsel..kpad) = -1; workgroup 0 also publishes it and the residual tensor
+// scale, which is returned.  Ends with a barrier.
+template <int PER>
+__device__ __forceinline__ float find_mask(const uint32_t *scores, int K, int nsel, int kpad, int32_t *sel,
+                                           uint32_t *slots, int32_t *sel_out, float *r_g_out) {
   const int tid = threadIdx.x;
-  const int cb = K / 16, nblk = kpad / 16;
-  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
-  const int64_t r_stop = min(r_begin + rows_per_wg, rows);
-
-  // Loads of a row group starting at row r0 (nb blocks; clamped addresses,
-  // slots past nb are skipped with a uniform test).
-  RawBlock<BF16> raw[kGroupSlots];
-  auto issue = [&](int64_t r0) {
-    const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
-    const int nb = nr * cb;
-#pragma unroll
-    for (int j = 0; j < kGroupSlots; ++j)
-      if (j * kThreads < nb) load_raw<BF16>(raw[j], x, x_codes, x_scales, r0 * cb + min(tid + j * kThreads, nb - 1));
-  };
-  const bool has_rows = kpad > 0 && r_begin < r_stop;
-  if (has_rows) issue(r_begin);
-
-  // 1. Mask.
   Keys<PER> ks;
   const int c0 = tid * PER;
   const int n_real = min(max(K - c0, 0), PER);  // multiple of 4 (K % 16 == 0)
@@ -342,6 +305,45 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
     for (int j = tid; j < kpad; j += kThreads) sel_out[j] = max(sel[j], 0);
     if (tid == 0) *r_g_out = gr;
   }
+  return gr;
+}
+
+// LDS: sel[kpad] int32 | dx rows [rb][K] fp32.  A row group has at most
+// kGroupSlots * kThreads blocks.
+//
+// Schedule per workgroup: the loads of the first row group are issued before
+// the mask search so that their latency overlaps it; afterwards, while group
+// g is gathered and quantized, the loads of group g+1 are in flight.
+template <bool BF16, int PER>
+__global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, int K, const uint8_t *x_codes,
+                                                  const uint8_t *x_scales, const float *x_g,
+                                                  const uint32_t *scores, int nsel, int kpad, int32_t *sel_out,
+                                                  float *r_g_out, uint8_t *r_codes, uint8_t *r_scales, int rb,
+                                                  int rows_per_wg) {
+  extern __shared__ uint4 lds_u4[];
+  int32_t *sel = reinterpret_cast<int32_t *>(lds_u4);
+  float *region = reinterpret_cast<float *>(lds_u4) + kpad;
+  __shared__ uint32_t slots[8 * (kThreads / 64)];
+  const int tid = threadIdx.x;
+  const int cb = K / 16, nblk = kpad / 16;
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int64_t r_stop = min(r_begin + rows_per_wg, rows);
+
+  // Loads of a row group starting at row r0 (nb blocks; clamped addresses,
+  // slots past nb are skipped with a uniform test).
+  RawBlock<BF16> raw[kGroupSlots];
+  auto issue = [&](int64_t r0) {
+    const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
+    const int nb = nr * cb;
+#pragma unroll
+    for (int j = 0; j < kGroupSlots; ++j)
+      if (j * kThreads < nb) load_raw<BF16>(raw[j], x, x_codes, x_scales, r0 * cb + min(tid + j * kThreads, nb - 1));
+  };
+  const bool has_rows = kpad > 0 && r_begin < r_stop;
+  if (has_rows) issue(r_begin);
+
+  // 1. Mask.
+  const float gr = find_mask<PER>(scores, K, nsel, kpad, sel, slots, sel_out, r_g_out);
   if (!has_rows) return;
 
   // 2-3. Residual rows.
@@ -352,8 +354,7 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
 #pragma unroll
     for (int j = 0; j < kGroupSlots; ++j) {
       const int b = tid + j * kThreads;
-      if (j * kThreads < nb && b < nb)
-        store_dx<BF16>(raw[j], gx, region + b * 16, MERGED ? xm + b * 16 : nullptr);
+      if (j * kThreads < nb && b < nb) store_dx<BF16>(raw[j], gx, region + b * 16);
     }
     if (r0 + rb < r_stop) issue(r0 + rb);
     __syncthreads();
@@ -370,38 +371,168 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
       const int64_t row = r0 + rr;
       reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
       r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);
-      if constexpr (MERGED) {
-        // Each selected channel of a row sits in exactly one gathered block.
-        const float ratio = gr / gx;
-        const float sr = e4m3_to_f32(q.scale);
-        uint16_t *xr = xm + rr * K;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = sel[jb * 16 + i];
-          if (c >= 0) {
-            const uint32_t code = ((i < 8 ? q.lo : q.hi) >> (4 * (i & 7))) & 0xFu;
-            const float xv = static_cast<float>(__builtin_bit_cast(_Float16, xr[c]));
-            xr[c] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(xv + dequant_code(code, sr) * ratio));
-          }
-        }
-      }
-    }
-    if constexpr (MERGED) {
-      __syncthreads();  // every block's residual is in xm
-      const int chunks = nr * K / 8;
-      for (int t = tid; t < chunks; t += kThreads)
-        reinterpret_cast<uint4 *>(merged + r0 * K)[t] = reinterpret_cast<const uint4 *>(xm)[t];
     }
     __syncthreads();  // dx region is rewritten by the next group
   }
 }
 
+// The 16 compact positions of a block's channels (32-byte aligned in LDS).
+__device__ __forceinline__ void block_pos(const int16_t *p, int (&ps)[16]) {
+  const uint4 a = reinterpret_cast<const uint4 *>(p)[0], b = reinterpret_cast<const uint4 *>(p)[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ps[2 * i] = static_cast<int16_t>(w[i] & 0xFFFFu);
+    ps[2 * i + 1] = static_cast<int16_t>(w[i] >> 16);
+  }
+}
+
+// The same mask and residual, plus the RAC-corrected activation as one fp16
+// operand merged[rows, K] = fp16(X' + fl32(R' * fl32(g_r / g_x))) on the
+// selected channels and X' elsewhere (units of g_x).
+//
+// LDS: sel[kpad] int32 | pos[K] int16 (channel -> index in sel, or -1) |
+// dx [rb][kpad] fp32 of the selected channels only, in mask order.
+//
+// Per row group:
+//   a. each thread computes dx and X' of its blocks; the selected channels'
+//      dx go to their compact slots, X' stays in registers;
+//   b. each residual block reads 16 consecutive slots, is quantized, and
+//      leaves its correction fl32(R' * ratio) in the same slots;
+//   c. each thread adds its selected channels' corrections to X', rounds once
+//      to fp16 and stores its blocks (32 bytes each, consecutive blocks of a
+//      row in consecutive threads).
+// The LDS footprint (about 25 KB at K = 2048, k = 50%, 4 rows) and, for bf16
+// input with K <= 8192, at most 128 VGPRs (4 workgroups per CU) let the 1024
+// workgroups of a launch be resident at once, so the redundant mask search is
+// paid once per launch, not once per round of workgroups.
+template <bool BF16, int PER>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 && PER <= 32 ? 4 : 1))) void k_rac_merged(const void *x, int64_t rows, int K, const uint8_t *x_codes,
+                                                         const uint8_t *x_scales, const float *x_g,
+                                                         const uint32_t *scores, int nsel, int kpad,
+                                                         int32_t *sel_out, float *r_g_out, uint8_t *r_codes,
+                                                         uint8_t *r_scales, int rb, int rows_per_wg,
+                                                         uint16_t *merged) {
+  extern __shared__ uint4 lds_u4[];
+  int32_t *sel = reinterpret_cast<int32_t *>(lds_u4);
+  int16_t *pos = reinterpret_cast<int16_t *>(sel + kpad);
+  float *region = reinterpret_cast<float *>(lds_u4) + kpad + (K + 7) / 8 * 4;  // pos rounded up to 16 bytes
+  __shared__ uint32_t slots[8 * (kThreads / 64)];
+  const int tid = threadIdx.x;
+  const int cb = K / 16, nblk = kpad / 16;
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int64_t r_stop = min(r_begin + rows_per_wg, rows);
+
+  RawBlock<BF16> raw[kGroupSlots];
+  auto issue = [&](int64_t r0) {
+    const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
+    const int nb = nr * cb;
+#pragma unroll
+    for (int j = 0; j < kGroupSlots; ++j)
+      if (j * kThreads < nb) load_raw<BF16>(raw[j], x, x_codes, x_scales, r0 * cb + min(tid + j * kThreads, nb - 1));
+  };
+  const bool has_rows = r_begin < r_stop;
+  if (has_rows) issue(r_begin);
+  for (int c = tid; c < K; c += kThreads) pos[c] = -1;  // ordered before use by find_mask's barriers
+
+  // 1. Mask, and its inverse map.
+  const float gr = find_mask<PER>(scores, K, nsel, kpad, sel, slots, sel_out, r_g_out);
+  if (!has_rows) return;
+  for (int j = tid; j < nsel; j += kThreads) pos[sel[j]] = static_cast<int16_t>(j);
+  __syncthreads();
+
+  const float gx = *x_g;
+  const float ratio = gr / gx;
+  for (int64_t r0 = r_begin; r0 < r_stop; r0 += rb) {
+    const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
+    const int nb = nr * cb;
+    // a.
+    uint2 kc[kGroupSlots];  // each slot's codes and scale, for X' in c.
+    uint32_t ksc[kGroupSlots];
+#pragma unroll
+    for (int j = 0; j < kGroupSlots; ++j) {
+      const int b = tid + j * kThreads;
+      if (j * kThreads < nb && b < nb) {
+        kc[j] = raw[j].codes;
+        ksc[j] = raw[j].scale;
+        float dx[16];
+        block_dx<BF16>(raw[j], gx, dx);
+        const int rr = b / cb, c0 = (b - rr * cb) * 16;
+        int ps[16];
+        block_pos(pos + c0, ps);
+        float *dst = region + rr * kpad;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (ps[i] >= 0) dst[ps[i]] = dx[i];
+      }
+    }
+    if (r0 + rb < r_stop) issue(r0 + rb);
+    __syncthreads();
+    // b.
+    for (int t = tid; t < nr * nblk; t += kThreads) {
+      const int rr = t / nblk, jb = t - rr * nblk;
+      float *src = region + rr * kpad + jb * 16;
+      float g16[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) g16[i] = jb * 16 + i < nsel ? src[i] : 0.0f;
+      const BlockQ q = quantize_block16(g16, gr, nullptr);
+      const int64_t row = r0 + rr;
+      reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
+      r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);
+      const float sr = e4m3_to_f32(q.scale);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t code = ((i < 8 ? q.lo : q.hi) >> (4 * (i & 7))) & 0xFu;
+        if (jb * 16 + i < nsel) src[i] = dequant_code(code, sr) * ratio;
+      }
+    }
+    __syncthreads();
+    // c.
+#pragma unroll
+    for (int j = 0; j < kGroupSlots; ++j) {
+      const int b = tid + j * kThreads;
+      if (j * kThreads < nb && b < nb) {
+        const int rr = b / cb, c0 = (b - rr * cb) * 16;
+        int ps[16];
+        block_pos(pos + c0, ps);
+        const float *cor = region + rr * kpad;
+        // X' from the code itself (a negative-zero code gives -0), exact in
+        // FP32; the selected channels add their correction, one rounding.
+        const float sd = e4m3_to_f32(ksc[j]);
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int e = 2 * i + u;
+            float v = dequant_code(((e < 8 ? kc[j].x : kc[j].y) >> (4 * (e & 7))) & 0xFu, sd);
+            if (ps[e] >= 0) v += cor[ps[e]];
+            pair |= static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v))) << (16 * u);
+          }
+          h[i] = pair;
+        }
+        uint4 *q = reinterpret_cast<uint4 *>(merged + (r0 * cb + b) * 16);
+        q[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        q[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      }
+    }
+    __syncthreads();  // the slots are rewritten by the next group
+  }
+}
+
 }  // namespace
 
+// LDS bytes of a workgroup holding rb rows.
+size_t rac_lds_bytes(int64_t cols, int64_t kpad, bool merged, int64_t rb) {
+  if (merged) return static_cast<size_t>(kpad * 4 + (cols + 7) / 8 * 16 + rb * kpad * 4);
+  return static_cast<size_t>(kpad * 4 + rb * cols * 4);
+}
+
 int rac_rows_per_group(int64_t cols, int64_t kpad, bool merged) {
-  const int64_t budget = 64 * 1024 - kpad * 4 - 64;
-  int64_t rb = budget / (cols * (merged ? 6 : 4));
-  if (rb > 4) rb = 4;  // ~40 KiB per workgroup at cols 2048: four workgroups per CU
+  const int64_t budget = 64 * 1024 - 64;
+  int64_t rb = 4;  // ~40 KiB (plain) / ~25 KiB (merged) per workgroup at cols 2048, k 50%
+  while (rb > 0 && rac_lds_bytes(cols, kpad, merged, rb) > static_cast<size_t>(budget)) --rb;
   const int64_t by_slots = static_cast<int64_t>(kGroupSlots) * kThreads / (cols / 16);
   if (rb > by_slots) rb = by_slots;  // a row group's blocks fit the per-thread load slots
   return static_cast<int>(rb);
@@ -411,17 +542,16 @@ namespace {
 template <bool BF16, int PER>
 void launch_rac_t(const RacLaunch &a, int64_t n_wg, int rb, int rows_per_wg, size_t lds, hipStream_t stream) {
   if (a.merged != nullptr)
-    hipLaunchKernelGGL((k_rac<BF16, PER, true>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
+    hipLaunchKernelGGL((k_rac_merged<BF16, PER>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
                        static_cast<int>(a.cols), a.x_codes, a.x_scales, a.x_gscale,
                        reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.nsel),
                        static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg,
                        a.merged);
   else
-    hipLaunchKernelGGL((k_rac<BF16, PER, false>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
+    hipLaunchKernelGGL((k_rac<BF16, PER>), dim3(n_wg), dim3(kThreads), lds, stream, a.x, a.rows,
                        static_cast<int>(a.cols), a.x_codes, a.x_scales, a.x_gscale,
                        reinterpret_cast<const uint32_t *>(a.scores), static_cast<int>(a.nsel),
-                       static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg,
-                       static_cast<uint16_t *>(nullptr));
+                       static_cast<int>(a.kpad), a.sel_idx, a.r_gscale, a.r_codes, a.r_scales, rb, rows_per_wg);
 }
 
 template <bool BF16>
@@ -454,7 +584,7 @@ hipError_t launch_rac_select(const RacLaunch &a_in, hipStream_t stream) {
     rows_per_wg = static_cast<int>(rb * iters);
     n_wg = (a.rows + rows_per_wg - 1) / rows_per_wg;
   }
-  const size_t lds = static_cast<size_t>(a.kpad) * 4 + static_cast<size_t>(rb) * a.cols * (merged ? 6 : 4);
+  const size_t lds = rac_lds_bytes(a.cols, a.kpad, merged, rb);
   if (a.x_bf16)
     launch_rac_per<true>(a, n_wg, rb, rows_per_wg, lds, stream);
   else
