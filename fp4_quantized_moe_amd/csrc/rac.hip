@@ -376,6 +376,30 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
   }
 }
 
+// The 16 values of a block's codes times d (d >= 0), exact in FP32, with the
+// code's sign also on zeros (the negative-zero code gives -0; the hardware
+// conversion alone gives +0 for it).
+template <int B>
+__device__ __forceinline__ void dequant_byte(uint32_t w, float d, float *v) {
+  const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t sign = (w << (28 - 4 * (2 * B + u))) & 0x80000000u;  // bit 3 of nibble 2B+u
+    v[u] = __uint_as_float(__float_as_uint(e[u] * d) | sign);
+  }
+}
+
+__device__ __forceinline__ void dequant16(uint2 codes, float d, float (&v)[16]) {
+  dequant_byte<0>(codes.x, d, v + 0);
+  dequant_byte<1>(codes.x, d, v + 2);
+  dequant_byte<2>(codes.x, d, v + 4);
+  dequant_byte<3>(codes.x, d, v + 6);
+  dequant_byte<0>(codes.y, d, v + 8);
+  dequant_byte<1>(codes.y, d, v + 10);
+  dequant_byte<2>(codes.y, d, v + 12);
+  dequant_byte<3>(codes.y, d, v + 14);
+}
+
 // The 16 compact positions of a block's channels (32-byte aligned in LDS).
 __device__ __forceinline__ void block_pos(const int16_t *p, int (&ps)[16]) {
   const uint4 a = reinterpret_cast<const uint4 *>(p)[0], b = reinterpret_cast<const uint4 *>(p)[1];
@@ -479,12 +503,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 &
       const int64_t row = r0 + rr;
       reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
       r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);
-      const float sr = e4m3_to_f32(q.scale);
+      float rv[16];
+      dequant16(make_uint2(q.lo, q.hi), e4m3_to_f32(q.scale), rv);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t code = ((i < 8 ? q.lo : q.hi) >> (4 * (i & 7))) & 0xFu;
-        if (jb * 16 + i < nsel) src[i] = dequant_code(code, sr) * ratio;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (jb * 16 + i < nsel) src[i] = rv[i] * ratio;
     }
     __syncthreads();
     // c.
@@ -496,9 +519,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 &
         int ps[16];
         block_pos(pos + c0, ps);
         const float *cor = region + rr * kpad;
-        // X' from the code itself (a negative-zero code gives -0), exact in
-        // FP32; the selected channels add their correction, one rounding.
-        const float sd = e4m3_to_f32(ksc[j]);
+        // X' (exact in FP32, signed zeros as coded); the selected channels
+        // add their correction, one rounding.
+        float xv[16];
+        dequant16(kc[j], e4m3_to_f32(ksc[j]), xv);
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -506,7 +530,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 &
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int e = 2 * i + u;
-            float v = dequant_code(((e < 8 ? kc[j].x : kc[j].y) >> (4 * (e & 7))) & 0xFu, sd);
+            float v = xv[e];
             if (ps[e] >= 0) v += cor[ps[e]];
             pair |= static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v))) << (16 * u);
           }
