@@ -5,8 +5,9 @@ grouped GEMM, selected per call with QUADS_RAC_GEMM:
 - merged: the correction added to the activation as one fp16 operand, with
   one more rounding per corrected element.
 Both are checked against the oracle's float64 extended-K reference at the
-1e-3 bar: dense and grouped shapes, ragged rows, a gathered row order, and
-the SwiGLU epilogue."""
+1e-3 bar: dense and grouped shapes, ragged rows, a gathered row order, the
+SwiGLU epilogue, and the full-size expert-GEMM workload through the
+caller-built merged operand."""
 import os
 
 import numpy as np
@@ -156,5 +157,37 @@ def test_gemm_with_caller_merged_operand(shape):
     _, _, _, we = O.quantize_weights(wa.f32, 1)
     ref = O.rac_linear(xa.f32, we, 50, rt, offs)["y"]
     err = rel_err(host(y), ref)
+    log(f"  rel err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("k", [25, 50, 100])
+def test_expert_gemm_full_size_merged_pipeline(k):
+    """The expert-GEMM workload at full size (X 4096 x 2048 bf16, W 1536 x 2048)
+    through the calls and launch configuration the throughput benchmark
+    times: quads_rac_select_merged, then the GEMM on the caller's merged
+    operand (128x128 DMA-staged tiles, merged steps). The operand is
+    bit-exact against the oracle's rac_merged_operand and Y is within 1e-3
+    of its float64 extended-K product."""
+    wl = S.expert_gemm()
+    M, K = wl.x.f32.shape
+    N = wl.w.f32.shape[0]
+    log(f"[gemm-rac] full-size merged pipeline {M}x{K}x{N} k={k}")
+    x = dev_act(wl.x)
+    wc, ws_, wg = quantize_weights_gpu(dev_act(wl.w)[None], 1)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    call = Q.SelectCall(x, q, scores, k, merged=True)
+    sel, res, nsel = call()
+    y = Q.moe_w4a4_gemm(w_codes=wc, w_scales=ws_, w_gscale=wg, N=N, K=K,
+                        expert_offsets=torch.tensor([0, M], dtype=torch.int32, device="cuda"), num_rows=M,
+                        x=q, res=res, sel_idx=sel, x_merged=call.merged)
+    oq = O.quantize_nvfp4(wl.x.f32)
+    osel, on = O.rac_select(O.rac_scores(wl.x.f32, oq), k)
+    assert nsel == on and np.array_equal(host(sel), osel)
+    orr = O.rac_quantize_residual(wl.x.f32, oq, osel, on)
+    want = O.rac_merged_operand(oq, orr, osel, on)
+    assert np.array_equal(host(call.merged).view(np.uint16), want.view(np.uint16))
+    _, _, _, we = O.quantize_weights(wl.w.f32[None], 1)
+    err = rel_err(host(y), O.rac_linear(wl.x.f32, we, k)["y"])
     log(f"  rel err {err:.2e}")
     assert err <= TOL
