@@ -21,10 +21,12 @@ def _outputs(q, scores, sel, res, y):
     return [t.clone() for t in ts]
 
 
-@pytest.mark.parametrize("k", [0, 50])
-def test_graph_replay_matches_eager(k):
+@pytest.mark.parametrize("k,merged", [(0, False), (50, False), (50, True)])
+def test_graph_replay_matches_eager(k, merged):
+    """merged: quads_rac_select_merged and the GEMM on that operand (the
+    benchmark's default pipeline); otherwise the extended-K form."""
     wl = S.expert_gemm(M=1024)
-    log(f"[graph] expert_gemm M=1024 k={k}")
+    log(f"[graph] expert_gemm M=1024 k={k} merged={merged}")
     x, wd = dev_act(wl.x), dev_act(wl.w)
     M, K = wl.x.f32.shape
     N = wl.w.f32.shape[0]
@@ -32,13 +34,14 @@ def test_graph_replay_matches_eager(k):
     offs = torch.tensor([0, M], dtype=torch.int32, device="cuda")
     qc = Q.QuantizeCall(x, want_scores=True)
     q, scores = qc()
-    sc = Q.SelectCall(x, q, scores, k)
+    sc = Q.SelectCall(x, q, scores, k, merged=merged)
     sel, res, nsel = sc()
     gc = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M,
-                    x=q, res=res if nsel else None, sel_idx=sel)
+                    x=q, res=res if nsel else None, sel_idx=sel, x_merged=sc.merged if merged else None)
     gc()
     torch.cuda.synchronize()
-    eager = _outputs(q, scores, sel, res, gc.y)
+    extra = (sc.merged,) if merged else ()
+    eager = _outputs(q, scores, sel, res, gc.y) + [t.clone() for t in extra]
 
     # the eager results are the oracle's
     ref = O.quantize_nvfp4(wl.x.f32)
@@ -59,12 +62,12 @@ def test_graph_replay_matches_eager(k):
     for rep in range(3):
         for t in (q.codes, q.scales, res.codes, res.scales, sel):
             t.fill_(0x5A if t.dtype == torch.uint8 else -7)
-        for t in (q.gscale, scores, res.gscale, gc.y):
+        for t in (q.gscale, scores, res.gscale, gc.y) + extra:
             t.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = _outputs(q, scores, sel, res, gc.y)
+        got = _outputs(q, scores, sel, res, gc.y) + list(extra)
         for a, b in zip(eager, got):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
         # eager work between replays: the same calls on other data, then back
