@@ -287,13 +287,22 @@ __device__ __forceinline__ void k_loop(int nk, uint4 (*As)[C::BM * 8], uint4 (*B
 // Map this workgroup to (expert e, rows [m0, min(m0+BM, mend)), n-tile nt).
 // XCD-aware remap: XCD x (= blockIdx % 8) gets logical tiles
 // [x * grid_per_xcd, (x + 1) * grid_per_xcd).  Returns false for surplus
-// workgroups (uniformly for the whole workgroup).
+// workgroups (uniformly for the whole workgroup).  One expert (a dense GEMM)
+// needs no tile list: its tiles are read off expert_offsets[0..1].
 template <class C>
 __device__ __forceinline__ bool tile_setup(const Params &p, int &nt, int &e, int &m0, int &mend, int &s_e, int &s_m0,
                                            int &s_mend) {
   const int logical = (blockIdx.x & 7) * p.grid_per_xcd + (blockIdx.x >> 3);
   const int mt = logical / p.n_tiles;
   nt = logical % p.n_tiles;
+  if (p.E == 1) {
+    const int lo = p.expert_offsets[0], hi = p.expert_offsets[1];
+    if (hi <= lo || mt >= (hi - lo + C::BM - 1) / C::BM) return false;
+    e = 0;
+    m0 = lo + mt * C::BM;
+    mend = hi;
+    return true;
+  }
   if (mt >= p.tile_offsets[p.E]) return false;
   if (threadIdx.x == 0) {
     int lo = 0, hi = p.E;  // largest e with tile_offsets[e] <= mt (skips empty experts)
@@ -1308,7 +1317,9 @@ hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
       const hipError_t e = launch_gemm_small_prepare(a, xm, stream);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(256), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
+    if (a.E > 1)
+      hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(256), 0, stream, a.expert_offsets, a.E, cfg_bm(c),
+                         tile_offsets);
   } else if (res) {
     uint16_t *wg = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
     const int64_t rows_total = static_cast<int64_t>(a.E) * a.N;
@@ -1317,7 +1328,7 @@ hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_gather_wcols, dim3((rows_total + 3) / 4 + 1), dim3(256), lds, stream, a.w_codes,
                        a.w_scales, rows_total, K, a.sel_idx, static_cast<int>(a.kpad), wg, a.expert_offsets, a.E,
                        cfg_bm(c), tile_offsets);
-  } else {
+  } else if (a.E > 1) {  // one expert: the kernels read its tiles off expert_offsets
     hipLaunchKernelGGL(k_tile_prefix, dim3(1), dim3(256), 0, stream, a.expert_offsets, a.E, cfg_bm(c), tile_offsets);
   }
   return hipGetLastError();
