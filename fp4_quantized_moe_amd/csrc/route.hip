@@ -4,7 +4,9 @@
 // mechanics; this is standard top-k softmax routing with deterministic ties.
 //
 //   k_route_topk     one wave per token: softmax statistics and top-k by
-//                    repeated wave argmax (ties to the lower expert index)
+//                    repeated wave argmax (ties to the lower expert index);
+//                    for E <= 256 k_route_topk_rank gives the same top-k by
+//                    ranking every logit against the token's others in LDS
 //   k_route_count    per 256-token block, per-expert counts (LDS atomics on
 //                    integers: exact and order-independent)
 //   k_route_scan     block offsets per expert and expert_offsets[E+1]
@@ -68,6 +70,75 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t
     if (lane == 0) {
       ids[t * top + j] = bi;
       wts[t * top + j] = expf(bv - mx) / sum;
+    }
+  }
+}
+
+// E <= 256, one wave per token: every lane ranks its own logits against the
+// token's E logits (held in LDS per wave).  rank(e) = number of logits that
+// are larger, or equal at a lower expert index, with NaN ranked as -inf, so
+// the ranks are a permutation of 0..E-1 and the experts of rank < top are the
+// top-k in the order the repeated wave argmax gives (ties to the lower
+// index).  The softmax statistics are those of k_route_topk, operation for
+// operation.
+template <int PER>
+__global__ __launch_bounds__(256) void k_route_topk_rank(const float *logits, int64_t T, int E, int top,
+                                                         int32_t *ids, float *wts) {
+  __shared__ __attribute__((aligned(16))) float lv[4][64 * PER];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const bool valid = t < T;  // no early return: every wave reaches the barrier
+  const float *row = logits + (valid ? t : 0) * E;
+  float v[PER];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e = q * 64 + lane;
+    v[q] = valid && e < E ? row[e] : -INFINITY;
+    mx = fmaxf(mx, v[q]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float sum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < PER; ++q)
+    if (q * 64 + lane < E) sum += expf(v[q] - mx);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  float key[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    key[q] = v[q] != v[q] ? -INFINITY : v[q];
+    if (q * 64 + lane < E) lv[wave][q * 64 + lane] = key[q];
+  }
+  __syncthreads();
+  uint32_t rank[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) rank[q] = 0;
+  const float *lw = lv[wave];
+  int j = 0;
+  for (; j + 4 <= E; j += 4) {
+    const float4 o = *reinterpret_cast<const float4 *>(lw + j);
+    const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < PER; ++q)
+        rank[q] += ov[u] > key[q] || (ov[u] == key[q] && j + u < q * 64 + lane);
+  }
+  for (; j < E; ++j) {
+    const float o = lw[j];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) rank[q] += o > key[q] || (o == key[q] && j < q * 64 + lane);
+  }
+  if (valid) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = q * 64 + lane;
+      if (e < E && rank[q] < static_cast<uint32_t>(top)) {
+        ids[t * top + rank[q]] = e;
+        wts[t * top + rank[q]] = expf(v[q] - mx) / sum;
+      }
     }
   }
 }
@@ -162,7 +233,11 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t 
   const int nblk = static_cast<int>((T + kTokBlk - 1) / kTokBlk);
   int32_t *blk = static_cast<int32_t *>(ws);
   if (T > 0) {
-    hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, top, ids, w);
+    const dim3 g((T + 3) / 4), b(256);
+    if (E <= 64) hipLaunchKernelGGL(k_route_topk_rank<1>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (E <= 128) hipLaunchKernelGGL(k_route_topk_rank<2>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (E <= 256) hipLaunchKernelGGL(k_route_topk_rank<4>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else hipLaunchKernelGGL(k_route_topk, g, b, 0, stream, logits, T, E, top, ids, w);
     hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kTokBlk), E * sizeof(int32_t), stream, ids, T, E,
                        top, blk);
   }
