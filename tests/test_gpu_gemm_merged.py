@@ -105,7 +105,9 @@ def test_grouped_swiglu_merged(rac_mode):
 
 
 @pytest.mark.parametrize("case", [("bf16", 300, 2048, 50), ("bf16", 300, 2048, 100), ("bf16", 77, 768, 25),
-                                  ("f32", 64, 256, 50), ("bf16", 40, 512, 0)])
+                                  ("f32", 64, 256, 50), ("bf16", 40, 512, 0),
+                                  # more than 1024 four-row groups: workgroups walk several groups
+                                  ("bf16", 6001, 768, 50), ("bf16", 5000, 2048, 25)])
 def test_rac_select_merged_bit_exact(case):
     """quads_rac_select_merged's fp16 operand equals the oracle's
     rac_merged_operand bit for bit (same fp32 operations, one rounding); the
@@ -191,3 +193,21 @@ def test_expert_gemm_full_size_merged_pipeline(k):
     err = rel_err(host(y), O.rac_linear(wl.x.f32, we, k)["y"])
     log(f"  rel err {err:.2e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("M,K,k", [(6001, 768, 50), (5000, 2048, 25)])
+def test_rac_select_many_rows_bit_exact(M, K, k):
+    """quads_rac_select (no merged operand) with more rows than 1024 groups of
+    four: mask, residual codes, scales and g_r bit-exact against the oracle."""
+    log(f"[rac] many rows M={M} K={K} k={k}")
+    rng = np.random.default_rng(606 + M)
+    xa = S.activation(rng, M, K, max(1, K // 100), 30.0, bf16=True)
+    x = dev_act(xa)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    sel, res, nsel = Q.rac_select(x, q, scores, k)
+    oq = O.quantize_nvfp4(xa.f32)
+    osel, on = O.rac_select(O.rac_scores(xa.f32, oq), k)
+    assert nsel == on and np.array_equal(host(sel), osel)
+    orr = O.rac_quantize_residual(xa.f32, oq, osel, on)
+    assert np.array_equal(host(res.codes), orr.codes) and np.array_equal(host(res.scales), orr.scales)
+    assert host(res.gscale)[0] == np.float32(orr.g)
