@@ -233,10 +233,14 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t 
   const int nblk = static_cast<int>((T + kTokBlk - 1) / kTokBlk);
   int32_t *blk = static_cast<int32_t *>(ws);
   if (T > 0) {
+    // Ranking wins where there is throughput to gain (measured: 16384 tokens x
+    // 64 experts 18 against 37 us); with few tokens and more than 64 experts
+    // the argmax rounds are shorter (256 x 128: 11.8 against 13.3 us).
     const dim3 g((T + 3) / 4), b(256);
-    if (E <= 64) hipLaunchKernelGGL(k_route_topk_rank<1>, g, b, 0, stream, logits, T, E, top, ids, w);
-    else if (E <= 128) hipLaunchKernelGGL(k_route_topk_rank<2>, g, b, 0, stream, logits, T, E, top, ids, w);
-    else if (E <= 256) hipLaunchKernelGGL(k_route_topk_rank<4>, g, b, 0, stream, logits, T, E, top, ids, w);
+    const bool rank = E <= 64 || (E <= 256 && T >= 2048);
+    if (rank && E <= 64) hipLaunchKernelGGL(k_route_topk_rank<1>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (rank && E <= 128) hipLaunchKernelGGL(k_route_topk_rank<2>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (rank) hipLaunchKernelGGL(k_route_topk_rank<4>, g, b, 0, stream, logits, T, E, top, ids, w);
     else hipLaunchKernelGGL(k_route_topk, g, b, 0, stream, logits, T, E, top, ids, w);
     hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kTokBlk), E * sizeof(int32_t), stream, ids, T, E,
                        top, blk);

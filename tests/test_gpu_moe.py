@@ -36,16 +36,20 @@ def test_route_ties_and_edge_shapes():
     _check_route(lg, 5, "ties")
     _check_route(rng.standard_normal((1, 16)).astype(np.float32), 16, "top=E")
     _check_route(rng.standard_normal((513, 1024)).astype(np.float32), 8, "E=1024")
-    # the rank-based top-k sizes (E <= 64, <= 128, <= 256): -inf logits,
-    # +0 / -0 ties, rounded-value ties, E not a multiple of 4
-    lg = rng.standard_normal((300, 130)).astype(np.float32)
-    lg[:, 5] = -np.inf
-    lg[::3, 7] = 0.0
-    lg[::3, 9] = -0.0
-    lg[::3, 11] = 0.0
-    _check_route(lg, 8, "E=130 -inf and signed-zero ties")
-    _check_route(np.round(rng.standard_normal((257, 200)) * 2).astype(np.float32), 8, "E=200 ties")
+    # both top-k kernels (ranking: E <= 64, or up to 256 experts with at
+    # least 2048 tokens; argmax rounds otherwise): -inf logits, +0 / -0 ties,
+    # rounded-value ties, E not a multiple of 4
+    for T in (300, 2048):
+        lg = rng.standard_normal((T, 130)).astype(np.float32)
+        lg[:, 5] = -np.inf
+        lg[::3, 7] = 0.0
+        lg[::3, 9] = -0.0
+        lg[::3, 11] = 0.0
+        _check_route(lg, 8, f"E=130 T={T} -inf and signed-zero ties")
+    for T in (257, 2100):
+        _check_route(np.round(rng.standard_normal((T, 200)) * 2).astype(np.float32), 8, f"E=200 T={T} ties")
     _check_route(np.round(rng.standard_normal((64, 63)) * 3).astype(np.float32), 6, "E=63 ties")
+    _check_route(np.round(rng.standard_normal((2048, 100)) * 2).astype(np.float32), 8, "E=100 T=2048 ties")
 
 
 def test_combine():
