@@ -123,7 +123,11 @@ quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4
  * x / dt: the activation that produced xq (batch 1); scores from
  * quads_quantize_nvfp4(QUADS_WANT_SCORES).  res.cols must equal kpad; with
  * k such that kpad == 0 only res.gscale[0] = 1 is written.
- * Channel count limit: cols <= 16384.
+ * Channel count limit: cols <= 16384, and a workgroup's shared memory must
+ * hold the mask and one row of work: 4*kpad + 4*cols <= 65472 bytes here,
+ * 8*kpad + 2*cols <= 65472 for quads_rac_select_merged (about cols <= 10912
+ * at k = 50%); larger shapes return QUADS_ERR_SHAPE before anything is
+ * enqueued.
  * ------------------------------------------------------------------------- */
 size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols);
 quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,

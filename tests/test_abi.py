@@ -79,6 +79,10 @@ def test_rac_select_validation(L):
     # the LDS budget: cols * 4 + kpad * 4 must stay under ~63 KiB
     wide = _nv(8, 16384)
     assert L.quads_rac_select(dummy, 0, ctypes.byref(wide), dummy, 0, dummy, _nv(8, 0), None, 0, None) == -2
+    # the merged variant's budget: 8 * kpad + 2 * cols (12288 channels at k=50%: 73728 bytes)
+    w12 = _nv(8, 12288)
+    assert L.quads_rac_select_merged(dummy, 0, ctypes.byref(w12), dummy, 50, dummy, _nv(8, 6144), dummy,
+                                     None, 0, None) == -2
 
 
 def _gemm_args(**kw):
