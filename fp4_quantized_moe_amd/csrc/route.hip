@@ -155,27 +155,57 @@ __global__ __launch_bounds__(kTokBlk) void k_route_count(const int32_t *ids, int
   for (int e = threadIdx.x; e < E; e += kTokBlk) blkcnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
+// Per expert e (thread e): the exclusive running count over token blocks,
+// loaded eight blocks at a time so that the loads of a batch are in flight
+// together; then an exclusive prefix over experts (wave scans and the wave
+// totals) gives expert_offsets, which is added to every block's entry.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t *blkcnt, int nblk, int E, int32_t *offsets) {
-  __shared__ int32_t tot[1025];
-  const int e = threadIdx.x;
+  __shared__ int32_t wtot[16];
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  constexpr int U = 8;
   int32_t run = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      int32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = blkcnt[static_cast<int64_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        blkcnt[static_cast<int64_t>(b + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       const int32_t c = blkcnt[static_cast<int64_t>(b) * E + e];
       blkcnt[static_cast<int64_t>(b) * E + e] = run;
       run += c;
     }
   }
-  tot[e + 1] = e < E ? run : 0;
-  if (e == 0) tot[0] = 0;
+  int32_t incl = run;  // 0 for threads past E
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wtot[wv] = incl;
   __syncthreads();
-  if (e == 0)
-    for (int i = 1; i <= E; ++i) tot[i] += tot[i - 1];
-  __syncthreads();
-  if (e < E) offsets[e] = tot[e];
-  if (e == 0) offsets[E] = tot[E];
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) blkcnt[static_cast<int64_t>(b) * E + e] += tot[e];
+  int32_t before = 0;
+  for (int w = 0; w < wv; ++w) before += wtot[w];
+  const int32_t excl = before + incl - run;
+  if (e < E) offsets[e] = excl;
+  if (e == E - 1) offsets[E] = excl + run;
+  if (e < E) {
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      int32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = blkcnt[static_cast<int64_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) blkcnt[static_cast<int64_t>(b + u) * E + e] = c[u] + excl;
+    }
+    for (; b < nblk; ++b) blkcnt[static_cast<int64_t>(b) * E + e] += excl;
+  }
 }
 
 __global__ __launch_bounds__(kTokBlk) void k_route_scatter(const int32_t *ids, int64_t T, int E, int top,
