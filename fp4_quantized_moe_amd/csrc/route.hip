@@ -22,13 +22,14 @@ namespace {
 
 constexpr int kTokBlk = 256;
 
+// kMaxPer = ceil(E / 64) slots per lane (E <= 64 * kMaxPer <= 1024).
+template <int kMaxPer>
 __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t T, int E, int top,
                                                     int32_t *ids, float *wts) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *row = logits + t * E;
-  constexpr int kMaxPer = 16;  // E <= 1024
   float v[kMaxPer];
   float mx = -INFINITY;
 #pragma unroll
@@ -271,7 +272,10 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t 
     if (rank && E <= 64) hipLaunchKernelGGL(k_route_topk_rank<1>, g, b, 0, stream, logits, T, E, top, ids, w);
     else if (rank && E <= 128) hipLaunchKernelGGL(k_route_topk_rank<2>, g, b, 0, stream, logits, T, E, top, ids, w);
     else if (rank) hipLaunchKernelGGL(k_route_topk_rank<4>, g, b, 0, stream, logits, T, E, top, ids, w);
-    else hipLaunchKernelGGL(k_route_topk, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (E <= 128) hipLaunchKernelGGL(k_route_topk<2>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (E <= 256) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else if (E <= 512) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, stream, logits, T, E, top, ids, w);
+    else hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, stream, logits, T, E, top, ids, w);
     hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kTokBlk), E * sizeof(int32_t), stream, ids, T, E,
                        top, blk);
   }

@@ -50,6 +50,7 @@ def test_route_ties_and_edge_shapes():
         _check_route(np.round(rng.standard_normal((T, 200)) * 2).astype(np.float32), 8, f"E=200 T={T} ties")
     _check_route(np.round(rng.standard_normal((64, 63)) * 3).astype(np.float32), 6, "E=63 ties")
     _check_route(np.round(rng.standard_normal((2048, 100)) * 2).astype(np.float32), 8, "E=100 T=2048 ties")
+    _check_route(np.round(rng.standard_normal((100, 300)) * 2).astype(np.float32), 8, "E=300 ties")
 
 
 def test_combine():
