@@ -13,6 +13,7 @@
 //   k_route_scatter  rank of a token among the block's tokens that chose the
 //                    same expert (popcount over an LDS bitmap), giving
 //                    row_token and inverse without any ordering race
+//   k_route_one_block  the last three in one workgroup when T <= 256
 //   k_combine        out[t] = sum over slots (in order) of w * y[row]
 #include "launch.hpp"
 #include "quads_device.hpp"
@@ -233,6 +234,72 @@ __global__ __launch_bounds__(kTokBlk) void k_route_scatter(const int32_t *ids, i
   }
 }
 
+// T <= kTokBlk (one token block, e.g. decode): count, scan and scatter in
+// one workgroup.  LDS: cnt[E] | bits[E][kTokBlk / 32] | pre[E].  Rows are
+// ordered by (expert, token, slot) exactly as by the three kernels above: a
+// token chooses an expert at most once, so a row's rank within its expert is
+// the number of earlier tokens in the expert's bitmap.
+__global__ __launch_bounds__(kTokBlk) void k_route_one_block(const int32_t *ids, int T, int E, int top,
+                                                             int32_t *offsets, int32_t *row_token,
+                                                             int32_t *inverse) {
+  extern __shared__ int32_t lds_i[];
+  constexpr int W = kTokBlk / 32;
+  int32_t *cnt = lds_i;
+  uint32_t *bits = reinterpret_cast<uint32_t *>(lds_i + E);
+  int32_t *pre = lds_i + E + E * W;
+  __shared__ int32_t wsum[kTokBlk / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < E; i += kTokBlk) cnt[i] = 0;
+  for (int i = t; i < E * W; i += kTokBlk) bits[i] = 0;
+  __syncthreads();
+  if (t < T)
+    for (int j = 0; j < top; ++j) {
+      const int e = ids[t * top + j];
+      atomicAdd(&cnt[e], 1);
+      atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+    }
+  __syncthreads();
+  // Exclusive prefix of cnt over experts: thread t owns experts [4t, 4t + 4).
+  int32_t c[4], own = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    c[q] = e < E ? cnt[e] : 0;
+    own += c[q];
+  }
+  int32_t incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int32_t run = incl - own;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * t + q;
+    if (e < E) {
+      pre[e] = run;
+      offsets[e] = run;
+    }
+    run += c[q];
+  }
+  if (t == kTokBlk - 1) offsets[E] = run;  // the last thread's running sum is the total
+  __syncthreads();
+  if (t >= T) return;
+  for (int j = 0; j < top; ++j) {
+    const int e = ids[t * top + j];
+    int rank = 0;
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(bits[e * W + w]);
+    rank += __popc(bits[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
+    const int32_t pos = pre[e] + rank;
+    row_token[pos] = t;
+    inverse[t * top + j] = pos;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_combine(const float *y, int64_t T, int top, int64_t N,
                                                  const int32_t *inverse, const float *w, float *out) {
   const int64_t n4 = N / 4;
@@ -276,8 +343,15 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t 
     else if (E <= 256) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, stream, logits, T, E, top, ids, w);
     else if (E <= 512) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, stream, logits, T, E, top, ids, w);
     else hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, stream, logits, T, E, top, ids, w);
-    hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kTokBlk), E * sizeof(int32_t), stream, ids, T, E,
-                       top, blk);
+    if (nblk > 1)
+      hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kTokBlk), E * sizeof(int32_t), stream, ids, T, E,
+                         top, blk);
+  }
+  if (nblk == 1) {  // one token block: count, scan and scatter in one workgroup
+    hipLaunchKernelGGL(k_route_one_block, dim3(1), dim3(kTokBlk),
+                       static_cast<size_t>(E) * (2 + kTokBlk / 32) * sizeof(int32_t), stream, ids,
+                       static_cast<int>(T), E, top, offsets, row_token, inverse);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, blk, nblk, E, offsets);
   if (T > 0)
