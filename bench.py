@@ -52,8 +52,8 @@ PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 CPU_BASELINE_MIN_S = 10.0  # repeat the oracle sample until at least this much CPU time
 # RAC steps write the merged fp16 activation (quads_rac_select_merged) and the
-# GEMMs read it; QUADS_RAC_GEMM=extended times the extended-K formulation.
-MERGED_RAC = os.environ.get("QUADS_RAC_GEMM") != "extended"
+# GEMMs read it; --rac-form exact times the extended-K formulation instead.
+MERGED_RAC = True
 
 
 def parse():
@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true", help="skip the plain W4A4 comparison run")
     ap.add_argument("--graph", action="store_true", help="replay the non-dominant stages as HIP graphs")
+    ap.add_argument("--rac-form", choices=["merged", "exact"], default="merged",
+                    help="RAC correction: merged fp16 operand from quads_rac_select_merged, or the exact "
+                         "extended-K contraction (QUADS_RAC_FORM_EXACT)")
     return ap.parse_args()
 
 
@@ -102,7 +105,8 @@ def setup_expert_gemm(Q, S, k):
     scall = Q.SelectCall(x, q, scores, k, merged=merged)
     sel, res, nsel = scall()
     gc = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M,
-                    x=q, res=res if nsel else None, sel_idx=sel, x_merged=scall.merged if merged else None)
+                    x=q, res=res if nsel else None, sel_idx=sel, x_merged=scall.merged if merged else None,
+                    rac_form=Q.RAC_FORM_MERGED if merged else Q.RAC_FORM_EXACT)
     # MFMA work the RAC GEMM executes: one contraction over K on the merged
     # operand, K + nsel with the extended contraction.
     flops = 2.0 * M * N * (K + (0 if merged else nsel))
@@ -159,24 +163,26 @@ def setup_moe(Q, S, k, decode):
     mr = MERGED_RAC and k > 0
     sx = Q.SelectCall(x, q, sc, k, merged=mr)
     sel, res, nsel_x = sx()
+    form = Q.RAC_FORM_MERGED if mr else Q.RAC_FORM_EXACT
     g1 = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
                     x=q, res=res if nsel_x else None, sel_idx=sel, row_token=rt, epilogue=Q.EPI_SWIGLU,
-                    x_merged=sx.merged if mr else None)
+                    x_merged=sx.merged if mr else None, rac_form=form)
     h = g1.y
     qh = Q.QuantizeCall(h, want_scores=True)
     hq, hsc = qh()
     sh = Q.SelectCall(h, hq, hsc, k, merged=mr)
     hsel, hres, nsel_h = sh()
     g2 = Q.GemmCall(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs, num_rows=R,
-                    x=hq, res=hres if nsel_h else None, sel_idx=hsel, x_merged=sh.merged if mr else None)
+                    x=hq, res=hres if nsel_h else None, sel_idx=hsel, x_merged=sh.merged if mr else None,
+                    rac_form=form)
     cc = Q.CombineCall(g2.y, inv, w)
     stages = [("route", rc), ("quantize_x", qx), ("rac_x", sx), ("gate_up_prepare", g1.prepare),
               ("gate_up", g1.run), ("quantize_h", qh), ("rac_h", sh), ("down_prepare", g2.prepare),
               ("down", g2.run), ("combine", cc)]
     # MFMA work the RAC GEMMs execute: both shapes add the correction to the
-    # activation operand (one contraction over K), unless QUADS_RAC_GEMM=extended
-    # forces the extended contraction (K + nsel) on the prefill's 256x256 tiles.
-    merged = mr or decode
+    # activation operand (one contraction over K), unless --rac-form exact
+    # forces the extended contraction (K + nsel).
+    merged = mr
     f1 = 2.0 * R * N2 * (H + (0 if merged else nsel_x))
     f2 = 2.0 * R * H * (I + (0 if merged else nsel_h))
     # plain W4A4 layer
@@ -440,6 +446,8 @@ def main():
     from fp4_quantized_moe_amd import _lib as Q
     from fp4_quantized_moe_amd import synthetic as S
 
+    global MERGED_RAC
+    MERGED_RAC = args.rac_form == "merged"
     torch.cuda.set_device(0)
     Q.load()
     if args.workload == "ablation":

@@ -20,6 +20,7 @@ F32, BF16 = 0, 1
 GSCALE_GIVEN, WANT_SCORES = 1, 2
 OPERANDS_W4A4, OPERANDS_BF16 = 0, 1
 EPI_NONE, EPI_SWIGLU = 0, 1
+RAC_FORM_AUTO, RAC_FORM_EXACT, RAC_FORM_MERGED = 0, 1, 2
 
 _c_i64, _c_i32, _c_u32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
 
@@ -43,7 +44,7 @@ class _GemmArgs(ctypes.Structure):
         ("w_codes", _vp), ("w_scales", _vp), ("w_gscale", _vp),
         ("x_bf16", _vp), ("w_bf16", _vp),
         ("row_token", _vp), ("expert_offsets", _vp),
-        ("y", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t), ("x_merged", _vp),
+        ("y", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t), ("x_merged", _vp), ("rac_form", _c_i32),
     ]
 
 
@@ -140,6 +141,24 @@ def _require_cuda(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise QuadsError("tensors must be contiguous and on the GPU")
+
+
+def _check_route_args(logits):
+    _require_cuda(logits)
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise QuadsError("moe_route expects float32 logits [T, E]")
+
+
+def _check_combine_args(y, inverse, topk_w):
+    _require_cuda(y, inverse, topk_w)
+    if y.dtype != torch.float32 or y.dim() != 2:
+        raise QuadsError("moe_combine expects float32 y [T*top, N]")
+    if inverse.dtype != torch.int32 or inverse.dim() != 2:
+        raise QuadsError("moe_combine expects int32 inverse [T, top]")
+    if topk_w.dtype != torch.float32 or tuple(topk_w.shape) != tuple(inverse.shape):
+        raise QuadsError("moe_combine expects float32 topk_w of inverse's shape [T, top]")
+    if y.shape[0] != inverse.numel():
+        raise QuadsError(f"moe_combine: y has {y.shape[0]} rows, expected T*top = {inverse.numel()}")
 
 
 def _workspace(nbytes: int, device):
@@ -257,14 +276,15 @@ class GemmCall:
     """One grouped-GEMM call with its arguments and workspace built once.
 
     W4A4 mode when `x` is given, bf16-operand (trainer W4A16) mode when
-    `x_bf16`/`w_bf16` are given.  ``prepare()`` + ``run()`` is the split form
+    `x_bf16`/`w_bf16` are given.  `rac_form` (RAC_FORM_AUTO / _EXACT /
+    _MERGED) picks the formulation of the RAC correction, see quads.h.  ``prepare()`` + ``run()`` is the split form
     (tile list and residual weight-column gather, then the GEMM kernel);
     calling the object does both."""
 
     def __init__(self, *, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
                  expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
                  sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
-                 x_bf16=None, w_bf16=None, y=None, x_merged=None):
+                 x_bf16=None, w_bf16=None, y=None, x_merged=None, rac_form=RAC_FORM_AUTO):
         L = load()
         E = int(expert_offsets.numel()) - 1
         bf16_mode = x_bf16 is not None
@@ -285,6 +305,7 @@ class GemmCall:
         a.n_seg = n_seg
         a.num_rows = num_rows
         a.N, a.K = N, K
+        a.rac_form = rac_form
         if bf16_mode:
             _require_cuda(x_bf16, w_bf16)
             a.act_rows = x_bf16.shape[0]
@@ -374,7 +395,7 @@ class RouteCall:
 
     def __init__(self, logits: torch.Tensor, top: int):
         L = load()
-        _require_cuda(logits)
+        _check_route_args(logits)
         T, E = logits.shape
         dev = logits.device
         self.logits, self.T, self.E, self.top = logits, T, E, top
@@ -396,7 +417,7 @@ class CombineCall:
     """quads_moe_combine with its output allocated once."""
 
     def __init__(self, y: torch.Tensor, inverse: torch.Tensor, topk_w: torch.Tensor):
-        _require_cuda(y, inverse, topk_w)
+        _check_combine_args(y, inverse, topk_w)
         self.y, self.inverse, self.w = y, inverse, topk_w
         self.T, self.top = inverse.shape
         self.N = y.shape[1]
@@ -412,7 +433,7 @@ def moe_route(logits: torch.Tensor, top: int):
     """-> (topk_ids [T, top] i32, topk_w [T, top] f32, expert_offsets [E+1] i32,
     row_token [T*top] i32, inverse [T, top] i32)."""
     L = load()
-    _require_cuda(logits)
+    _check_route_args(logits)
     T, E = logits.shape
     dev = logits.device
     ids = torch.empty(T, top, dtype=torch.int32, device=dev)
@@ -428,7 +449,7 @@ def moe_route(logits: torch.Tensor, top: int):
 
 def moe_combine(y: torch.Tensor, inverse: torch.Tensor, topk_w: torch.Tensor):
     L = load()
-    _require_cuda(y, inverse, topk_w)
+    _check_combine_args(y, inverse, topk_w)
     T, top = inverse.shape
     N = y.shape[1]
     out = torch.empty(T, N, dtype=torch.float32, device=y.device)

@@ -190,7 +190,12 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
     return fail(QUADS_ERR_ARG, "gemm: arrays must be 16-byte aligned");
   if (a->row_token == nullptr && a->act_rows < a->num_rows)
     return fail(QUADS_ERR_SHAPE, "gemm: identity rows need act_rows >= num_rows");
+  if (a->rac_form != QUADS_RAC_FORM_AUTO && a->rac_form != QUADS_RAC_FORM_EXACT && a->rac_form != QUADS_RAC_FORM_MERGED)
+    return fail(QUADS_ERR_ARG, "gemm: bad rac_form %d", a->rac_form);
+  if (a->rac_form == QUADS_RAC_FORM_EXACT && a->x_merged != nullptr)
+    return fail(QUADS_ERR_ARG, "gemm: x_merged is the merged form; rac_form EXACT needs x_merged == NULL");
   g = quads::GemmLaunch{};
+  g.rac_form = a->rac_form;
   g.mode = a->operand_mode == QUADS_OPERANDS_BF16 ? 1 : 0;
   g.epilogue = a->epilogue;
   g.y_bf16 = a->y_dtype == QUADS_BF16;

@@ -1133,13 +1133,11 @@ __global__ __launch_bounds__(256) void k_gather_wcols(const uint8_t *w_codes, co
 }
 
 using CfgS = Cfg<128, 128, 2, 2, 2>;  // general / ragged shapes: 256 threads, 2 workgroups per CU
-using CfgM = Cfg<128, 192, 2, 2, 1>;  // N % 192 == 0 dense shapes: 64x96 wave tiles
 using CfgL = Cfg<256, 256, 2, 4, 1>;  // large grouped shapes: 512 threads, 128x64 wave tiles
-using CfgW = Cfg<256, 256, 2, 2, 1>;  // large grouped shapes: 256 threads, 128x128 wave tiles
-using CfgS8a = Cfg<128, 128, 4, 2, 2>;  // 512 threads, 32x64 wave tiles
-using CfgS8b = Cfg<128, 128, 2, 4, 2>;  // 512 threads, 64x32 wave tiles
 
-enum TileCfg { kS = 0, kM = 1, kL = 2, kW = 3, kP = 4, kS8a = 5, kS8b = 6, kD = 7, kD3 = 8 };
+// kS: register-staged 128x128; kL: register-staged 256x256 (NVFP4 operands);
+// kP: ping-pong 256x256 (bf16 operands); kD: DMA-staged 128x128 (NVFP4).
+enum TileCfg { kS = 0, kL = 2, kP = 4, kD = 7 };
 
 // The DMA-staged kernel's shape limits: NVFP4 operands, 128-element main
 // steps, 64-element residual steps.
@@ -1154,19 +1152,6 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // on the device): estimated CU occupancy x expected per-workgroup efficiency
 // x fraction of tile rows that are real rows.
 TileCfg pick_cfg(const GemmLaunch &a) {
-  // Optional override for tuning: QUADS_GEMM_TILE=128x128 | 128x192 | 256x256.
-  static const char *force = getenv("QUADS_GEMM_TILE");
-  if (force != nullptr) {
-    if (strcmp(force, "256x256") == 0 && a.N % 256 == 0) return kL;
-    if (strcmp(force, "128x192") == 0 && a.N % 192 == 0 && a.epilogue == 0) return kM;
-    if (strcmp(force, "128x128") == 0) return kS;
-    if (strcmp(force, "256x256w4") == 0 && a.N % 256 == 0) return kW;
-    if (strcmp(force, "256x256pp") == 0 && a.N % 256 == 0) return kP;
-    if (strcmp(force, "128x128w8a") == 0) return kS8a;
-    if (strcmp(force, "128x128w8b") == 0 && a.epilogue == 0) return kS8b;  // SwiGLU needs 2 tiles per wave
-    if (strcmp(force, "128x128dma") == 0 && dma_fits(a)) return kD;
-    if (strcmp(force, "128x192dma") == 0 && dma_fits(a) && a.N % 192 == 0 && a.epilogue == 0) return kD3;
-  }
   struct Cand {
     TileCfg c;
     int bm, bn, slots;
@@ -1179,7 +1164,6 @@ TileCfg pick_cfg(const GemmLaunch &a) {
   const TileCfg large = a.mode == 1 ? kP : kL;
   for (const Cand &c : cands) {
     if (a.N % c.bn) continue;
-    if (c.c == kM && a.epilogue != 0) continue;  // SWIGLU pairs need an even tile count per wave
     const double m_est = static_cast<double>((a.num_rows + c.bm - 1) / c.bm) + (a.E > 1 ? a.E / 2.0 : 0.0);
     const double wgs = m_est * static_cast<double>(a.N / c.bn);
     const double rounds = wgs > 0 ? static_cast<double>(static_cast<int64_t>((wgs + c.slots - 1) / c.slots)) : 1.0;
@@ -1198,10 +1182,8 @@ TileCfg pick_cfg(const GemmLaunch &a) {
   return best;
 }
 
-int cfg_bm(TileCfg c) { return (c == kL || c == kW || c == kP) ? 256 : 128; }
-int cfg_bn(TileCfg c) {
-  return (c == kL || c == kW || c == kP) ? 256 : ((c == kM || c == kD3) ? CfgM::BN : CfgS::BN);
-}
+int cfg_bm(TileCfg c) { return (c == kL || c == kP) ? 256 : 128; }
+int cfg_bn(TileCfg c) { return (c == kL || c == kP) ? 256 : CfgS::BN; }
 
 template <class C, int MODE, int EPI, bool RES>
 void launch_k(const Params &p, int grid, hipStream_t s) {
@@ -1263,32 +1245,26 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
 }
 
 // RAC calls with many rows per expert: which formulation of the correction.
-// The merged fp16 activation operand (MODE 2: one MFMA pass over K, after a
-// merge pass) wins where the extended-K GEMM would run on the large
-// register-staged tiles (measured on the 16384-token prefill layer: 0.94 vs
-// 1.30 ms gate_up, 0.64 vs 0.83 ms down, merge passes included); on the
-// 128x128 DMA-staged shapes the merge pass costs what the shorter GEMM saves
-// (4096 x 1536 x 2048: 18 + 48 vs 5 + 62 us), so the exact extended-K kernel
-// stays.  A merged operand the caller built (quads_rac_select_merged) is
-// always taken: the DMA-staged 128x128 kernel reads it as well.
-// QUADS_RAC_GEMM=extended | merged overrides the choice; it is read on every
-// call, so one process can compare the two.
+// QUADS_RAC_FORM_EXACT and _MERGED choose it; QUADS_RAC_FORM_AUTO takes the
+// merged fp16 activation operand (MODE 2: one MFMA pass over K, after a merge
+// pass) where the extended-K GEMM would run on the large register-staged
+// tiles (measured on the 16384-token prefill layer: 0.94 vs 1.30 ms gate_up,
+// 0.64 vs 0.83 ms down, merge passes included); on the 128x128 DMA-staged
+// shapes the merge pass costs what the shorter GEMM saves (4096 x 1536 x
+// 2048: 18 + 48 vs 5 + 62 us), so the exact extended-K kernel stays.  A
+// merged operand the caller built (quads_rac_select_merged) is always taken:
+// the DMA-staged 128x128 kernel reads it as well.
 bool use_merged(const GemmLaunch &a) {
   if (a.mode != 0 || a.r_codes == nullptr || a.kpad == 0 || gemm_use_small(a)) return false;
-  if (a.x_merged != nullptr) return true;  // the caller built it: no merge pass to pay for
-  if (const char *f = getenv("QUADS_RAC_GEMM")) {
-    if (strcmp(f, "extended") == 0) return false;
-    if (strcmp(f, "merged") == 0) return true;
-  }
+  if (a.x_merged != nullptr || a.rac_form == QUADS_RAC_FORM_MERGED) return true;
+  if (a.rac_form == QUADS_RAC_FORM_EXACT) return false;
   const TileCfg c = pick_cfg(a);
-  return c == kL || c == kW || c == kP;
+  return c == kL || c == kP;
 }
 
 TileCfg pick_cfg_for(const GemmLaunch &a) {
   TileCfg c = pick_cfg(a);
-  if (use_merged(a)) {
-    if (c == kD3 || c == kP) c = c == kD3 ? kM : kL;  // kD has a merged form
-  }
+  if (use_merged(a) && c == kP) c = kL;  // kD and kL have a merged form
   return c;
 }
 
@@ -1375,13 +1351,8 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   p.grid_per_xcd = static_cast<int>(grid / 8);
   const int g = static_cast<int>(grid);
   if (c == kD) launch_dma<2>(a, p, g, res, stream, merged);
-  else if (c == kD3) launch_dma<3>(a, p, g, res, stream);
   else if (c == kP) launch_pp_cfg(a, p, g, res, stream);
-  else if (c == kW) launch_cfg<CfgW>(a, p, g, res, stream, merged);
-  else if (c == kS8a) launch_cfg<CfgS8a>(a, p, g, res, stream, merged);
-  else if (c == kS8b) launch_cfg<CfgS8b>(a, p, g, res, stream, merged);
   else if (c == kL) launch_cfg<CfgL>(a, p, g, res, stream, merged);
-  else if (c == kM) launch_cfg<CfgM>(a, p, g, res, stream, merged);
   else launch_cfg<CfgS>(a, p, g, res, stream, merged);
   return hipGetLastError();
 }

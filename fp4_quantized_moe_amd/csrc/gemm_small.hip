@@ -498,10 +498,9 @@ __global__ __launch_bounds__(256) void k_merge_residual(const uint8_t *__restric
 bool gemm_use_small(const GemmLaunch &a) {
   // K in whole pairs of 256-element steps (the K loop is unrolled by two)
   if (a.mode != 0 || a.K % (2 * kSK) != 0 || a.K > 16384 || a.N % kSBN != 0) return false;
-  if (const char *f = getenv("QUADS_GEMM_TILE")) {
-    if (strcmp(f, "small") == 0) return true;
-    if (strcmp(f, "128x128") == 0 || strncmp(f, "256x256", 7) == 0 || strcmp(f, "128x192") == 0) return false;
-  }
+  // This kernel adds the RAC correction to the activation operand only (one
+  // fp16 operand); the exact form runs on the many-rows kernels.
+  if (a.rac_form == QUADS_RAC_FORM_EXACT && a.r_codes != nullptr && a.kpad > 0) return false;
   return a.num_rows <= static_cast<int64_t>(kSM) * a.E;  // about one pass of rows per expert
 }
 

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/quads.h"
+
 namespace quads {
 
 // ---- quantize.hip --------------------------------------------------------
@@ -63,6 +65,7 @@ struct GemmLaunch {
   void *y;
   void *ws;
   const uint16_t *x_merged;  // caller's RAC-merged fp16 activation, or null
+  int rac_form;              // QUADS_RAC_FORM_AUTO | _EXACT | _MERGED
 };
 size_t gemm_ws_bytes(const GemmLaunch &a);
 // prepare: tile list + residual weight-column gather; main: the GEMM kernel.

@@ -23,6 +23,19 @@ namespace {
 
 constexpr int kTokBlk = 256;
 
+// Selection key of a logit: an unsigned integer that orders like the value,
+// with -0 equal to +0 and NaN below -inf (key 0; -inf is 0x007FFFFF).  Both
+// top-k kernels pick experts by (key descending, index ascending), so every
+// written id is a valid expert whatever the logits hold, and a NaN logit is
+// chosen only after every real one (-inf included), as a stable descending
+// sort puts it.
+__device__ __forceinline__ uint32_t route_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (v != v) return 0u;
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 // kMaxPer = ceil(E / 64) slots per lane (E <= 64 * kMaxPer <= 1024).
 template <int kMaxPer>
 __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t T, int E, int top,
@@ -47,23 +60,32 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t
     if (q * 64 + lane < E) sum += expf(v[q] - mx);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  uint32_t key[kMaxPer];
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) key[q] = route_key(v[q]);
   uint32_t taken = 0;  // bit q: slot q of this lane already chosen
   for (int j = 0; j < top; ++j) {
+    // (key 0, index INT_MAX) loses to every untaken expert, and top <= E
+    // leaves at least one, so bi ends as a valid expert index.
+    uint32_t bk = 0u;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int q = 0; q < kMaxPer; ++q) {
       const int e = q * 64 + lane;
-      if (e < E && !((taken >> q) & 1u) && (v[q] > bv || (v[q] == bv && e < bi))) {
+      if (e < E && !((taken >> q) & 1u) && (key[q] > bk || (key[q] == bk && e < bi))) {
+        bk = key[q];
         bv = v[q];
         bi = e;
       }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t ok = __shfl_xor(bk, off);
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
+      if (ok > bk || (ok == bk && oi < bi)) {
+        bk = ok;
         bv = ov;
         bi = oi;
       }
@@ -78,15 +100,14 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t
 
 // E <= 256, one wave per token: every lane ranks its own logits against the
 // token's E logits (held in LDS per wave).  rank(e) = number of logits that
-// are larger, or equal at a lower expert index, with NaN ranked as -inf, so
-// the ranks are a permutation of 0..E-1 and the experts of rank < top are the
-// top-k in the order the repeated wave argmax gives (ties to the lower
-// index).  The softmax statistics are those of k_route_topk, operation for
+// have a larger selection key (route_key), or an equal one at a lower expert
+// index, so the ranks are a permutation of 0..E-1 and the experts of rank <
+// top are the top-k in the order the repeated wave argmax gives.  The softmax statistics are those of k_route_topk, operation for
 // operation.
 template <int PER>
 __global__ __launch_bounds__(256) void k_route_topk_rank(const float *logits, int64_t T, int E, int top,
                                                          int32_t *ids, float *wts) {
-  __shared__ __attribute__((aligned(16))) float lv[4][64 * PER];
+  __shared__ __attribute__((aligned(16))) uint32_t lv[4][64 * PER];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   const bool valid = t < T;  // no early return: every wave reaches the barrier
@@ -107,21 +128,21 @@ __global__ __launch_bounds__(256) void k_route_topk_rank(const float *logits, in
     if (q * 64 + lane < E) sum += expf(v[q] - mx);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  float key[PER];
+  uint32_t key[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    key[q] = v[q] != v[q] ? -INFINITY : v[q];
+    key[q] = route_key(v[q]);
     if (q * 64 + lane < E) lv[wave][q * 64 + lane] = key[q];
   }
   __syncthreads();
   uint32_t rank[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) rank[q] = 0;
-  const float *lw = lv[wave];
+  const uint32_t *lw = lv[wave];
   int j = 0;
   for (; j + 4 <= E; j += 4) {
-    const float4 o = *reinterpret_cast<const float4 *>(lw + j);
-    const float ov[4] = {o.x, o.y, o.z, o.w};
+    const uint4 o = *reinterpret_cast<const uint4 *>(lw + j);
+    const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -129,7 +150,7 @@ __global__ __launch_bounds__(256) void k_route_topk_rank(const float *logits, in
         rank[q] += ov[u] > key[q] || (ov[u] == key[q] && j + u < q * 64 + lane);
   }
   for (; j < E; ++j) {
-    const float o = lw[j];
+    const uint32_t o = lw[j];
 #pragma unroll
     for (int q = 0; q < PER; ++q) rank[q] += o > key[q] || (o == key[q] && j < q * 64 + lane);
   }

@@ -164,15 +164,26 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  * quantized output: the same sum.  With r_codes == NULL (or kpad == 0) it is
  * plain W4A4.
  *
- * Rounding: with the correction as an extended contraction the GEMM
- * accumulates exact operand values in FP32.  Where that is slower -- few rows
- * per expert (num_rows <= 32 * num_experts, the decode shape) and large
- * grouped shapes that run on 256 x 256 tiles -- the correction is instead
- * added to the activation before the GEMM, as one fp16 operand per element
- * X + (gr/gx) R in units of gx, so each corrected element is rounded once
- * more (relative 2^-11).  The environment variable QUADS_RAC_GEMM=extended |
- * merged forces either form for many-rows calls.  Both stay within
- * max|Y - Y_exact| <= 1e-3 max|Y_exact| on the seeded workloads.
+ * Form of the RAC correction (quads_moe_gemm_args.rac_form; both stay within
+ * max|Y - Y_exact| <= 1e-3 max|Y_exact| on the seeded workloads):
+ *   QUADS_RAC_FORM_EXACT   the correction is an extended contraction over
+ *                          the gathered weight columns: the GEMM accumulates
+ *                          exact operand values in FP32 (accumulation
+ *                          rounding only).  x_merged must be NULL.
+ *   QUADS_RAC_FORM_MERGED  the correction is added to the activation before
+ *                          the GEMM, as one fp16 operand per element
+ *                          X' + fl32(R' * fl32(gr/gx)) in units of gx (the
+ *                          quads_rac_select_merged definition; built by the
+ *                          prepare step unless x_merged is given), so each
+ *                          corrected element is rounded once more (relative
+ *                          2^-11), and the GEMM contracts over K alone.
+ *   QUADS_RAC_FORM_AUTO    (0, the default) MERGED when x_merged is given,
+ *                          for few rows per expert (num_rows <= 32 *
+ *                          num_experts with K % 512 == 0, K <= 16384 and
+ *                          N % 128 == 0: the decode shape) and where the
+ *                          tile choice gives 256 x 256 tiles (large grouped
+ *                          shapes); EXACT otherwise.  The choice depends
+ *                          only on the arguments, so prepare and main agree.
  *
  * operand_mode QUADS_OPERANDS_BF16 is the trainer's W4A16 forward [Gist
  * 2.2-A]: x_bf16 [act_rows, K] times w_bf16 [E, N, K] (QDQ'd weights),
@@ -183,8 +194,7 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  * the up projection) writes h [num_rows, N/2] BF16 with
  * h = silu(Y_gate) * Y_up.
  *
- * Shapes: K % 16 == 0, N % 64 == 0 (N % 128 == 0 for SWIGLU), num_experts
- * in [1, 1024].  expert_offsets is a DEVICE array of num_experts + 1
+ * Shapes: K % 16 == 0, N % 128 == 0, num_experts in [1, 1024].  expert_offsets is a DEVICE array of num_experts + 1
  * non-decreasing int32 with expert_offsets[0] = 0 and
  * expert_offsets[E] = num_rows (not checked on the host: reading it would
  * synchronize).
@@ -194,6 +204,11 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
 #define QUADS_OPERANDS_BF16 1
 #define QUADS_EPI_NONE 0
 #define QUADS_EPI_SWIGLU 1
+
+/* quads_moe_gemm_args.rac_form */
+#define QUADS_RAC_FORM_AUTO 0
+#define QUADS_RAC_FORM_EXACT 1
+#define QUADS_RAC_FORM_MERGED 2
 
 /* quads_moe_gemm_args.flags */
 #define QUADS_GEMM_PREPARED 1u /* workspace already filled by quads_moe_gemm_prepare for
@@ -235,9 +250,10 @@ typedef struct {
   size_t ws_bytes;
   /* Optional [act_rows, K] fp16 RAC-merged activation from
      quads_rac_select_merged (units of x_gscale), or NULL.  With a residual
-     present the GEMM then contracts it over K alone (the merged form below),
+     present the GEMM then contracts it over K alone (the merged form above),
      whatever the shape, and builds no merged operand of its own. */
   const void *x_merged;
+  int32_t rac_form; /* QUADS_RAC_FORM_AUTO | _EXACT | _MERGED (see above) */
 } quads_moe_gemm_args;
 
 size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a);
@@ -277,6 +293,10 @@ quads_status_t quads_weight_qdq(const void *w_bf16, int64_t batch, int64_t rows,
  * permutation that groups routed rows by (expert, token): expert_offsets
  * [E+1], row_token [T*top] (token of each routed row), inverse [T, top]
  * (routed row of each (token, slot)).  E <= 1024, 1 <= top <= min(E, 16).
+ * Non-finite logits: every written id is still a valid expert in [0, E);
+ * experts are taken by value descending with -0 == +0, -inf after every
+ * real value, NaN after -inf, ties to the lower index (the weights of a
+ * NaN row are unspecified).
  * ------------------------------------------------------------------------- */
 size_t quads_moe_route_workspace_bytes(int64_t T, int32_t E);
 quads_status_t quads_moe_route(const float *logits, int64_t T, int32_t E, int32_t top,

@@ -104,12 +104,30 @@ def test_gemm_validation(L):
         (dict(struct_size=8), -1), (dict(operand_mode=5), -1), (dict(epilogue=3), -1),
         (dict(K=100), -2), (dict(N=96), -2), (dict(num_experts=0), -2), (dict(n_seg=3), -2),
         (dict(epilogue=1, n_seg=1), -2), (dict(y=None), -1), (dict(w_codes=None), -1),
-        (dict(act_rows=8, row_token=None), -2), (dict(r_codes=16, kpad=40), -2),
+        (dict(act_rows=8, row_token=None), -2), (dict(r_codes=16, kpad=40), -2), (dict(N=192), -2),
+        (dict(rac_form=3), -1), (dict(rac_form=-1), -1), (dict(rac_form=1, x_merged=16), -1),
     ]
     for kw, want in cases:
         a = _gemm_args(**kw)
         assert L.quads_moe_w4a4_gemm(ctypes.byref(a), None) == want, kw
         assert L.quads_last_error() != b""
+
+
+def test_gemm_rac_form_field(L):
+    """The RAC formulation is an explicit argument (no environment or other
+    hidden input): the workspace holds the gathered weight columns
+    (E*N*kpad fp16) for the exact form and the merged activation
+    (act_rows*K fp16) for the merged form, whatever the process environment."""
+    res = dict(r_codes=16, r_scales=16, r_gscale=16, sel_idx=16, kpad=128, num_rows=4096, act_rows=4096,
+               N=1536, K=2048)
+    exact = L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(rac_form=1, **res)))
+    merged = L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(rac_form=2, **res)))
+    auto = L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(rac_form=0, **res)))
+    assert exact >= 1536 * 128 * 2 and exact < 4096 * 2048 * 2
+    assert merged >= 4096 * 2048 * 2
+    assert auto == exact  # 128x128 DMA-staged tiles: the exact form by default
+    given = L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(rac_form=0, x_merged=16, **res)))
+    assert given < 4096  # the caller's merged operand: only the tile list
 
 
 def test_qdq_route_combine_validation(L):

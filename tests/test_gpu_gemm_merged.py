@@ -1,15 +1,14 @@
-"""GPU parity of both formulations of the RAC correction in the many-rows
-grouped GEMM, selected per call with QUADS_RAC_GEMM:
-- extended: the correction as an extended contraction, exact up to FP32
-  accumulation;
-- merged: the correction added to the activation as one fp16 operand, with
-  one more rounding per corrected element.
+"""GPU parity of both formulations of the RAC correction in the grouped GEMM,
+chosen per call with the rac_form argument:
+- exact (QUADS_RAC_FORM_EXACT): the correction as an extended contraction,
+  exact up to FP32 accumulation;
+- merged (QUADS_RAC_FORM_MERGED): the correction added to the activation as
+  one fp16 operand, with one more rounding per corrected element.
 Both are checked against the oracle's float64 extended-K reference at the
-1e-3 bar: dense and grouped shapes, ragged rows, a gathered row order, the
-SwiGLU epilogue, and the full-size expert-GEMM workload through the
-caller-built merged operand."""
-import os
-
+1e-3 bar (the exact form also at the accumulation-only bar EXACT_TOL):
+dense and grouped shapes, ragged rows, a gathered row order, the SwiGLU
+epilogue, the few-rows (decode) shape in both forms, and the full-size
+expert-GEMM workload through the caller-built merged operand."""
 import numpy as np
 import pytest
 import torch
@@ -21,20 +20,9 @@ from tests.gpu_util import dev_act, host, log, quantize_weights_gpu, rel_err
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
-
-
-@pytest.fixture
-def rac_mode():
-    old = os.environ.get("QUADS_RAC_GEMM")
-
-    def set_mode(m):
-        os.environ["QUADS_RAC_GEMM"] = m
-
-    yield set_mode
-    if old is None:
-        os.environ.pop("QUADS_RAC_GEMM", None)
-    else:
-        os.environ["QUADS_RAC_GEMM"] = old
+# The exact form differs from the float64 reference by FP32 accumulation only.
+EXACT_TOL = 2e-5
+FORMS = {"exact": Q.RAC_FORM_EXACT, "merged": Q.RAC_FORM_MERGED}
 
 
 def _grouped(seed, counts, T, K, N, n_seg=1):
@@ -46,7 +34,7 @@ def _grouped(seed, counts, T, K, N, n_seg=1):
     return xa, wa, offs, rt
 
 
-def _run(xa, wa, offs, rt, k, n_seg=1, epilogue=Q.EPI_NONE):
+def _run(xa, wa, offs, rt, k, n_seg=1, epilogue=Q.EPI_NONE, rac_form=Q.RAC_FORM_AUTO):
     x = dev_act(xa)
     E, N, K = wa.f32.shape
     wc, ws_, wg = quantize_weights_gpu(dev_act(wa), n_seg)
@@ -56,46 +44,57 @@ def _run(xa, wa, offs, rt, k, n_seg=1, epilogue=Q.EPI_NONE):
     return Q.moe_w4a4_gemm(w_codes=wc, w_scales=ws_, w_gscale=wg, n_seg=n_seg, N=N, K=K,
                            expert_offsets=torch.from_numpy(offs).cuda(), num_rows=R, x=q,
                            res=res if nsel else None, sel_idx=sel,
-                           row_token=None if rt is None else torch.from_numpy(rt).cuda(), epilogue=epilogue)
+                           row_token=None if rt is None else torch.from_numpy(rt).cuda(), epilogue=epilogue,
+                           rac_form=rac_form)
 
 
-@pytest.mark.parametrize("mode", ["extended", "merged"])
+def _check(y, ref, mode):
+    err = rel_err(y, ref)
+    log(f"  rel err {err:.2e}")
+    assert err <= (EXACT_TOL if mode == "exact" else TOL)
+
+
+@pytest.mark.parametrize("mode", ["exact", "merged"])
 @pytest.mark.parametrize("k", [25, 50, 100])
-def test_dense_both_formulations(rac_mode, mode, k):
-    rac_mode(mode)
+def test_dense_both_formulations(mode, k):
     wl = S.expert_gemm(M=1024)
     log(f"[gemm-rac] dense 1024x2048x1536 k={k} {mode}")
     offs = np.array([0, 1024], np.int32)
-    y = host(_run(wl.x, S.Activation(wl.w.f32[None], wl.w.bits[None]), offs, None, k))
+    y = host(_run(wl.x, S.Activation(wl.w.f32[None], wl.w.bits[None]), offs, None, k, rac_form=FORMS[mode]))
     _, _, _, we = O.quantize_weights(wl.w.f32[None], 1)
-    ref = O.rac_linear(wl.x.f32, we, k)["y"]
-    err = rel_err(y, ref)
-    log(f"  rel err {err:.2e}")
-    assert err <= TOL
+    _check(y, O.rac_linear(wl.x.f32, we, k)["y"], mode)
 
 
-@pytest.mark.parametrize("mode", ["extended", "merged"])
-def test_grouped_gathered_both_formulations(rac_mode, mode):
-    rac_mode(mode)
+@pytest.mark.parametrize("mode", ["exact", "merged"])
+def test_grouped_gathered_both_formulations(mode):
     counts = [300, 0, 257, 511, 64, 1, 200, 129]
     xa, wa, offs, rt = _grouped(601, counts, 700, 768, 512)
     log(f"[gemm-rac] grouped experts {counts} K=768 N=512 k=50 {mode}")
-    y = host(_run(xa, wa, offs, rt, 50))
+    y = host(_run(xa, wa, offs, rt, 50, rac_form=FORMS[mode]))
     _, _, _, we = O.quantize_weights(wa.f32, 1)
-    ref = O.rac_linear(xa.f32, we, 50, rt, offs)["y"]
-    err = rel_err(y, ref)
-    log(f"  rel err {err:.2e}")
-    assert err <= TOL
+    _check(y, O.rac_linear(xa.f32, we, 50, rt, offs)["y"], mode)
 
 
-def test_grouped_swiglu_merged(rac_mode):
+@pytest.mark.parametrize("mode", ["exact", "merged"])
+def test_decode_shape_both_formulations(mode):
+    """Few rows per expert (the decode shape, which defaults to the merged
+    operand on the few-rows kernel): the exact form runs on the many-rows
+    kernels and reaches the accumulation-only bar."""
+    counts = [16, 0, 9, 16, 31, 1, 16, 12, 16, 16, 3, 16, 20, 16, 16, 8]
+    xa, wa, offs, rt = _grouped(607, counts, 200, 512, 256)
+    log(f"[gemm-rac] decode shape experts {counts} K=512 N=256 k=50 {mode}")
+    y = host(_run(xa, wa, offs, rt, 50, rac_form=FORMS[mode]))
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    _check(y, O.rac_linear(xa.f32, we, 50, rt, offs)["y"], mode)
+
+
+def test_grouped_swiglu_merged():
     """gate/up stacked along N with two tensor scales, SwiGLU epilogue, merged
     operand: h against silu(gate) * up of the oracle's float64 product."""
-    rac_mode("merged")
     counts = [400, 333, 0, 291]
     xa, wa, offs, rt = _grouped(602, counts, 600, 512, 512)
     log(f"[gemm-rac] grouped SwiGLU experts {counts} K=512 N=512 merged")
-    h = host(_run(xa, wa, offs, rt, 50, n_seg=2, epilogue=Q.EPI_SWIGLU).float())
+    h = host(_run(xa, wa, offs, rt, 50, n_seg=2, epilogue=Q.EPI_SWIGLU, rac_form=Q.RAC_FORM_MERGED).float())
     _, _, _, we = O.quantize_weights(wa.f32, 2)
     y = O.rac_linear(xa.f32, we, 50, rt, offs)["y"]
     I = y.shape[1] // 2

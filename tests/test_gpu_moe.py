@@ -53,6 +53,35 @@ def test_route_ties_and_edge_shapes():
     _check_route(np.round(rng.standard_normal((100, 300)) * 2).astype(np.float32), 8, "E=300 ties")
 
 
+def test_route_nan_logits():
+    """Rows with NaN logits, fewer real logits than top, NaN mixed with -inf:
+    every id is a valid expert and the ids, offsets and rows equal the
+    oracle's (its stable descending sort puts NaN after -inf, ties to the
+    lower index).  Covers the argmax-round kernel (E=128 T=256, E=300) and
+    the ranking kernel (E=64 T=2048).  Weights of NaN rows are unspecified
+    and not compared."""
+    rng = np.random.default_rng(83)
+    for T, E in ((256, 128), (100, 300), (2048, 64), (2048, 130)):
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        lg[::2, :] = np.nan                      # whole rows NaN
+        lg[1::4, 3:] = np.nan                    # three real logits, then NaN
+        lg[3::4, ::2] = np.nan                   # NaN interleaved with -inf and reals
+        lg[3::4, 1::3] = -np.inf
+        lg[5::8, :E - 2] = -np.inf               # two reals, the rest -inf
+        log(f"[route] NaN rows T={T} E={E}")
+        ids, w, offs, rt, inv = Q.moe_route(torch.from_numpy(lg).cuda(), 8)
+        rids, rw, roffs, rrt, rinv = O.route(lg, 8)
+        h = host(ids)
+        assert h.min() >= 0 and h.max() < E
+        assert np.array_equal(h, rids)
+        assert np.array_equal(host(offs), roffs)
+        assert np.array_equal(host(rt), rrt)
+        assert np.array_equal(host(inv), rinv)
+        fin = np.isfinite(lg).all(axis=1)
+        if fin.any():
+            assert np.allclose(host(w)[fin], rw[fin], rtol=2e-6, atol=1e-9)
+
+
 def test_combine():
     rng = np.random.default_rng(82)
     T, top, N = 123, 8, 256

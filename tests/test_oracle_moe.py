@@ -32,6 +32,32 @@ def test_route_topk_brute_force_and_ties():
     assert np.array_equal(w, np.take_along_axis(p, ids.astype(np.int64), 1))
 
 
+def test_route_nan_order():
+    """Non-finite logits (outside the method's domain, but the library must
+    stay memory-safe and agree with the oracle): experts are chosen by value
+    descending, -inf after every real value, NaN after -inf, ties to the
+    lower index; -0 ties +0.  Brute force with an explicit class rank."""
+    rng = np.random.default_rng(64)
+    lg = rng.standard_normal((40, 12)).astype(np.float32)
+    lg[::2, ::3] = np.nan
+    lg[1::3, 1::2] = -np.inf
+    lg[::5, 4] = 0.0
+    lg[::5, 5] = -0.0
+    lg[7] = np.nan
+    ids, *_ = O.route(lg, 10)
+
+    def rank(t, e):
+        v = float(lg[t, e])
+        if np.isnan(v):
+            return (2, 0.0, e)
+        if v == -np.inf:
+            return (1, 0.0, e)
+        return (0, -v, e)
+
+    for t in range(40):
+        assert list(ids[t]) == sorted(range(12), key=lambda e: rank(t, e))[:10]
+
+
 def test_route_permutation_invariants():
     wl = S.moe_decode()
     ids, w, offs, rt, inv = O.route(wl.logits, 8)
