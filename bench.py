@@ -31,8 +31,19 @@ synthetic, seeded input already resident in HBM:
 
 `value` is tokens per second of the whole step; `roofline` describes the
 dominant kernel (its average duration from HIP events recorded on the
-stream it runs on, inside the timed steps); `cpu_baseline` is the CPU oracle
-timed on a bounded sample of the same workload on the host cores.
+stream it runs on, inside the timed steps): `achieved` counts the
+algorithmic work of the survey's per-unit figures (2*M*N*(K+nsel) flops for
+a RAC GEMM, bytes for a bandwidth-bound kernel) and `executed` the MFMA work
+the kernel really issues; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+
+The default run also measures the prefill-shaped (moe_prefill) and
+decode-shaped (moe_decode) MoE layers and one trainer layer's weight QDQ,
+each in its own block under `workloads` with its step time, tokens/s, RAC
+overhead over plain W4A4, roofline and CPU baseline (--no-moe skips them).
+Bandwidth-bound stages report algorithmic GB/s twice: back to back (20 calls
+in a HIP graph; inputs may sit in the 256 MB Infinity Cache) and cold (one
+call between HIP events after a 1 GiB write evicts the cache).
 """
 from __future__ import annotations
 
@@ -68,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true", help="skip the plain W4A4 comparison run")
     ap.add_argument("--graph", action="store_true", help="replay the non-dominant stages as HIP graphs")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="expert_gemm: skip the prefill, decode and QDQ blocks")
     ap.add_argument("--rac-form", choices=["merged", "exact"], default="merged",
                     help="RAC correction: merged fp16 operand from quads_rac_select_merged, or the exact "
                          "extended-K contraction (QUADS_RAC_FORM_EXACT)")
@@ -91,6 +104,18 @@ def _weights_nvfp4(Q, w_dev, n_seg):
     return q.codes.reshape(E, N, K // 2), q.scales.reshape(E, N, K // 16), q.gscale
 
 
+def _act_bytes(rows, K, kpad, merged):
+    """Algorithmic bytes of the bandwidth-bound activation stages on a bf16
+    [rows, K] activation: quantize with scores reads x (2 B) and writes codes
+    (0.5 B) and block scales (1/16 B) per element, plus the K fp32 scores;
+    RAC re-reads x, codes and scales and writes the residual NVFP4 tensor
+    (0.5625 B per selected element) and, in the merged form, the fp16
+    corrected activation (2 B per element)."""
+    q = rows * K * 2.5625 + 4.0 * K
+    rac = rows * K * 2.5625 + 4.0 * K + rows * kpad * 0.5625 + (rows * K * 2.0 if merged else 0.0)
+    return q, rac
+
+
 def setup_expert_gemm(Q, S, k):
     import torch
     wl = S.expert_gemm()
@@ -107,19 +132,22 @@ def setup_expert_gemm(Q, S, k):
     gc = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M,
                     x=q, res=res if nsel else None, sel_idx=sel, x_merged=scall.merged if merged else None,
                     rac_form=Q.RAC_FORM_MERGED if merged else Q.RAC_FORM_EXACT)
-    # MFMA work the RAC GEMM executes: one contraction over K on the merged
-    # operand, K + nsel with the extended contraction.
-    flops = 2.0 * M * N * (K + (0 if merged else nsel))
+    # Algorithmic work of the RAC GEMM: the extended contraction, 2*M*N*(K +
+    # nsel).  MFMA work it executes: one contraction over K on the merged
+    # operand (the correction is summed into it), K + nsel otherwise.
+    flops_alg = 2.0 * M * N * (K + nsel)
+    flops_exec = 2.0 * M * N * (K + (0 if merged else nsel))
     stages = [("quantize_scores", qc), ("rac_select_residual", scall), ("gemm_prepare", gc.prepare),
               ("gemm", gc.run)]
     qp = Q.QuantizeCall(x, want_scores=False)
     qpl, _ = qp()
     gp = Q.GemmCall(w_codes=wc, w_scales=wsc, w_gscale=wg, N=N, K=K, expert_offsets=offs, num_rows=M, x=qpl)
     plain = [("quantize", qp), ("gemm_prepare", gp.prepare), ("gemm", gp.run)]
+    qb, rb = _act_bytes(M, K, res.cols, merged)
     cfg = {"workload": "expert_gemm", "tokens": M, "K": K, "N": N, "k_percent": k, "nsel": nsel,
            "x": "bf16 N(0,1), 1% outlier channels x30", "w": "bf16 N(0,0.02) -> NVFP4 (offline)",
-           "rac_gemm": ("merged fp16 operand from quads_rac_select_merged (flops 2*M*N*K)" if merged else
-                        "extended K (flops 2*M*N*(K+nsel))")}
+           "rac_gemm": ("merged fp16 operand from quads_rac_select_merged (executes 2*M*N*K)" if merged else
+                        "extended K (executes 2*M*N*(K+nsel))")}
 
     def cpu_baseline():
         """The oracle's quantize + RAC + fp64 GEMM over all M tokens (the same
@@ -140,9 +168,67 @@ def setup_expert_gemm(Q, S, k):
     kern = ("k_gemm_dma<2, 0, false, true> (merged RAC operand x NVFP4 weights, 128x128 DMA-staged tiles)"
             if merged else "k_gemm_dma<2, 0, true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)")
     summary = (f"k_gemm_merged_expert_gemm_k{k}_traffic.txt" if merged else f"k_gemm_dma_expert_gemm_k{k}_traffic.txt")
-    return dict(stages=stages, plain=plain, tokens=M, flops=flops, dominant="gemm", dominant_flops=flops,
-                dominant_kernel=kern, config=cfg, cpu_baseline=cpu_baseline,
-                traffic_summary=os.path.join(ROOT, "profiles", summary))
+    return dict(stages=stages, plain=plain, tokens=M, flops=flops_alg, dominant="gemm", bound="mfma",
+                dominant_work=flops_alg, dominant_exec=flops_exec, dominant_kernel=kern, config=cfg,
+                cpu_baseline=cpu_baseline, traffic_summary=os.path.join(ROOT, "profiles", summary),
+                stage_bytes={"quantize_scores": qb, "rac_select_residual": rb},
+                plain_stage_bytes={"quantize": M * K * 2.5625})
+
+
+def cpu_baseline_moe(wl, k, every):
+    """The oracle on a bounded sample of one MoE layer step: routing, and
+    quantize + scores + mask + residual of the whole X (one mask per batch),
+    timed in full; gate_up (fp64 GEMM with the RAC correction), SwiGLU
+    rounded to bf16, quantize + RAC of those rows of h and the down GEMM,
+    timed for every `every`-th expert and scaled to all routed rows by row
+    count (the combine is not included).  Weights of the sampled experts are
+    quantized beforehand, as on the GPU.  Returns (tokens/s, seconds, sample)."""
+    from oracle import quads_oracle as O
+    T, H = wl.x.f32.shape
+    E = wl.logits.shape[1]
+    I = wl.w_down.f32.shape[2]
+    sample = list(range(0, E, every))
+    wgu = {e: O.quantize_weights(wl.w_gate_up.f32[e:e + 1], 2)[3][0] for e in sample}
+    wdn = {e: O.quantize_weights(wl.w_down.f32[e:e + 1], 1)[3][0] for e in sample}
+    t0 = time.perf_counter()
+    ids, wts, offs, rt, inv = O.route(wl.logits, wl.top)
+    t_route = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    x = wl.x.f32
+    q = O.quantize_nvfp4(x)
+    sel, nsel = O.rac_select(O.rac_scores(x, q), k)
+    r = O.rac_quantize_residual(x, q, sel, nsel)
+    xe = O.dequant_exact(q.codes, q.scales, q.g)
+    re = O.dequant_exact(r.codes, r.scales, r.g) if nsel else None
+    t_x = time.perf_counter() - t0
+    # the sampled experts are cycled until CPU_BASELINE_MIN_S of row work
+    # has been timed (at least one pass)
+    rows_done, passes, t0 = 0, 0, time.perf_counter()
+    for e in sample * 1000:
+        if e == sample[0] and rows_done and time.perf_counter() - t0 >= CPU_BASELINE_MIN_S:
+            break
+        passes += e == sample[0]
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        rows = rt[a:b]
+        y = O.gemm_ref(xe[rows], wgu[e], None if re is None else re[rows], sel if nsel else None)
+        h = O.swiglu(y[:, :I], y[:, I:])
+        hb = O.f32_from_bf16_bits(O.bf16_bits_from_f32(h.astype(np.float32)))
+        hq = O.quantize_nvfp4(hb)
+        hsel, hn = O.rac_select(O.rac_scores(hb, hq), k)
+        hr = O.rac_quantize_residual(hb, hq, hsel, hn)
+        O.gemm_ref(O.dequant_exact(hq.codes, hq.scales, hq.g), wdn[e],
+                   O.dequant_exact(hr.codes, hr.scales, hr.g) if hn else None, hsel if hn else None)
+        rows_done += b - a
+    t_rows = time.perf_counter() - t0
+    R = T * wl.top
+    est = t_route + t_x + t_rows * R / max(rows_done, 1)
+    return T / est, t_route + t_x + t_rows, (
+        f"routing and quantize + RAC of X ({T}x{H}) in full ({t_route + t_x:.1f} s); gate_up + SwiGLU + "
+        f"quantize/RAC of h + down for experts {sample[0]}, {sample[0] + every}, ... ({len(sample)} of {E}, "
+        f"{passes} passes, {rows_done} routed rows of the layer's {R}, {t_rows:.1f} s) scaled by rows to the "
+        f"full layer ({est:.1f} s estimated); combine not included")
 
 
 def setup_moe(Q, S, k, decode):
@@ -179,12 +265,12 @@ def setup_moe(Q, S, k, decode):
     stages = [("route", rc), ("quantize_x", qx), ("rac_x", sx), ("gate_up_prepare", g1.prepare),
               ("gate_up", g1.run), ("quantize_h", qh), ("rac_h", sh), ("down_prepare", g2.prepare),
               ("down", g2.run), ("combine", cc)]
-    # MFMA work the RAC GEMMs execute: both shapes add the correction to the
-    # activation operand (one contraction over K), unless --rac-form exact
-    # forces the extended contraction (K + nsel).
-    merged = mr
-    f1 = 2.0 * R * N2 * (H + (0 if merged else nsel_x))
-    f2 = 2.0 * R * H * (I + (0 if merged else nsel_h))
+    # Algorithmic GEMM work: the extended contraction (K + nsel).  Executed
+    # MFMA work: one contraction over K on the merged operand, unless
+    # --rac-form exact forces the extended contraction.
+    f1 = 2.0 * R * N2 * (H + nsel_x)
+    f2 = 2.0 * R * H * (I + nsel_h)
+    f1x = 2.0 * R * N2 * (H + (0 if mr else nsel_x))
     # plain W4A4 layer
     qxp = Q.QuantizeCall(x)
     qp, _ = qxp()
@@ -200,16 +286,56 @@ def setup_moe(Q, S, k, decode):
     cnt = np.diff(offs.cpu().numpy())
     cfg = {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "top": wl.top, "intermediate": I,
            "k_percent": k, "nsel_x": nsel_x, "nsel_h": nsel_h,
-           "rac_gemm": "merged fp16 operand (flops 2*R*N*K)" if merged else "extended K (flops 2*R*N*(K+nsel))",
+           "rac_gemm": "merged fp16 operand (executes 2*R*N*K)" if mr else "extended K (executes 2*R*N*(K+nsel))",
            "rows_per_expert": {"min": int(cnt.min()), "max": int(cnt.max()), "mean": float(cnt.mean())}}
-    wdec = {"gate_up": E * N2 * H * 0.5625, "down": E * H * I * 0.5625}
+    wbytes = {"gate_up": E * N2 * H * 0.5625, "down": E * H * I * 0.5625}
+    qxb, rxb = _act_bytes(T, H, res.cols, mr)
+    qhb, rhb = _act_bytes(R, I, hres.cols, mr)
+    sb = {"quantize_x": qxb, "rac_x": rxb, "quantize_h": qhb, "rac_h": rhb}
+    if decode:
+        # HBM-bound: the gate_up launch streams every expert's NVFP4 weights
+        # once, reads its routed rows of the fp16 activation operand and
+        # writes h (bf16).
+        gu_bytes = wbytes["gate_up"] + R * H * (2.0 if mr else 0.5625) + R * I * 2.0
+        dom = dict(bound="hbm", dominant_work=gu_bytes, dominant_exec=gu_bytes,
+                   dominant_kernel="k_gemm_small<1, true> (gate_up, SwiGLU, merged RAC operand, few rows per expert)",
+                   layer_floor_bytes=wbytes["gate_up"] + wbytes["down"])
+    else:
+        dom = dict(bound="mfma", dominant_work=f1, dominant_exec=f1x,
+                   dominant_kernel=("k_gemm<Cfg<256, 256, 2, 4, 1>, 2, 1, false> (gate_up, SwiGLU, merged RAC operand)"
+                                    if mr else "k_gemm<Cfg<256, 256, 2, 4, 1>, 0, 1, true> (gate_up, SwiGLU, extended K)"))
+    return dict(stages=stages, plain=plain, tokens=T, flops=f1 + f2, dominant="gate_up", config=cfg,
+                cpu_baseline=lambda: cpu_baseline_moe(wl, k, 8 if decode else 16), weight_bytes=wbytes,
+                stage_bytes=sb, plain_stage_bytes={"quantize_x": T * H * 2.5625, "quantize_h": R * I * 2.5625},
+                **dom)
 
-    return dict(stages=stages, plain=plain, tokens=T, flops=f1 + f2, dominant="gate_up", dominant_flops=f1,
-                dominant_kernel=("k_gemm_small<1, true> (gate_up, SwiGLU, merged RAC operand, few rows per expert)"
-                                 if decode else
-                                 ("k_gemm<Cfg<256, 256, 2, 4, 1>, 2, 1, false> (gate_up, SwiGLU, merged RAC operand)"
-                                  if merged else "k_gemm<Cfg<256, 256, 2, 4, 1>, 0, 1, true> (gate_up, SwiGLU, extended K)")),
-                config=cfg, cpu_baseline=None, weight_bytes=wdec)
+
+def setup_qdq_layer(Q, S):
+    """One trainer layer's weight QDQ (128 experts x gate, up and down bf16
+    masters of 2048 x 1024, 1.61 GB in and out): the bandwidth-bound step of
+    the trainer-side W4A16 QAT forward."""
+    E, H, I = 128, 2048, 1024
+    gu_m, dn_m = S.trainer_layer_weights_device(5, 0, E, H, I)
+    q1, q2 = Q.QdqCall(gu_m), Q.QdqCall(dn_m)
+    elems = gu_m.numel() + dn_m.numel()
+
+    def cpu_baseline():
+        from oracle import quads_oracle as O
+        mats = [gu_m[i].float().cpu().numpy() for i in (0, 1, 2, 3)] + [dn_m[i].float().cpu().numpy() for i in (0, 1)]
+        n, reps, t0 = 0, 0, time.perf_counter()
+        while True:
+            for m in mats:
+                O.weight_qdq(m)
+                n += m.size
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= CPU_BASELINE_MIN_S / 2:
+                break
+        return n * 4.0 / secs / 1e9, secs, (f"oracle weight QDQ of 4 gate/up and 2 down master matrices of layer 0 "
+                                            f"x {reps} repetitions, as GB/s of bf16 in + out")
+
+    return dict(stages=[("qdq_gate_up", q1), ("qdq_down", q2)], bytes=4.0 * elems, elems=elems,
+                cpu_baseline=cpu_baseline, keep=(gu_m, dn_m))
 
 
 def setup_trainer(Q, S, layers):
@@ -245,7 +371,8 @@ def setup_trainer(Q, S, layers):
            "layers": layers, "master_weights_bytes": 2 * layers * (masters[0][0].numel() + masters[0][1].numel()),
            "note": "QDQ of every layer's masters + bf16 grouped forward; same synthetic input for every layer"}
     return dict(stages=stages, plain=None, tokens=T, flops=flops_layer * layers, dominant=None,
-                dominant_stage_for_roofline="L0.gate_up", dominant_flops=2.0 * R * (2 * I) * H,
+                dominant_stage_for_roofline="L0.gate_up", bound="mfma", dominant_work=2.0 * R * (2 * I) * H,
+                dominant_exec=2.0 * R * (2 * I) * H,
                 dominant_kernel="k_gemm<bf16 operands, SWIGLU> (gate_up)", config=cfg, cpu_baseline=None,
                 qdq_bytes_layer=qdq_bytes_layer, layer0_stages=[st for st in stages if st[0].startswith(("route", "L0."))])
 
@@ -297,7 +424,7 @@ def setup_trainer_bwd(Q, S):
                                                "in float64), scaled to the full step by flops")
 
     return dict(stages=stages, plain=None, tokens=T, flops=flops, dominant="gate_up.wgrad",
-                dominant_flops=2.0 * R * (2 * I) * H,
+                bound="mfma", dominant_work=2.0 * R * (2 * I) * H, dominant_exec=2.0 * R * (2 * I) * H,
                 dominant_kernel="gate_up dW: k_pad_map + 2 gather-transposes + k_wgrad (bf16 MFMA, FP32 dW)",
                 config=cfg, cpu_baseline=cpu_baseline,
                 cpu_cores_note="float64 products on the BLAS threads; the weight QDQ single-threaded NumPy")
@@ -436,6 +563,113 @@ def blas_threads():
         return 1
 
 
+def cold_stage_times(stages, names, reps=10):
+    """Device time of one call of each named stage with the Infinity Cache
+    flushed first: a 1 GiB buffer is overwritten, then HIP events on the
+    stream the call uses bracket that one call (the events include the
+    launch gap of about 1-2 us).  Returns {name: mean ms}."""
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    fns = dict(stages)
+    out = {}
+    for name in names:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            flush.zero_()
+            a.record()
+            fns[name]()
+            b.record()
+        torch.cuda.synchronize()
+        out[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del flush
+    return out
+
+
+def _bw(stage_bytes, warm, cold):
+    """{stage: {bytes, GB/s warm and cold, fraction of HBM peak (cold)}}."""
+    out = {}
+    for name, nb in stage_bytes.items():
+        gw = nb / (warm[name] * 1e-3) / 1e9
+        gc = nb / (cold[name] * 1e-3) / 1e9
+        out[name] = {"algorithmic_bytes": nb, "ms_warm": warm[name], "ms_cold": cold[name], "GBps_warm": gw,
+                     "GBps_cold": gc, "frac_hbm_cold": gc / PEAK_HBM_GBS}
+    return out
+
+
+def _roofline(wl, dom_ms, traffic=None, tinfo=None):
+    work, ex = wl["dominant_work"], wl["dominant_exec"]
+    if wl["bound"] == "hbm":
+        ach = work / (dom_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "kernel": wl["dominant_kernel"], "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "bytes_per_launch": work, "avg_launch_ms": dom_ms}
+    else:
+        ach = work / (dom_ms * 1e-3) / 1e12
+        exe = ex / (dom_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "kernel": wl["dominant_kernel"], "achieved": ach, "peak": PEAK_F16_TFLOPS,
+             "unit": "TFLOP/s", "frac": ach / PEAK_F16_TFLOPS, "traffic": traffic,
+             "flops_per_launch": work, "avg_launch_ms": dom_ms,
+             "work_note": "achieved counts the algorithmic RAC GEMM work 2*rows*N*(K+nsel); executed counts the MFMA "
+                          "work the kernel issues",
+             "executed": {"flops_per_launch": ex, "achieved": exe, "frac": exe / PEAK_F16_TFLOPS}}
+    if tinfo is not None:
+        r["traffic_note"] = tinfo
+    return r
+
+
+def _cpu(wl, note_default):
+    rate, cpu_s, sample = wl["cpu_baseline"]()
+    return {"value": rate, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle", "sample": sample,
+            "seconds": cpu_s, "host_cpus": os.cpu_count(), "cores_note": wl.get("cpu_cores_note", note_default)}
+
+
+CPU_NOTE = "fp64 GEMM on the BLAS threads; quantize and RAC single-threaded NumPy"
+
+
+def measure_layer(wl, args):
+    """One MoE layer block: step time, tokens/s, plain W4A4 step and RAC
+    overhead, roofline of gate_up, per-stage times and bandwidths, oracle."""
+    import torch
+    secs, _, dom_ms = run_steps(wl["stages"], args.steps, args.warmup, wl["dominant"], args.graph)
+    ms = secs * 1e3 / args.steps
+    warm = stage_times(wl["stages"])
+    cold = cold_stage_times(wl["stages"], list(wl["stage_bytes"]))
+    blk = {"config": wl["config"], "ms_per_step": ms, "tokens_per_s": wl["tokens"] * args.steps / secs,
+           "tflops_step_algorithmic": wl["flops"] / (ms * 1e-3) / 1e12, "stages_ms": warm,
+           "stage_bandwidth": _bw(wl["stage_bytes"], warm, cold), "roofline": _roofline(wl, dom_ms)}
+    if wl.get("layer_floor_bytes"):
+        fl = wl["layer_floor_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+        blk["hbm_floor"] = {"weight_bytes": wl["layer_floor_bytes"], "floor_ms": fl, "frac_of_step": fl / ms}
+    if not args.no_plain and wl.get("plain"):
+        psecs, _, _ = run_steps(wl["plain"], args.steps, args.warmup, None, args.graph)
+        blk["plain_w4a4_ms_per_step"] = psecs * 1e3 / args.steps
+        blk["plain_stages_ms"] = stage_times(wl["plain"])
+        blk["rac_overhead_pct"] = 100.0 * (secs / psecs - 1.0)
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline and wl.get("cpu_baseline") is not None:
+        blk["cpu_baseline"] = _cpu(wl, CPU_NOTE)
+    return blk
+
+
+def measure_qdq(Q, S, args):
+    ql = setup_qdq_layer(Q, S)
+    warm = stage_times(ql["stages"])
+    cold = cold_stage_times(ql["stages"], [n for n, _ in ql["stages"]])
+    ms_w, ms_c = sum(warm.values()), sum(cold.values())
+    blk = {"config": {"workload": "trainer_qdq_layer", "matrices": "128 experts x (gate, up, down) of 2048x1024 bf16",
+                      "elements": ql["elems"]},
+           "algorithmic_bytes": ql["bytes"], "ms_warm": ms_w, "ms_cold": ms_c,
+           "roofline": {"bound": "hbm", "kernel": "k_quantize<bf16, QDQ> (quads_weight_qdq)",
+                        "achieved": ql["bytes"] / (ms_c * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": ql["bytes"] / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                        "bytes_per_launch": ql["bytes"] / 2, "avg_launch_ms": ms_c / 2},
+           "GBps_warm": ql["bytes"] / (ms_w * 1e-3) / 1e9}
+    if not args.no_cpu_baseline:
+        rate, cpu_s, sample = ql["cpu_baseline"]()
+        blk["cpu_baseline"] = {"value": rate, "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample,
+                               "seconds": cpu_s, "host_cpus": os.cpu_count()}
+    return blk
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -469,11 +703,13 @@ def main():
         dom_ms = per[wl["dominant_stage_for_roofline"]]
     ms = secs * 1e3 / args.steps
     tokens_per_s = wl["tokens"] * args.steps / secs
-    dom_tflops = wl["dominant_flops"] / (dom_ms * 1e-3) / 1e12
     from fp4_quantized_moe_amd.profiling import read_traffic
     traffic, tinfo = (None, "no traffic summary for this workload")
     if wl.get("traffic_summary"):
         traffic, tinfo = read_traffic(wl["traffic_summary"])
+        if traffic is not None:
+            tinfo = (f"HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain copy), "
+                     f"{os.path.relpath(wl['traffic_summary'], ROOT)}")
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -489,21 +725,18 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": wl["config"],
-        "tflops_step": wl["flops"] / (ms * 1e-3) / 1e12,
-        "gemm_tflops": dom_tflops,
-        "pct_mfma_peak_f16": 100.0 * dom_tflops / PEAK_F16_TFLOPS,
+        "tflops_step_algorithmic": wl["flops"] / (ms * 1e-3) / 1e12,
         "stages_ms": per,
         "timing": ("stages launched directly (host runs ahead of the device)" if not args.graph else
                    "stages before/after the dominant one replayed as HIP graphs") +
                   "; roofline.avg_launch_ms from HIP events around the dominant kernel in every timed step; "
-                  "stages_ms from graphs of 20 back-to-back calls of one stage",
-        "roofline": {"bound": "mfma", "kernel": wl["dominant_kernel"], "achieved": dom_tflops,
-                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_F16_TFLOPS,
-                     "traffic": traffic, "flops_per_launch": wl["dominant_flops"], "avg_launch_ms": dom_ms,
-                     "traffic_note": tinfo if traffic is None else
-                     f"HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain copy), "
-                     f"{os.path.relpath(wl['traffic_summary'], ROOT)}"},
+                  "stages_ms from graphs of 20 back-to-back calls of one stage; stage_bandwidth cold from one call "
+                  "after a 1 GiB write that evicts the Infinity Cache",
+        "roofline": _roofline(wl, dom_ms, traffic, tinfo),
     }
+    if wl.get("stage_bytes"):
+        cold = cold_stage_times(wl["stages"], list(wl["stage_bytes"]))
+        out["stage_bandwidth"] = _bw(wl["stage_bytes"], per, cold)
     if wl.get("qdq_bytes_layer"):
         qdq_ms = per["L0.qdq_gate_up"] + per["L0.qdq_down"]
         out["qdq"] = {"bytes_per_layer": wl["qdq_bytes_layer"], "ms_per_layer": qdq_ms,
@@ -514,12 +747,20 @@ def main():
         out["plain_stages_ms"] = stage_times(wl["plain"])
         out["rac_overhead_pct"] = 100.0 * (secs / psecs - 1.0)
     if not args.no_cpu_baseline and wl.get("cpu_baseline") is not None:
-        rate, cpu_s, sample = wl["cpu_baseline"]()
-        out["cpu_baseline"] = {"value": rate, "unit": "tokens/s", "cores": blas_threads(),
-                               "kind": "oracle", "sample": sample, "seconds": cpu_s,
-                               "host_cpus": os.cpu_count(),
-                               "cores_note": wl.get("cpu_cores_note",
-                                                    "fp64 GEMM on the BLAS threads; quantize and RAC single-threaded NumPy")}
+        out["cpu_baseline"] = _cpu(wl, CPU_NOTE)
+    if args.workload == "expert_gemm" and not args.no_moe:
+        del wl
+        torch.cuda.empty_cache()
+        out["workloads"] = {}
+        for name, decode in (("moe_prefill", False), ("moe_decode", True)):
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            lw = setup_moe(Q, S, args.k, decode)
+            torch.cuda.synchronize()
+            out["workloads"][name] = measure_layer(lw, args)
+            del lw
+            torch.cuda.empty_cache()
+        print("[bench] trainer_qdq_layer", file=sys.stderr, flush=True)
+        out["workloads"]["trainer_qdq_layer"] = measure_qdq(Q, S, args)
     print(json.dumps(out), flush=True)
 
 
