@@ -50,7 +50,7 @@ class _GemmArgs(ctypes.Structure):
 
 EXPORTS = [
     "quads_last_error", "quads_version", "quads_rac_nsel", "quads_rac_kpad",
-    "quads_quantize_workspace_bytes", "quads_quantize_nvfp4",
+    "quads_quantize_workspace_bytes", "quads_quantize_nvfp4", "quads_quantize_nvfp4_noalloc",
     "quads_rac_select_workspace_bytes", "quads_rac_select", "quads_rac_select_merged",
     "quads_moe_gemm_workspace_bytes", "quads_moe_w4a4_gemm", "quads_moe_gemm_prepare",
     "quads_weight_qdq_workspace_bytes", "quads_weight_qdq",
@@ -79,6 +79,8 @@ def load(path: str = LIB_PATH):
     L.quads_quantize_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64]
     L.quads_quantize_nvfp4.restype = ctypes.c_int
     L.quads_quantize_nvfp4.argtypes = [_vp, ctypes.c_int, _NVFP4, _c_u32, _vp, _vp, ctypes.c_size_t, _vp]
+    L.quads_quantize_nvfp4_noalloc.restype = ctypes.c_int
+    L.quads_quantize_nvfp4_noalloc.argtypes = [_vp, ctypes.c_int, _NVFP4, _c_u32, _vp, _vp]
     L.quads_rac_select_workspace_bytes.restype = ctypes.c_size_t
     L.quads_rac_select_workspace_bytes.argtypes = [_c_i64, _c_i64]
     L.quads_rac_select.restype = ctypes.c_int

@@ -69,24 +69,30 @@ size_t quads_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
   return quads::quantize_ws_bytes(batch, rows, cols);
 }
 
-quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4_t out, uint32_t flags,
-                                    float *scores, void *ws, size_t ws_bytes, void *stream) {
+// Argument checks shared by quads_quantize_nvfp4 and its no-allocation
+// variant; QUADS_OK with *done set when there is nothing to enqueue.
+static quads_status_t quantize_check(const void *x, quads_dtype_t dt, const quads_nvfp4_t &out, uint32_t flags,
+                                     float *scores, bool *done) {
+  *done = false;
   if (dt != QUADS_F32 && dt != QUADS_BF16) return fail(QUADS_ERR_ARG, "quantize: bad dtype %d", dt);
   if (flags & ~(QUADS_GSCALE_GIVEN | QUADS_WANT_SCORES)) return fail(QUADS_ERR_ARG, "quantize: unknown flags");
   if (out.batch < 1 || out.rows < 0 || out.cols <= 0) return fail(QUADS_ERR_SHAPE, "quantize: bad shape");
   if (out.cols % 16) return fail(QUADS_ERR_SHAPE, "quantize: cols (%lld) must be a multiple of 16", (long long)out.cols);
   if (!mul_ok(out.rows, out.cols, kMaxElems) || !mul_ok(out.batch, out.rows * out.cols, kMaxElems))
     return fail(QUADS_ERR_SHAPE, "quantize: size overflow");
-  const bool want_scores = (flags & QUADS_WANT_SCORES) != 0;
-  if (want_scores && (out.batch != 1 || scores == nullptr))
+  if ((flags & QUADS_WANT_SCORES) && (out.batch != 1 || scores == nullptr))
     return fail(QUADS_ERR_ARG, "quantize: QUADS_WANT_SCORES needs batch == 1 and a scores buffer");
-  if (out.rows == 0) return ok();
+  if (out.rows == 0) {
+    *done = true;
+    return ok();
+  }
   if (!x || !out.codes || !out.scales || !out.gscale) return fail(QUADS_ERR_ARG, "quantize: null pointer");
   if (misaligned({x, out.codes, out.scales})) return fail(QUADS_ERR_ARG, "quantize: arrays must be 16-byte aligned");
-  const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
-  if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(out.batch, out.rows, out.cols)))
-    return fail(QUADS_ERR_WORKSPACE, "quantize: workspace too small (need %zu)",
-                quads::quantize_ws_bytes(out.batch, out.rows, out.cols));
+  return QUADS_OK;
+}
+
+static quads::QuantizeLaunch quantize_launch(const void *x, quads_dtype_t dt, const quads_nvfp4_t &out,
+                                             uint32_t flags, float *scores, void *ws) {
   quads::QuantizeLaunch a{};
   a.x = x;
   a.x_bf16 = dt == QUADS_BF16;
@@ -96,11 +102,47 @@ quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4
   a.codes = out.codes;
   a.scales = out.scales;
   a.gscale = out.gscale;
-  a.gscale_given = given;
-  a.scores = want_scores ? scores : nullptr;
+  a.gscale_given = (flags & QUADS_GSCALE_GIVEN) != 0;
+  a.scores = (flags & QUADS_WANT_SCORES) ? scores : nullptr;
   a.qdq_out = nullptr;
   a.ws = ws;
-  return device_status(quads::launch_quantize(a, static_cast<hipStream_t>(stream)), "quantize");
+  return a;
+}
+
+quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, quads_nvfp4_t out, uint32_t flags,
+                                            float *scores, void *stream) {
+  bool done = false;
+  const quads_status_t st = quantize_check(x, dt, out, flags, scores, &done);
+  if (st != QUADS_OK || done) return st;
+  const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
+  float *ws = nullptr;
+  if (!given) {
+    const size_t need = quads::quantize_partials_bytes(out.batch, out.rows, out.cols);
+    if (need > quads::kNoAllocScratchBytes)
+      return fail(QUADS_ERR_WORKSPACE,
+                  "quantize_noalloc: %zu bytes of amax partials exceed the %zu-byte scratch (batch %lld; "
+                  "use quads_quantize_nvfp4 with a workspace)",
+                  need, quads::kNoAllocScratchBytes, (long long)out.batch);
+    const hipError_t e = quads::quantize_scratch(&ws);
+    if (e != hipSuccess) return device_status(e, "quantize_noalloc: scratch lookup");
+  }
+  return device_status(
+      quads::launch_quantize(quantize_launch(x, dt, out, flags, scores, ws), static_cast<hipStream_t>(stream)),
+      "quantize_noalloc");
+}
+
+quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4_t out, uint32_t flags,
+                                    float *scores, void *ws, size_t ws_bytes, void *stream) {
+  bool done = false;
+  const quads_status_t st = quantize_check(x, dt, out, flags, scores, &done);
+  if (st != QUADS_OK || done) return st;
+  const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
+  if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(out.batch, out.rows, out.cols)))
+    return fail(QUADS_ERR_WORKSPACE, "quantize: workspace too small (need %zu)",
+                quads::quantize_ws_bytes(out.batch, out.rows, out.cols));
+  return device_status(
+      quads::launch_quantize(quantize_launch(x, dt, out, flags, scores, ws), static_cast<hipStream_t>(stream)),
+      "quantize");
 }
 
 size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols) {

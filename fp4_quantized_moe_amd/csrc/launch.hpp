@@ -27,6 +27,13 @@ struct QuantizeLaunch {
 int amax_partials_per_tensor(int64_t n_elem);
 size_t quantize_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
 hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream);
+// quads_quantize_nvfp4_noalloc: the amax partials (batch * P floats) in the
+// library's per-device scratch array of kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+size_t quantize_partials_bytes(int64_t batch, int64_t rows, int64_t cols);
+// Device address of the current device's scratch array (looked up once per
+// device; no allocation).
+hipError_t quantize_scratch(float **out);
 
 // ---- rac.hip ---------------------------------------------------------------
 struct RacLaunch {

@@ -16,6 +16,8 @@
 //                   loads, 8-byte code stores, optional bf16 QDQ stores, and a
 //                   per-workgroup column max of |x - dq| merged with one u32
 //                   atomicMax per column (order-independent, so deterministic).
+#include <mutex>
+
 #include "launch.hpp"
 #include "quads_device.hpp"
 
@@ -258,6 +260,40 @@ int amax_partials_per_tensor(int64_t n_elem) {
 size_t quantize_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
   const int P = amax_partials_per_tensor(rows * cols);
   return static_cast<size_t>(batch) * P * sizeof(float) + 256;
+}
+
+size_t quantize_partials_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  return static_cast<size_t>(batch) * amax_partials_per_tensor(rows * cols) * sizeof(float);
+}
+
+// The amax partials of quads_quantize_nvfp4_noalloc live in this file-scope
+// device array instead of a caller workspace: one copy per GPU the library
+// runs on, held until the process ends, shared by every such call on that
+// GPU (each call writes every partial it reads, so nothing needs clearing).
+// Host code never uses the array's name as an address: its device address is
+// looked up once per device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t quantize_scratch(float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<float *>(g_scratch_ptr[dev]);
+  return hipSuccess;
 }
 
 hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {

@@ -110,6 +110,24 @@ quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4
                                     uint32_t flags, float *scores, void *ws, size_t ws_bytes,
                                     void *stream);
 
+/* quads_quantize_nvfp4_noalloc -- quads_quantize_nvfp4 for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): no workspace argument; the amax
+ * partials live in a fixed 1 MiB scratch array inside the library, one copy
+ * per GPU, held until the process ends.  The caller still passes x, out and
+ * scores.  The call allocates nothing and calls no allocating routine.
+ * Limit: batch * P * 4 bytes <= 1 MiB, with P = min(1024, max(1,
+ * ceil(rows * cols / 16384))) partials per matrix (e.g. up to 256 matrices
+ * of at least 16 M elements, or 2048 matrices of at most 2 M elements);
+ * larger calls return QUADS_ERR_WORKSPACE before anything is enqueued.
+ * With QUADS_GSCALE_GIVEN no scratch is used.  The scratch of the calling
+ * thread's current device is used, so `stream` must belong to that device.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from different threads) race; calls ordered
+ * on one stream do not.  Results are identical to quads_quantize_nvfp4's. */
+quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, quads_nvfp4_t out,
+                                            uint32_t flags, float *scores, void *stream);
+
 /* ---------------------------------------------------------------------------
  * quads_rac_select -- RAC channel mask and second-pass residual quantization
  * [Gist 2.2-B].

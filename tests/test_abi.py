@@ -85,6 +85,21 @@ def test_rac_select_validation(L):
                                      None, 0, None) == -2
 
 
+def test_quantize_noalloc_validation(L):
+    """The no-allocation quantizer checks its arguments like the workspace
+    form and rejects calls whose amax partials exceed its fixed 1 MiB scratch
+    before enqueueing anything."""
+    dummy = ctypes.c_void_p(16)
+    assert L.quads_quantize_nvfp4_noalloc(dummy, 0, _nv(4, 10), 0, None, None) == -2
+    assert L.quads_quantize_nvfp4_noalloc(dummy, 7, _nv(4, 16), 0, None, None) == -1
+    assert L.quads_quantize_nvfp4_noalloc(None, 0, _nv(4, 16), 0, None, None) == -1
+    assert L.quads_quantize_nvfp4_noalloc(dummy, 0, _nv(4, 16, batch=2), 2, dummy, None) == -1
+    # 300 matrices of 4096 x 4096: 1024 partials each, 1.2 MB > 1 MiB
+    assert L.quads_quantize_nvfp4_noalloc(dummy, 1, _nv(4096, 4096, batch=300), 0, None, None) == -3
+    assert b"scratch" in L.quads_last_error()
+    assert L.quads_quantize_nvfp4_noalloc(dummy, 1, _nv(0, 4096), 0, None, None) == 0  # nothing to do
+
+
 def _gemm_args(**kw):
     a = _lib._GemmArgs()
     a.struct_size = ctypes.sizeof(_lib._GemmArgs)
