@@ -76,6 +76,9 @@ def parse():
                     choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq", "trainer_bwd", "ablation"])
     ap.add_argument("--k", type=int, default=50, help="RAC k percent")
     ap.add_argument("--layers", type=int, default=48, help="trainer_qdq: layers per step")
+    ap.add_argument("--qdq", choices=["separate", "in_gemm", "codes"], default="separate",
+                    help="trainer_qdq: weight QDQ as a separate pass, inside the GEMMs (QUADS_OPERANDS_BF16_QDQ), "
+                         "or as an NVFP4 encoding the GEMMs decode (QUADS_OPERANDS_BF16_W4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true", help="skip the plain W4A4 comparison run")
     ap.add_argument("--graph", action="store_true", help="replay the non-dominant stages as HIP graphs")
@@ -338,43 +341,86 @@ def setup_qdq_layer(Q, S):
                 cpu_baseline=cpu_baseline, keep=(gu_m, dn_m))
 
 
-def setup_trainer(Q, S, layers):
+def setup_trainer(Q, S, layers, qdq="separate"):
     """Trainer-side W4A16 QAT forward: per layer, NVFP4 QDQ of the bf16 master
     weights of 128 experts x (gate, up, down) into one reused bf16 buffer,
     then the bf16 grouped forward of 8192 tokens (top-8 routing computed once
     per step; every layer sees the same synthetic input, so no cast kernel
-    sits between layers)."""
+    sits between layers).  qdq="in_gemm": the QDQ happens inside the GEMMs
+    (QUADS_OPERANDS_BF16_QDQ), per layer only the masters' tensor scales are
+    computed first (QUADS_SCALES_ONLY); qdq="codes": per layer the masters
+    are quantized to NVFP4 and the GEMMs decode the codes to their QDQ values
+    (QUADS_OPERANDS_BF16_W4).  Either way W_qdq is never written."""
     import torch
     T, H, E, I, top = 8192, 2048, 128, 1024, 8
     rng = np.random.default_rng(5)
     x = _dev(S.activation(rng, T, H, 0, 1.0, bf16=True))
     logits = torch.from_numpy(S.gaussian_logits(rng, T, E)).cuda()
     masters = [S.trainer_layer_weights_device(5, l, E, H, I) for l in range(layers)]
-    wq_gu = torch.empty_like(masters[0][0])  # [2E, I, H]: matrix 2e = gate of expert e, 2e+1 = up
-    wq_dn = torch.empty_like(masters[0][1])  # [E, H, I]
     rc = Q.RouteCall(logits, top)
     ids, w, offs, rt, inv = rc()
     R = T * top
-    gu = Q.GemmCall(N=2 * I, K=H, expert_offsets=offs, num_rows=R, row_token=rt, x_bf16=x,
-                    w_bf16=wq_gu.view(E, 2 * I, H), epilogue=Q.EPI_SWIGLU)
-    dn = Q.GemmCall(N=H, K=I, expert_offsets=offs, num_rows=R, x_bf16=gu.y, w_bf16=wq_dn)
-    cc = Q.CombineCall(dn.y, inv, w)
     stages = [("route", rc)]
-    for l in range(layers):
-        stages += [(f"L{l}.qdq_gate_up", Q.QdqCall(masters[l][0], out=wq_gu)),
-                   (f"L{l}.qdq_down", Q.QdqCall(masters[l][1], out=wq_dn)),
-                   (f"L{l}.gate_up_prepare", gu.prepare), (f"L{l}.gate_up", gu.run),
-                   (f"L{l}.down_prepare", dn.prepare), (f"L{l}.down", dn.run), (f"L{l}.combine", cc)]
+    if qdq == "codes":
+        qgu = Q.empty_nvfp4(2 * E, I, H, "cuda")
+        qdn = Q.empty_nvfp4(E, H, I, "cuda")
+        h = torch.empty(R, I, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty(R, H, dtype=torch.float32, device="cuda")
+        gu = Q.GemmCall(N=2 * I, K=H, expert_offsets=offs, num_rows=R, row_token=rt, x_bf16=x,
+                        w_codes=qgu.codes.view(E, 2 * I, H // 2), w_scales=qgu.scales.view(E, 2 * I, H // 16),
+                        w_gscale=qgu.gscale, n_seg=2, epilogue=Q.EPI_SWIGLU, y=h)
+        dn = Q.GemmCall(N=H, K=I, expert_offsets=offs, num_rows=R, x_bf16=h, w_codes=qdn.codes,
+                        w_scales=qdn.scales, w_gscale=qdn.gscale, y=y)
+        cc = Q.CombineCall(y, inv, w)
+        for l in range(layers):
+            stages += [(f"L{l}.quantize_gate_up", Q.QuantizeCall(masters[l][0], out=qgu)),
+                       (f"L{l}.quantize_down", Q.QuantizeCall(masters[l][1], out=qdn)),
+                       (f"L{l}.gate_up_prepare", gu.prepare), (f"L{l}.gate_up", gu.run),
+                       (f"L{l}.down_prepare", dn.prepare), (f"L{l}.down", dn.run), (f"L{l}.combine", cc)]
+        kern = "k_gemm_pp<bf16 x NVFP4 weights decoded to QDQ values, SWIGLU> (gate_up)"
+    elif qdq == "in_gemm":
+        g_gu = torch.empty(2 * E, dtype=torch.float32, device="cuda")
+        g_dn = torch.empty(E, dtype=torch.float32, device="cuda")
+        h = torch.empty(R, I, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty(R, H, dtype=torch.float32, device="cuda")
+        for l in range(layers):
+            gu = Q.GemmCall(N=2 * I, K=H, expert_offsets=offs, num_rows=R, row_token=rt, x_bf16=x,
+                            w_bf16=masters[l][0].view(E, 2 * I, H), w_gscale=g_gu, n_seg=2, qdq=True,
+                            epilogue=Q.EPI_SWIGLU, y=h)
+            dn = Q.GemmCall(N=H, K=I, expert_offsets=offs, num_rows=R, x_bf16=h, w_bf16=masters[l][1],
+                            w_gscale=g_dn, qdq=True, y=y)
+            cc = Q.CombineCall(y, inv, w)
+            stages += [(f"L{l}.scales_gate_up", Q.ScalesCall(masters[l][0], g_gu)),
+                       (f"L{l}.scales_down", Q.ScalesCall(masters[l][1], g_dn)),
+                       (f"L{l}.gate_up_prepare", gu.prepare), (f"L{l}.gate_up", gu.run),
+                       (f"L{l}.down_prepare", dn.prepare), (f"L{l}.down", dn.run), (f"L{l}.combine", cc)]
+        kern = "k_gemm_pp<QDQ-fused bf16 masters, SWIGLU> (gate_up)"
+    else:
+        wq_gu = torch.empty_like(masters[0][0])  # [2E, I, H]: matrix 2e = gate of expert e, 2e+1 = up
+        wq_dn = torch.empty_like(masters[0][1])  # [E, H, I]
+        gu = Q.GemmCall(N=2 * I, K=H, expert_offsets=offs, num_rows=R, row_token=rt, x_bf16=x,
+                        w_bf16=wq_gu.view(E, 2 * I, H), epilogue=Q.EPI_SWIGLU)
+        dn = Q.GemmCall(N=H, K=I, expert_offsets=offs, num_rows=R, x_bf16=gu.y, w_bf16=wq_dn)
+        cc = Q.CombineCall(dn.y, inv, w)
+        for l in range(layers):
+            stages += [(f"L{l}.qdq_gate_up", Q.QdqCall(masters[l][0], out=wq_gu)),
+                       (f"L{l}.qdq_down", Q.QdqCall(masters[l][1], out=wq_dn)),
+                       (f"L{l}.gate_up_prepare", gu.prepare), (f"L{l}.gate_up", gu.run),
+                       (f"L{l}.down_prepare", dn.prepare), (f"L{l}.down", dn.run), (f"L{l}.combine", cc)]
+        kern = "k_gemm_pp<bf16 operands, SWIGLU> (gate_up)"
     flops_layer = 2.0 * R * (2 * I) * H + 2.0 * R * H * I
     qdq_bytes_layer = 4.0 * (masters[0][0].numel() + masters[0][1].numel())  # bf16 in + bf16 out
     cfg = {"workload": "trainer_qdq", "tokens": T, "hidden": H, "experts": E, "top": top, "intermediate": I,
            "layers": layers, "master_weights_bytes": 2 * layers * (masters[0][0].numel() + masters[0][1].numel()),
+           "qdq": {"in_gemm": "fused into the GEMMs (scales-only pass + QUADS_OPERANDS_BF16_QDQ)",
+                   "codes": "masters quantized to NVFP4, decoded to QDQ values in the GEMMs (QUADS_OPERANDS_BF16_W4)",
+                   "separate": "separate quads_weight_qdq into a bf16 buffer"}[qdq],
            "note": "QDQ of every layer's masters + bf16 grouped forward; same synthetic input for every layer"}
     return dict(stages=stages, plain=None, tokens=T, flops=flops_layer * layers, dominant=None,
                 dominant_stage_for_roofline="L0.gate_up", bound="mfma", dominant_work=2.0 * R * (2 * I) * H,
-                dominant_exec=2.0 * R * (2 * I) * H,
-                dominant_kernel="k_gemm<bf16 operands, SWIGLU> (gate_up)", config=cfg, cpu_baseline=None,
-                qdq_bytes_layer=qdq_bytes_layer, layer0_stages=[st for st in stages if st[0].startswith(("route", "L0."))])
+                dominant_exec=2.0 * R * (2 * I) * H, dominant_kernel=kern, config=cfg, cpu_baseline=None,
+                qdq_bytes_layer=qdq_bytes_layer if qdq == "separate" else None,
+                layer0_stages=[st for st in stages if st[0].startswith(("route", "L0."))])
 
 
 def setup_trainer_bwd(Q, S):
@@ -650,6 +696,22 @@ def measure_layer(wl, args):
     return blk
 
 
+def measure_trainer_layer(Q, S, args):
+    """One trainer layer's W4A16 forward (8192 tokens, 128 experts, top-8),
+    with the weight QDQ as a separate pass and in both fused forms."""
+    out = {}
+    for name, mode in (("separate_qdq", "separate"), ("qdq_in_gemm", "in_gemm"), ("nvfp4_decode_in_gemm", "codes")):
+        wl = setup_trainer(Q, S, 1, mode)
+        secs, _, _ = run_steps(wl["stages"], args.steps, args.warmup)
+        per = stage_times(wl["stages"])
+        out[name] = {"ms_per_layer": secs * 1e3 / args.steps, "stages_ms": per,
+                     "tflops_layer": wl["flops"] / (secs / args.steps) / 1e12}
+        del wl
+    for name in ("qdq_in_gemm", "nvfp4_decode_in_gemm"):
+        out[name]["speedup_vs_separate"] = out["separate_qdq"]["ms_per_layer"] / out[name]["ms_per_layer"]
+    return out
+
+
 def measure_qdq(Q, S, args):
     ql = setup_qdq_layer(Q, S)
     warm = stage_times(ql["stages"])
@@ -694,7 +756,7 @@ def main():
     elif args.workload in ("moe_prefill", "moe_decode"):
         wl = setup_moe(Q, S, args.k, args.workload == "moe_decode")
     else:
-        wl = setup_trainer(Q, S, args.layers)
+        wl = setup_trainer(Q, S, args.layers, args.qdq)
     torch.cuda.synchronize()
 
     secs, ev_ms, dom_ms = run_steps(wl["stages"], args.steps, args.warmup, wl["dominant"], args.graph)
@@ -761,6 +823,9 @@ def main():
             torch.cuda.empty_cache()
         print("[bench] trainer_qdq_layer", file=sys.stderr, flush=True)
         out["workloads"]["trainer_qdq_layer"] = measure_qdq(Q, S, args)
+        torch.cuda.empty_cache()
+        print("[bench] trainer_forward_layer", file=sys.stderr, flush=True)
+        out["workloads"]["trainer_forward_layer"] = measure_trainer_layer(Q, S, args)
     print(json.dumps(out), flush=True)
 
 

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libquads.so")
 
 F32, BF16 = 0, 1
 GSCALE_GIVEN, WANT_SCORES = 1, 2
-OPERANDS_W4A4, OPERANDS_BF16 = 0, 1
+OPERANDS_W4A4, OPERANDS_BF16, OPERANDS_BF16_QDQ, OPERANDS_BF16_W4 = 0, 1, 2, 3
+SCALES_ONLY = 4
 EPI_NONE, EPI_SWIGLU = 0, 1
 RAC_FORM_AUTO, RAC_FORM_EXACT, RAC_FORM_MERGED = 0, 1, 2
 
@@ -278,18 +279,24 @@ class GemmCall:
     """One grouped-GEMM call with its arguments and workspace built once.
 
     W4A4 mode when `x` is given, bf16-operand (trainer W4A16) mode when
-    `x_bf16`/`w_bf16` are given.  `rac_form` (RAC_FORM_AUTO / _EXACT /
-    _MERGED) picks the formulation of the RAC correction, see quads.h.  ``prepare()`` + ``run()`` is the split form
+    `x_bf16`/`w_bf16` are given; with `qdq=True` the bf16 weights are the
+    masters, fake-quantized inside the GEMM with their tensor scales
+    `w_gscale` (QUADS_OPERANDS_BF16_QDQ); with `x_bf16` and NVFP4 weights
+    (`w_codes`, `w_scales`, `w_gscale`) the weights are decoded to their QDQ
+    bf16 values inside the GEMM (QUADS_OPERANDS_BF16_W4).  `rac_form` (RAC_FORM_AUTO /
+    _EXACT / _MERGED) picks the formulation of the RAC correction, see
+    quads.h.  ``prepare()`` + ``run()`` is the split form
     (tile list and residual weight-column gather, then the GEMM kernel);
     calling the object does both."""
 
     def __init__(self, *, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
                  expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
                  sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
-                 x_bf16=None, w_bf16=None, y=None, x_merged=None, rac_form=RAC_FORM_AUTO):
+                 x_bf16=None, w_bf16=None, y=None, x_merged=None, rac_form=RAC_FORM_AUTO, qdq=False):
         L = load()
         E = int(expert_offsets.numel()) - 1
-        bf16_mode = x_bf16 is not None
+        bf16_mode = x_bf16 is not None and w_bf16 is not None
+        w4_mode = x_bf16 is not None and w_bf16 is None
         dev = expert_offsets.device
         if y is None:
             if epilogue == EPI_SWIGLU:
@@ -300,7 +307,8 @@ class GemmCall:
         self._keep = [w_codes, w_scales, w_gscale, expert_offsets, x, res, sel_idx, row_token, x_bf16, w_bf16, x_merged]
         a = _GemmArgs()
         a.struct_size = ctypes.sizeof(_GemmArgs)
-        a.operand_mode = OPERANDS_BF16 if bf16_mode else OPERANDS_W4A4
+        a.operand_mode = ((OPERANDS_BF16_QDQ if qdq else OPERANDS_BF16) if bf16_mode else
+                          OPERANDS_BF16_W4 if w4_mode else OPERANDS_W4A4)
         a.epilogue = epilogue
         a.y_dtype = BF16 if y.dtype == torch.bfloat16 else F32
         a.num_experts = E
@@ -310,8 +318,22 @@ class GemmCall:
         a.rac_form = rac_form
         if bf16_mode:
             _require_cuda(x_bf16, w_bf16)
+            if x_bf16.dtype != torch.bfloat16 or w_bf16.dtype != torch.bfloat16:
+                raise QuadsError("bf16-operand GEMM expects bf16 x_bf16 and w_bf16")
             a.act_rows = x_bf16.shape[0]
             a.x_bf16, a.w_bf16 = x_bf16.data_ptr(), w_bf16.data_ptr()
+            if qdq:
+                _require_cuda(w_gscale)
+                if w_gscale.dtype != torch.float32 or w_gscale.numel() != E * n_seg:
+                    raise QuadsError("qdq=True needs float32 w_gscale with one scale per (expert, segment)")
+                a.w_gscale = w_gscale.data_ptr()
+        elif w4_mode:
+            _require_cuda(x_bf16, w_codes, w_scales, w_gscale)
+            if x_bf16.dtype != torch.bfloat16 or w_gscale.dtype != torch.float32 or w_gscale.numel() != E * n_seg:
+                raise QuadsError("BF16_W4 GEMM expects bf16 x_bf16 and float32 w_gscale [E * n_seg]")
+            a.act_rows = x_bf16.shape[0]
+            a.x_bf16 = x_bf16.data_ptr()
+            a.w_codes, a.w_scales, a.w_gscale = w_codes.data_ptr(), w_scales.data_ptr(), w_gscale.data_ptr()
         else:
             a.act_rows = x.rows
             a.x_codes, a.x_scales, a.x_gscale = x.codes.data_ptr(), x.scales.data_ptr(), x.gscale.data_ptr()
@@ -374,6 +396,33 @@ class QdqCall:
                                        ctypes.byref(self._qs) if self._qs is not None else None, 0, _ptr(self.ws),
                                        self.ws.numel(), _stream()), "quads_weight_qdq")
         return self.out, self.q
+
+
+class ScalesCall:
+    """quads_weight_qdq with QUADS_SCALES_ONLY: the FP32 tensor scale of each
+    of the bf16 master matrices w ([rows, cols] or [batch, rows, cols]) into
+    `self.gscale` [batch] -- the input of the fused-QDQ GEMM."""
+
+    def __init__(self, w: torch.Tensor, gscale: torch.Tensor | None = None):
+        L = load()
+        _require_cuda(w, gscale)
+        if w.dtype != torch.bfloat16:
+            raise QuadsError("weight scales expect bf16 master weights")
+        self.w = w
+        self.batch, self.rows, self.cols = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+        self.gscale = torch.empty(self.batch, dtype=torch.float32, device=w.device) if gscale is None else gscale
+        self._qs = _NVFP4(None, None, self.gscale.data_ptr(), self.batch, self.rows, self.cols)
+        self.ws = _workspace(L.quads_weight_qdq_workspace_bytes(self.batch, self.rows, self.cols), w.device)
+
+    def __call__(self):
+        _check(load().quads_weight_qdq(_ptr(self.w), self.batch, self.rows, self.cols, None, ctypes.byref(self._qs),
+                                       SCALES_ONLY, _ptr(self.ws), self.ws.numel(), _stream()), "quads_weight_qdq")
+        return self.gscale
+
+
+def weight_scales(w: torch.Tensor):
+    """Tensor scale of each bf16 master matrix (QUADS_SCALES_ONLY)."""
+    return ScalesCall(w)()
 
 
 def weight_qdq(w: torch.Tensor, export: bool = False):

@@ -212,7 +212,8 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
   if (a->struct_size != sizeof(quads_moe_gemm_args))
     return fail(QUADS_ERR_ARG, "gemm: struct_size %u != %zu", a->struct_size, sizeof(quads_moe_gemm_args));
   if (a->flags & ~QUADS_GEMM_PREPARED) return fail(QUADS_ERR_ARG, "gemm: unknown flags");
-  if (a->operand_mode != QUADS_OPERANDS_W4A4 && a->operand_mode != QUADS_OPERANDS_BF16)
+  if (a->operand_mode != QUADS_OPERANDS_W4A4 && a->operand_mode != QUADS_OPERANDS_BF16 &&
+      a->operand_mode != QUADS_OPERANDS_BF16_QDQ && a->operand_mode != QUADS_OPERANDS_BF16_W4)
     return fail(QUADS_ERR_ARG, "gemm: bad operand_mode");
   if (a->epilogue != QUADS_EPI_NONE && a->epilogue != QUADS_EPI_SWIGLU) return fail(QUADS_ERR_ARG, "gemm: bad epilogue");
   if (a->y_dtype != QUADS_F32 && a->y_dtype != QUADS_BF16) return fail(QUADS_ERR_ARG, "gemm: bad y_dtype");
@@ -220,7 +221,7 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
   if (a->n_seg < 1 || a->N <= 0 || a->N % a->n_seg) return fail(QUADS_ERR_SHAPE, "gemm: bad n_seg");
   if (a->K <= 0 || a->K % 16) return fail(QUADS_ERR_SHAPE, "gemm: K must be a positive multiple of 16");
   if (a->N % 128) return fail(QUADS_ERR_SHAPE, "gemm: N must be a multiple of 128");
-  if (a->epilogue == QUADS_EPI_SWIGLU && a->n_seg != 2 && a->operand_mode == QUADS_OPERANDS_W4A4)
+  if (a->epilogue == QUADS_EPI_SWIGLU && a->n_seg != 2 && a->operand_mode != QUADS_OPERANDS_BF16)
     return fail(QUADS_ERR_SHAPE, "gemm: SWIGLU needs n_seg == 2 (gate, up)");
   if (a->num_rows < 0 || a->act_rows < 0 || a->num_rows > (int64_t(1) << 31) - 1 || a->act_rows > (int64_t(1) << 31) - 1)
     return fail(QUADS_ERR_SHAPE, "gemm: row counts must fit int32");
@@ -238,7 +239,10 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
     return fail(QUADS_ERR_ARG, "gemm: x_merged is the merged form; rac_form EXACT needs x_merged == NULL");
   g = quads::GemmLaunch{};
   g.rac_form = a->rac_form;
-  g.mode = a->operand_mode == QUADS_OPERANDS_BF16 ? 1 : 0;
+  g.mode = a->operand_mode == QUADS_OPERANDS_BF16       ? 1
+           : a->operand_mode == QUADS_OPERANDS_BF16_QDQ ? 2
+           : a->operand_mode == QUADS_OPERANDS_BF16_W4  ? 3
+                                                        : 0;
   g.epilogue = a->epilogue;
   g.y_bf16 = a->y_dtype == QUADS_BF16;
   g.E = a->num_experts;
@@ -270,10 +274,21 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
       g.kpad = a->kpad;
       g.x_merged = static_cast<const uint16_t *>(a->x_merged);
     }
+  } else if (g.mode == 3) {
+    if (!a->x_bf16 || !a->w_codes || !a->w_scales || !a->w_gscale)
+      return fail(QUADS_ERR_ARG, "gemm: BF16_W4 needs x_bf16 and the NVFP4 weights (w_codes, w_scales, w_gscale)");
+    g.x_bf16 = static_cast<const uint16_t *>(a->x_bf16);
+    g.w_codes = a->w_codes;
+    g.w_scales = a->w_scales;
+    g.w_g = a->w_gscale;
   } else {
     if (!a->x_bf16 || !a->w_bf16) return fail(QUADS_ERR_ARG, "gemm: null bf16 operand");
     g.x_bf16 = static_cast<const uint16_t *>(a->x_bf16);
     g.w_bf16 = static_cast<const uint16_t *>(a->w_bf16);
+    if (g.mode == 2) {
+      if (!a->w_gscale) return fail(QUADS_ERR_ARG, "gemm: BF16_QDQ needs the masters' tensor scales (w_gscale)");
+      g.w_g = a->w_gscale;
+    }
   }
   return QUADS_OK;
 }
@@ -314,7 +329,25 @@ size_t quads_weight_qdq_workspace_bytes(int64_t batch, int64_t rows, int64_t col
 quads_status_t quads_weight_qdq(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols, void *w_out_bf16,
                                 const quads_nvfp4_t *q_out, uint32_t flags, void *ws, size_t ws_bytes,
                                 void *stream) {
-  if (flags & ~QUADS_GSCALE_GIVEN) return fail(QUADS_ERR_ARG, "weight_qdq: unknown flags");
+  if (flags & ~(QUADS_GSCALE_GIVEN | QUADS_SCALES_ONLY)) return fail(QUADS_ERR_ARG, "weight_qdq: unknown flags");
+  if (flags & QUADS_SCALES_ONLY) {
+    if (flags & QUADS_GSCALE_GIVEN) return fail(QUADS_ERR_ARG, "weight_qdq: QUADS_SCALES_ONLY with QUADS_GSCALE_GIVEN");
+    if (batch < 1 || rows < 0 || cols <= 0 || cols % 16)
+      return fail(QUADS_ERR_SHAPE, "weight_qdq: bad shape (cols must be a positive multiple of 16)");
+    if (!mul_ok(rows, cols, kMaxElems) || !mul_ok(batch, rows * cols, kMaxElems))
+      return fail(QUADS_ERR_SHAPE, "weight_qdq: size overflow");
+    if (!q_out || !q_out->gscale) return fail(QUADS_ERR_ARG, "weight_qdq: QUADS_SCALES_ONLY needs q_out->gscale");
+    if (q_out->batch != batch || q_out->rows != rows || q_out->cols != cols)
+      return fail(QUADS_ERR_SHAPE, "weight_qdq: q_out shape mismatch");
+    if (rows > 0 && !w_bf16) return fail(QUADS_ERR_ARG, "weight_qdq: null pointer");
+    if (misaligned({w_bf16})) return fail(QUADS_ERR_ARG, "weight_qdq: arrays must be 16-byte aligned");
+    if (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(batch, rows, cols))
+      return fail(QUADS_ERR_WORKSPACE, "weight_qdq: workspace too small (need %zu)",
+                  quads::quantize_ws_bytes(batch, rows, cols));
+    return device_status(quads::launch_tensor_scales(w_bf16, true, batch, rows, cols, q_out->gscale, ws,
+                                                     static_cast<hipStream_t>(stream)),
+                         "weight_qdq");
+  }
   if (batch < 1 || rows < 0 || cols <= 0 || cols % 16)
     return fail(QUADS_ERR_SHAPE, "weight_qdq: bad shape (cols must be a positive multiple of 16)");
   if (!mul_ok(rows, cols, kMaxElems) || !mul_ok(batch, rows * cols, kMaxElems))

@@ -95,6 +95,52 @@ struct Params {
   int y_bf16;
 };
 
+// MODE 3 weight rows: bf16 master values, fake-quantized (QDQ) to NVFP4 and
+// back to bf16 on the way into LDS, with the tensor scale of their (expert,
+// segment).  A 16-element block of a row is two 8-value chunks held by the
+// lane pair (2j, 2j+1) -- chunk c of a row is staged by the lane with
+// threadIdx & 7 == c -- so each lane takes its half's max and the pair
+// exchanges it (DPP quad permute [1,0,3,2]).  Every lane runs the exchange,
+// so no lane sits out of the DPP.
+__device__ __forceinline__ uint4 qdq_chunk(const uint4 &v, bool ok, const TensorScale &g) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false));
+  m = fmaxf(m, other);
+  const uint4 q = qdq8_bf16(x, m, g);
+  return ok ? q : make_uint4(0, 0, 0, 0);
+}
+
+// MODE 4 weight rows: NVFP4 codes and block scales decoded to their QDQ bf16
+// values bf16(fl32(level * fl32(dec(s) * g))) -- the values quads_weight_qdq
+// writes for the same codes -- as two 8-value chunks of one 16-block.  A
+// block past the end of K stores zeros.
+__device__ __forceinline__ void qdq_decode16(const uint2 &w, uint32_t s, float g, bool ok, uint4 &c0, uint4 &c1) {
+  const float d = e4m3_to_f32(s) * g;
+  float dq[8];
+  dequant8(w.x, d, dq);
+  c0 = ok ? make_uint4(pack_bf16x2(dq[0], dq[1]), pack_bf16x2(dq[2], dq[3]), pack_bf16x2(dq[4], dq[5]),
+                       pack_bf16x2(dq[6], dq[7]))
+          : make_uint4(0, 0, 0, 0);
+  dequant8(w.y, d, dq);
+  c1 = ok ? make_uint4(pack_bf16x2(dq[0], dq[1]), pack_bf16x2(dq[2], dq[3]), pack_bf16x2(dq[4], dq[5]),
+                       pack_bf16x2(dq[6], dq[7]))
+          : make_uint4(0, 0, 0, 0);
+}
+
+// Tensor scale of weight row `wrow` of expert e (segment = wrow / (N/n_seg)).
+__device__ __forceinline__ float w_scale_of(const Params &p, int e, int64_t wrow) {
+  return p.w_g[e * p.n_seg + wrow / (p.N / p.n_seg)];
+}
+
 // ---- operand stagers -------------------------------------------------------
 // NVFP4 rows: 4 blocks per row per K step; thread t stages blocks
 // (row fp4_row(t) + p*THREADS/4, block t%4).  `base[p]` is the row's first block
@@ -171,6 +217,28 @@ __device__ __forceinline__ void raw_store(const RawStage<P> &st, uint4 *tile, in
   for (int q = 0; q < P; ++q)
     if (q % 4 == part)
       tile[swz((threadIdx.x >> 3) + q * (THREADS / 8), c)] = st.ok ? st.v[q] : make_uint4(0, 0, 0, 0);
+}
+
+template <int P, int THREADS>
+__device__ __forceinline__ void fp4_qdq_store(const Fp4Stage<P> &st, uint4 *tile, int part, const float (&g)[P]) {
+  const int c = (threadIdx.x & 3) * 2;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (p % 4 != part) continue;
+    const int r = fp4_row(threadIdx.x) + p * (THREADS / 4);
+    uint4 c0, c1;
+    qdq_decode16(st.w[p], st.s[p], g[p], st.ok, c0, c1);
+    tile[swz(r, c)] = c0;
+    tile[swz(r, c + 1)] = c1;
+  }
+}
+
+template <int P, int THREADS>
+__device__ __forceinline__ void qdq_store(const RawStage<P> &st, uint4 *tile, int part, const TensorScale (&g)[P]) {
+  const int c = threadIdx.x & 7;
+#pragma unroll
+  for (int q = 0; q < P; ++q)
+    if (q % 4 == part) tile[swz((threadIdx.x >> 3) + q * (THREADS / 8), c)] = qdq_chunk(st.v[q], st.ok, g[q]);
 }
 
 // Operand fragments of one 16-wide K sub-step for this wave.
@@ -334,7 +402,7 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
     for (int ni = 0; ni < C::NI; ++ni) {
       const int64_t col = static_cast<int64_t>(nt) * C::BN + wn * C::TN + ni * 32 + (lane & 31);
       float sc = ascale;
-      if constexpr (MODE != 1) sc = p.w_g[e * p.n_seg + col / seg_len] * ascale;
+      if constexpr (MODE < 3 && MODE != 1) sc = p.w_g[e * p.n_seg + col / seg_len] * ascale;
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -354,7 +422,7 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
     static_assert(EPI == 0 || C::NI % 2 == 0, "SWIGLU needs an even number of 32-column tiles per wave");
     const int64_t I = p.N / 2;
     float sg = ascale, su = ascale;
-    if constexpr (MODE != 1) {
+    if constexpr (MODE < 3 && MODE != 1) {
       sg = p.w_g[e * 2] * ascale;
       su = p.w_g[e * 2 + 1] * ascale;
     }
@@ -380,7 +448,12 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
 // MODE 0: NVFP4 operands (+ residual segment if HAS_RES), fp16 MFMA;
 // MODE 1: bf16 operands, bf16 MFMA;
 // MODE 2: the RAC-merged fp16 activation (X' + (gr/gx) R', built by the GEMM
-// prepare step) times NVFP4 weights, fp16 MFMA over K alone.
+// prepare step) times NVFP4 weights, fp16 MFMA over K alone;
+// MODE 3: bf16 activations times bf16 master weights fake-quantized in
+// registers (the trainer's W4A16 forward with the QDQ fused), bf16 MFMA;
+// MODE 4: bf16 activations times NVFP4 weights decoded to their QDQ bf16
+// values on the way into LDS (the same forward, W_qdq never written), bf16
+// MFMA.
 template <class C, int MODE, int EPI, bool HAS_RES>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
   __shared__ uint4 As[2][C::BM * 8];
@@ -462,6 +535,41 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
         [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
         [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
         [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+  } else if constexpr (MODE == 4) {
+    const int nblk = static_cast<int>(p.K / 16);
+    int64_t abase[C::HA], bbase[C::FB];
+    float gq[C::FB];
+#pragma unroll
+    for (int q = 0; q < C::HA; ++q) abase[q] = act_row((threadIdx.x >> 3) + q * (T / 8)) * p.K;
+#pragma unroll
+    for (int q = 0; q < C::FB; ++q) {
+      const int64_t wr = w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N);
+      bbase[q] = (wbase + wr) * nblk;
+      gq[q] = w_scale_of(p, e, wr);
+    }
+    k_loop<C, false, RawStage<C::HA>, Fp4Stage<C::FB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt); },
+        [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
+        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
+        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_qdq_store<C::FB, T>(st, tile, part, gq); });
+  } else if constexpr (MODE == 3) {
+    int64_t abase[C::HA], bbase[C::HB];
+    TensorScale gq[C::HB];
+#pragma unroll
+    for (int q = 0; q < C::HA; ++q) abase[q] = act_row((threadIdx.x >> 3) + q * (T / 8)) * p.K;
+#pragma unroll
+    for (int q = 0; q < C::HB; ++q) {
+      const int64_t wr = w_row_of<C, EPI>((threadIdx.x >> 3) + q * (T / 8), nt, p.N);
+      bbase[q] = (wbase + wr) * p.K;
+      gq[q] = tensor_scale(w_scale_of(p, e, wr));
+    }
+    k_loop<C, false, RawStage<C::HA>, RawStage<C::HB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt); },
+        [&](RawStage<C::HB> &st, int kt) { raw_fetch(st, p.w_bf16, bbase, static_cast<int>(p.K), kt); },
+        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
+        [&](const RawStage<C::HB> &st, uint4 *tile, int part) { qdq_store<C::HB, T>(st, tile, part, gq); });
   } else {
     int64_t abase[C::HA], bbase[C::HB];
 #pragma unroll
@@ -627,27 +735,80 @@ __global__ __launch_bounds__(CfgPP::THREADS, 1) void k_gemm_pp(Params p) {
                     [&] { rfetch(0); rstore(0); rfetch(1); },
                     [&](int k, int buf) { rstore(buf); rfetch(k + 2); });
     }
-  } else {
+  } else if constexpr (MODE == 4) {
     const int K = static_cast<int>(p.K);
-    int arows[4];
-    int64_t abase[4], bbase[4];
+    const int nblk = K / 16;
+    int arows[4], brows[2];
+    int64_t abase[4], bbase[2];
+    float gq[2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       arows[q] = g * 128 + (tg >> 3) + q * 32;
       abase[q] = act_row(arows[q]) * p.K;
-      bbase[q] = (wbase + w_row_of<C, EPI>(arows[q], nt, p.N)) * p.K;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      brows[q] = g * 128 + fp4_row(tg) + q * 64;
+      const int64_t wr = w_row_of<C, EPI>(brows[q], nt, p.N);
+      bbase[q] = (wbase + wr) * nblk;
+      gq[q] = w_scale_of(p, e, wr);
+    }
+    RawStage<4> sa;
+    Fp4Stage<2> sb;
+    auto fetch = [&](int kt) __attribute__((always_inline)) {
+      raw_fetch(sa, p.x_bf16, abase, K, kt);
+      fp4_fetch(sb, p.w_codes, p.w_scales, bbase, nblk, kt);
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+      raw_store_rows(sa, As[buf], arows);
+      const int c = (tg & 3) * 2;
+      uint4 c0, c1;
+      qdq_decode16(sb.w[0], sb.s[0], gq[0], sb.ok, c0, c1);
+      Bs[buf][swz(brows[0], c)] = c0;
+      Bs[buf][swz(brows[0], c + 1)] = c1;
+      qdq_decode16(sb.w[1], sb.s[1], gq[1], sb.ok, c0, c1);
+      Bs[buf][swz(brows[1], c)] = c0;
+      Bs[buf][swz(brows[1], c + 1)] = c1;
+    };
+    pp_loop<false>((K + BK - 1) / BK, As, Bs, acc, g, wm, wn, lane,
+                   [&]() __attribute__((always_inline)) { fetch(0); store(0); fetch(1); },
+                   [&](int k, int buf) __attribute__((always_inline)) { store(buf); fetch(k + 2); });
+  } else {
+    const int K = static_cast<int>(p.K);
+    int arows[4];
+    int64_t abase[4], bbase[4];
+    TensorScale gq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      arows[q] = g * 128 + (tg >> 3) + q * 32;
+      abase[q] = act_row(arows[q]) * p.K;
+      const int64_t wr = w_row_of<C, EPI>(arows[q], nt, p.N);
+      bbase[q] = (wbase + wr) * p.K;
+      gq[q] = tensor_scale(MODE == 3 ? w_scale_of(p, e, wr) : 1.0f);
     }
     RawStage<4> sa, sb;
-    auto fetch = [&](int kt) {
+    // The lambdas are forced inline: with the QDQ body they exceed the
+    // inliner's budget, and a lambda left as a call keeps the arrays it
+    // captures by reference in scratch memory.
+    auto fetch = [&](int kt) __attribute__((always_inline)) {
       raw_fetch(sa, p.x_bf16, abase, K, kt);
       raw_fetch(sb, p.w_bf16, bbase, K, kt);
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf) __attribute__((always_inline)) {
       raw_store_rows(sa, As[buf], arows);
-      raw_store_rows(sb, Bs[buf], arows);
+      if constexpr (MODE == 3) {
+        const int c = threadIdx.x & 7;
+        Bs[buf][swz(arows[0], c)] = qdq_chunk(sb.v[0], sb.ok, gq[0]);
+        Bs[buf][swz(arows[1], c)] = qdq_chunk(sb.v[1], sb.ok, gq[1]);
+        Bs[buf][swz(arows[2], c)] = qdq_chunk(sb.v[2], sb.ok, gq[2]);
+        Bs[buf][swz(arows[3], c)] = qdq_chunk(sb.v[3], sb.ok, gq[3]);
+      } else {
+        raw_store_rows(sb, Bs[buf], arows);
+      }
     };
-    pp_loop<false>((K + BK - 1) / BK, As, Bs, acc, g, wm, wn, lane, [&] { fetch(0); store(0); fetch(1); },
-                   [&](int k, int buf) { store(buf); fetch(k + 2); });
+    pp_loop<false>((K + BK - 1) / BK, As, Bs, acc, g, wm, wn, lane,
+                   [&]() __attribute__((always_inline)) { fetch(0); store(0); fetch(1); },
+                   [&](int k, int buf) __attribute__((always_inline)) { store(buf); fetch(k + 2); });
   }
   epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
 }
@@ -1161,7 +1322,7 @@ TileCfg pick_cfg(const GemmLaunch &a) {
   double best_score = -1.0;
   // Large tiles: the ping-pong kernel wins for bf16 operands, the plain
   // 8-wave kernel for NVFP4 operands (whose decode already overlaps the MFMAs).
-  const TileCfg large = a.mode == 1 ? kP : kL;
+  const TileCfg large = a.mode != 0 ? kP : kL;
   for (const Cand &c : cands) {
     if (a.N % c.bn) continue;
     const double m_est = static_cast<double>((a.num_rows + c.bm - 1) / c.bm) + (a.E > 1 ? a.E / 2.0 : 0.0);
@@ -1199,6 +1360,12 @@ void launch_pp_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStr
   if (a.mode == 1) {
     if (a.epilogue == 0) launch_pp<1, 0, false>(p, g, stream);
     else launch_pp<1, 1, false>(p, g, stream);
+  } else if (a.mode == 2) {
+    if (a.epilogue == 0) launch_pp<3, 0, false>(p, g, stream);
+    else launch_pp<3, 1, false>(p, g, stream);
+  } else if (a.mode == 3) {
+    if (a.epilogue == 0) launch_pp<4, 0, false>(p, g, stream);
+    else launch_pp<4, 1, false>(p, g, stream);
   } else if (res) {
     if (a.epilogue == 0) launch_pp<0, 0, true>(p, g, stream);
     else launch_pp<0, 1, true>(p, g, stream);
@@ -1232,9 +1399,21 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
   if (merged) {
     if (a.epilogue == 0) launch_k<C, 2, 0, false>(p, g, stream);
     else if constexpr (C::NI % 2 == 0) launch_k<C, 2, 1, false>(p, g, stream);
-  } else if (a.mode == 1) {
-    if (a.epilogue == 0) launch_k<C, 1, 0, false>(p, g, stream);
-    else if constexpr (C::NI % 2 == 0) launch_k<C, 1, 1, false>(p, g, stream);
+  } else if (a.mode != 0) {
+    // bf16 operands: large tiles run on the ping-pong kernel (pick_cfg), so
+    // only the 128 x 128 register-staged kernel is instantiated for them
+    if constexpr (C::BM == 128) {
+      if (a.mode == 1) {
+        if (a.epilogue == 0) launch_k<C, 1, 0, false>(p, g, stream);
+        else launch_k<C, 1, 1, false>(p, g, stream);
+      } else if (a.mode == 2) {
+        if (a.epilogue == 0) launch_k<C, 3, 0, false>(p, g, stream);
+        else launch_k<C, 3, 1, false>(p, g, stream);
+      } else {
+        if (a.epilogue == 0) launch_k<C, 4, 0, false>(p, g, stream);
+        else launch_k<C, 4, 1, false>(p, g, stream);
+      }
+    }
   } else if (res) {
     if (a.epilogue == 0) launch_k<C, 0, 0, true>(p, g, stream);
     else if constexpr (C::NI % 2 == 0) launch_k<C, 0, 1, true>(p, g, stream);

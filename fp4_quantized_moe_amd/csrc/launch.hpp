@@ -27,6 +27,10 @@ struct QuantizeLaunch {
 int amax_partials_per_tensor(int64_t n_elem);
 size_t quantize_ws_bytes(int64_t batch, int64_t rows, int64_t cols);
 hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream);
+// The tensor scale g of each of `batch` matrices only (amax partials in ws,
+// then one folding workgroup per matrix).
+hipError_t launch_tensor_scales(const void *x, bool x_bf16, int64_t batch, int64_t rows, int64_t cols, float *gscale,
+                                void *ws, hipStream_t stream);
 // quads_quantize_nvfp4_noalloc: the amax partials (batch * P floats) in the
 // library's per-device scratch array of kNoAllocScratchBytes.
 constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
@@ -55,7 +59,8 @@ hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream);
 
 // ---- gemm.hip --------------------------------------------------------------
 struct GemmLaunch {
-  int mode;       // 0: W4A4 (+ residual), 1: bf16 operands
+  int mode;       // 0: W4A4 (+ residual), 1: bf16 operands, 2: bf16 x QDQ(bf16 masters),
+                  // 3: bf16 x NVFP4 weights decoded to their QDQ bf16 values
   int epilogue;   // 0: none, 1: swiglu
   bool y_bf16;
   int E, n_seg;

@@ -82,7 +82,7 @@ struct BlockQ {
   uint32_t scale;
 };
 
-// RN(a / d) for finite a >= 0 and normal d > 0, given r = RN(1 / d):
+// RN(a / d) for finite a >= 0 and d in [2^-125, 2^126), given r = RN(1 / d):
 // q = RN(a r) is within one ulp of a/d, the remainder a - d q is exact in one
 // FMA, and RN(q + (a - d q) r) is the correctly rounded quotient (Markstein's
 // theorem for round-to-nearest).  Quotients small enough to underflow are far
@@ -93,63 +93,142 @@ __device__ __forceinline__ float div_rn_with_rcp(float a, float d, float r) {
   return __builtin_fmaf(e, r, q);
 }
 
-// Quantize 16 values with tensor scale g.  The E2M1 rounding (nearest, ties
-// to even, saturating at 6, sign kept for zeros) and the nibble packing are
-// done by v_cvt_scalef32_pk_fp4_f32 with a unit scale on the exact quotient
-// fl32(x / d); its rounding equals the threshold rule of e2m1_index on every
-// FP32 input (checked exhaustively over the rounding-relevant range).  If
-// `dq_out` is non-null, writes dq = sign * fl32(level * d), decoding the codes
-// back with v_cvt_scalef32_pk_f32_fp4.
-__device__ __forceinline__ BlockQ quantize_block16(const float (&x)[16], float g, float *dq_out) {
+// A tensor scale g with its rounded reciprocal, for the block-scale division
+// fl32(a / g).  `fast` holds where the reciprocal-corrected division is the
+// correctly rounded quotient (g and 1/g normal).
+struct TensorScale {
+  float g, rg;
+  bool fast;
+};
+
+__device__ __forceinline__ TensorScale tensor_scale(float g) {
+  return {g, 1.0f / g, g >= 0x1p-125f && g < 0x1p126f};
+}
+
+// Block scale of a 16-element block with amax `amax` under tensor scale g:
+// s = E4M3(fl32(fl32(amax / 6) / g)) and d = fl32(dec(s) * g).  Both
+// divisions are the correctly rounded quotients: fl32(amax / 6) by the
+// reciprocal-corrected division with RN(1/6) while the quotient is a normal
+// number (amax >= 2^-100), and fl32(a / g) by the same with RN(1/g), the
+// dividend capped at 1024 g (quotients above 448 saturate the scale whatever
+// their value, and the cap keeps the corrected division from overflowing);
+// other operands take a plain division.
+struct BlockScale {
+  uint32_t s;
+  float d;
+};
+
+__device__ __forceinline__ BlockScale block_scale(float amax, const TensorScale &ts) {
+  constexpr float kRcp6 = 0x1.555556p-3f;  // RN(1/6)
+  float s6, s_real;
+  if (__builtin_expect(amax >= 0x1p-100f, 1)) s6 = div_rn_with_rcp(amax, 6.0f, kRcp6);
+  else s6 = amax / 6.0f;
+  if (__builtin_expect(ts.fast, 1)) s_real = div_rn_with_rcp(fminf(s6, 1024.0f * ts.g), ts.g, ts.rg);
+  else s_real = s6 / ts.g;
+  const uint32_t s = f32_to_e4m3(s_real);
+  return {s, e4m3_to_f32(s) * ts.g};
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> packed bf16 (a in the low half), nearest-even, with
+// gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Signed quotients of N elements of one block, branch-free, that round to
+// the same E2M1 codes as the exact v[i] = fl32(x[i] / d):
+//   - d outside [2^-125, 2^126) is first brought into that range by an exact
+//     power-of-two scaling of both operands (2^64 up or down), which leaves
+//     the quotient's real value unchanged, so the reciprocal-corrected
+//     division below is the correctly rounded quotient (and dividends that
+//     lose bits when scaled down have quotients far below the first rounding
+//     threshold, 0.25);
+//   - the dividend is capped at 8 d: every quotient above 5 takes the top
+//     level (6) whatever its value, and the cap keeps the corrected division
+//     from overflowing (possible when a given tensor scale is far too small
+//     for the data);
+//   - d == 0 gives zero with the sign of x.
+template <int N>
+__device__ __forceinline__ void block_quotients(const float (&x)[N], float d, float (&v)[N]) {
+  const float sc = d < 0x1p-125f ? 0x1p64f : (d >= 0x1p126f ? 0x1p-64f : 1.0f);
+  const float dd = d * sc;
+  const float r = 1.0f / dd;
+  const float cap = 8.0f * dd;
+  const bool live = d > 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float a = fminf(fabsf(x[i]) * sc, cap);
+    v[i] = __builtin_copysignf(live ? div_rn_with_rcp(a, dd, r) : 0.0f, x[i]);
+  }
+}
+
+// E2M1 codes of 8 quotients (element i in nibble i): nearest, ties to even,
+// saturating at 6, sign kept for zeros.  v_cvt_scalef32_pk_fp4_f32 with a
+// unit scale rounds exactly as the threshold rule of e2m1_index on every
+// FP32 input (checked exhaustively over the rounding-relevant range).
+__device__ __forceinline__ uint32_t pack8_fp4(const float *v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
+// dq = sign * fl32(level * d) of the 8 codes of a word, decoded with
+// v_cvt_scalef32_pk_f32_fp4 (unit scale: the exact signed level).
+template <int B>
+__device__ __forceinline__ void dequant_byte(uint32_t w, float d, float *dq) {
+  const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  dq[2 * B] = e[0] * d;
+  dq[2 * B + 1] = e[1] * d;
+}
+
+__device__ __forceinline__ void dequant8(uint32_t w, float d, float *dq) {
+  dequant_byte<0>(w, d, dq);
+  dequant_byte<1>(w, d, dq);
+  dequant_byte<2>(w, d, dq);
+  dequant_byte<3>(w, d, dq);
+}
+
+// Quantize 16 values with tensor scale g: the block scale from their amax,
+// the quotients fl32(x / d), their E2M1 codes, and (if `dq_out` is non-null)
+// the dequantized values.
+__device__ __forceinline__ BlockQ quantize_block16(const float (&x)[16], const TensorScale &ts, float *dq_out) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  const float s_real = (amax / 6.0f) / g;
-  const uint32_t s = f32_to_e4m3(s_real);
-  const float d = e4m3_to_f32(s) * g;
+  const BlockScale bs = block_scale(amax, ts);
   float v[16];
-  if (d >= 0x1p-125f) {
-    const float r = 1.0f / d;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(div_rn_with_rcp(fabsf(x[i]), d, r), x[i]);
-  } else if (d > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = x[i] / d;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(0.0f, x[i]);
-  }
+  block_quotients<16>(x, bs.d, v);
   BlockQ q;
-  q.scale = s;
-  uint32_t lo = 0, hi = 0;
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0], v[1], 1.0f, 0);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2], v[3], 1.0f, 1);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4], v[5], 1.0f, 2);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6], v[7], 1.0f, 3);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8], v[9], 1.0f, 0);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10], v[11], 1.0f, 1);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12], v[13], 1.0f, 2);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14], v[15], 1.0f, 3);
-  q.lo = lo;
-  q.hi = hi;
+  q.scale = bs.s;
+  q.lo = pack8_fp4(v);
+  q.hi = pack8_fp4(v + 8);
   if (dq_out) {
-#define QUADS_DQ_BYTE(word, byte, base)                                            \
-  {                                                                                \
-    const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, byte);     \
-    dq_out[(base)] = e[0] * d;                                                     \
-    dq_out[(base) + 1] = e[1] * d;                                                 \
-  }
-    QUADS_DQ_BYTE(lo, 0, 0)
-    QUADS_DQ_BYTE(lo, 1, 2)
-    QUADS_DQ_BYTE(lo, 2, 4)
-    QUADS_DQ_BYTE(lo, 3, 6)
-    QUADS_DQ_BYTE(hi, 0, 8)
-    QUADS_DQ_BYTE(hi, 1, 10)
-    QUADS_DQ_BYTE(hi, 2, 12)
-    QUADS_DQ_BYTE(hi, 3, 14)
-#undef QUADS_DQ_BYTE
+    dequant8(q.lo, bs.d, dq_out);
+    dequant8(q.hi, bs.d, dq_out + 8);
   }
   return q;
+}
+
+// Fake-quantized (QDQ) bf16 values of one half (8 consecutive elements) of a
+// 16-element block, given the whole block's amax: bf16_RNE(dq) with the same
+// operations quantize_block16 applies to each element, so the bits equal the
+// quantizer's QDQ output for that block.  Returns the 8 bf16 values packed
+// two per word, element 0 in the low half of word 0.
+__device__ __forceinline__ uint4 qdq8_bf16(const float (&x)[8], float amax, const TensorScale &ts) {
+  const BlockScale bs = block_scale(amax, ts);
+  float v[8];
+  block_quotients<8>(x, bs.d, v);
+  float dq[8];
+  dequant8(pack8_fp4(v), bs.d, dq);
+  return make_uint4(pack_bf16x2(dq[0], dq[1]), pack_bf16x2(dq[2], dq[3]), pack_bf16x2(dq[4], dq[5]),
+                    pack_bf16x2(dq[6], dq[7]));
 }
 
 // Dequantized FP32 value of one code given the block's d = fl32(dec(s) * g).

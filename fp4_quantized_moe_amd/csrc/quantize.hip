@@ -131,6 +131,21 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const void *x, int64_
   }
 }
 
+// Tensor scale of matrix blockIdx.x from its P amax partials (the fold
+// k_quantize does for its own tensor).
+__global__ __launch_bounds__(kThreads) void k_fold_gscale(const float *partials, int P, float *gscale) {
+  __shared__ float red[kThreads / 64];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < P; i += kThreads) m = fmaxf(m, partials[static_cast<int64_t>(blockIdx.x) * P + i]);
+  const float g = tensor_scale_from_amax(block_max(m, red));
+  if (threadIdx.x == 0) gscale[blockIdx.x] = g;
+}
+
+__global__ __launch_bounds__(kThreads) void k_fill_one(float *p, int64_t n) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (i < n) p[i] = 1.0f;
+}
+
 __global__ __launch_bounds__(kThreads) void k_zero_f32(float *p, int64_t n) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads)
@@ -169,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
     if (p.gscale != nullptr && rc == 0 && cc == 0 && threadIdx.x == 0) p.gscale[b] = g;
   }
 
+  const TensorScale ts = tensor_scale(g);
   const int bcol = threadIdx.x % p.BC, rg = threadIdx.x / p.BC;
   const int64_t gbc = static_cast<int64_t>(cc) * p.BC + bcol;
   const bool active = rg < p.RG && gbc < p.cb;
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
         float v[16];
         to_f32<BF16>(u ? x1 : x0, v);
         float dq[16];
-        const BlockQ q = quantize_block16(v, g, (SCORES || QDQ) ? dq : nullptr);
+        const BlockQ q = quantize_block16(v, ts, (SCORES || QDQ) ? dq : nullptr);
         if constexpr (CODES) {
           reinterpret_cast<uint2 *>(p.codes)[row * p.cb + gbc] = make_uint2(q.lo, q.hi);
           p.scales[row * p.cb + gbc] = static_cast<uint8_t>(q.scale);
@@ -210,8 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
         if constexpr (QDQ) {
           uint32_t w[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            w[i] = f32_to_bf16_bits(dq[2 * i]) | (f32_to_bf16_bits(dq[2 * i + 1]) << 16);
+          for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(dq[2 * i], dq[2 * i + 1]);
           uint4 *o = reinterpret_cast<uint4 *>(p.qdq + row * p.cols + gbc * 16);
           o[0] = make_uint4(w[0], w[1], w[2], w[3]);
           o[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -260,6 +275,27 @@ int amax_partials_per_tensor(int64_t n_elem) {
 size_t quantize_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
   const int P = amax_partials_per_tensor(rows * cols);
   return static_cast<size_t>(batch) * P * sizeof(float) + 256;
+}
+
+hipError_t launch_tensor_scales(const void *x, bool x_bf16, int64_t batch, int64_t rows, int64_t cols, float *gscale,
+                                void *ws, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  const int P = amax_partials_per_tensor(n);
+  float *partials = static_cast<float *>(ws);
+  if (n == 0) {
+    hipLaunchKernelGGL(k_fill_one, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, gscale, batch);
+    return hipGetLastError();
+  }
+  int64_t chunk = (n + P - 1) / P;
+  chunk = (chunk + 15) / 16 * 16;
+  if (x_bf16)
+    hipLaunchKernelGGL(k_amax_partial<true>, dim3(batch * P), dim3(kThreads), 0, stream, x, n, P, chunk, partials,
+                       nullptr, cols);
+  else
+    hipLaunchKernelGGL(k_amax_partial<false>, dim3(batch * P), dim3(kThreads), 0, stream, x, n, P, chunk, partials,
+                       nullptr, cols);
+  hipLaunchKernelGGL(k_fold_gscale, dim3(batch), dim3(kThreads), 0, stream, partials, P, gscale);
+  return hipGetLastError();
 }
 
 size_t quantize_partials_bytes(int64_t batch, int64_t rows, int64_t cols) {

@@ -347,6 +347,7 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
   if (!has_rows) return;
 
   // 2-3. Residual rows.
+  const TensorScale tsr = tensor_scale(gr);
   const float gx = *x_g;
   for (int64_t r0 = r_begin; r0 < r_stop; r0 += rb) {
     const int nr = static_cast<int>(min(static_cast<int64_t>(rb), r_stop - r0));
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void k_rac(const void *x, int64_t rows, i
         const int c = sel[jb * 16 + i];
         g16[i] = c >= 0 ? src[c] : 0.0f;
       }
-      const BlockQ q = quantize_block16(g16, gr, nullptr);
+      const BlockQ q = quantize_block16(g16, tsr, nullptr);
       const int64_t row = r0 + rr;
       reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
       r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);
@@ -465,6 +466,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 &
   for (int j = tid; j < nsel; j += kThreads) pos[sel[j]] = static_cast<int16_t>(j);
   __syncthreads();
 
+  const TensorScale tsr = tensor_scale(gr);
   const float gx = *x_g;
   const float ratio = gr / gx;
   for (int64_t r0 = r_begin; r0 < r_stop; r0 += rb) {
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BF16 &
       float g16[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) g16[i] = jb * 16 + i < nsel ? src[i] : 0.0f;
-      const BlockQ q = quantize_block16(g16, gr, nullptr);
+      const BlockQ q = quantize_block16(g16, tsr, nullptr);
       const int64_t row = r0 + rr;
       reinterpret_cast<uint2 *>(r_codes)[row * nblk + jb] = make_uint2(q.lo, q.hi);
       r_scales[row * nblk + jb] = static_cast<uint8_t>(q.scale);

@@ -207,6 +207,26 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  * 2.2-A]: x_bf16 [act_rows, K] times w_bf16 [E, N, K] (QDQ'd weights),
  * no scales, no residual.
  *
+ * operand_mode QUADS_OPERANDS_BF16_QDQ is the same forward with the weight
+ * QDQ fused in [Gist 2.2-A: every forward sees the discretized weights]:
+ * w_bf16 holds the bf16 MASTER weights and w_gscale [E * n_seg] their tensor
+ * scales (quads_weight_qdq with QUADS_SCALES_ONLY, one per (expert,
+ * segment) matrix); each weight block is quantized to NVFP4 and dequantized
+ * to bf16 in registers on its way to the matrix cores, with exactly the
+ * operations of quads_weight_qdq (QUADS_GSCALE_GIVEN), so the product equals
+ * quads_weight_qdq followed by QUADS_OPERANDS_BF16 bit for bit (same tile
+ * schedule) while W_qdq is never written to memory.  K % 16 == 0; SWIGLU
+ * needs n_seg == 2 (gate and up matrices with their own scales).
+ *
+ * operand_mode QUADS_OPERANDS_BF16_W4 is the same forward from the masters'
+ * NVFP4 encoding: w_codes / w_scales / w_gscale hold the masters quantized
+ * by quads_quantize_nvfp4 (one tensor scale per (expert, segment) matrix --
+ * the codes quads_weight_qdq exports, and the trainer-to-rollout weight-sync
+ * payload); each weight is decoded on its way to the matrix cores to its QDQ
+ * value bf16(fl32(e2m1 * fl32(dec(s) * g))), so the product again equals
+ * quads_weight_qdq followed by QUADS_OPERANDS_BF16 bit for bit, the GEMM
+ * reads 0.5625 instead of 2 bytes per weight and W_qdq is never written.
+ *
  * Epilogues: QUADS_EPI_NONE writes y [num_rows, N] (F32 or BF16);
  * QUADS_EPI_SWIGLU (n_seg must be 2: W rows [0, N/2) are the gate, [N/2, N)
  * the up projection) writes h [num_rows, N/2] BF16 with
@@ -220,6 +240,8 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  * ------------------------------------------------------------------------- */
 #define QUADS_OPERANDS_W4A4 0
 #define QUADS_OPERANDS_BF16 1
+#define QUADS_OPERANDS_BF16_QDQ 2
+#define QUADS_OPERANDS_BF16_W4 3
 #define QUADS_EPI_NONE 0
 #define QUADS_EPI_SWIGLU 1
 
@@ -254,13 +276,14 @@ typedef struct {
   const float *r_gscale;
   const int32_t *sel_idx;
   int64_t kpad;
-  /* W4A4 weights: codes [E, N, K/2], scales [E, N, K/16], gscale [E * n_seg] */
+  /* W4A4 weights: codes [E, N, K/2], scales [E, N, K/16], gscale [E * n_seg]
+     (BF16_QDQ: w_gscale only, the masters' tensor scales) */
   const uint8_t *w_codes;
   const uint8_t *w_scales;
   const float *w_gscale;
-  /* BF16 operands (operand_mode == QUADS_OPERANDS_BF16) */
+  /* BF16 operands (operand_mode QUADS_OPERANDS_BF16 or _BF16_QDQ) */
   const void *x_bf16; /* [act_rows, K] */
-  const void *w_bf16; /* [E, N, K] */
+  const void *w_bf16; /* [E, N, K]: QDQ'd weights (BF16) or masters (BF16_QDQ) */
   const int32_t *row_token;      /* [num_rows] or NULL (identity) */
   const int32_t *expert_offsets; /* [E + 1], device */
   void *y;
@@ -294,8 +317,12 @@ quads_status_t quads_moe_gemm_prepare(const quads_moe_gemm_args *a, void *stream
  * codes/scales/gscale also receive the NVFP4 tensor -- identical to
  * quads_quantize_nvfp4 on the same input (the shared path that aligns trainer
  * and rollout weights).  flags: QUADS_GSCALE_GIVEN reads the tensor scales
- * from q_out->gscale (q_out required).
+ * from q_out->gscale (q_out required); QUADS_SCALES_ONLY computes only the
+ * tensor scales into q_out->gscale (q_out required, its codes/scales and
+ * w_out_bf16 unused and may be NULL) -- the input of the fused
+ * QUADS_OPERANDS_BF16_QDQ forward.
  * ------------------------------------------------------------------------- */
+#define QUADS_SCALES_ONLY 4u
 size_t quads_weight_qdq_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
 quads_status_t quads_weight_qdq(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols,
                                 void *w_out_bf16, const quads_nvfp4_t *q_out, uint32_t flags,
