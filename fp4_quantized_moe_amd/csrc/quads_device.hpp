@@ -152,17 +152,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 //     from overflowing (possible when a given tensor scale is far too small
 //     for the data);
 //   - d == 0 gives zero with the sign of x.
+// Blocks with d in the normal range (all but degenerate tensors) take the
+// short form: cap, corrected division, sign.
 template <int N>
 __device__ __forceinline__ void block_quotients(const float (&x)[N], float d, float (&v)[N]) {
-  const float sc = d < 0x1p-125f ? 0x1p64f : (d >= 0x1p126f ? 0x1p-64f : 1.0f);
-  const float dd = d * sc;
-  const float r = 1.0f / dd;
-  const float cap = 8.0f * dd;
-  const bool live = d > 0.0f;
+  if (__builtin_expect(d >= 0x1p-125f && d < 0x1p126f, 1)) {
+    const float r = 1.0f / d;
+    const float cap = 8.0f * d;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float a = fminf(fabsf(x[i]) * sc, cap);
-    v[i] = __builtin_copysignf(live ? div_rn_with_rcp(a, dd, r) : 0.0f, x[i]);
+    for (int i = 0; i < N; ++i) v[i] = __builtin_copysignf(div_rn_with_rcp(fminf(fabsf(x[i]), cap), d, r), x[i]);
+  } else {
+    const float sc = d < 0x1p-125f ? 0x1p64f : 0x1p-64f;
+    const float dd = d * sc;
+    const float r = 1.0f / dd;
+    const float cap = 8.0f * dd;
+    const bool live = d > 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float a = fminf(fabsf(x[i]) * sc, cap);
+      v[i] = __builtin_copysignf(live ? div_rn_with_rcp(a, dd, r) : 0.0f, x[i]);
+    }
   }
 }
 
