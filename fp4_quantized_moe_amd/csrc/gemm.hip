@@ -44,6 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "dma.hpp"
 #include "fp4_mfma.hpp"
 #include "launch.hpp"
 #include "quads_device.hpp"
@@ -862,46 +863,12 @@ struct Lay {
   static constexpr int STAGE = STAGE0 > XEND ? STAGE0 : XEND;
 };
 
-typedef __attribute__((address_space(3))) void lds_t;
-
-// One DMA instruction (16 or 4 bytes per lane): lane l's bytes land at
-// lds_base + l * bytes.  Issued as inline assembly so that the compiler's
-// wait-count pass, which cannot tell the LDS stages apart, does not add a
-// wait for every DMA in flight before each LDS read; the waits are explicit
-// (below).  M0 holds the wave's LDS base; one wait state separates its write
-// from the load.  M0 is not otherwise used by these kernels, so clobbering it
-// is safe here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma(const void *g, uint8_t *lds_base, int bytes) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_t *)lds_base));
-  if (bytes == 16)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Wait until at most the newest P (resp. 0) vector-memory operations of this
-// wave are outstanding (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4 and lgkmcnt 11:8 left at their maxima).
+// DMA staging helpers (dma, wait_vm, barrier_no_fence): dma.hpp.
 template <int P>
 __device__ __forceinline__ void wait_all_but_one_step() {
-  static_assert(P >= 0 && P < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | P);
+  wait_vm<P>();
 }
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Workgroup barrier without a memory fence: __syncthreads() would also wait
-// for every DMA in flight (vmcnt(0)), including the stages being prefetched.
-// LDS visibility comes from the explicit vmcnt wait before the barrier (DMA
-// writes) and from every fragment read having been consumed before it; the
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+__device__ __forceinline__ void wait_all() { wait_vm<0>(); }
 
 // Chunk slot swizzles (16-byte units) that make the fragment reads
 // bank-conflict-free: 64-byte rows, 32-byte rows, 128-byte rows.

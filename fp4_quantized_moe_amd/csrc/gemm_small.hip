@@ -21,24 +21,32 @@
 // W4A4 (no residual) stages and decodes the activation codes instead and is
 // exact up to accumulation.
 //
-// k_gemm_small: a workgroup of 4 waves per (expert, 128 output columns); wave
-// w owns 32 weight rows (output columns) and runs v_mfma_f32_32x32x16_f16 with
-// the expert's rows (32 per pass) as the A operand.  A K step is 256 elements:
-// one 128-byte line of codes per weight row.  Operands go from global memory
-// straight to LDS (global_load_lds_dwordx4) with every load instruction
-// covering whole 128-byte lines (8 lanes per line) -- on MI355X a wave load
-// spread over 32 rows at 32 bytes per row streams at a quarter of the HBM rate
-// that whole lines reach.  Each wave stages its own weight rows; the
-// activation rows (codes and scales, or the merged fp16 operand) are staged
-// once per workgroup, a quarter by each wave.  16-byte chunks are XOR-swizzled
-// per row (by choosing which chunk each lane fetches) so that the MFMA
-// fragment reads are bank-conflict-free.  Two LDS stages: step k+1 is in
-// flight while step k is decoded (cvt + pk_mul, exact) and multiplied.  The
-// contraction order inside a step is permuted identically for both operands
-// (lane half h takes elements [128h, 128h+128), 8 per MFMA).
+// k_gemm_small: a workgroup of kSW = 4 waves per (expert, 128 output
+// columns); wave w owns 32 weight rows (output columns) and runs
+// v_mfma_f32_32x32x16_f16 with the expert's rows (32 per pass) as the A
+// operand.  A K step is 256 elements: one 128-byte line of codes per weight
+// row.  Operands go from global memory straight to LDS (global_load_lds) with
+// every load instruction covering whole 128-byte lines (8 lanes per line) --
+// on MI355X a wave load spread over 32 rows at 32 bytes per row streams at a
+// quarter of the HBM rate that whole lines reach.  Each wave stages its own
+// weight rows; the activation rows (codes and scales, or the merged fp16
+// operand) are staged once per workgroup, shared by its columns.  16-byte
+// chunks are XOR-swizzled per row (by choosing which chunk each lane fetches)
+// so that the MFMA fragment reads are bank-conflict-free.  The contraction
+// order inside a step is permuted identically for both operands (lane half h
+// takes elements [128h, 128h+128), 8 per MFMA).
+//
+// kSStages = 2 LDS stages (two workgroups per CU): step k+1 is in flight
+// while step k is decoded (cvt + pk_mul, exact) and multiplied.  The loop
+// handles up to four stages with partial vmcnt waits; deeper pipelines (three
+// or four stages, 8-wave 256-column workgroups, one workgroup per CU) were
+// measured and were not faster on the decode-shaped layer (gate_up 86-104 us
+// against 83-87 us), so the weight stream is not limited by the bytes in
+// flight per CU.
 #include <stdlib.h>
 #include <string.h>
 
+#include "dma.hpp"
 #include "fp4_mfma.hpp"
 #include "launch.hpp"
 #include "quads_device.hpp"
@@ -46,9 +54,11 @@
 namespace quads {
 namespace {
 
-constexpr int kSK = 256;   // K per step
-constexpr int kSBN = 128;  // output columns per workgroup: 4 waves x 32
-constexpr int kSM = 32;    // rows per pass
+constexpr int kSK = 256;           // K per step
+constexpr int kSW = 4;             // waves per workgroup
+constexpr int kSBN = 32 * kSW;     // weight rows (output columns) per workgroup
+constexpr int kSM = 32;            // rows per pass
+constexpr int kSStages = 2;        // LDS stages
 
 struct SmallParams {
   const int32_t *expert_offsets, *row_token;
@@ -68,66 +78,80 @@ struct SmallParams {
 // slot c ^ ((r >> 1) & 7) (32 merged-operand chunks per row: slot c ^ (r & 15)).
 template <bool RES>
 struct StageLds {
-  uint4 w[4 * 32 * 8];             // [wave][row][slot] weight codes
-  uint32_t ws[4 * 32 * 4];         // [wave][row][4 words] weight block scales
-  uint4 x[RES ? 1 : 32 * 8];       // [row][slot] activation codes (plain W4A4)
-  uint32_t xs[RES ? 1 : 32 * 4];   // [row][4 words] activation block scales (plain W4A4)
-  uint4 r[RES ? 32 * 32 : 1];      // [row][slot] merged fp16 activation (RAC)
+  uint4 w[kSW * 32 * 8];            // [wave][row][slot] weight codes
+  uint32_t ws[kSW * 32 * 4];        // [wave][row][4 words] weight block scales
+  uint4 x[RES ? 1 : 32 * 8];        // [row][slot] activation codes (plain W4A4)
+  uint32_t xs[RES ? 1 : 32 * 4];    // [row][4 words] activation block scales (plain W4A4)
+  uint4 r[RES ? 32 * 32 : 1];       // [row][slot] merged fp16 activation (RAC)
 };
 
-typedef __attribute__((address_space(3))) void lds_t;
+// Activation staging of a step is split into 8 (plain W4A4) or 16 (merged
+// operand) DMA jobs, kSA per wave.  Merged operand: job j stages rows 2j and
+// 2j+1 (32 chunks each); in a 16-row pass job j stages rows 2(j % 8) and
+// 2(j % 8)+1, so jobs 8-15 repeat jobs 0-7.  Plain W4A4: jobs 0-3 stage the
+// code lines of rows 8j..8j+7, jobs 4-5 the scale words of rows
+// 16(j-4)..16(j-4)+15, jobs 6-7 repeat jobs 2-3.  Repeats write identical
+// bytes to the same LDS words; they keep every wave's DMA count equal.
+template <bool RES>
+constexpr int kSA = (RES ? 16 : 8) / kSW;
+static_assert((16 / kSW) * kSW == 16 && (8 / kSW) * kSW == 8, "activation jobs must split evenly over the waves");
 
-// One DMA instruction: lane l's `bytes` bytes land at lds_base + l * bytes.
-__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_t *)(lds_base), 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_t *)(lds_base), 4, 0, 0);
-}
+// DMA instructions per wave per step: 4 weight-code lines, 2 weight-scale
+// words and the activation jobs.
+template <bool RES>
+constexpr int kSP = 6 + kSA<RES>;
 
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 // Per-lane row bookkeeping for the staging loads of one pass.
 struct SmallRows {
-  int64_t wrow[4];  // weight rows of this wave's 4 code loads (rows 8q + lane/8)
-  int64_t wsrow[2]; // weight rows of the 2 scale loads (rows (64i + lane)/4)
-  int64_t xrow;     // activation row of the code load (pass row 8*wave + lane/8)
-  int64_t xsrow;    // activation row of the scale load (pass row (64*wave + lane)/4, waves 0-1)
-  int64_t rrow[4];  // activation rows of the residual loads (pass row 2*(4*wave + q) + lane/32)
+  int64_t wrow[4];           // weight rows of this wave's 4 code loads (rows 8q + lane/8)
+  int64_t wsrow[2];          // weight rows of the 2 scale loads (rows (64i + lane)/4)
+  int64_t arow[16 / kSW];    // activation rows of this wave's activation jobs
 };
 
-// `rows16`: a 16-row pass, which reads activation and residual rows 0-15 only
-// (staged by waves 0-1; wave 0 the scales).
+// Pass row that lane `lane` stages in activation job j.
+template <bool RES>
+__device__ __forceinline__ int act_job_row(int j, int lane, bool rows16) {
+  if constexpr (RES) {
+    return 2 * (rows16 ? (j & 7) : j) + (lane >> 5);
+  } else {
+    if (j >= 4 && j < 6) return (64 * (j - 4) + lane) / 4;
+    return 8 * (j & 3) + (lane >> 3);
+  }
+}
+
 template <bool RES>
 __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, const SmallRows &rw, int kt,
-                                      int wave, int lane, bool rows16 = false) {
+                                      int wave, int lane, bool rows16) {
   const int64_t K = p.K;
   const int slot = lane & 7;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 8 * q + (lane >> 3);
     const int chunk = slot ^ swz8(r);
-    dma16(p.w_codes + rw.wrow[q] * (K / 2) + kt * 128 + chunk * 16, &st.w[(wave * 32 + 8 * q) * 8]);
+    dma(p.w_codes + rw.wrow[q] * (K / 2) + kt * 128 + chunk * 16, &st.w[(wave * 32 + 8 * q) * 8], 16);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    dma4(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i]);
-  if constexpr (!RES) {
-    if (!rows16 || wave < 2) {
-      const int r = 8 * wave + (lane >> 3);
-      const int chunk = slot ^ swz8(r);
-      dma16(p.x_codes + rw.xrow * (K / 2) + kt * 128 + chunk * 16, &st.x[8 * wave * 8]);
-    }
-    if (wave < (rows16 ? 1 : 2)) dma4(p.x_scales + rw.xsrow * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * wave]);
-  } else {
-    if (!rows16 || wave < 2) {
+    dma(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i], 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = 4 * wave + q;
-        const int r = 2 * b + (lane >> 5);
-        const int chunk = (lane & 31) ^ (r & 15);
-        dma16(p.r_dense + rw.rrow[q] * K + kt * 256 + chunk * 8, &st.r[2 * b * 32]);
-      }
+  for (int q = 0; q < kSA<RES>; ++q) {
+    const int j = wave * kSA<RES> + q;  // wave-uniform
+    // Repeat jobs only keep the per-wave DMA counts equal for the partial
+    // waits of three or more stages; with two, every wait is vmcnt(0).
+    const bool repeat = RES ? (rows16 && j >= 8) : j >= 6;
+    if (kSStages == 2 && repeat) continue;
+    const int r = act_job_row<RES>(j, lane, rows16);
+    if constexpr (RES) {
+      const int r_pair = 2 * (rows16 ? (j & 7) : j);
+      const int chunk = (lane & 31) ^ (r & 15);
+      dma(p.r_dense + rw.arow[q] * K + kt * 256 + chunk * 8, &st.r[r_pair * 32], 16);
+    } else if (j >= 4 && j < 6) {
+      dma(p.x_scales + rw.arow[q] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.xs[64 * (j - 4)], 4);
+    } else {
+      const int chunk = slot ^ swz8(r);
+      dma(p.x_codes + rw.arow[q] * (K / 2) + kt * 128 + chunk * 16, &st.x[8 * (j & 3) * 8], 16);
     }
   }
 }
@@ -228,14 +252,47 @@ __device__ __forceinline__ void store_out(const SmallParams &p, int64_t row, int
     static_cast<float *>(p.y)[row * ld + col] = v;
 }
 
-// EPI 0: Y fp32/bf16 [rows, N].  EPI 1 (SwiGLU): waves 0-1 own gate columns
-// and waves 2-3 the matching up columns; h = silu(gate) * up -> bf16 [rows, N/2].
+// The K loop of one pass over the kSStages LDS stages: steps kt+1 ..
+// kt+kSStages-2 are in flight while step kt is multiplied by `comp(stage)`.
+// Step s lives in stage s % kSStages; step kt+kSStages-1 is issued into the
+// stage step kt-1 used, after the barrier that follows every wave's last read
+// of it.
+template <bool RES, class Comp>
+__device__ __forceinline__ void stream_k(StageLds<RES> (&st)[kSStages], const SmallParams &p, const SmallRows &rw,
+                                         int nk, int wave, int lane, bool rows16, Comp comp) {
+  constexpr int P = kSP<RES>;
+  static_assert(kSStages >= 2 && kSStages <= 4, "stages");
+#pragma unroll
+  for (int s = 0; s < kSStages - 1; ++s)
+    if (s < nk) issue<RES>(st[s], p, rw, s, wave, lane, rows16);
+  int cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // This wave's part of step kt has landed once at most its loads of the
+    // steps issued after kt are outstanding ...
+    const int ahead = min(kSStages - 2, nk - 1 - kt);
+    if (ahead >= 2) wait_vm<2 * P>();
+    else if (ahead == 1) wait_vm<P>();
+    else wait_vm<0>();
+    barrier_no_fence();  // ... and every wave's part; step kt-1 is no longer read
+    const int nxt = kt + kSStages - 1;
+    if (nxt < nk) {
+      const int b = cur + kSStages - 1 >= kSStages ? cur - 1 : cur + kSStages - 1;
+      issue<RES>(st[b], p, rw, nxt, wave, lane, rows16);
+    }
+    comp(st[cur]);
+    cur = cur + 1 == kSStages ? 0 : cur + 1;
+  }
+}
+
+// EPI 0: Y fp32/bf16 [rows, N].  EPI 1 (SwiGLU): the first half of the waves
+// own gate columns and the second half the matching up columns;
+// h = silu(gate) * up -> bf16 [rows, N/2].
 template <int EPI, bool RES>
-__global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
-  __shared__ StageLds<RES> st0;
-  __shared__ StageLds<RES> st1;
+__global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(SmallParams p) {
+  __shared__ StageLds<RES> st[kSStages];
   const int e = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = p.expert_offsets[e], mend = p.expert_offsets[e + 1];
   if (m0 >= mend) return;
 
@@ -245,13 +302,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
     col0 = static_cast<int64_t>(nt) * kSBN + 32 * wave;
     wcol0 = col0;
   } else {
-    col0 = static_cast<int64_t>(nt) * (kSBN / 2) + 32 * (wave & 1);
-    wcol0 = (wave >> 1) * (p.N / 2) + col0;
+    col0 = static_cast<int64_t>(nt) * (kSBN / 2) + 32 * (wave % (kSW / 2));
+    wcol0 = (wave / (kSW / 2)) * (p.N / 2) + col0;
   }
   const int64_t wrow0 = static_cast<int64_t>(e) * p.N + wcol0;
   const float gw = p.w_g[e * p.n_seg + static_cast<int>(wcol0) / static_cast<int>(p.N / p.n_seg)];
   const float gx = *p.x_g;
-  const int nk = static_cast<int>(p.K / kSK);  // even
+  const int nk = static_cast<int>(p.K / kSK);
 
   auto act_row = [&](int pm, int r) -> int64_t {
     const int i = min(pm + r, mend - 1);  // rows past the expert re-read a valid row, never stored
@@ -259,36 +316,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
   };
 
   for (int pm = m0; pm < mend; pm += kSM) {
+    const bool rows16 = mend - pm <= 16;  // last pass of at most 16 rows: 16-row MFMAs, half the work
     SmallRows rw;
 #pragma unroll
     for (int q = 0; q < 4; ++q) rw.wrow[q] = wrow0 + 8 * q + (lane >> 3);
 #pragma unroll
     for (int i = 0; i < 2; ++i) rw.wsrow[i] = wrow0 + (64 * i + lane) / 4;
-    rw.xrow = act_row(pm, 8 * wave + (lane >> 3));
-    rw.xsrow = act_row(pm, (64 * (wave & 1) + lane) / 4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rw.rrow[q] = RES ? act_row(pm, 2 * (4 * wave + q) + (lane >> 5)) : 0;
+    for (int q = 0; q < kSA<RES>; ++q) rw.arow[q] = act_row(pm, act_job_row<RES>(wave * kSA<RES> + q, lane, rows16));
 
     __syncthreads();  // the previous pass (or its epilogue) no longer reads the stages
-    if (mend - pm <= 16) {  // last pass of at most 16 rows: 16-row MFMAs, half the work
+    if (rows16) {
       f32x4 ax[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          ax[cb][v] = 0.0f;
-        }
-      issue<RES>(st0, p, rw, 0, wave, lane, true);
-      for (int kt = 0; kt < nk; kt += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        issue<RES>(st1, p, rw, kt + 1, wave, lane, true);
-        compute16<RES>(st0, wave, lane, ax);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 2 < nk) issue<RES>(st0, p, rw, kt + 2, wave, lane, true);
-        compute16<RES>(st1, wave, lane, ax);
-      }
+        for (int v = 0; v < 4; ++v) ax[cb][v] = 0.0f;
+      stream_k<RES>(st, p, rw, nk, wave, lane, true, [&](const StageLds<RES> &s) __attribute__((always_inline)) {
+        compute16<RES>(s, wave, lane, ax);
+      });
       // Element v of accumulator cb is row 4*(lane/16) + v of the pass,
       // column 16*cb + lane%16 of the wave's 32.
       const int q = lane >> 4;
@@ -296,8 +342,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          v16[cb][v] = ax[cb][v] * (gw * gx);  // the merged operand is in units of gx too
+        for (int v = 0; v < 4; ++v) v16[cb][v] = ax[cb][v] * (gw * gx);  // the merged operand is in units of gx too
       if constexpr (EPI == 0) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
@@ -307,16 +352,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
             if (row < mend) store_out(p, row, col0 + 16 * cb + (lane & 15), p.N, v16[cb][v]);
           }
       } else {
-        float *up = reinterpret_cast<float *>(st0.w);  // free after the K loop
+        float *up = reinterpret_cast<float *>(st[0].w);  // free after the K loop
         __syncthreads();
-        if (wave >= 2) {
+        if (wave >= kSW / 2) {
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) up[(((wave - 2) * 2 + cb) * 4 + v) * 64 + lane] = v16[cb][v];
+            for (int v = 0; v < 4; ++v) up[(((wave - kSW / 2) * 2 + cb) * 4 + v) * 64 + lane] = v16[cb][v];
         }
         __syncthreads();
-        if (wave < 2) {
+        if (wave < kSW / 2) {
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -336,17 +381,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
     f32x16 acc_x;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_x[r] = 0.0f;
-    issue<RES>(st0, p, rw, 0, wave, lane);
-    for (int kt = 0; kt < nk; kt += 2) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of step kt has landed in LDS
-      __syncthreads();                // ... and every wave's; step kt-1 is no longer read
-      issue<RES>(st1, p, rw, kt + 1, wave, lane);
-      compute<RES>(st0, wave, lane, acc_x);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (kt + 2 < nk) issue<RES>(st0, p, rw, kt + 2, wave, lane);
-      compute<RES>(st1, wave, lane, acc_x);
-    }
+    stream_k<RES>(st, p, rw, nk, wave, lane, false, [&](const StageLds<RES> &s) __attribute__((always_inline)) {
+      compute<RES>(s, wave, lane, acc_x);
+    });
 
     // Element r of the accumulator is row 8*(r/4) + 4*h + r%4 of the pass,
     // column lane%32 of the wave's 32.
@@ -361,14 +398,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_small(SmallParams p) {
         if (row < mend) store_out(p, row, col, p.N, v[r]);
       }
     } else {
-      float *up = reinterpret_cast<float *>(st0.w);  // 8 KB of stage 0, free after the K loop
+      float *up = reinterpret_cast<float *>(st[0].w);  // 16 KB of stage 0, free after the K loop
       __syncthreads();
-      if (wave >= 2) {
+      if (wave >= kSW / 2) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) up[((wave - 2) * 16 + r) * 64 + lane] = v[r];
+        for (int r = 0; r < 16; ++r) up[((wave - kSW / 2) * 16 + r) * 64 + lane] = v[r];
       }
       __syncthreads();
-      if (wave < 2) {
+      if (wave < kSW / 2) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = pm + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -496,8 +533,8 @@ __global__ __launch_bounds__(256) void k_merge_residual(const uint8_t *__restric
 }  // namespace
 
 bool gemm_use_small(const GemmLaunch &a) {
-  // K in whole pairs of 256-element steps (the K loop is unrolled by two)
-  if (a.mode != 0 || a.K % (2 * kSK) != 0 || a.K > 16384 || a.N % kSBN != 0) return false;
+  // K in whole 256-element steps, N in whole 256-column workgroup tiles
+  if (a.mode != 0 || a.K % kSK != 0 || a.K > 16384 || a.N % kSBN != 0) return false;
   // This kernel adds the RAC correction to the activation operand only (one
   // fp16 operand); the exact form runs on the many-rows kernels.
   if (a.rac_form == QUADS_RAC_FORM_EXACT && a.r_codes != nullptr && a.kpad > 0) return false;
@@ -540,13 +577,13 @@ hipError_t launch_gemm_small(const GemmLaunch &a, const uint16_t *r_dense, hipSt
   p.y = a.y;
   p.y_bf16 = a.y_bf16 ? 1 : 0;
   const bool res = r_dense != nullptr;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.E) * p.n_tiles));
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.E) * p.n_tiles)), block(kSW * 64);
   if (a.epilogue == 0) {
-    if (res) hipLaunchKernelGGL((k_gemm_small<0, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((k_gemm_small<0, false>), grid, dim3(256), 0, stream, p);
+    if (res) hipLaunchKernelGGL((k_gemm_small<0, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_gemm_small<0, false>), grid, block, 0, stream, p);
   } else {
-    if (res) hipLaunchKernelGGL((k_gemm_small<1, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((k_gemm_small<1, false>), grid, dim3(256), 0, stream, p);
+    if (res) hipLaunchKernelGGL((k_gemm_small<1, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_gemm_small<1, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

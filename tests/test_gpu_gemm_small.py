@@ -28,12 +28,14 @@ def _swiglu_tol(y, h_ref):
     return 2.0 ** -8 * np.abs(h_ref) + 2e-3 * ymax * (np.abs(y[:, I:]) + np.abs(y[:, :I]) + 1)
 
 
-@pytest.mark.parametrize("k", [0, 50, 100])
-def test_small_m_grouped(k):
+@pytest.mark.parametrize("k,H", [(0, 256), (50, 256), (100, 256), (50, 768), (50, 2048)])
+def test_small_m_grouped(k, H):
     """Experts with 0, 5, 16, 31, 32, 33, 40 and 70 rows (several 32-row passes,
-    an empty expert), gathered token rows, both epilogues."""
+    an empty expert), gathered token rows, both epilogues; K of 1, 3 and 8
+    256-element steps (the three-stage pipeline with fewer steps than
+    stages, one rotation, several)."""
     rng = np.random.default_rng(91)
-    T, H, I = 100, 256, 128
+    T, I = 100, 128
     counts = [0, 5, 16, 31, 32, 33, 40, 70]
     E = len(counts)
     offs, rt = _ragged_groups(rng, counts, T)
@@ -46,7 +48,7 @@ def test_small_m_grouped(k):
     q, scores = Q.quantize_nvfp4(x, want_scores=True)
     sel, res, nsel = Q.rac_select(x, q, scores, k)
     offs_d, rt_d = torch.from_numpy(offs).cuda(), torch.from_numpy(rt).cuda()
-    log(f"[gemm-small] grouped E={E} R={R} k={k}")
+    log(f"[gemm-small] grouped E={E} R={R} K={H} k={k}")
     y = Q.moe_w4a4_gemm(w_codes=wc, w_scales=wsc, w_gscale=wg, n_seg=2, N=2 * I, K=H, expert_offsets=offs_d,
                         num_rows=R, x=q, res=res if nsel else None, sel_idx=sel, row_token=rt_d)
     _, _, _, we = O.quantize_weights(wgu.f32, 2)

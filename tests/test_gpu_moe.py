@@ -226,3 +226,54 @@ def test_prefill_layer_full_size_sampled_experts():
         err = rel_err(yd[a:b], yr)
         log(f"  down expert {e} rows {b - a}: rel err {err:.2e}")
         assert err <= 1e-3, e
+
+
+def test_prefill_merged_pipeline_full_size_sampled_experts():
+    """The prefill layer's gate_up exactly as the benchmark launches it
+    (16384 tokens, 64 Zipf-routed experts, k=50): quads_rac_select_merged
+    writes the corrected fp16 activation, bit-exact against the oracle's
+    rac_merged_operand on every element, and the grouped GEMM reads it as
+    x_merged on 256 x 256 tiles (MODE 2), with FP32 output and with the
+    SwiGLU epilogue; the largest, smallest and one random non-empty expert
+    are checked against the oracle's float64 extended-K product."""
+    wl = S.moe_prefill()
+    T, H = wl.x.f32.shape
+    E, N2, _ = wl.w_gate_up.f32.shape
+    I = N2 // 2
+    k = wl.k_percent
+    log(f"[moe] prefill merged pipeline full size T={T} E={E} H={H} I={I} k={k}")
+    ids, w, offs, rt, inv = Q.moe_route(torch.from_numpy(wl.logits).cuda(), wl.top)
+    _, _, roffs, rrt, _ = O.route(wl.logits, wl.top)
+    assert np.array_equal(host(offs), roffs) and np.array_equal(host(rt), rrt)
+    R = int(roffs[-1])
+    x = dev_act(wl.x)
+    guc, gus, gug = quantize_weights_gpu(dev_act(wl.w_gate_up), 2)
+    q, sc = Q.quantize_nvfp4(x, want_scores=True)
+    call = Q.SelectCall(x, q, sc, k, merged=True)
+    sel, res, nsel = call()
+    xq = O.quantize_nvfp4(wl.x.f32)
+    xsel, xn = O.rac_select(O.rac_scores(wl.x.f32, xq), k)
+    xr = O.rac_quantize_residual(wl.x.f32, xq, xsel, xn)
+    assert nsel == xn and np.array_equal(host(sel), xsel)
+    want = O.rac_merged_operand(xq, xr, xsel, xn)
+    assert np.array_equal(host(call.merged).view(np.uint16), want.view(np.uint16))
+    args = dict(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
+                x=q, res=res, sel_idx=sel, row_token=rt, x_merged=call.merged, rac_form=Q.RAC_FORM_MERGED)
+    y = host(Q.moe_w4a4_gemm(**args))
+    h = host(Q.moe_w4a4_gemm(epilogue=Q.EPI_SWIGLU, **args).float())
+    xe = O.dequant_exact(xq.codes, xq.scales, xq.g)
+    re = O.dequant_exact(xr.codes, xr.scales, xr.g)
+    cnt = np.diff(roffs)
+    nz = np.flatnonzero(cnt)
+    pick = sorted({int(nz[np.argmax(cnt[nz])]), int(nz[np.argmin(cnt[nz])]),
+                   int(np.random.default_rng(98).choice(nz))})
+    for e in pick:
+        a, b = int(roffs[e]), int(roffs[e + 1])
+        _, _, _, we = O.quantize_weights(wl.w_gate_up.f32[e:e + 1], 2)
+        yr = O.gemm_ref(xe[rrt[a:b]], we[0], re[rrt[a:b]], xsel)
+        err = rel_err(y[a:b], yr)
+        log(f"  expert {e} rows {b - a}: gate_up rel err {err:.2e}")
+        assert err <= 1e-3
+        hr = O.swiglu(yr[:, :I], yr[:, I:])
+        tol = 2.0 ** -8 * np.abs(hr) + 2e-3 * np.abs(yr).max() * (np.abs(yr[:, I:]) + np.abs(yr[:, :I]) + 1)
+        assert (np.abs(h[a:b] - hr) <= tol).all()
