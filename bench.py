@@ -307,7 +307,10 @@ def setup_moe(Q, S, k, decode):
         dom = dict(bound="mfma", dominant_work=f1, dominant_exec=f1x,
                    dominant_kernel=("k_gemm<Cfg<256, 256, 2, 4, 1>, 2, 1, false> (gate_up, SwiGLU, merged RAC operand)"
                                     if mr else "k_gemm<Cfg<256, 256, 2, 4, 1>, 0, 1, true> (gate_up, SwiGLU, extended K)"))
+    tname = (f"k_gemm_small_gate_up_moe_decode_k{k}_traffic.txt" if decode else
+             f"k_gemm_gate_up_moe_prefill_k{k}_traffic.txt")
     return dict(stages=stages, plain=plain, tokens=T, flops=f1 + f2, dominant="gate_up", config=cfg,
+                traffic_summary=os.path.join(ROOT, "profiles", tname) if mr else None,
                 cpu_baseline=lambda: cpu_baseline_moe(wl, k, 8 if decode else 16), weight_bytes=wbytes,
                 stage_bytes=sb, plain_stage_bytes={"quantize_x": T * H * 2.5625, "quantize_h": R * I * 2.5625},
                 **dom)
@@ -662,6 +665,19 @@ def _roofline(wl, dom_ms, traffic=None, tinfo=None):
     return r
 
 
+def _traffic(wl):
+    """(HBM bytes per launch of the dominant kernel, note) from its committed
+    rocprofv3 traffic summary, or (None, reason)."""
+    from fp4_quantized_moe_amd.profiling import read_traffic
+    if not wl.get("traffic_summary"):
+        return None, "no traffic summary for this workload"
+    traffic, tinfo = read_traffic(wl["traffic_summary"])
+    if traffic is not None:
+        tinfo = (f"HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain copy), "
+                 f"{os.path.relpath(wl['traffic_summary'], ROOT)}")
+    return traffic, tinfo
+
+
 def _cpu(wl, note_default):
     rate, cpu_s, sample = wl["cpu_baseline"]()
     return {"value": rate, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle", "sample": sample,
@@ -679,9 +695,10 @@ def measure_layer(wl, args):
     ms = secs * 1e3 / args.steps
     warm = stage_times(wl["stages"])
     cold = cold_stage_times(wl["stages"], list(wl["stage_bytes"]))
+    traffic, tinfo = _traffic(wl)
     blk = {"config": wl["config"], "ms_per_step": ms, "tokens_per_s": wl["tokens"] * args.steps / secs,
            "tflops_step_algorithmic": wl["flops"] / (ms * 1e-3) / 1e12, "stages_ms": warm,
-           "stage_bandwidth": _bw(wl["stage_bytes"], warm, cold), "roofline": _roofline(wl, dom_ms)}
+           "stage_bandwidth": _bw(wl["stage_bytes"], warm, cold), "roofline": _roofline(wl, dom_ms, traffic, tinfo)}
     if wl.get("layer_floor_bytes"):
         fl = wl["layer_floor_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
         blk["hbm_floor"] = {"weight_bytes": wl["layer_floor_bytes"], "floor_ms": fl, "frac_of_step": fl / ms}
@@ -765,13 +782,7 @@ def main():
         dom_ms = per[wl["dominant_stage_for_roofline"]]
     ms = secs * 1e3 / args.steps
     tokens_per_s = wl["tokens"] * args.steps / secs
-    from fp4_quantized_moe_amd.profiling import read_traffic
-    traffic, tinfo = (None, "no traffic summary for this workload")
-    if wl.get("traffic_summary"):
-        traffic, tinfo = read_traffic(wl["traffic_summary"])
-        if traffic is not None:
-            tinfo = (f"HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a plain copy), "
-                     f"{os.path.relpath(wl['traffic_summary'], ROOT)}")
+    traffic, tinfo = _traffic(wl)
     out = {
         "metric": METRIC,
         "value": tokens_per_s,

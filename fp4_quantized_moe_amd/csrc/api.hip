@@ -273,6 +273,11 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
       g.sel_idx = a->sel_idx;
       g.kpad = a->kpad;
       g.x_merged = static_cast<const uint16_t *>(a->x_merged);
+      // The merge step stages one row of K floats plus the mask in LDS.
+      if (a->rac_form == QUADS_RAC_FORM_MERGED && a->x_merged == nullptr &&
+          quads::rac_rows_per_group(a->K, a->kpad, true) < 1)
+        return fail(QUADS_ERR_SHAPE, "gemm: K %lld too large for the merge step (pass x_merged or rac_form EXACT)",
+                    (long long)a->K);
     }
   } else if (g.mode == 3) {
     if (!a->x_bf16 || !a->w_codes || !a->w_scales || !a->w_gscale)

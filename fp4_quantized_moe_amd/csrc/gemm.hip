@@ -1403,7 +1403,7 @@ void launch_cfg(const GemmLaunch &a, const Params &p, int g, bool res, hipStream
 bool use_merged(const GemmLaunch &a) {
   if (a.mode != 0 || a.r_codes == nullptr || a.kpad == 0 || gemm_use_small(a)) return false;
   if (a.x_merged != nullptr || a.rac_form == QUADS_RAC_FORM_MERGED) return true;
-  if (a.rac_form == QUADS_RAC_FORM_EXACT) return false;
+  if (a.rac_form == QUADS_RAC_FORM_EXACT || rac_rows_per_group(a.K, a.kpad, true) < 1) return false;
   const TileCfg c = pick_cfg(a);
   return c == kL || c == kP;
 }

@@ -7,9 +7,10 @@
 // summary section 2.2-B adds the second-pass residual of the selected
 // channels to the quantized activation before the GEMM
 // (Y = W_q (X_q + M * dX_q)).  Here that sum is formed once per activation
-// element (k_merge_residual), in units of the activation's tensor scale:
+// element, in units of the activation's tensor scale, by the RAC row kernel
+// (from the residual codes when the caller passes the residual itself):
 //
-//   A[t, k] = fp16( X'[t, k] + (gr / gx) * R'[t, j] )   (k = sel_j; X' alone elsewhere)
+//   A[t, k] = fp16( X'[t, k] + fl32(R'[t, j] * fl32(gr / gx)) )   (k = sel_j; X' alone elsewhere)
 //   Y[i, n] = gw * gx * sum_k W'[n, k] A[t(i), k]
 //
 // X' and R' are the exact e2m1 * e4m3 values (no tensor scale).  The
@@ -434,102 +435,6 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
 // 8 channels.
 // Loads for one 8-channel chunk, issued before any of the chunks it is
 // batched with is computed.
-struct MergeChunk {
-  uint32_t xw, rw0, rw1;
-  uint8_t xs, rs0, rs1;
-  int16_t jv[8];
-  int jf, base;
-};
-
-__global__ __launch_bounds__(256) void k_merge_residual(const uint8_t *__restrict__ x_codes,
-                                                        const uint8_t *__restrict__ x_scales,
-                                                        const float *__restrict__ x_g,
-                                                        const uint8_t *__restrict__ r_codes,
-                                                        const uint8_t *__restrict__ r_scales,
-                                                        const float *__restrict__ r_g, int64_t rows, int K, int kpad,
-                                                        const int32_t *__restrict__ sel, uint16_t *__restrict__ out,
-                                                        int rows_per_wg) {
-  extern __shared__ int16_t inv[];
-  for (int k = threadIdx.x; k < K; k += 256) inv[k] = -1;
-  __syncthreads();
-  for (int j = threadIdx.x; j < kpad; j += 256) {
-    const int c = sel[j];
-    if (j == 0 || c != 0) inv[c] = static_cast<int16_t>(j);
-  }
-  __syncthreads();
-  const float ratio = *r_g / *x_g;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
-  const int64_t r1 = min(r0 + rows_per_wg, rows);
-  const int chunks = K / 8, rb = kpad / 2, sb = kpad / 16;  // residual code / scale bytes per row
-  const int64_t total = (r1 - r0) * chunks;
-  constexpr int U = 4;  // chunks per thread whose loads are in flight together
-  for (int64_t t0 = threadIdx.x; t0 < total; t0 += 256 * U) {
-    MergeChunk c[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = min(t0 + 256 * u, total - 1);  // past the end: re-read the last chunk, not stored
-      const int64_t row = r0 + t / chunks;
-      const int k0 = static_cast<int>(t % chunks) * 8;
-      c[u].xw = reinterpret_cast<const uint32_t *>(x_codes + row * (K / 2))[k0 / 8];
-      c[u].xs = x_scales[row * (K / 16) + k0 / 16];
-      const uint4 iv = *reinterpret_cast<const uint4 *>(inv + k0);
-      const uint32_t w[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[u].jv[2 * q] = static_cast<int16_t>(w[q] & 0xFFFFu);
-        c[u].jv[2 * q + 1] = static_cast<int16_t>(w[q] >> 16);
-      }
-      int jf = kpad;  // first (smallest) residual index among the chunk's selected channels
-#pragma unroll
-      for (int q = 7; q >= 0; --q)
-        if (c[u].jv[q] >= 0) jf = c[u].jv[q];
-      c[u].jf = jf;
-      // Codes of j in [jf, jf + 8): bytes [jf/2, jf/2 + 4] inside the aligned
-      // window [base, base + 8); when base is the row's last word those bytes
-      // all lie in it and the clamped second word is not used.  A chunk with
-      // no selected channel reads the row's first word and scale (unused).
-      const int jc = min(jf, kpad - 1);
-      const int base = (jc >> 1) & ~3;
-      c[u].base = base;
-      const uint8_t *rc = r_codes + row * rb;
-      c[u].rw0 = *reinterpret_cast<const uint32_t *>(rc + base);
-      c[u].rw1 = *reinterpret_cast<const uint32_t *>(rc + min(base + 4, rb - 4));
-      const uint8_t *rs = r_scales + row * sb;
-      c[u].rs0 = rs[jc >> 4];
-      c[u].rs1 = rs[min((jc >> 4) + 1, sb - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = t0 + 256 * u;
-      if (t >= total) break;
-      const int64_t row = r0 + t / chunks;
-      const int k0 = static_cast<int>(t % chunks) * 8;
-      const float xs = e4m3_to_f32(c[u].xs);
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = dequant_code((c[u].xw >> (4 * q)) & 0xFu, xs);
-      if (c[u].jf < kpad) {
-        const uint64_t win = static_cast<uint64_t>(c[u].rw0) | (static_cast<uint64_t>(c[u].rw1) << 32);
-        const int s0 = c[u].jf >> 4;
-        const float d0 = e4m3_to_f32(c[u].rs0), d1 = e4m3_to_f32(c[u].rs1);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int j = c[u].jv[q];
-          if (j >= 0) {
-            const uint32_t code = static_cast<uint32_t>(win >> (4 * (j - 2 * c[u].base))) & 0xFu;
-            v[q] += dequant_code(code, (j >> 4) == s0 ? d0 : d1) * ratio;
-          }
-        }
-      }
-      uint32_t hv[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) hv[q] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[q]));
-      reinterpret_cast<uint4 *>(out + row * K)[k0 / 8] =
-          make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
-    }
-  }
-}
-
 }  // namespace
 
 bool gemm_use_small(const GemmLaunch &a) {
@@ -547,14 +452,8 @@ size_t gemm_small_res_bytes(const GemmLaunch &a) {
 
 hipError_t launch_gemm_small_prepare(const GemmLaunch &a, uint16_t *r_dense, hipStream_t stream) {
   if (a.r_codes == nullptr || a.kpad == 0 || a.act_rows == 0) return hipSuccess;
-  // One row per workgroup up to 4096 rows, more rows beyond (the inverse map
-  // is rebuilt by every workgroup: K/256 + kpad/256 LDS stores per thread).
-  const int rows_per_wg = static_cast<int>((a.act_rows + 4095) / 4096);
-  const int64_t grid = (a.act_rows + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(k_merge_residual, dim3(grid), dim3(256), a.K * sizeof(int16_t), stream, a.x_codes,
-                     a.x_scales, a.x_g, a.r_codes, a.r_scales, a.r_g, a.act_rows, static_cast<int>(a.K),
-                     static_cast<int>(a.kpad), a.sel_idx, r_dense, rows_per_wg);
-  return hipGetLastError();
+  return launch_rac_merge_codes(a.x_codes, a.x_scales, a.x_g, a.r_codes, a.r_scales, a.r_g, a.act_rows, a.K, a.kpad,
+                                a.sel_idx, r_dense, stream);
 }
 
 hipError_t launch_gemm_small(const GemmLaunch &a, const uint16_t *r_dense, hipStream_t stream) {

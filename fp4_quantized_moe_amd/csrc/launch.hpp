@@ -53,9 +53,17 @@ struct RacLaunch {
   float *r_gscale;
   uint16_t *merged;  // [rows, cols] fp16 RAC-merged activation, or null
 };
-// Rows of dx staged per pass by the RAC kernel (< 1: the shape does not fit in LDS).
+// Rows per group of the RAC row kernel (< 1: the shape does not fit in LDS).
 int rac_rows_per_group(int64_t cols, int64_t kpad, bool merged = false);
 hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream);
+// The RAC-merged fp16 operand [rows, cols] from the NVFP4 codes of the
+// activation and of its residual (the same row kernel and merge arithmetic
+// as quads_rac_select_merged, reading R' instead of computing it); sel_idx
+// [kpad] ascending with pad entries 0.
+hipError_t launch_rac_merge_codes(const uint8_t *x_codes, const uint8_t *x_scales, const float *x_g,
+                                  const uint8_t *r_codes, const uint8_t *r_scales, const float *r_g, int64_t rows,
+                                  int64_t cols, int64_t kpad, const int32_t *sel_idx, uint16_t *merged,
+                                  hipStream_t stream);
 
 // ---- gemm.hip --------------------------------------------------------------
 struct GemmLaunch {

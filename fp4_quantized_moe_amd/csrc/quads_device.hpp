@@ -204,6 +204,54 @@ __device__ __forceinline__ void dequant8(uint32_t w, float d, float *dq) {
   dequant_byte<3>(w, d, dq);
 }
 
+// The 16 values of a block's codes (codes.x: elements 0-7, codes.y: 8-15)
+// times d >= 0, exact in FP32, with the code's sign also on zeros: the
+// negative-zero code gives -0 (the hardware conversion alone gives +0).
+template <int B>
+__device__ __forceinline__ void dequant_byte_signed(uint32_t w, float d, float *v) {
+  const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t sign = (w << (28 - 4 * (2 * B + u))) & 0x80000000u;  // bit 3 of nibble 2B+u
+    v[2 * B + u] = __uint_as_float(__float_as_uint(e[u] * d) | sign);
+  }
+}
+
+__device__ __forceinline__ void dequant16_signed(uint2 codes, float d, float (&v)[16]) {
+  dequant_byte_signed<0>(codes.x, d, v);
+  dequant_byte_signed<1>(codes.x, d, v);
+  dequant_byte_signed<2>(codes.x, d, v);
+  dequant_byte_signed<3>(codes.x, d, v);
+  dequant_byte_signed<0>(codes.y, d, v + 8);
+  dequant_byte_signed<1>(codes.y, d, v + 8);
+  dequant_byte_signed<2>(codes.y, d, v + 8);
+  dequant_byte_signed<3>(codes.y, d, v + 8);
+}
+
+// One 16-element block of the RAC-merged fp16 operand (units of the
+// activation's tensor scale g_x): element i is X'_i, or, where bit i of
+// `sel` is set, fl32(X'_i + cor_i) with cor_i = fl32(R' * fl32(g_r / g_x))
+// its channel's correction; then one rounding to fp16 (RNE).  X' and R' are
+// the exact e2m1 * e4m3 values.  Element 0 lands in the low half of lo.x.
+__device__ __forceinline__ void merged_block16(const float (&xv)[16], const float (&cor)[16], uint32_t sel,
+                                               uint4 &lo, uint4 &hi) {
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = 2 * i + u;
+      const float s = xv[e] + cor[e];
+      v[u] = (sel >> e) & 1u ? s : xv[e];
+    }
+    h[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[0]))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[1]))) << 16);
+  }
+  lo = make_uint4(h[0], h[1], h[2], h[3]);
+  hi = make_uint4(h[4], h[5], h[6], h[7]);
+}
+
 // Quantize 16 values with tensor scale g: the block scale from their amax,
 // the quotients fl32(x / d), their E2M1 codes, and (if `dq_out` is non-null)
 // the dequantized values.

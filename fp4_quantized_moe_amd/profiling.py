@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "k_gemm_small": ["csrc/gemm_small.hip", "csrc/fp4_mfma.hpp", "csrc/quads_device.hpp", "csrc/launch.hpp"],
     "k_rac": ["csrc/rac.hip", "csrc/quads_device.hpp", "csrc/launch.hpp"],
     "k_quantize": ["csrc/quantize.hip", "csrc/quads_device.hpp", "csrc/launch.hpp"],
+    "k_combine": ["csrc/route.hip", "csrc/launch.hpp"],
 }
 
 

@@ -141,11 +141,9 @@ quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, qua
  * x / dt: the activation that produced xq (batch 1); scores from
  * quads_quantize_nvfp4(QUADS_WANT_SCORES).  res.cols must equal kpad; with
  * k such that kpad == 0 only res.gscale[0] = 1 is written.
- * Channel count limit: cols <= 16384, and a workgroup's shared memory must
- * hold the mask and one row of work: 4*kpad + 4*cols <= 65472 bytes here,
- * 8*kpad + 2*cols <= 65472 for quads_rac_select_merged (about cols <= 10912
- * at k = 50%); larger shapes return QUADS_ERR_SHAPE before anything is
- * enqueued.
+ * Channel count limit: cols <= 16384 (larger shapes return QUADS_ERR_SHAPE
+ * before anything is enqueued).  Two kernels are enqueued on `stream`: the
+ * mask (one workgroup), then the rows.
  * ------------------------------------------------------------------------- */
 size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols);
 quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
@@ -195,9 +193,13 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  *                          prepare step unless x_merged is given), so each
  *                          corrected element is rounded once more (relative
  *                          2^-11), and the GEMM contracts over K alone.
+ *                          The prepare step's merge holds a row of K floats
+ *                          and the mask on chip: 4*kpad + 4*K + K/8 <=
+ *                          163584 bytes (any K <= 16384), else
+ *                          QUADS_ERR_SHAPE (AUTO then takes EXACT).
  *   QUADS_RAC_FORM_AUTO    (0, the default) MERGED when x_merged is given,
  *                          for few rows per expert (num_rows <= 32 *
- *                          num_experts with K % 512 == 0, K <= 16384 and
+ *                          num_experts with K % 256 == 0, K <= 16384 and
  *                          N % 128 == 0: the decode shape) and where the
  *                          tile choice gives 256 x 256 tiles (large grouped
  *                          shapes); EXACT otherwise.  The choice depends

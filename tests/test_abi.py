@@ -76,12 +76,10 @@ def test_rac_select_validation(L):
     assert L.quads_rac_select(dummy, 0, None, dummy, 50, dummy, _nv(8, 128), None, 0, None) == -1
     st = L.quads_rac_select(ctypes.c_void_p(40), 0, ctypes.byref(xq), dummy, 50, dummy, _nv(8, 128), None, 0, None)
     assert st == -1 and b"aligned" in L.quads_last_error()
-    # the LDS budget: cols * 4 + kpad * 4 must stay under ~63 KiB
-    wide = _nv(8, 16384)
+    # channel limit 16384 (a row of FP32 residuals and the mask in one workgroup's LDS), both forms
+    wide = _nv(8, 16400)
     assert L.quads_rac_select(dummy, 0, ctypes.byref(wide), dummy, 0, dummy, _nv(8, 0), None, 0, None) == -2
-    # the merged variant's budget: 8 * kpad + 2 * cols (12288 channels at k=50%: 73728 bytes)
-    w12 = _nv(8, 12288)
-    assert L.quads_rac_select_merged(dummy, 0, ctypes.byref(w12), dummy, 50, dummy, _nv(8, 6144), dummy,
+    assert L.quads_rac_select_merged(dummy, 0, ctypes.byref(wide), dummy, 50, dummy, _nv(8, 8208), dummy,
                                      None, 0, None) == -2
 
 
@@ -143,6 +141,13 @@ def test_gemm_rac_form_field(L):
     assert auto == exact  # 128x128 DMA-staged tiles: the exact form by default
     given = L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(rac_form=0, x_merged=16, **res)))
     assert given < 4096  # the caller's merged operand: only the tile list
+    # the merge step holds a row of K floats and the mask on chip: K = 32768 does
+    # not fit, so MERGED without x_merged is rejected and AUTO keeps the exact form
+    big = dict(num_rows=64, act_rows=64, N=128, K=32768, r_codes=16, r_scales=16, r_gscale=16, sel_idx=16, kpad=16384)
+    a = _gemm_args(rac_form=2, **big)
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(a), None) == -2 and b"merge step" in L.quads_last_error()
+    assert L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(rac_form=0, **big))) >= 128 * 16384 * 2
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(_gemm_args(rac_form=2, x_merged=16, **big)), None) == -3
 
 
 def test_qdq_route_combine_validation(L):

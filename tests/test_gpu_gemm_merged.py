@@ -106,7 +106,9 @@ def test_grouped_swiglu_merged():
 @pytest.mark.parametrize("case", [("bf16", 300, 2048, 50), ("bf16", 300, 2048, 100), ("bf16", 77, 768, 25),
                                   ("f32", 64, 256, 50), ("bf16", 40, 512, 0),
                                   # more than 1024 four-row groups: workgroups walk several groups
-                                  ("bf16", 6001, 768, 50), ("bf16", 5000, 2048, 25)])
+                                  ("bf16", 6001, 768, 50), ("bf16", 5000, 2048, 25),
+                                  # wide rows: four load slots, one row per group, LDS beyond 64 KiB
+                                  ("bf16", 5, 16384, 100), ("f32", 7, 8208, 50), ("bf16", 33, 9984, 25)])
 def test_rac_select_merged_bit_exact(case):
     """quads_rac_select_merged's fp16 operand equals the oracle's
     rac_merged_operand bit for bit (same fp32 operations, one rounding); the
@@ -194,10 +196,46 @@ def test_expert_gemm_full_size_merged_pipeline(k):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("M,K,k", [(6001, 768, 50), (5000, 2048, 25)])
+@pytest.mark.parametrize("K", [2048, 8448])
+def test_gemm_merge_step_operand_bit_exact(K):
+    """The GEMM's own merge step (residual handed over, rac_form MERGED, no
+    x_merged) builds the operand with the same row kernel as
+    quads_rac_select_merged: its copy in the workspace (after the tile list,
+    at byte align256(4 * (E + 1)), [act_rows, K] fp16) equals the oracle's
+    rac_merged_operand bit for bit, for rows of at most 512 blocks and wider
+    ones (K = 8448: four load slots per thread, one row per group), and Y
+    is within the bar.  Decode-shaped counts: the few-rows kernel."""
+    counts = [16, 9, 0, 31, 16, 1, 12, 16]
+    T = 120
+    xa, wa, offs, rt = _grouped(611 + K, counts, T, K, 256)
+    log(f"[gemm-rac] merge step K={K} rows={T} k=50")
+    x = dev_act(xa)
+    E, N, _ = wa.f32.shape
+    wc, ws_, wg = quantize_weights_gpu(dev_act(wa), 1)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    sel, res, nsel = Q.rac_select(x, q, scores, 50)
+    call = Q.GemmCall(w_codes=wc, w_scales=ws_, w_gscale=wg, N=N, K=K, expert_offsets=torch.from_numpy(offs).cuda(),
+                      num_rows=int(offs[-1]), x=q, res=res, sel_idx=sel, row_token=torch.from_numpy(rt).cuda(),
+                      rac_form=Q.RAC_FORM_MERGED)
+    call.prepare()
+    torch.cuda.synchronize()
+    off = (4 * (E + 1) + 255) // 256 * 256
+    got = call.ws[off:off + T * K * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(T, K)
+    oq = O.quantize_nvfp4(xa.f32)
+    osel, on = O.rac_select(O.rac_scores(xa.f32, oq), 50)
+    orr = O.rac_quantize_residual(xa.f32, oq, osel, on)
+    want = O.rac_merged_operand(oq, orr, osel, on)
+    assert np.array_equal(got, want.view(np.uint16)), np.argwhere(got != want.view(np.uint16))[:5]
+    call.run()
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    _check(host(call.y), O.rac_linear(xa.f32, we, 50, rt, offs)["y"], "merged")
+
+
+@pytest.mark.parametrize("M,K,k", [(6001, 768, 50), (5000, 2048, 25), (3, 16384, 100), (9, 8208, 50)])
 def test_rac_select_many_rows_bit_exact(M, K, k):
-    """quads_rac_select (no merged operand) with more rows than 1024 groups of
-    four: mask, residual codes, scales and g_r bit-exact against the oracle."""
+    """quads_rac_select (no merged operand) with more rows than 1024 row
+    groups, and on the widest rows: mask, residual codes, scales and g_r
+    bit-exact against the oracle."""
     log(f"[rac] many rows M={M} K={K} k={k}")
     rng = np.random.default_rng(606 + M)
     xa = S.activation(rng, M, K, max(1, K // 100), 30.0, bf16=True)
