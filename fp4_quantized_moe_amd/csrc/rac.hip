@@ -40,13 +40,30 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
+// Wave-wide inclusive scans with DPP moves (no LDS round trip): shifts by
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of row r
+// is added to row r + 1 (row_bcast:15) and lane 31 to rows 2 and 3
+// (row_bcast:31).  Lanes whose source is outside the row keep 0, the
+// identity of both operations here (unsigned sum and max).
+template <bool MAX>
+__device__ __forceinline__ uint32_t dpp_op(uint32_t a, uint32_t b) {
+  return MAX ? (a > b ? a : b) : a + b;
+}
+
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
   return v;
+}
+
+// The value of lane 63 (after a scan: the wave total), as a uniform value.
+__device__ __forceinline__ uint32_t last_lane(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // Per-thread channel runs of the mask search: thread t owns channels
@@ -63,10 +80,8 @@ __device__ __forceinline__ void block_sum_and_scan(uint32_t v, uint32_t w, uint3
                                                    uint32_t &w_before) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int W = kThreads / 64;
-  const uint32_t w_incl = wave_incl_scan(w, lane);
-  uint32_t vs = v;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) vs += static_cast<uint32_t>(__shfl_xor(static_cast<int>(vs), off));
+  const uint32_t w_incl = wave_scan<false>(w);
+  const uint32_t vs = last_lane(wave_scan<false>(v));
   if (lane == 63) {
     slot[wave] = vs;
     slot[W + wave] = w_incl;
@@ -107,13 +122,8 @@ __device__ __forceinline__ uint32_t radix_threshold(const Keys<PER> &ks, int n_r
     // lane l holds bins 4l..4l+3: suffix sums within the lane, then over lanes
     const uint4 b = reinterpret_cast<const uint4 *>(h)[lane];
     const uint32_t s3 = b.w, s2 = b.z + s3, s1 = b.y + s2, s0 = b.x + s1;
-    uint32_t t = s0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t u = static_cast<uint32_t>(__shfl_down(static_cast<int>(t), off));
-      if (lane + off < 64) t += u;
-    }
-    const uint32_t above = t - s0;  // keys in the bins above this lane's
+    const uint32_t incl_lanes = wave_scan<false>(s0);  // lanes 0..l
+    const uint32_t above = last_lane(incl_lanes) - incl_lanes;  // keys in the bins above this lane's
     const uint32_t incl[4] = {above + s0, above + s1, above + s2, above + s3};
     const uint32_t cnt[4] = {b.x, b.y, b.z, b.w};
     int dsel = -1;
@@ -125,10 +135,10 @@ __device__ __forceinline__ uint32_t radix_threshold(const Keys<PER> &ks, int n_r
         excl = incl[q] - cnt[q];
         c = cnt[q];
       }
-    const int src = __ffsll(static_cast<unsigned long long>(__ballot(dsel >= 0))) - 1;
-    const uint32_t d = static_cast<uint32_t>(__shfl(dsel, src));
-    need -= static_cast<uint32_t>(__shfl(static_cast<int>(excl), src));
-    c = static_cast<uint32_t>(__shfl(static_cast<int>(c), src));
+    const int src = (__ffsll(static_cast<unsigned long long>(__ballot(dsel >= 0))) - 1) & 63;
+    const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(dsel, src)) & 255u;
+    need -= static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(excl), src));
+    c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c), src));
     prefix = (prefix << 8) | d;
     if (c == need) return prefix << shift;
   }
@@ -176,7 +186,7 @@ __device__ void block_select(const Keys<PER> &ks, int n_real, int nsel, uint32_t
     const bool eq = ks.k[i] == T;
     const bool kk = ks.k[i] > T || (eq && e < need_eq);
     e += eq;
-    if (kk) sel_out[pos] = c0 + i;
+    if (kk && pos < static_cast<uint32_t>(nsel)) sel_out[pos] = c0 + i;
     pos += kk;
   }
 }
@@ -213,8 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_rac_mask(const uint32_t *scores, i
   uint32_t mx = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) mx = max(mx, ks.k[i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
+  mx = last_lane(wave_scan<true>(mx));
   if ((tid & 63) == 0) slots[4 * (kThreads / 64) + (tid >> 6)] = mx;
   __syncthreads();
   uint32_t mx_total = 0;
@@ -246,10 +255,20 @@ __device__ __forceinline__ void load_raw(RawBlock<BF16> &r, const void *x, const
   r.scale = scales[blk_global];
 }
 
+// Dense LDS rows hold each 16-element block as four 16-byte chunks, chunk q
+// of the row's block cb at position q ^ ((cb >> 2) & 3): consecutive lanes,
+// which take consecutive blocks, then spread a chunk access over all banks.
+__device__ __forceinline__ int chunk_pos(int cblk, int q) { return q ^ ((cblk >> 2) & 3); }
+
+// Float offset of channel c inside its dense LDS row (0 only for c == 0).
+__device__ __forceinline__ int chan_offset(int c) {
+  return (c & ~15) + chunk_pos(c >> 4, (c >> 2) & 3) * 4 + (c & 3);
+}
+
 // dx = x - dq for one block (the quantizer's FP32 operations: dq = level * d
-// with d = dec(scale) * g), stored as 16 floats.
+// with d = dec(scale) * g), stored as block cblk of the row at `row`.
 template <bool BF16>
-__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *dst) {
+__device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, float *row, int cblk) {
   float v[16];
   if constexpr (BF16) {
     const uint32_t w[8] = {r.x[0].x, r.x[0].y, r.x[0].z, r.x[0].w, r.x[1].x, r.x[1].y, r.x[1].z, r.x[1].w};
@@ -271,10 +290,10 @@ __device__ __forceinline__ void store_dx(const RawBlock<BF16> &r, float gx, floa
   const float d = e4m3_to_f32(r.scale) * gx;
   dequant8(r.codes.x, d, dq);
   dequant8(r.codes.y, d, dq + 8);
-  float4 *o = reinterpret_cast<float4 *>(dst);
+  float4 *o = reinterpret_cast<float4 *>(row + cblk * 16);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    o[q] = make_float4(v[4 * q] - dq[4 * q], v[4 * q + 1] - dq[4 * q + 1], v[4 * q + 2] - dq[4 * q + 2],
+    o[chunk_pos(cblk, q)] = make_float4(v[4 * q] - dq[4 * q], v[4 * q + 1] - dq[4 * q + 1], v[4 * q + 2] - dq[4 * q + 2],
                        v[4 * q + 3] - dq[4 * q + 3]);
 }
 
@@ -305,12 +324,14 @@ struct RowsArgs {
 // Mask bitmap words (one bit per channel), rounded up to 16 bytes.
 __host__ __device__ constexpr int bitmap_words(int64_t K) { return static_cast<int>((K + 127) / 128 * 4); }
 
-// LDS: sel[kpad] uint16 | bitmap (merged operand only) | dense rows [rb][K]
-// fp32 (dx, and after b the corrections on the selected channels).  A row
-// group has at most SLOTS * kThreads blocks.  Mask entry j is a real channel
-// when j == 0 or sel[j] != 0 (nsel >= 1 whenever kpad > 0, the real entries
-// ascend and the pads are 0); an entry >= K (possible only in a caller's
-// mask handed to the GEMM) counts as a pad, so no LDS access leaves the rows.
+// LDS: sel[kpad] uint16 (each mask entry's offset in a dense row) | bitmap
+// (merged operand only) | dense rows [rb][K] fp32 (dx, and after b the
+// corrections on the selected channels).  A row group has at most SLOTS *
+// kThreads blocks.  The real mask entries are the first n_real: entry 0, and
+// every later entry up to the last nonzero one (nsel >= 1 whenever kpad > 0,
+// the real entries ascend and the pads are 0).  An entry >= K (possible only
+// in a caller's mask handed to the GEMM) is read as channel 0, so no LDS
+// access leaves the rows.
 template <bool BF16, int MODE, int SLOTS>
 __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
   constexpr bool kX = MODE != kFromCodes;    // reads x and computes the residual
@@ -338,15 +359,24 @@ __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
   };
   issue(r_begin);
 
-  for (int j = tid; j < kpad; j += kThreads) sel[j] = static_cast<uint16_t>(p.sel[j]);  // < K <= 16384
-  if constexpr (kOut) {
+  __shared__ int s_nreal;
+  if (tid == 0) s_nreal = 1;
+  if constexpr (kOut)
     for (int w = tid; w < bitmap_words(K); w += kThreads) bits[w] = 0;
-    __syncthreads();
-    for (int j = tid; j < kpad; j += kThreads) {
-      const int c = sel[j];
-      if ((j == 0 || c != 0) && c < K) atomicOr(&bits[c >> 5], 1u << (c & 31));
-    }
+  __syncthreads();
+  uint32_t last = 0;  // 1 + this thread's last nonzero entry
+  for (int j = tid; j < kpad; j += kThreads) {
+    int c = p.sel[j];
+    c = c >= 0 && c < K ? c : 0;
+    sel[j] = static_cast<uint16_t>(chan_offset(c));  // < K <= 16384
+    if (c != 0) last = j + 1;
+    if constexpr (kOut)
+      if (j == 0 || c != 0) atomicOr(&bits[c >> 5], 1u << (c & 31));
   }
+  last = last_lane(wave_scan<true>(last));
+  if ((tid & 63) == 0 && last > 1) atomicMax(&s_nreal, static_cast<int>(last));
+  __syncthreads();
+  const int n_real = s_nreal;
   // (sel is read in b after at least one barrier; the bitmap in c after the
   // barrier that ends b.)
   const float gx = *p.x_g;
@@ -366,7 +396,10 @@ __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
       if (j * kThreads < nb && b < nb) {
         kc[j] = raw[j].codes;
         ksc[j] = raw[j].scale;
-        if constexpr (kX) store_dx<BF16>(raw[j], gx, region + b * 16);  // row rr = b / cb at rr * K
+        if constexpr (kX) {
+          const int rr = b / cb;
+          store_dx<BF16>(raw[j], gx, region + rr * K, b - rr * cb);
+        }
       }
     }
     if (r0 + rb < r_stop) issue(r0 + rb);
@@ -376,22 +409,20 @@ __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
       const int rr = t / nblk, jb = t - rr * nblk;
       const int64_t row = r0 + rr;
       float *src = region + rr * K;
-      // the block's 16 channel indices, two per word
+      // the block's 16 channel offsets, two per word
       const uint4 s0 = reinterpret_cast<const uint4 *>(sel + jb * 16)[0];
       const uint4 s1 = reinterpret_cast<const uint4 *>(sel + jb * 16)[1];
       const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      auto idx = [&](int i) { return static_cast<int>((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); };
-      uint32_t real = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        real |= static_cast<uint32_t>((jb * 16 + i == 0 || idx(i) != 0) && idx(i) < K) << i;
+      auto off = [&](int i) { return static_cast<int>((sw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); };
+      const int nr16 = min(max(n_real - jb * 16, 0), 16);
+      const uint32_t real = (1u << nr16) - 1u;  // entries jb*16 + i < n_real
       uint2 rcodes;
       uint32_t rscale;
       if constexpr (kX) {
         float g16[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float v = src[(real >> i) & 1u ? idx(i) : 0];  // pads are zeroed
+          const float v = src[off(i)];  // pads (offset 0) are zeroed
           g16[i] = (real >> i) & 1u ? v : 0.0f;
         }
         const BlockQ q = quantize_block16(g16, tsr, nullptr);
@@ -408,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
         dequant16_signed(rcodes, e4m3_to_f32(rscale), rv);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if ((real >> i) & 1u) src[idx(i)] = rv[i] * ratio;
+          if ((real >> i) & 1u) src[off(i)] = rv[i] * ratio;
       }
     }
     if constexpr (kOut) {
@@ -418,13 +449,13 @@ __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
       for (int j = 0; j < SLOTS; ++j) {
         const int b = tid + j * kThreads;
         if (j * kThreads < nb && b < nb) {
-          const int c0 = (b % cb) * 16;
+          const int cblk = b % cb, c0 = cblk * 16;
           const uint32_t m = (bits[c0 >> 5] >> (c0 & 16)) & 0xFFFFu;
           float cor[16], xv[16];
-          const float4 *cp = reinterpret_cast<const float4 *>(region + b * 16);
+          const float4 *cp = reinterpret_cast<const float4 *>(region + b * 16);  // row b / cb, block cblk
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 v = cp[q];
+            const float4 v = cp[chunk_pos(cblk, q)];
             cor[4 * q] = v.x;
             cor[4 * q + 1] = v.y;
             cor[4 * q + 2] = v.z;
@@ -462,6 +493,11 @@ hipError_t allow_lds(const void *fn, size_t bytes) {
 template <bool BF16, int MODE, int SLOTS>
 hipError_t launch_rows_s(RowsArgs p, hipStream_t stream) {
   const bool out = MODE != kResidual;
+  // Few rows (decode-sized calls): smaller groups, so that the launch still
+  // spreads over every CU and each workgroup's chain of loads, barriers and
+  // stores is short.
+  const int64_t spread = (p.rows + 255) / 256;
+  if (spread < p.rb) p.rb = static_cast<int>(std::max<int64_t>(1, spread));
   int64_t n_wg = (p.rows + p.rb - 1) / p.rb;
   p.rows_per_wg = p.rb;
   if (n_wg > 1024) {  // about as many workgroups as are resident at once

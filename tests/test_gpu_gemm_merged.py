@@ -133,14 +133,22 @@ def test_rac_select_merged_bit_exact(case):
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
-@pytest.mark.parametrize("shape", ["dense", "grouped", "decode"])
+@pytest.mark.parametrize("shape", ["dense", "grouped", "decode", "dense_wide", "grouped_wide"])
 def test_gemm_with_caller_merged_operand(shape):
     """The GEMM reads the operand quads_rac_select_merged wrote (no merge pass
-    of its own) on the DMA-tile, large-tile and few-rows shapes."""
+    of its own) on the DMA-tile, large-tile and few-rows shapes; the *_wide
+    shapes (N = 1536, about 30 row tiles, more tiles than CUs) add a ragged
+    last row tile and, grouped, gathered rows and an empty expert."""
     if shape == "dense":
         wl = S.expert_gemm(M=512)
         xa, wa = wl.x, S.Activation(wl.w.f32[None], wl.w.bits[None])
         offs, rt = np.array([0, 512], np.int32), None
+    elif shape == "dense_wide":
+        wl = S.expert_gemm(M=4000)
+        xa, wa = wl.x, S.Activation(wl.w.f32[None], wl.w.bits[None])
+        offs, rt = np.array([0, 4000], np.int32), None
+    elif shape == "grouped_wide":
+        xa, wa, offs, rt = _grouped(609, [1100, 0, 777, 1123], 1500, 768, 1536)
     elif shape == "grouped":
         xa, wa, offs, rt = _grouped(604, [300, 0, 257, 511, 64, 1, 200, 129], 700, 768, 512)
     else:
