@@ -66,13 +66,14 @@ __device__ __forceinline__ void to_f32(const Raw16<BF16> &r, float (&v)[16]) {
   }
 }
 
+// Max over the wave of non-negative floats (amax values), on their bit
+// patterns, which order like the values.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  return __uint_as_float(last_lane(wave_scan<true>(__float_as_uint(v))));
 }
 
-// Block-wide max over kThreads threads; result valid in every thread.
+// Block-wide max of non-negative floats over kThreads threads; result valid
+// in every thread.
 __device__ __forceinline__ float block_max(float v, float *red) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,17 +175,6 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
   const int rem = blockIdx.x % per_tensor;
   const int rc = rem / p.col_chunks, cc = rem % p.col_chunks;
 
-  float g;
-  if (p.gscale_given) {
-    g = p.gscale[b];
-  } else {
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < p.P; i += kThreads) m = fmaxf(m, p.partials[b * p.P + i]);
-    g = tensor_scale_from_amax(block_max(m, red));
-    if (p.gscale != nullptr && rc == 0 && cc == 0 && threadIdx.x == 0) p.gscale[b] = g;
-  }
-
-  const TensorScale ts = tensor_scale(g);
   const int bcol = threadIdx.x % p.BC, rg = threadIdx.x / p.BC;
   const int64_t gbc = static_cast<int64_t>(cc) * p.BC + bcol;
   const bool active = rg < p.RG && gbc < p.cb;
@@ -201,7 +191,18 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
     load_raw16<BF16>(p.x, row0 * p.cols + gbc * 16, x0);
     load_raw16<BF16>(p.x, row1 * p.cols + gbc * 16, x1);
   };
-  if (active && r < r_end) issue();
+  if (active && r < r_end) issue();  // in flight while the tensor scale is folded
+
+  float g;
+  if (p.gscale_given) {
+    g = p.gscale[b];
+  } else {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < p.P; i += kThreads) m = fmaxf(m, p.partials[b * p.P + i]);
+    g = tensor_scale_from_amax(block_max(m, red));
+    if (p.gscale != nullptr && rc == 0 && cc == 0 && threadIdx.x == 0) p.gscale[b] = g;
+  }
+  const TensorScale ts = tensor_scale(g);
 
   float smax[16];
 #pragma unroll

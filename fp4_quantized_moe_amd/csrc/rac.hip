@@ -40,32 +40,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Wave-wide inclusive scans with DPP moves (no LDS round trip): shifts by
-// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of row r
-// is added to row r + 1 (row_bcast:15) and lane 31 to rows 2 and 3
-// (row_bcast:31).  Lanes whose source is outside the row keep 0, the
-// identity of both operations here (unsigned sum and max).
-template <bool MAX>
-__device__ __forceinline__ uint32_t dpp_op(uint32_t a, uint32_t b) {
-  return MAX ? (a > b ? a : b) : a + b;
-}
-
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
-  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
-  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
-  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
-  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
-  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
-  v = dpp_op<MAX>(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
-  return v;
-}
-
-// The value of lane 63 (after a scan: the wave total), as a uniform value.
-__device__ __forceinline__ uint32_t last_lane(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
-}
-
 // Per-thread channel runs of the mask search: thread t owns channels
 // [t*PER, t*PER + PER), so the selected indices come out in ascending order
 // from prefix sums over threads.
