@@ -46,6 +46,7 @@ class _GemmArgs(ctypes.Structure):
         ("x_bf16", _vp), ("w_bf16", _vp),
         ("row_token", _vp), ("expert_offsets", _vp),
         ("y", _vp), ("ws", _vp), ("ws_bytes", ctypes.c_size_t), ("x_merged", _vp), ("rac_form", _c_i32),
+        ("y_gscale", _vp),
     ]
 
 
@@ -201,10 +202,12 @@ def rac_kpad(nsel: int) -> int:
 
 class QuantizeCall:
     """quads_quantize_nvfp4 with output buffers and workspace allocated once.
-    x: [rows, cols] or [batch, rows, cols] (bf16/fp32)."""
+    x: [rows, cols] or [batch, rows, cols] (bf16/fp32).  `gscale` copies given
+    tensor scales once; `gscale_given=True` uses whatever self.q.gscale holds
+    at each call (e.g. a GEMM's y_gscale written just before)."""
 
     def __init__(self, x: torch.Tensor, want_scores: bool = False, gscale: torch.Tensor | None = None,
-                 out: NVFP4Tensor | None = None):
+                 out: NVFP4Tensor | None = None, gscale_given: bool = False):
         L = load()
         _require_cuda(x)
         self.x = x
@@ -213,6 +216,8 @@ class QuantizeCall:
         self.flags = 0
         if gscale is not None:
             self.q.gscale.copy_(gscale.reshape(-1))
+            self.flags |= GSCALE_GIVEN
+        elif gscale_given:  # self.q.gscale is filled by another call (e.g. a GEMM's y_gscale) before each use
             self.flags |= GSCALE_GIVEN
         self.scores = None
         if want_scores:
@@ -285,14 +290,17 @@ class GemmCall:
     (`w_codes`, `w_scales`, `w_gscale`) the weights are decoded to their QDQ
     bf16 values inside the GEMM (QUADS_OPERANDS_BF16_W4).  `rac_form` (RAC_FORM_AUTO /
     _EXACT / _MERGED) picks the formulation of the RAC correction, see
-    quads.h.  ``prepare()`` + ``run()`` is the split form
+    quads.h.  ``y_gscale`` (float32 [1], device) receives the NVFP4 tensor
+    scale of the bf16 output, formed by the GEMM (hand it to a QuantizeCall
+    with ``gscale_given=True``).  ``prepare()`` + ``run()`` is the split form
     (tile list and residual weight-column gather, then the GEMM kernel);
     calling the object does both."""
 
     def __init__(self, *, w_codes=None, w_scales=None, w_gscale=None, n_seg=1, N, K,
                  expert_offsets, num_rows, x: NVFP4Tensor | None = None, res: NVFP4Tensor | None = None,
                  sel_idx=None, row_token=None, epilogue=EPI_NONE, y_dtype=torch.float32,
-                 x_bf16=None, w_bf16=None, y=None, x_merged=None, rac_form=RAC_FORM_AUTO, qdq=False):
+                 x_bf16=None, w_bf16=None, y=None, x_merged=None, rac_form=RAC_FORM_AUTO, qdq=False,
+                 y_gscale=None):
         L = load()
         E = int(expert_offsets.numel()) - 1
         bf16_mode = x_bf16 is not None and w_bf16 is not None
@@ -304,7 +312,8 @@ class GemmCall:
             else:
                 y = torch.empty(num_rows, N, dtype=y_dtype, device=dev)
         self.y = y
-        self._keep = [w_codes, w_scales, w_gscale, expert_offsets, x, res, sel_idx, row_token, x_bf16, w_bf16, x_merged]
+        self._keep = [w_codes, w_scales, w_gscale, expert_offsets, x, res, sel_idx, row_token, x_bf16, w_bf16, x_merged,
+                      y_gscale]
         a = _GemmArgs()
         a.struct_size = ctypes.sizeof(_GemmArgs)
         a.operand_mode = ((OPERANDS_BF16_QDQ if qdq else OPERANDS_BF16) if bf16_mode else
@@ -345,6 +354,11 @@ class GemmCall:
                 if x_merged is not None:
                     _require_cuda(x_merged)
                     a.x_merged = x_merged.data_ptr()
+        if y_gscale is not None:
+            _require_cuda(y_gscale)
+            if y_gscale.dtype != torch.float32 or y_gscale.numel() < 1:
+                raise QuadsError("y_gscale must be a float32 device tensor with at least one element")
+            a.y_gscale = y_gscale.data_ptr()
         a.row_token = None if row_token is None else row_token.data_ptr()
         a.expert_offsets = expert_offsets.data_ptr()
         a.y = y.data_ptr()

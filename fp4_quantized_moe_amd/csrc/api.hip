@@ -237,8 +237,12 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
     return fail(QUADS_ERR_ARG, "gemm: bad rac_form %d", a->rac_form);
   if (a->rac_form == QUADS_RAC_FORM_EXACT && a->x_merged != nullptr)
     return fail(QUADS_ERR_ARG, "gemm: x_merged is the merged form; rac_form EXACT needs x_merged == NULL");
+  if (a->y_gscale != nullptr &&
+      (a->operand_mode != QUADS_OPERANDS_W4A4 || (a->epilogue != QUADS_EPI_SWIGLU && a->y_dtype != QUADS_BF16)))
+    return fail(QUADS_ERR_ARG, "gemm: y_gscale needs W4A4 operands and a bf16 output (SWIGLU or y_dtype BF16)");
   g = quads::GemmLaunch{};
   g.rac_form = a->rac_form;
+  g.y_gscale = a->y_gscale;
   g.mode = a->operand_mode == QUADS_OPERANDS_BF16       ? 1
            : a->operand_mode == QUADS_OPERANDS_BF16_QDQ ? 2
            : a->operand_mode == QUADS_OPERANDS_BF16_W4  ? 3
@@ -324,7 +328,9 @@ quads_status_t quads_moe_w4a4_gemm(const quads_moe_gemm_args *a, void *stream) {
     const hipError_t e = quads::launch_gemm_prepare(g, s);
     if (e != hipSuccess) return device_status(e, "gemm_prepare");
   }
-  return device_status(quads::launch_gemm_main(g, s), "gemm");
+  const hipError_t e = quads::launch_gemm_main(g, s);
+  if (e != hipSuccess) return device_status(e, "gemm");
+  return device_status(quads::launch_fold_amax(g, s), "gemm: output tensor scale");
 }
 
 size_t quads_weight_qdq_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {

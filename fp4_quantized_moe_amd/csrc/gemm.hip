@@ -94,6 +94,7 @@ struct Params {
   const uint16_t *x_f16;  // MODE 2: RAC-merged fp16 activation [act_rows, K], units of x_g
   void *y;
   int y_bf16;
+  uint32_t *amax_ws;  // zeroed words gathering the amax of bf16 y when its tensor scale is wanted, else null
 };
 
 // MODE 3 weight rows: bf16 master values, fake-quantized (QDQ) to NVFP4 and
@@ -392,8 +393,9 @@ __device__ __forceinline__ bool tile_setup(const Params &p, int &nt, int &e, int
 
 // Scale, optional SwiGLU, and store one wave's accumulators.
 template <class C, int MODE, int EPI, bool HAS_RES>
-__device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C::NI], int e, int m0, int mend,
-                                         int nt, int wm, int wn, int lane) {
+__device__ __forceinline__ float epilogue(const Params &p, f32x16 (&acc)[C::MI][C::NI], int e, int m0, int mend,
+                                          int nt, int wm, int wn, int lane) {
+  float hmax = 0.0f;  // largest |stored bf16 value| (NaN skipped), for the output's tensor scale
   float ascale = 1.0f;
   if constexpr (MODE == 0) ascale = HAS_RES ? *p.r_g : *p.x_g;
   if constexpr (MODE == 2) ascale = *p.x_g;
@@ -411,11 +413,13 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
           const int i = m0 + wm * C::TM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (i < mend) {
             const float v = acc[mi][ni][r] * sc;
-            if (p.y_bf16)
-              static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * p.N + col] =
-                  static_cast<uint16_t>(f32_to_bf16_bits(v));
-            else
+            if (p.y_bf16) {
+              const uint32_t hb = f32_to_bf16_bits(v);
+              static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * p.N + col] = static_cast<uint16_t>(hb);
+              hmax = fmaxf(hmax, fabsf(bf16_bits_to_f32(hb)));
+            } else {
               static_cast<float *>(p.y)[static_cast<int64_t>(i) * p.N + col] = v;
+            }
           }
         }
     }
@@ -438,12 +442,14 @@ __device__ __forceinline__ void epilogue(const Params &p, f32x16 (&acc)[C::MI][C
           if (i < mend) {
             const float g = acc[mi][ni][r] * sg;
             const float u = acc[mi][ni + C::NI / 2][r] * su;
-            static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * I + col] =
-                static_cast<uint16_t>(f32_to_bf16_bits(silu(g) * u));
+            const uint32_t hb = f32_to_bf16_bits(silu(g) * u);
+            static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * I + col] = static_cast<uint16_t>(hb);
+            hmax = fmaxf(hmax, fabsf(bf16_bits_to_f32(hb)));
           }
         }
     }
   }
+  return hmax;
 }
 
 // MODE 0: NVFP4 operands (+ residual segment if HAS_RES), fp16 MFMA;
@@ -585,7 +591,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
         [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
   }
 
-  epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  const float hmax = epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  if (p.amax_ws != nullptr) amax_gather(p.amax_ws, hmax);
 }
 
 // ---- 8-wave ping-pong kernel for 256x256 tiles ------------------------------
@@ -1168,7 +1175,9 @@ __global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Pa
         for (int r = 0; r < 16; ++r) acc[mi][ni][r] += red[((wq * NI + ni) * 16 + r) * 64 + lane];
     }
   }
-  if (g == 0) epilogue<C, MERGED ? 2 : 0, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  float hmax = 0.0f;
+  if (g == 0) hmax = epilogue<C, MERGED ? 2 : 0, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  if (p.amax_ws != nullptr) amax_gather(p.amax_ws, hmax);  // every thread: it holds a barrier
 }
 
 // Exclusive scan of per-expert m-tile counts ceil(rows_e / bm) ->
@@ -1416,7 +1425,8 @@ TileCfg pick_cfg_for(const GemmLaunch &a) {
 
 }  // namespace
 
-size_t gemm_ws_bytes(const GemmLaunch &a) {
+namespace {
+size_t gemm_ws_base(const GemmLaunch &a) {
   size_t b = align256(static_cast<size_t>(a.E + 1) * sizeof(int32_t));
   if (a.mode == 0 && a.r_codes != nullptr && a.kpad > 0 && a.x_merged == nullptr)
     b += (gemm_use_small(a) || use_merged(a)) ? align256(gemm_small_res_bytes(a))
@@ -1424,9 +1434,45 @@ size_t gemm_ws_bytes(const GemmLaunch &a) {
   return b;
 }
 
+// The amax word is only touched with system-scope atomics (where the
+// gathering atomic maxima from every XCD are performed).
+__global__ __launch_bounds__(64) void k_zero_words(uint32_t *p, int n) {
+  if (static_cast<int>(threadIdx.x) < n) __hip_atomic_store(p + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// The output's tensor scale from the amax the GEMM gathered (the fold the
+// quantizer applies to its own amax), and the words cleared for the next call.
+__global__ __launch_bounds__(64) void k_fold_amax(uint32_t *words, float *gscale) {
+  static_assert(kAmaxWords == 64, "one word per lane");
+  const uint32_t m = __hip_atomic_exchange(words + threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint32_t t = last_lane(wave_scan<true>(m));
+  if (threadIdx.x == 0) *gscale = tensor_scale_from_amax(__uint_as_float(t));
+}
+}  // namespace
+
+size_t gemm_ws_bytes(const GemmLaunch &a) {
+  return gemm_ws_base(a) + (a.y_gscale != nullptr ? kAmaxWords * sizeof(uint32_t) : 0);
+}
+
+hipError_t launch_fold_amax(const GemmLaunch &a, hipStream_t stream) {
+  if (a.y_gscale == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(k_fold_amax, dim3(1), dim3(64), 0, stream, gemm_amax_words(a), a.y_gscale);
+  return hipGetLastError();
+}
+
+uint32_t *gemm_amax_words(const GemmLaunch &a) {
+  if (a.y_gscale == nullptr) return nullptr;
+  return reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(a.ws) + gemm_ws_base(a));
+}
+
 hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream) {
   uint8_t *ws = static_cast<uint8_t *>(a.ws);
   int32_t *tile_offsets = reinterpret_cast<int32_t *>(ws);
+  if (uint32_t *words = gemm_amax_words(a)) {  // the main kernel's amax word starts at zero
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, stream, words, kAmaxWords);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bool res = a.mode == 0 && a.r_codes != nullptr && a.kpad > 0;
   if (gemm_use_small(a)) {
     uint16_t *rd = reinterpret_cast<uint16_t *>(ws + align256((a.E + 1) * sizeof(int32_t)));
@@ -1490,6 +1536,7 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   p.x_f16 = merged ? wg : nullptr;
   p.y = a.y;
   p.y_bf16 = a.y_bf16 ? 1 : 0;
+  p.amax_ws = gemm_amax_words(a);
   p.n_tiles = static_cast<int>(a.N / bn);
   const int64_t m_tiles = (a.num_rows + bm - 1) / bm + a.E;
   int64_t grid = m_tiles * p.n_tiles;

@@ -73,6 +73,7 @@ struct SmallParams {
   const float *w_g;
   void *y;
   int y_bf16;
+  uint32_t *amax_ws;  // zeroed words gathering the amax of bf16 y when its tensor scale is wanted, else null
 };
 
 // One LDS stage.  Rows of 128 bytes hold 8 chunks; chunk c of row r sits in
@@ -246,11 +247,22 @@ __device__ __forceinline__ void compute16(const StageLds<RES> &st, int wave, int
   }
 }
 
-__device__ __forceinline__ void store_out(const SmallParams &p, int64_t row, int64_t col, int64_t ld, float v) {
-  if (p.y_bf16)
-    static_cast<uint16_t *>(p.y)[row * ld + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-  else
-    static_cast<float *>(p.y)[row * ld + col] = v;
+// Stores one output; returns |stored value| for bf16 output (0 for FP32).
+__device__ __forceinline__ float store_out(const SmallParams &p, int64_t row, int64_t col, int64_t ld, float v) {
+  if (p.y_bf16) {
+    const uint32_t hb = f32_to_bf16_bits(v);
+    static_cast<uint16_t *>(p.y)[row * ld + col] = static_cast<uint16_t>(hb);
+    return fabsf(bf16_bits_to_f32(hb));
+  }
+  static_cast<float *>(p.y)[row * ld + col] = v;
+  return 0.0f;
+}
+
+// h = silu(g) * u stored as bf16; returns |stored value|.
+__device__ __forceinline__ float store_swiglu(const SmallParams &p, int64_t idx, float g, float u) {
+  const uint32_t hb = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
+  static_cast<uint16_t *>(p.y)[idx] = static_cast<uint16_t>(hb);
+  return fabsf(bf16_bits_to_f32(hb));
 }
 
 // The K loop of one pass over the kSStages LDS stages: steps kt+1 ..
@@ -296,6 +308,7 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = p.expert_offsets[e], mend = p.expert_offsets[e + 1];
   if (m0 >= mend) return;
+  float hmax = 0.0f;  // largest |stored bf16 value| (NaN skipped), for the output's tensor scale
 
   // First weight row (output column) of this wave.
   int64_t col0, wcol0;
@@ -350,7 +363,7 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int row = pm + 4 * q + v;
-            if (row < mend) store_out(p, row, col0 + 16 * cb + (lane & 15), p.N, v16[cb][v]);
+            if (row < mend) hmax = fmaxf(hmax, store_out(p, row, col0 + 16 * cb + (lane & 15), p.N, v16[cb][v]));
           }
       } else {
         float *up = reinterpret_cast<float *>(st[0].w);  // free after the K loop
@@ -371,8 +384,8 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
               const float u = up[((wave * 2 + cb) * 4 + v) * 64 + lane];
               const float g = v16[cb][v];
               if (row < mend)
-                static_cast<uint16_t *>(p.y)[static_cast<int64_t>(row) * (p.N / 2) + col0 + 16 * cb + (lane & 15)] =
-                    static_cast<uint16_t>(f32_to_bf16_bits(g / (1.0f + expf(-g)) * u));
+                hmax = fmaxf(hmax, store_swiglu(p, static_cast<int64_t>(row) * (p.N / 2) + col0 + 16 * cb + (lane & 15),
+                                                g, u));
             }
         }
       }
@@ -396,7 +409,7 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = pm + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < mend) store_out(p, row, col, p.N, v[r]);
+        if (row < mend) hmax = fmaxf(hmax, store_out(p, row, col, p.N, v[r]));
       }
     } else {
       float *up = reinterpret_cast<float *>(st[0].w);  // 16 KB of stage 0, free after the K loop
@@ -412,29 +425,14 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
           const int row = pm + 8 * (r >> 2) + 4 * h + (r & 3);
           const float u = up[(wave * 16 + r) * 64 + lane];
           const float g = v[r];
-          if (row < mend)
-            static_cast<uint16_t *>(p.y)[static_cast<int64_t>(row) * (p.N / 2) + col] =
-                static_cast<uint16_t>(f32_to_bf16_bits(g / (1.0f + expf(-g)) * u));
+          if (row < mend) hmax = fmaxf(hmax, store_swiglu(p, static_cast<int64_t>(row) * (p.N / 2) + col, g, u));
         }
       }
     }
   }
+  if (p.amax_ws != nullptr) amax_gather(p.amax_ws, hmax);
 }
 
-// The RAC-corrected activation as one fp16 operand [rows, K], in units of
-// the activation's tensor scale gx: A[t, k] = fp16(X'[t, k] + (gr / gx) *
-// R'[t, j]) for a selected channel k = sel_j, X'[t, k] elsewhere, with the
-// exact e2m1 * e4m3 values X' and R' (fp32 sum, one rounding to fp16).  The
-// inverse of sel_idx is built in LDS first.  sel_idx is strictly ascending
-// over the nsel real entries and padded with index 0 (zero residual): an entry
-// j > 0 that points at channel 0 is padding and skipped.
-// A thread handles 8 consecutive channels.  Because sel_idx ascends, their
-// selected channels have consecutive residual indices j, whose codes lie in
-// one 8-byte window of the residual row and whose scales are at most two
-// bytes: one 16-byte LDS read of the inverse map and a few vector loads per
-// 8 channels.
-// Loads for one 8-channel chunk, issued before any of the chunks it is
-// batched with is computed.
 }  // namespace
 
 bool gemm_use_small(const GemmLaunch &a) {
@@ -475,6 +473,7 @@ hipError_t launch_gemm_small(const GemmLaunch &a, const uint16_t *r_dense, hipSt
   p.w_g = a.w_g;
   p.y = a.y;
   p.y_bf16 = a.y_bf16 ? 1 : 0;
+  p.amax_ws = gemm_amax_words(a);
   const bool res = r_dense != nullptr;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.E) * p.n_tiles)), block(kSW * 64);
   if (a.epilogue == 0) {

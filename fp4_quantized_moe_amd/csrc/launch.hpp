@@ -86,8 +86,13 @@ struct GemmLaunch {
   void *ws;
   const uint16_t *x_merged;  // caller's RAC-merged fp16 activation, or null
   int rac_form;              // QUADS_RAC_FORM_AUTO | _EXACT | _MERGED
+  float *y_gscale;           // NVFP4 tensor scale of the bf16 output, formed by the GEMM, or null
 };
 size_t gemm_ws_bytes(const GemmLaunch &a);
+// The workspace words gathering the output amax behind y_gscale, or null.
+uint32_t *gemm_amax_words(const GemmLaunch &a);
+// After the main kernel: y_gscale from the gathered amax (no-op without it).
+hipError_t launch_fold_amax(const GemmLaunch &a, hipStream_t stream);
 // prepare: tile list + residual weight-column gather; main: the GEMM kernel.
 hipError_t launch_gemm_prepare(const GemmLaunch &a, hipStream_t stream);
 hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream);

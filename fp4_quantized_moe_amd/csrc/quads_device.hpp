@@ -314,6 +314,30 @@ __device__ __forceinline__ uint32_t last_lane(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
+// The amax of a kernel's bf16 output, gathered while the kernel writes it:
+// each thread passes the largest |value| it stored (fmaxf of the stored bf16
+// values, so NaN is skipped as the quantizer's amax skips it); the workgroup
+// reduces them (non-negative floats order like their bit patterns) and one
+// atomic max per workgroup lands in words[blockIdx.x % kAmaxWords], spread
+// so that few atomics meet at one address.  System scope, so that maxima
+// from every XCD meet in one place; no value is awaited.  The words must be
+// zero before the launch; a later launch folds them (k_fold_amax).  Contains
+// a barrier: every thread of the workgroup calls it.
+constexpr int kAmaxWords = 64;
+
+__device__ __forceinline__ void amax_gather(uint32_t *words, float m) {
+  __shared__ uint32_t red[16];
+  const uint32_t wm = last_lane(wave_scan<true>(__float_as_uint(m)));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = wm;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < static_cast<int>((blockDim.x + 63) >> 6); ++w) t = max(t, red[w]);
+    if (t != 0u)
+      __hip_atomic_fetch_max(words + blockIdx.x % kAmaxWords, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // Dequantized FP32 value of one code given the block's d = fl32(dec(s) * g).
 __device__ __forceinline__ float dequant_code(uint32_t code, float d) {
   const float m = e2m1_level(code & 7u) * d;

@@ -297,6 +297,18 @@ typedef struct {
      whatever the shape, and builds no merged operand of its own. */
   const void *x_merged;
   int32_t rac_form; /* QUADS_RAC_FORM_AUTO | _EXACT | _MERGED (see above) */
+  /* Optional [1] float, device: the NVFP4 tensor scale of the bf16 output y
+     (W4A4 operands with EPI_SWIGLU or y_dtype BF16 only), formed while y is
+     written: amax over the stored bf16 values (NaN skipped) / 2688, 1 for an
+     all-zero y -- bit for bit what quads_quantize_nvfp4 computes for y, so a
+     following quads_quantize_nvfp4(y, ..., QUADS_GSCALE_GIVEN) with
+     out.gscale = y_gscale skips its amax pass over y [Gist 2.2-B: fused
+     kernels keep the RAC overhead small].  The GEMM's workgroups gather
+     the amax in 64 workspace words (256 more workspace bytes, cleared by
+     quads_moe_gemm_prepare; a QUADS_GEMM_PREPARED call relies on an earlier
+     prepare of the same workspace) and a one-wave kernel enqueued after the
+     GEMM folds them into y_gscale and clears them.  NULL: not computed. */
+  float *y_gscale;
 } quads_moe_gemm_args;
 
 size_t quads_moe_gemm_workspace_bytes(const quads_moe_gemm_args *a);

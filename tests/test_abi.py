@@ -126,6 +126,17 @@ def test_gemm_validation(L):
         assert L.quads_last_error() != b""
 
 
+def test_gemm_y_gscale_field(L):
+    """The output tensor scale is formed only for the W4A4 GEMM's bf16 output
+    (SwiGLU or y_dtype BF16) and costs 256 workspace bytes (its two words)."""
+    base = L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(y_dtype=1)))
+    assert L.quads_moe_gemm_workspace_bytes(ctypes.byref(_gemm_args(y_dtype=1, y_gscale=16))) == base + 256
+    for kw in (dict(y_gscale=16), dict(y_gscale=16, operand_mode=1, x_bf16=16, w_bf16=16, y_dtype=1)):
+        a = _gemm_args(**kw)
+        assert L.quads_moe_w4a4_gemm(ctypes.byref(a), None) == -1 and b"y_gscale" in L.quads_last_error()
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(_gemm_args(epilogue=1, n_seg=2, y_gscale=16)), None) == -3
+
+
 def test_gemm_rac_form_field(L):
     """The RAC formulation is an explicit argument (no environment or other
     hidden input): the workspace holds the gathered weight columns
