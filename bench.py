@@ -253,14 +253,17 @@ def setup_moe(Q, S, k, decode):
     sx = Q.SelectCall(x, q, sc, k, merged=mr)
     sel, res, nsel_x = sx()
     form = Q.RAC_FORM_MERGED if mr else Q.RAC_FORM_EXACT
-    # h's NVFP4 tensor scale is formed by the gate_up GEMM while it writes h
-    # (y_gscale), so quantize_h runs with it given and needs no amax pass.
+    # Prefill: h's NVFP4 tensor scale is formed by the gate_up GEMM while it
+    # writes h (y_gscale), so quantize_h runs with it given and skips its
+    # amax pass over h (about 200 MB).  Decode keeps the quantizer's own amax
+    # pass: on a 4 MB h the fold and zeroing launches cost more than it.
+    fuse = not decode
     hq_out = Q.empty_nvfp4(1, R, I, x.device)
     g1 = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
                     x=q, res=res if nsel_x else None, sel_idx=sel, row_token=rt, epilogue=Q.EPI_SWIGLU,
-                    x_merged=sx.merged if mr else None, rac_form=form, y_gscale=hq_out.gscale)
+                    x_merged=sx.merged if mr else None, rac_form=form, y_gscale=hq_out.gscale if fuse else None)
     h = g1()
-    qh = Q.QuantizeCall(h, want_scores=True, out=hq_out, gscale_given=True)
+    qh = Q.QuantizeCall(h, want_scores=True, out=hq_out, gscale_given=fuse)
     hq, hsc = qh()
     sh = Q.SelectCall(h, hq, hsc, k, merged=mr)
     hsel, hres, nsel_h = sh()
@@ -282,9 +285,9 @@ def setup_moe(Q, S, k, decode):
     qp, _ = qxp()
     hqp_out = Q.empty_nvfp4(1, R, I, x.device)
     g1p = Q.GemmCall(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=N2, K=H, expert_offsets=offs, num_rows=R,
-                     x=qp, row_token=rt, epilogue=Q.EPI_SWIGLU, y_gscale=hqp_out.gscale)
+                     x=qp, row_token=rt, epilogue=Q.EPI_SWIGLU, y_gscale=hqp_out.gscale if fuse else None)
     g1p()
-    qhp = Q.QuantizeCall(g1p.y, out=hqp_out, gscale_given=True)
+    qhp = Q.QuantizeCall(g1p.y, out=hqp_out, gscale_given=fuse)
     hqp, _ = qhp()
     g2p = Q.GemmCall(w_codes=dnc, w_scales=dns, w_gscale=dng, n_seg=1, N=H, K=I, expert_offsets=offs, num_rows=R,
                      x=hqp)
@@ -295,7 +298,8 @@ def setup_moe(Q, S, k, decode):
     cfg = {"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "top": wl.top, "intermediate": I,
            "k_percent": k, "nsel_x": nsel_x, "nsel_h": nsel_h,
            "rac_gemm": "merged fp16 operand (executes 2*R*N*K)" if mr else "extended K (executes 2*R*N*(K+nsel))",
-           "h_tensor_scale": "formed in the gate_up epilogue (y_gscale); quantize_h has no amax pass",
+           "h_tensor_scale": ("quantizer's own amax pass" if decode else
+                              "formed in the gate_up epilogue (y_gscale); quantize_h has no amax pass"),
            "rows_per_expert": {"min": int(cnt.min()), "max": int(cnt.max()), "mean": float(cnt.mean())}}
     wbytes = {"gate_up": E * N2 * H * 0.5625, "down": E * H * I * 0.5625}
     qxb, rxb = _act_bytes(T, H, res.cols, mr)

@@ -119,16 +119,17 @@ __device__ __forceinline__ uint32_t radix_threshold(const Keys<PER> &ks, int n_r
   return prefix;
 }
 
-// Writes the nsel selected channel indices (largest scores first by value,
-// ties to the lower index) in ascending order to sel_out[0..nsel).  Keys are
+// Emits the nsel selected channel indices (largest scores first by value,
+// ties to the lower index) as emit(position, channel), positions 0..nsel-1 in
+// ascending channel order.  Keys are
 // the FP32 score bit patterns: non-negative, so below 2^31 and ordered like
 // the scores.  Keys beyond K (padding) are 0 and come after every real
 // channel: they are never above T, and when T == 0 they only follow the real
 // zeros among the ties, of which there are at least need_eq, so no padding
 // channel is kept.
-template <int PER>
-__device__ void block_select(const Keys<PER> &ks, int n_real, int nsel, uint32_t (*hist)[256], uint32_t *slots,
-                             int32_t *sel_out) {
+template <int PER, class Emit>
+__device__ __forceinline__ void block_select(const Keys<PER> &ks, int n_real, int nsel, uint32_t (*hist)[256],
+                                             uint32_t *slots, Emit emit) {
   const int c0 = threadIdx.x * PER;
   const uint32_t T = radix_threshold<PER>(ks, n_real, static_cast<uint32_t>(nsel), hist);
   uint32_t n_gt = 0, n_eq = 0;
@@ -160,20 +161,20 @@ __device__ void block_select(const Keys<PER> &ks, int n_real, int nsel, uint32_t
     const bool eq = ks.k[i] == T;
     const bool kk = ks.k[i] > T || (eq && e < need_eq);
     e += eq;
-    if (kk && pos < static_cast<uint32_t>(nsel)) sel_out[pos] = c0 + i;
+    if (kk && pos < static_cast<uint32_t>(nsel)) emit(pos, c0 + i);
     pos += kk;
   }
 }
 
-// The mask, written ascending to sel_out[0..nsel) with pad entries
-// sel_out[nsel..kpad) = 0, and the residual tensor scale (from the largest
-// score, which is always selected when nsel >= 1).  One workgroup.
-template <int PER>
-__global__ __launch_bounds__(kThreads) void k_rac_mask(const uint32_t *scores, int K, int nsel, int kpad,
-                                                       int32_t *sel_out, float *r_g_out) {
+// The whole mask computed by one workgroup of kThreads threads: the channel
+// scores are loaded (PER per thread), the selection is emitted through
+// `emit`, and the largest key (the largest score) is returned.  `hist` and
+// `slots` are the workgroup's LDS scratch.  Ends after a barrier when
+// nsel > 0 (the selection's scans).
+template <int PER, class Emit>
+__device__ __forceinline__ uint32_t workgroup_mask(const uint32_t *scores, int K, int nsel, uint32_t (*hist)[256],
+                                                   uint32_t *slots, Emit emit) {
   static_assert(kThreads == 256, "one histogram bin per thread when zeroing");
-  __shared__ uint32_t hist[4][256];
-  __shared__ uint32_t slots[6 * (kThreads / 64)];
   const int tid = threadIdx.x;
   Keys<PER> ks;
   const int c0 = tid * PER;
@@ -189,7 +190,6 @@ __global__ __launch_bounds__(kThreads) void k_rac_mask(const uint32_t *scores, i
     ks.k[i + 2] = v.z & m;
     ks.k[i + 3] = v.w & m;
   }
-  for (int j = nsel + tid; j < kpad; j += kThreads) sel_out[j] = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) hist[r][tid] = 0;
   // Largest key over the workgroup (slots 16..19; the selection's scans use
@@ -203,8 +203,22 @@ __global__ __launch_bounds__(kThreads) void k_rac_mask(const uint32_t *scores, i
   uint32_t mx_total = 0;
 #pragma unroll
   for (int i = 0; i < kThreads / 64; ++i) mx_total = max(mx_total, slots[4 * (kThreads / 64) + i]);
-  if (nsel > 0) block_select<PER>(ks, n_real, nsel, hist, slots, sel_out);
-  if (tid == 0) *r_g_out = tensor_scale_from_amax(nsel > 0 ? __uint_as_float(mx_total) : 0.0f);
+  if (nsel > 0) block_select<PER>(ks, n_real, nsel, hist, slots, emit);
+  return mx_total;
+}
+
+// The mask, written ascending to sel_out[0..nsel) with pad entries
+// sel_out[nsel..kpad) = 0, and the residual tensor scale (from the largest
+// score, which is always selected when nsel >= 1).  One workgroup.
+template <int PER>
+__global__ __launch_bounds__(kThreads) void k_rac_mask(const uint32_t *scores, int K, int nsel, int kpad,
+                                                       int32_t *sel_out, float *r_g_out) {
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t slots[6 * (kThreads / 64)];
+  for (int j = nsel + threadIdx.x; j < kpad; j += kThreads) sel_out[j] = 0;
+  const uint32_t mx = workgroup_mask<PER>(scores, K, nsel, hist, slots,
+                                          [&](uint32_t pos, int c) { sel_out[pos] = c; });
+  if (threadIdx.x == 0) *r_g_out = tensor_scale_from_amax(nsel > 0 ? __uint_as_float(mx) : 0.0f);
 }
 
 // One 16-element block of x with its FP4 codes and E4M3 scale, as loaded
@@ -288,8 +302,14 @@ struct RowsArgs {
   int K, kpad;
   const uint8_t *x_codes, *x_scales;
   const float *x_g;
-  const int32_t *sel;  // [kpad] ascending, pad entries 0
+  const int32_t *sel;  // [kpad] ascending, pad entries 0 (mask from a previous launch)
   const float *r_g;
+  // In-workgroup mask (MASK_PER > 0): the scores and nsel; workgroup 0
+  // publishes the mask to sel_out and the residual tensor scale to r_g_out.
+  const uint32_t *scores;
+  int nsel;
+  int32_t *sel_out;
+  float *r_g_out;
   uint8_t *r_codes, *r_scales;  // written, or read in kFromCodes
   uint16_t *merged;              // [rows, K] fp16, or null in kResidual
   int rb, rows_per_wg;
@@ -306,7 +326,12 @@ __host__ __device__ constexpr int bitmap_words(int64_t K) { return static_cast<i
 // the real entries ascend and the pads are 0).  An entry >= K (possible only
 // in a caller's mask handed to the GEMM) is read as channel 0, so no LDS
 // access leaves the rows.
-template <bool BF16, int MODE, int SLOTS>
+//
+// MASK_PER > 0 (calls of at most one workgroup per CU): every workgroup
+// computes the mask itself from the scores (workgroup_mask, PER = MASK_PER
+// channels per thread), with its row loads already in flight, instead of
+// waiting for a mask launch; workgroup 0 publishes it.
+template <bool BF16, int MODE, int SLOTS, int MASK_PER>
 __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
   constexpr bool kX = MODE != kFromCodes;    // reads x and computes the residual
   constexpr bool kOut = MODE != kResidual;   // writes the merged operand
@@ -333,28 +358,53 @@ __global__ __launch_bounds__(kThreads) void k_rac_rows(RowsArgs p) {
   };
   issue(r_begin);
 
-  __shared__ int s_nreal;
-  if (tid == 0) s_nreal = 1;
-  if constexpr (kOut)
-    for (int w = tid; w < bitmap_words(K); w += kThreads) bits[w] = 0;
-  __syncthreads();
-  uint32_t last = 0;  // 1 + this thread's last nonzero entry
-  for (int j = tid; j < kpad; j += kThreads) {
-    int c = p.sel[j];
-    c = c >= 0 && c < K ? c : 0;
-    sel[j] = static_cast<uint16_t>(chan_offset(c));  // < K <= 16384
-    if (c != 0) last = j + 1;
+  int n_real;
+  float gr;
+  if constexpr (MASK_PER > 0) {
+    __shared__ uint32_t hist[4][256];
+    __shared__ uint32_t mslots[6 * (kThreads / 64)];
+    const bool pub = blockIdx.x == 0;
+    for (int j = p.nsel + tid; j < kpad; j += kThreads) {
+      sel[j] = 0;
+      if (pub) p.sel_out[j] = 0;
+    }
     if constexpr (kOut)
-      if (j == 0 || c != 0) atomicOr(&bits[c >> 5], 1u << (c & 31));
+      for (int w = tid; w < bitmap_words(K); w += kThreads) bits[w] = 0;
+    // (the bitmap is cleared before workgroup_mask's first barrier, which
+    // precedes every emit)
+    const uint32_t mx = workgroup_mask<MASK_PER>(p.scores, K, p.nsel, hist, mslots, [&](uint32_t pos, int c) {
+      sel[pos] = static_cast<uint16_t>(chan_offset(c));
+      if constexpr (kOut) atomicOr(&bits[c >> 5], 1u << (c & 31));
+      if (pub) p.sel_out[pos] = c;
+    });
+    gr = tensor_scale_from_amax(__uint_as_float(mx));  // nsel >= 1 here
+    if (pub && tid == 0) *p.r_g_out = gr;
+    n_real = p.nsel;
+    __syncthreads();
+  } else {
+    __shared__ int s_nreal;
+    if (tid == 0) s_nreal = 1;
+    if constexpr (kOut)
+      for (int w = tid; w < bitmap_words(K); w += kThreads) bits[w] = 0;
+    __syncthreads();
+    uint32_t last = 0;  // 1 + this thread's last nonzero entry
+    for (int j = tid; j < kpad; j += kThreads) {
+      int c = p.sel[j];
+      c = c >= 0 && c < K ? c : 0;
+      sel[j] = static_cast<uint16_t>(chan_offset(c));  // < K <= 16384
+      if (c != 0) last = j + 1;
+      if constexpr (kOut)
+        if (j == 0 || c != 0) atomicOr(&bits[c >> 5], 1u << (c & 31));
+    }
+    last = last_lane(wave_scan<true>(last));
+    if ((tid & 63) == 0 && last > 1) atomicMax(&s_nreal, static_cast<int>(last));
+    __syncthreads();
+    n_real = s_nreal;
+    gr = *p.r_g;
   }
-  last = last_lane(wave_scan<true>(last));
-  if ((tid & 63) == 0 && last > 1) atomicMax(&s_nreal, static_cast<int>(last));
-  __syncthreads();
-  const int n_real = s_nreal;
   // (sel is read in b after at least one barrier; the bitmap in c after the
   // barrier that ends b.)
   const float gx = *p.x_g;
-  const float gr = *p.r_g;
   const TensorScale tsr = tensor_scale(gr);
   const float ratio = gr / gx;
 
@@ -464,12 +514,10 @@ hipError_t allow_lds(const void *fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-template <bool BF16, int MODE, int SLOTS>
-hipError_t launch_rows_s(RowsArgs p, hipStream_t stream) {
-  const bool out = MODE != kResidual;
-  // Few rows (decode-sized calls): smaller groups, so that the launch still
-  // spreads over every CU and each workgroup's chain of loads, barriers and
-  // stores is short.
+// Row groups and grid of a call: few rows (decode-sized calls) take smaller
+// groups, so that the launch still spreads over every CU and each
+// workgroup's chain of loads, barriers and stores is short.
+int64_t rows_grid(RowsArgs &p) {
   const int64_t spread = (p.rows + 255) / 256;
   if (spread < p.rb) p.rb = static_cast<int>(std::max<int64_t>(1, spread));
   int64_t n_wg = (p.rows + p.rb - 1) / p.rb;
@@ -478,16 +526,24 @@ hipError_t launch_rows_s(RowsArgs p, hipStream_t stream) {
     p.rows_per_wg = static_cast<int>(p.rb * ((n_wg + 1023) / 1024));
     n_wg = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
   }
+  return n_wg;
+}
+
+template <bool BF16, int MODE, int SLOTS, int MASK_PER>
+hipError_t launch_rows_s(const RowsArgs &p, int64_t n_wg, hipStream_t stream) {
+  const bool out = MODE != kResidual;
   const size_t lds = rows_lds_bytes(p.K, p.kpad, out, p.rb);
-  const hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_rac_rows<BF16, MODE, SLOTS>), lds);
+  const hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_rac_rows<BF16, MODE, SLOTS, MASK_PER>), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_rac_rows<BF16, MODE, SLOTS>), dim3(n_wg), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((k_rac_rows<BF16, MODE, SLOTS, MASK_PER>), dim3(n_wg), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
 template <bool BF16, int MODE>
 hipError_t launch_rows_t(RowsArgs p, hipStream_t stream) {
-  return rows_slots(p.K) == 2 ? launch_rows_s<BF16, MODE, 2>(p, stream) : launch_rows_s<BF16, MODE, kMaxSlots>(p, stream);
+  const int64_t n_wg = rows_grid(p);
+  return rows_slots(p.K) == 2 ? launch_rows_s<BF16, MODE, 2, 0>(p, n_wg, stream)
+                              : launch_rows_s<BF16, MODE, kMaxSlots, 0>(p, n_wg, stream);
 }
 
 template <int PER>
@@ -519,8 +575,6 @@ int rac_rows_per_group(int64_t cols, int64_t kpad, bool merged) {
 
 hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
   if (a.cols > 64 * kThreads) return hipErrorInvalidValue;  // the API bounds cols first
-  hipError_t e = launch_mask(a, stream);
-  if (e != hipSuccess || a.kpad == 0 || a.rows == 0) return e;
   const bool merged = a.merged != nullptr;
   RowsArgs p{};
   p.x = a.x;
@@ -535,8 +589,27 @@ hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
   p.r_codes = a.r_codes;
   p.r_scales = a.r_scales;
   p.merged = a.merged;
+  p.scores = reinterpret_cast<const uint32_t *>(a.scores);
+  p.nsel = static_cast<int>(a.nsel);
+  p.sel_out = a.sel_idx;
+  p.r_g_out = a.r_gscale;
   p.rb = rac_rows_per_group(a.cols, a.kpad, merged);
-  if (p.rb < 1) return hipErrorInvalidValue;
+  if (a.kpad > 0 && a.rows > 0 && p.rb < 1) return hipErrorInvalidValue;
+  // Calls of at most one workgroup per CU with bf16 rows of up to 2048
+  // channels: each workgroup finds the mask itself (one launch).
+  if (a.kpad > 0 && a.rows > 0 && a.x_bf16 && a.cols <= 2 * kThreads * 4) {
+    RowsArgs q = p;
+    const int64_t n_wg = rows_grid(q);
+    if (n_wg <= 256 && rows_slots(q.K) == 2) {
+      if (a.cols <= 4 * kThreads)
+        return merged ? launch_rows_s<true, kMerged, 2, 4>(q, n_wg, stream)
+                      : launch_rows_s<true, kResidual, 2, 4>(q, n_wg, stream);
+      return merged ? launch_rows_s<true, kMerged, 2, 8>(q, n_wg, stream)
+                    : launch_rows_s<true, kResidual, 2, 8>(q, n_wg, stream);
+    }
+  }
+  const hipError_t e = launch_mask(a, stream);
+  if (e != hipSuccess || a.kpad == 0 || a.rows == 0) return e;
   if (a.x_bf16)
     return merged ? launch_rows_t<true, kMerged>(p, stream) : launch_rows_t<true, kResidual>(p, stream);
   return merged ? launch_rows_t<false, kMerged>(p, stream) : launch_rows_t<false, kResidual>(p, stream);

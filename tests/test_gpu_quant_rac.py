@@ -106,6 +106,25 @@ def test_rac_select_ties_and_ragged():
         assert rg[0] == rres.g and np.array_equal(rc, rres.codes) and np.array_equal(rs, rres.scales)
 
 
+@pytest.mark.parametrize("cols", [256, 1024, 2048])
+def test_rac_select_ties_bf16_one_launch(cols):
+    """bf16 rows with many exactly tied scores, few rows (each workgroup of the
+    row kernel finds the mask itself: one launch), nsel not a multiple of
+    16, both RAC entry points: mask, residual and g_r bit-exact."""
+    rng = np.random.default_rng(19 + cols)
+    xv = np.round(rng.standard_normal((37, cols)) * 4).astype(np.float32) / 4
+    a = S.Activation(xv, O.bf16_bits_from_f32(xv))
+    x, q, scores, ref, sref = _check_quant(a, f"ties bf16 {cols}")
+    for k in (1, 10, 33, 77, 100):
+        for merged in (False, True):
+            sel, res, nsel = Q.SelectCall(x, q, scores, k, merged=merged)()
+            rsel, rn = O.rac_select(sref, k)
+            assert nsel == rn and np.array_equal(host(sel), rsel), (k, merged)
+            rres = O.rac_quantize_residual(xv, ref, rsel, rn)
+            rc, rs, rg = nvfp4_host(res)
+            assert rg[0] == rres.g and np.array_equal(rc, rres.codes) and np.array_equal(rs, rres.scales), (k, merged)
+
+
 def test_weight_qdq_bit_exact():
     rng = np.random.default_rng(10)
     w = S.weights(rng, (5, 96, 256), 0.02, bf16=True)
