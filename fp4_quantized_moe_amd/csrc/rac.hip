@@ -595,12 +595,15 @@ hipError_t launch_rac_select(const RacLaunch &a, hipStream_t stream) {
   p.r_g_out = a.r_gscale;
   p.rb = rac_rows_per_group(a.cols, a.kpad, merged);
   if (a.kpad > 0 && a.rows > 0 && p.rb < 1) return hipErrorInvalidValue;
-  // Calls of at most one workgroup per CU with bf16 rows of up to 2048
-  // channels: each workgroup finds the mask itself (one launch).
+  // bf16 rows of up to 2048 channels, in calls of at most one workgroup per
+  // CU or with at least 8 row groups per workgroup: each workgroup finds the
+  // mask itself (one launch).  Measured: decode x 11.5 -> 8.9 us, prefill h
+  // 117 -> 113 us; with one row group per workgroup and four workgroups per
+  // CU (4096 x 2048) the separate mask launch is faster (20.2 against 22.8 us).
   if (a.kpad > 0 && a.rows > 0 && a.x_bf16 && a.cols <= 2 * kThreads * 4) {
     RowsArgs q = p;
     const int64_t n_wg = rows_grid(q);
-    if (n_wg <= 256 && rows_slots(q.K) == 2) {
+    if ((n_wg <= 256 || q.rows_per_wg >= 8 * q.rb) && rows_slots(q.K) == 2) {
       if (a.cols <= 4 * kThreads)
         return merged ? launch_rows_s<true, kMerged, 2, 4>(q, n_wg, stream)
                       : launch_rows_s<true, kResidual, 2, 4>(q, n_wg, stream);

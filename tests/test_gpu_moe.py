@@ -163,7 +163,9 @@ def test_prefill_layer_full_size_sampled_experts():
     experts with Zipf-skewed top-8 routing, intermediate 768, k=50) as the
     benchmark launches it; the oracle recomputes the rows of the largest,
     smallest and one random non-empty expert of the gate_up GEMM (FP32 and
-    SwiGLU outputs) and of the down GEMM on a seeded h."""
+    SwiGLU outputs) and of the down GEMM on a seeded h; the RAC of that h
+    (131072 x 768) is checked bit for bit, with and without the merged
+    operand."""
     wl = S.moe_prefill()
     T, H = wl.x.f32.shape
     E, N2, _ = wl.w_gate_up.f32.shape
@@ -217,6 +219,15 @@ def test_prefill_layer_full_size_sampled_experts():
     osel, on = O.rac_select(O.rac_scores(ha.f32, oq), k)
     orr = O.rac_quantize_residual(ha.f32, oq, osel, on)
     assert np.array_equal(host(hsel), osel) and np.array_equal(host(hres.codes), orr.codes)
+    # the same h through quads_rac_select_merged: 131072 rows of 768 channels,
+    # many row groups per workgroup (each workgroup finds the mask itself)
+    mcall = Q.SelectCall(hd, hq, hsc, k, merged=True)
+    msel, mres, _ = mcall()
+    assert np.array_equal(host(msel), osel) and np.array_equal(host(mres.codes), orr.codes)
+    assert np.array_equal(host(mres.scales), orr.scales) and host(mres.gscale)[0] == np.float32(orr.g)
+    want = O.rac_merged_operand(oq, orr, osel, on)
+    assert np.array_equal(host(mcall.merged).view(np.uint16), want.view(np.uint16))
+    del want
     he = O.dequant_exact(oq.codes, oq.scales, oq.g)
     hre = O.dequant_exact(orr.codes, orr.scales, orr.g)
     for e in pick:
