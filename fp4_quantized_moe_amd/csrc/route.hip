@@ -321,6 +321,38 @@ __global__ __launch_bounds__(kTokBlk) void k_route_one_block(const int32_t *ids,
   }
 }
 
+// The same sum for a compile-time top: every slot's index and weight, then
+// every slot's row chunk, are loaded before the first multiply, so a thread
+// has all its loads in flight at once; the sum keeps the slot order and the
+// operations of k_combine, so the result is the same bit for bit.
+template <int TOP>
+__global__ __launch_bounds__(256) void k_combine_top(const float *y, int64_t T, int64_t N, const int32_t *inverse,
+                                                     const float *w, float *out) {
+  const int64_t n4 = N / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= T * n4) return;
+  const int64_t t = idx / n4, c = idx % n4;
+  int32_t rows[TOP];
+  float wj[TOP];
+#pragma unroll
+  for (int j = 0; j < TOP; ++j) {
+    rows[j] = inverse[t * TOP + j];
+    wj[j] = w[t * TOP + j];
+  }
+  float4 v[TOP];
+#pragma unroll
+  for (int j = 0; j < TOP; ++j) v[j] = reinterpret_cast<const float4 *>(y + static_cast<int64_t>(rows[j]) * N)[c];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < TOP; ++j) {
+    acc.x = acc.x + wj[j] * v[j].x;
+    acc.y = acc.y + wj[j] * v[j].y;
+    acc.z = acc.z + wj[j] * v[j].z;
+    acc.w = acc.w + wj[j] * v[j].w;
+  }
+  reinterpret_cast<float4 *>(out + t * N)[c] = acc;
+}
+
 __global__ __launch_bounds__(256) void k_combine(const float *y, int64_t T, int top, int64_t N,
                                                  const int32_t *inverse, const float *w, float *out) {
   const int64_t n4 = N / 4;
@@ -384,9 +416,14 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int top, int32_t 
 hipError_t launch_combine(const float *y, int64_t T, int top, int64_t N, const int32_t *inverse,
                           const float *w, float *out, hipStream_t stream) {
   const int64_t total = T * (N / 4);
-  if (total > 0)
-    hipLaunchKernelGGL(k_combine, dim3((total + 255) / 256), dim3(256), 0, stream, y, T, top, N, inverse,
-                       w, out);
+  if (total > 0) {
+    if (top == 8)
+      hipLaunchKernelGGL(k_combine_top<8>, dim3((total + 255) / 256), dim3(256), 0, stream, y, T, N, inverse, w,
+                         out);
+    else
+      hipLaunchKernelGGL(k_combine, dim3((total + 255) / 256), dim3(256), 0, stream, y, T, top, N, inverse,
+                         w, out);
+  }
   return hipGetLastError();
 }
 

@@ -82,16 +82,25 @@ def test_route_nan_logits():
             assert np.allclose(host(w)[fin], rw[fin], rtol=2e-6, atol=1e-9)
 
 
-def test_combine():
-    rng = np.random.default_rng(82)
-    T, top, N = 123, 8, 256
+@pytest.mark.parametrize("top", [8, 4])
+def test_combine(top):
+    """Combine against the oracle's float64 sum, and bit for bit against the
+    FP32 sum in slot order (each product rounded, then added), the kernel's
+    stated operation order (top 8 has its own kernel with all loads hoisted)."""
+    rng = np.random.default_rng(82 + top)
+    T, N = 123, 256
     logits = S.gaussian_logits(rng, T, 16)
     *_, (rids, rw, roffs, rrt, rinv) = _check_route(logits, top, "combine")
     y = rng.standard_normal((T * top, N)).astype(np.float32)
     w32 = rw.astype(np.float32)
-    out = Q.moe_combine(torch.from_numpy(y).cuda(), torch.from_numpy(rinv).cuda(), torch.from_numpy(w32).cuda())
+    out = host(Q.moe_combine(torch.from_numpy(y).cuda(), torch.from_numpy(rinv).cuda(),
+                             torch.from_numpy(w32).cuda()))
     ref = O.combine(y, rinv, w32.astype(np.float64))
-    assert rel_err(host(out), ref) <= 1e-6
+    assert rel_err(out, ref) <= 1e-6
+    acc = np.zeros((T, N), np.float32)
+    for j in range(top):
+        acc = (acc + (w32[:, j:j + 1] * y[rinv[:, j]]).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(out.view(np.uint32), acc.view(np.uint32))
 
 
 def _layer_setup(seed=83, T=192, H=256, E=16, I=128, top=4):
