@@ -70,8 +70,8 @@ MERGED_RAC = True
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="expert_gemm",
                     choices=["expert_gemm", "moe_prefill", "moe_decode", "trainer_qdq", "trainer_bwd", "ablation"])
     ap.add_argument("--k", type=int, default=50, help="RAC k percent")
@@ -538,15 +538,21 @@ def capture(fns, reps=1):
     return g
 
 
+EVENT_EVERY = 10  # timed steps per step whose dominant stage is bracketed by HIP events
+
+
 def run_steps(stages, steps, warmup, dominant=None, graph=False):
     """Run `warmup` untimed steps, then `steps` timed steps bracketed by device
     synchronisation.  Every library call only enqueues work, so the host runs
     ahead of the device and the kernels of consecutive steps execute back to
-    back; HIP events recorded on the stream every call uses, around the
-    dominant stage of each timed step, give that kernel's duration inside the
-    timed region.  With graph=True the stages before and after the dominant
-    one are replayed as HIP graphs instead (on this stack a graph launch costs
-    more host time than the few direct launches it replaces).
+    back.  HIP events recorded on the stream every call uses, around the
+    dominant stage of every EVENT_EVERY-th timed step (at least one), give
+    that kernel's duration inside the timed region: each timing event is a
+    barrier packet that stops the kernels around it from overlapping their
+    launch, about 13 us per event pair on the expert-GEMM step, so recording
+    them in every step would time the instrumentation too.  With graph=True
+    the stages before and after the dominant one are replayed as HIP graphs
+    instead (on this stack no faster than direct launches).
     Returns (wall seconds, event ms over all steps, dominant-stage ms per step)."""
     import torch
     for _, fn in stages:  # eager pass: lazy allocations happen outside any capture
@@ -578,7 +584,9 @@ def run_steps(stages, steps, warmup, dominant=None, graph=False):
 
     for _ in range(warmup):
         step()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    every = max(1, min(EVENT_EVERY, steps))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if s % every == 0 else None
+           for s in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -588,7 +596,7 @@ def run_steps(stages, steps, warmup, dominant=None, graph=False):
     e1.record()
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0
-    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) if dom else None
+    dom_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs if ev is not None])) if dom else None
     return secs, e0.elapsed_time(e1), dom_ms
 
 
@@ -812,7 +820,8 @@ def main():
         "stages_ms": per,
         "timing": ("stages launched directly (host runs ahead of the device)" if not args.graph else
                    "stages before/after the dominant one replayed as HIP graphs") +
-                  "; roofline.avg_launch_ms from HIP events around the dominant kernel in every timed step; "
+                  f"; roofline.avg_launch_ms from HIP events around the dominant kernel in every {EVENT_EVERY}th "
+                  "timed step (each event pair is a barrier packet that costs the step about 13 us); "
                   "stages_ms from graphs of 20 back-to-back calls of one stage; stage_bandwidth cold from one call "
                   "after a 1 GiB write that evicts the Infinity Cache",
         "roofline": _roofline(wl, dom_ms, traffic, tinfo),
