@@ -44,6 +44,13 @@ __device__ __forceinline__ void wait_vm() {
 // LDS visibility comes from the explicit vmcnt wait before the barrier (DMA
 // writes) and from every fragment read having been consumed before it; the
 // empty asm statements keep the compiler from moving memory accesses across.
+// This wave's LDS (and scalar memory) accesses are complete.
+__device__ __forceinline__ void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

@@ -967,23 +967,40 @@ __device__ __forceinline__ void compute_res(const uint8_t *st, f32x16 (&acc)[2][
   }
 }
 
-// Group g's half of one merged step (64 elements): A = the merged fp16
-// activation rows, B = weight codes decoded with their block scales.  The
-// contraction order is the residual step's with the operands swapped: lane
-// half h of group g takes elements [32h + 16g, +16) of the step.
+// A merged step's B code words and scale bytes for a wave, read from LDS a
+// step ahead of their use so that the B decode can start right after the
+// barrier.  Group g's half of one merged step is 64 elements: A = the merged
+// fp16 activation rows, B = weight codes decoded with their block scales;
+// the contraction order is the residual step's with the operands swapped
+// (lane half h of group g takes elements [32h + 16g, +16) of the step).
 template <int NI>
-__device__ __forceinline__ void compute_merged(const uint8_t *st, f32x16 (&acc)[2][NI], int wm, int wn, int g,
-                                               int lane) {
+struct MergedB {
+  uint2 cb[NI];
+  uint32_t sb[NI];
+};
+
+template <int NI>
+__device__ __forceinline__ void read_merged_b(const uint8_t *st, MergedB<NI> &f, int wn, int g, int lane) {
   using L = Lay<NI>;
   const int r = lane & 31, h = lane >> 5;
-  uint2 cb[NI];
-  h2 sb[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = wn * 32 * NI + i * 32 + r;
-    cb[i] = *reinterpret_cast<const uint2 *>(st + L::XB + row * 32 + slot32(row, h) * 16 + 8 * g);
-    sb[i] = scale_h2(st[L::XBS + row * 4 + 2 * h + g]);
+    f.cb[i] = *reinterpret_cast<const uint2 *>(st + L::XB + row * 32 + slot32(row, h) * 16 + 8 * g);
+    f.sb[i] = st[L::XBS + row * 4 + 2 * h + g];
   }
+}
+
+// One merged step with the B fragments already read: A rows from LDS, B
+// decoded, 2 * NI MFMAs per half.
+template <int NI>
+__device__ __forceinline__ void mma_merged(const uint8_t *st, const MergedB<NI> &f, f32x16 (&acc)[2][NI], int wm,
+                                           int g, int lane) {
+  using L = Lay<NI>;
+  const int r = lane & 31, h = lane >> 5;
+  h2 sb[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) sb[i] = scale_h2(f.sb[i]);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint4 a[2], b[NI];
@@ -993,7 +1010,7 @@ __device__ __forceinline__ void compute_merged(const uint8_t *st, f32x16 (&acc)[
       a[i] = *reinterpret_cast<const uint4 *>(st + L::XA + row * 128 + slot128(row, 4 * h + 2 * g + j) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) b[i] = decode8_f16(j ? cb[i].y : cb[i].x, sb[i]);
+    for (int i = 0; i < NI; ++i) b[i] = decode8_f16(j ? f.cb[i].y : f.cb[i].x, sb[i]);
     mfmas<NI>(a, b, acc);
   }
 }
@@ -1011,7 +1028,7 @@ struct Dma {
 // (NI == 2 only): A is the RAC-merged fp16 activation p.x_f16, contracted
 // over K alone in 64-element steps; no residual segment.
 template <int NI, int EPI, bool HAS_RES, bool MERGED = false>
-__global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Params p) {
+__global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 4 : 1) void k_gemm_dma(Params p) {
   static_assert(!MERGED || (NI == 2 && !HAS_RES), "merged DMA steps: 128x128 tiles, no residual segment");
   using namespace dmak;
   using L = Lay<NI>;
@@ -1110,13 +1127,31 @@ __global__ __launch_bounds__(dmak::kThreads, NI == 2 ? 2 : 1) void k_gemm_dma(Pa
 #pragma unroll
       for (int q = 0; q < P; ++q) dma(dx[q].g + static_cast<int64_t>(k) * dx[q].stride, st + dx[q].lds, dx[q].bytes);
     };
+    // Step k+1's B codes and scales are read into registers right after the
+    // barrier of step k, so step k+1's decode starts without an LDS wait;
+    // step k's A rows are read from its stage.  Step k+2 is issued into the
+    // stage of step k-1, whose reads every wave has finished (each waits for
+    // its LDS reads before the barrier); step k+1 must have landed by the
+    // barrier of step k, one step of DMA look-ahead.
     issue_m(0);
     if (total > 1) issue_m(1);
-    for (int k = 0; k < total; ++k) {
-      if (k + 1 < total) wait_all_but_one_step<P>(); else wait_all();
-      barrier_no_fence();
-      if (k + 2 < total) issue_m(k + 2);
-      compute_merged<NI>(stage_m(k), acc, wm, wn, g, lane);
+    if (total > 1) wait_all_but_one_step<P>(); else wait_all();
+    barrier_no_fence();
+    MergedB<NI> f0, f1;
+    read_merged_b<NI>(stage_m(0), f0, wn, g, lane);
+    auto step = [&](int k, const MergedB<NI> &cur, MergedB<NI> &next) __attribute__((always_inline)) {
+      if (k + 1 < total) {
+        wait_all();
+        wait_lgkm0();
+        barrier_no_fence();
+        if (k + 2 < total) issue_m(k + 2);
+        read_merged_b<NI>(stage_m(k + 1), next, wn, g, lane);
+      }
+      mma_merged<NI>(stage_m(k), cur, acc, wm, g, lane);
+    };
+    for (int k = 0; k < total; k += 2) {
+      step(k, f0, f1);
+      if (k + 1 < total) step(k + 1, f1, f0);
     }
   } else {
   const int nm = static_cast<int>(K / kStepM);
