@@ -81,7 +81,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 struct Params {
   const int32_t *expert_offsets;
   const int32_t *tile_offsets;  // per-expert prefix of BM-row m-tiles
-  int E, n_seg, n_tiles, grid_per_xcd;
+  int E, n_seg, n_tiles;
   int64_t N, K, kpad;
   const int32_t *row_token;
   const uint8_t *x_codes, *x_scales;
@@ -158,19 +158,21 @@ struct Fp4Stage {
 
 template <int P>
 __device__ __forceinline__ void fp4_fetch(Fp4Stage<P> &st, const uint8_t *codes, const uint8_t *scales,
-                                          const int64_t (&base)[P], int nblk, int kt) {
+                                          const int64_t (&base)[P], int nblk, int kt, int part = -1) {
   const int blk = kt * 4 + (threadIdx.x & 3);
   st.ok = blk < nblk;
   const int off = st.ok ? blk : 0;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
+    if (part >= 0 && p % 4 != part) continue;
     st.w[p] = *reinterpret_cast<const uint2 *>(codes + (base[p] + off) * 8);
     st.s[p] = scales[base[p] + off];
   }
 }
 
 // Decode and store the blocks p of the stage with p % 4 == part (the store is
-// split in four parts so each can follow one MFMA sub-step).
+// split in four parts so each can follow one MFMA sub-step; the fetches take
+// the same parts, part -1 being the whole stage).
 // Row staged by thread t's lane quad: bits 0 and 1 of the quad index t/4 are
 // swapped, so each group of 8 lanes (the granularity at which a 16-byte LDS
 // write is serviced) covers two rows whose swizzle keys differ in bit 0 and
@@ -204,12 +206,13 @@ struct RawStage {
 
 template <int P>
 __device__ __forceinline__ void raw_fetch(RawStage<P> &st, const uint16_t *src, const int64_t (&base)[P],
-                                          int kdim, int kt) {
+                                          int kdim, int kt, int part = -1) {
   const int k = kt * BK + (threadIdx.x & 7) * 8;
   st.ok = k < kdim;
   const int off = st.ok ? k : 0;
 #pragma unroll
-  for (int q = 0; q < P; ++q) st.v[q] = *reinterpret_cast<const uint4 *>(src + base[q] + off);
+  for (int q = 0; q < P; ++q)
+    if (part < 0 || q % 4 == part) st.v[q] = *reinterpret_cast<const uint4 *>(src + base[q] + off);
 }
 
 template <int P, int THREADS>
@@ -310,14 +313,15 @@ __device__ __forceinline__ int64_t w_row_of(int tr, int nt, int64_t N) {
   }
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Branch-free two-buffer pipeline.  Before half h of an iteration, LDS buffer
 // h holds step kt+h and register stage 1-h holds step kt+h+1 (fetched one
-// step earlier); half h fetches step kt+h+2 into stage h, runs the MFMAs on
-// buffer h, decodes+stores stage 1-h into buffer 1-h, then synchronizes.
-// Fetch indices are clamped to the last step, so the tail re-reads (in
-// bounds) data it never uses.
+// step earlier); half h runs the MFMAs on buffer h and, after each of its
+// four sub-steps, fetches a quarter of step kt+h+2 into stage h and decodes+
+// stores a quarter of stage 1-h into buffer 1-h, then synchronizes.  Spread
+// this way, the loads of a step do not queue up behind each other at its
+// start.  Fetch indices are clamped to the last step, so the tail re-reads
+// (in bounds) data it never uses.
 template <class C, bool F16, class SA, class SB, class FetchA, class FetchB, class StoreA, class StoreB>
 __device__ __forceinline__ void k_loop(int nk, uint4 (*As)[C::BM * 8], uint4 (*Bs)[C::BN * 8],
                                        f32x16 (&acc)[C::MI][C::NI], int wm, int wn, int lane, FetchA fa,
@@ -326,10 +330,10 @@ __device__ __forceinline__ void k_loop(int nk, uint4 (*As)[C::BM * 8], uint4 (*B
   // blocks are past the end of K), so the loop body has no exit in between.
   SA s0, s1;
   SB t0, t1;
-  fa(s0, 0);
-  fb(t0, 0);
-  fa(s1, 1);
-  fb(t1, 1);
+  fa(s0, 0, -1);
+  fb(t0, 0, -1);
+  fa(s1, 1, -1);
+  fb(t1, 1, -1);
 #pragma unroll
   for (int part = 0; part < 4; ++part) {
     sta(s0, As[0], part);
@@ -337,16 +341,16 @@ __device__ __forceinline__ void k_loop(int nk, uint4 (*As)[C::BM * 8], uint4 (*B
   }
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    fa(s0, kt + 2);
-    fb(t0, kt + 2);
     mfma_step<C, F16>(As[0], Bs[0], acc, wm, wn, lane, [&](int part) {
+      fa(s0, kt + 2, part);
+      fb(t0, kt + 2, part);
       sta(s1, As[1], part);
       stb(t1, Bs[1], part);
     });
     __syncthreads();
-    fa(s1, kt + 3);
-    fb(t1, kt + 3);
     mfma_step<C, F16>(As[1], Bs[1], acc, wm, wn, lane, [&](int part) {
+      fa(s1, kt + 3, part);
+      fb(t1, kt + 3, part);
       sta(s0, As[0], part);
       stb(t0, Bs[0], part);
     });
@@ -355,34 +359,46 @@ __device__ __forceinline__ void k_loop(int nk, uint4 (*As)[C::BM * 8], uint4 (*B
 }
 
 // Map this workgroup to (expert e, rows [m0, min(m0+BM, mend)), n-tile nt).
-// XCD-aware remap: XCD x (= blockIdx % 8) gets logical tiles
-// [x * grid_per_xcd, (x + 1) * grid_per_xcd).  Returns false for surplus
-// workgroups (uniformly for the whole workgroup).  One expert (a dense GEMM)
-// needs no tile list: its tiles are read off expert_offsets[0..1].
+// The grid is an upper bound of the tile count (ragged experts); the real
+// count T comes from the tile list (or, for one expert, from its row range)
+// and is split into 8 contiguous ranges of ceil(T/8) tiles, range x on XCD x
+// (= blockIdx % 8), so every XCD gets the same share of real tiles and keeps
+// consecutive tiles (the n-tiles of one m-tile, then the m-tiles of one
+// expert) in its own L2.  Returns false for surplus workgroups (uniformly
+// for the whole workgroup).  One expert (a dense GEMM) needs no tile list.
 template <class C>
 __device__ __forceinline__ bool tile_setup(const Params &p, int &nt, int &e, int &m0, int &mend, int &s_e, int &s_m0,
                                            int &s_mend) {
-  const int logical = (blockIdx.x & 7) * p.grid_per_xcd + (blockIdx.x >> 3);
+  int lo = 0, hi = 0, mtiles;
+  if (p.E == 1) {
+    lo = p.expert_offsets[0];
+    hi = p.expert_offsets[1];
+    mtiles = hi > lo ? (hi - lo + C::BM - 1) / C::BM : 0;
+  } else {
+    mtiles = p.tile_offsets[p.E];
+  }
+  const int per_xcd = (mtiles * p.n_tiles + 7) / 8;
+  const int j = blockIdx.x >> 3;
+  if (j >= per_xcd) return false;
+  const int logical = (blockIdx.x & 7) * per_xcd + j;
   const int mt = logical / p.n_tiles;
   nt = logical % p.n_tiles;
+  if (mt >= mtiles) return false;
   if (p.E == 1) {
-    const int lo = p.expert_offsets[0], hi = p.expert_offsets[1];
-    if (hi <= lo || mt >= (hi - lo + C::BM - 1) / C::BM) return false;
     e = 0;
     m0 = lo + mt * C::BM;
     mend = hi;
     return true;
   }
-  if (mt >= p.tile_offsets[p.E]) return false;
   if (threadIdx.x == 0) {
-    int lo = 0, hi = p.E;  // largest e with tile_offsets[e] <= mt (skips empty experts)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tile_offsets[mid] <= mt) lo = mid; else hi = mid;
+    int l = 0, h = p.E;  // largest e with tile_offsets[e] <= mt (skips empty experts)
+    while (h - l > 1) {
+      const int mid = (l + h) >> 1;
+      if (p.tile_offsets[mid] <= mt) l = mid; else h = mid;
     }
-    s_e = lo;
-    s_m0 = p.expert_offsets[lo] + (mt - p.tile_offsets[lo]) * C::BM;
-    s_mend = p.expert_offsets[lo + 1];
+    s_e = l;
+    s_m0 = p.expert_offsets[l] + (mt - p.tile_offsets[l]) * C::BM;
+    s_mend = p.expert_offsets[l + 1];
   }
   __syncthreads();
   e = s_e;
@@ -502,8 +518,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
       bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
     k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
         static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](Fp4Stage<C::FA> &st, int kt) { fp4_fetch(st, p.x_codes, p.x_scales, abase, nblk, kt); },
-        [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
+        [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch(st, p.x_codes, p.x_scales, abase, nblk, kt, part); },
+        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
         [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
         [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
     if constexpr (HAS_RES) {
@@ -523,8 +539,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
         gbase[q] = (wbase + w_row_of<C, EPI>((threadIdx.x >> 3) + q * (T / 8), nt, p.N)) * p.kpad;
       k_loop<C, true, Fp4Stage<C::FA>, RawStage<C::HB>>(
           static_cast<int>((p.kpad + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-          [&](Fp4Stage<C::FA> &st, int kt) { fp4_fetch(st, p.r_codes, p.r_scales, rbase, rblk, kt); },
-          [&](RawStage<C::HB> &st, int kt) { raw_fetch(st, p.wg_f16, gbase, static_cast<int>(p.kpad), kt); },
+          [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch(st, p.r_codes, p.r_scales, rbase, rblk, kt, part); },
+          [&](RawStage<C::HB> &st, int kt, int part) { raw_fetch(st, p.wg_f16, gbase, static_cast<int>(p.kpad), kt, part); },
           [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
           [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
     }
@@ -538,8 +554,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
       bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
     k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
         static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt); },
-        [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
+        [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt, part); },
+        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
         [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
         [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
   } else if constexpr (MODE == 4) {
@@ -556,8 +572,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
     }
     k_loop<C, false, RawStage<C::HA>, Fp4Stage<C::FB>>(
         static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt); },
-        [&](Fp4Stage<C::FB> &st, int kt) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt); },
+        [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt, part); },
+        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
         [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
         [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_qdq_store<C::FB, T>(st, tile, part, gq); });
   } else if constexpr (MODE == 3) {
@@ -573,8 +589,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
     }
     k_loop<C, false, RawStage<C::HA>, RawStage<C::HB>>(
         static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt); },
-        [&](RawStage<C::HB> &st, int kt) { raw_fetch(st, p.w_bf16, bbase, static_cast<int>(p.K), kt); },
+        [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt, part); },
+        [&](RawStage<C::HB> &st, int kt, int part) { raw_fetch(st, p.w_bf16, bbase, static_cast<int>(p.K), kt, part); },
         [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
         [&](const RawStage<C::HB> &st, uint4 *tile, int part) { qdq_store<C::HB, T>(st, tile, part, gq); });
   } else {
@@ -585,8 +601,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
     for (int q = 0; q < C::HB; ++q) bbase[q] = (wbase + w_row_of<C, EPI>((threadIdx.x >> 3) + q * (T / 8), nt, p.N)) * p.K;
     k_loop<C, false, RawStage<C::HA>, RawStage<C::HB>>(
         static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](RawStage<C::HA> &st, int kt) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt); },
-        [&](RawStage<C::HB> &st, int kt) { raw_fetch(st, p.w_bf16, bbase, static_cast<int>(p.K), kt); },
+        [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_bf16, abase, static_cast<int>(p.K), kt, part); },
+        [&](RawStage<C::HB> &st, int kt, int part) { raw_fetch(st, p.w_bf16, bbase, static_cast<int>(p.K), kt, part); },
         [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
         [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
   }
@@ -1576,7 +1592,6 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   const int64_t m_tiles = (a.num_rows + bm - 1) / bm + a.E;
   int64_t grid = m_tiles * p.n_tiles;
   grid = (grid + 7) / 8 * 8;
-  p.grid_per_xcd = static_cast<int>(grid / 8);
   const int g = static_cast<int>(grid);
   if (c == kD) launch_dma<2>(a, p, g, res, stream, merged);
   else if (c == kP) launch_pp_cfg(a, p, g, res, stream);

@@ -260,7 +260,7 @@ __device__ __forceinline__ float store_out(const SmallParams &p, int64_t row, in
 
 // h = silu(g) * u stored as bf16; returns |stored value|.
 __device__ __forceinline__ float store_swiglu(const SmallParams &p, int64_t idx, float g, float u) {
-  const uint32_t hb = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
+  const uint32_t hb = f32_to_bf16_bits(silu(g) * u);
   static_cast<uint16_t *>(p.y)[idx] = static_cast<uint16_t>(hb);
   return fabsf(bf16_bits_to_f32(hb));
 }

@@ -75,6 +75,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// silu(z) = z / (1 + e^-z) in FP32 for the SwiGLU epilogues: e^-z as
+// 2^(-z log2 e) (v_exp_f32) and the quotient as z times the hardware
+// reciprocal (v_rcp_f32), a few ulp of FP32 against the bf16 rounding (2^-9)
+// of the stored product.  Large |z| give the limits: z >> 0 -> z, z << 0 -> -0.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
+
 // One 16-element block quantized: packed codes (element i in nibble i of the
 // 64-bit word lo | hi << 32) and the E4M3 scale byte.
 struct BlockQ {
