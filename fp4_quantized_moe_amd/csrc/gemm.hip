@@ -215,13 +215,16 @@ __device__ __forceinline__ void raw_fetch(RawStage<P> &st, const uint16_t *src, 
     if (part < 0 || q % 4 == part) st.v[q] = *reinterpret_cast<const uint4 *>(src + base[q] + off);
 }
 
-template <int P, int THREADS>
+// ZERO: chunks past the end of K are stored as zeros.  An activation operand
+// whose weight operand is zeroed there (every NVFP4 or bf16 weight stager
+// here) skips it: its re-read in-bounds values meet zero weights.
+template <int P, int THREADS, bool ZERO = true>
 __device__ __forceinline__ void raw_store(const RawStage<P> &st, uint4 *tile, int part) {
   const int c = threadIdx.x & 7;
 #pragma unroll
   for (int q = 0; q < P; ++q)
     if (q % 4 == part)
-      tile[swz((threadIdx.x >> 3) + q * (THREADS / 8), c)] = st.ok ? st.v[q] : make_uint4(0, 0, 0, 0);
+      tile[swz((threadIdx.x >> 3) + q * (THREADS / 8), c)] = (!ZERO || st.ok) ? st.v[q] : make_uint4(0, 0, 0, 0);
 }
 
 template <int P, int THREADS>
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
         static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
         [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt, part); },
         [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
-        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T>(st, tile, part); },
+        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
         [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
   } else if constexpr (MODE == 4) {
     const int nblk = static_cast<int>(p.K / 16);

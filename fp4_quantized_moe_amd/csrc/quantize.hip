@@ -181,17 +181,22 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
   const int64_t r_end = min(static_cast<int64_t>(rc + 1) * p.RW, p.rows);
   int64_t r = static_cast<int64_t>(rc) * p.RW + rg;
 
-  Raw16<BF16> x0, x1;
-  bool two = false;
-  int64_t row0 = 0, row1 = 0;
-  auto issue = [&]() {
-    two = r + p.RG < r_end;
-    row0 = static_cast<int64_t>(b) * p.rows + r;
-    row1 = row0 + (two ? p.RG : 0);
-    load_raw16<BF16>(p.x, row0 * p.cols + gbc * 16, x0);
-    load_raw16<BF16>(p.x, row1 * p.cols + gbc * 16, x1);
+  // Rows are taken in pairs (r, r + RG); the next pair's loads are in
+  // flight while the current pair is quantized.
+  struct Pair {
+    Raw16<BF16> x[2];
+    int64_t row[2];
+    bool two;
   };
-  if (active && r < r_end) issue();  // in flight while the tensor scale is folded
+  Pair pa, pb;
+  auto issue = [&](Pair &q, int64_t rr) {
+    q.two = rr + p.RG < r_end;
+    q.row[0] = static_cast<int64_t>(b) * p.rows + rr;
+    q.row[1] = q.row[0] + (q.two ? p.RG : 0);
+    load_raw16<BF16>(p.x, q.row[0] * p.cols + gbc * 16, q.x[0]);
+    load_raw16<BF16>(p.x, q.row[1] * p.cols + gbc * 16, q.x[1]);
+  };
+  if (active && r < r_end) issue(pa, r);  // in flight while the tensor scale is folded
 
   float g;
   if (p.gscale_given) {
@@ -208,37 +213,44 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) smax[i] = 0.0f;
 
-  if (active) {
-    // Two row steps per iteration: both loads are in flight before either
-    // block is quantized.
-    while (r < r_end) {
+  auto quantize_pair = [&](const Pair &q) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (u == 1 && !two) break;
-        const int64_t row = u ? row1 : row0;
-        float v[16];
-        to_f32<BF16>(u ? x1 : x0, v);
-        float dq[16];
-        const BlockQ q = quantize_block16(v, ts, (SCORES || QDQ) ? dq : nullptr);
-        if constexpr (CODES) {
-          reinterpret_cast<uint2 *>(p.codes)[row * p.cb + gbc] = make_uint2(q.lo, q.hi);
-          p.scales[row * p.cb + gbc] = static_cast<uint8_t>(q.scale);
-        }
-        if constexpr (QDQ) {
-          uint32_t w[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(dq[2 * i], dq[2 * i + 1]);
-          uint4 *o = reinterpret_cast<uint4 *>(p.qdq + row * p.cols + gbc * 16);
-          o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-          o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        }
-        if constexpr (SCORES) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) smax[i] = fmaxf(smax[i], fabsf(v[i] - dq[i]));
-        }
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !q.two) break;
+      const int64_t row = q.row[u];
+      float v[16];
+      to_f32<BF16>(q.x[u], v);
+      float dq[16];
+      const BlockQ bq = quantize_block16(v, ts, (SCORES || QDQ) ? dq : nullptr);
+      if constexpr (CODES) {
+        reinterpret_cast<uint2 *>(p.codes)[row * p.cb + gbc] = make_uint2(bq.lo, bq.hi);
+        p.scales[row * p.cb + gbc] = static_cast<uint8_t>(bq.scale);
       }
-      r += 2 * p.RG;
-      if (r < r_end) issue();
+      if constexpr (QDQ) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(dq[2 * i], dq[2 * i + 1]);
+        uint4 *o = reinterpret_cast<uint4 *>(p.qdq + row * p.cols + gbc * 16);
+        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+      if constexpr (SCORES) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) smax[i] = fmaxf(smax[i], fabsf(v[i] - dq[i]));
+      }
+    }
+  };
+  if (active && r < r_end) {
+    for (;;) {
+      const int64_t r1 = r + 2 * p.RG;
+      if (r1 < r_end) issue(pb, r1);
+      quantize_pair(pa);
+      if (r1 >= r_end) break;
+      const int64_t r2 = r1 + 2 * p.RG;
+      if (r2 < r_end) issue(pa, r2);
+      quantize_pair(pb);
+      if (r2 >= r_end) break;
+      r = r2;
     }
   }
 
@@ -366,7 +378,11 @@ hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
   qp.RG = kThreads / qp.BC;
   qp.col_chunks = static_cast<int>((qp.cb + qp.BC - 1) / qp.BC);
   const int64_t steps = a.batch * ((a.rows + qp.RG - 1) / qp.RG) * qp.col_chunks;
+  // About 1024 workgroups, but at least 4 row steps (two pipelined pairs) per
+  // workgroup while that still leaves 512 of them (4096 x 2048 bf16 with
+  // scores: 15.3 -> 13.9 us per call).
   int64_t iters = steps / 1024;
+  if (iters < 4) iters = steps / 512 < 4 ? steps / 512 : 4;
   if (iters < 1) iters = 1;
   if (iters > 64) iters = 64;
   qp.RW = static_cast<int>(qp.RG * iters);
