@@ -83,6 +83,7 @@ struct Params {
   const int32_t *tile_offsets;  // per-expert prefix of BM-row m-tiles
   int E, n_seg, n_tiles;
   int64_t N, K, kpad;
+  int64_t act_rows;  // rows of the activation tensors
   const int32_t *row_token;
   const uint8_t *x_codes, *x_scales;
   const float *x_g;
@@ -218,6 +219,47 @@ __device__ __forceinline__ void raw_fetch(RawStage<P> &st, const uint16_t *src, 
 // ZERO: chunks past the end of K are stored as zeros.  An activation operand
 // whose weight operand is zeroed there (every NVFP4 or bf16 weight stager
 // here) skips it: its re-read in-bounds values meet zero weights.
+// Buffer-resource forms of the two fetchers (large tiles): each lane's byte
+// offset inside the resource is fixed for the tile and the K step goes into
+// the scalar offset, so a step's loads take no address arithmetic.  Reads
+// past the resource's end return 0, and the stagers zero what lies past K,
+// so no offset is clamped.  Offsets and sizes fit 32 bits (host-checked).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int64_t bytes) {
+  // word 3: 32-bit data format (gfx9 raw buffer)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(static_cast<uint32_t>(bytes)), 0x00020000);
+}
+
+// blk0[p]: the lane's first block index in the resource (row * nblk + t % 4).
+template <int P>
+__device__ __forceinline__ void fp4_fetch_buf(Fp4Stage<P> &st, __amdgpu_buffer_rsrc_t codes,
+                                              __amdgpu_buffer_rsrc_t scales, const uint32_t (&blk0)[P], int nblk,
+                                              int kt, int part) {
+  st.ok = kt * 4 + (threadIdx.x & 3) < nblk;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (part >= 0 && p % 4 != part) continue;
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(codes, blk0[p] * 8u, kt * 32, 0);
+    st.w[p] = make_uint2(w[0], w[1]);
+    st.s[p] = __builtin_amdgcn_raw_buffer_load_b8(scales, blk0[p], kt * 4, 0);
+  }
+}
+
+// ofs[q]: the lane's byte offset of step 0 (2 * (row * kdim + (t % 8) * 8)).
+template <int P>
+__device__ __forceinline__ void raw_fetch_buf(RawStage<P> &st, __amdgpu_buffer_rsrc_t src, const uint32_t (&ofs)[P],
+                                              int kdim, int kt, int part) {
+  st.ok = kt * BK + (threadIdx.x & 7) * 8 < kdim;
+#pragma unroll
+  for (int q = 0; q < P; ++q)
+    if (part < 0 || q % 4 == part) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(src, ofs[q], kt * (2 * BK), 0);
+      st.v[q] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
 template <int P, int THREADS, bool ZERO = true>
 __device__ __forceinline__ void raw_store(const RawStage<P> &st, uint4 *tile, int part) {
   const int c = threadIdx.x & 7;
@@ -519,12 +561,31 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
 #pragma unroll
     for (int q = 0; q < C::FB; ++q)
       bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
-    k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
-        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch(st, p.x_codes, p.x_scales, abase, nblk, kt, part); },
-        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
-        [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
-        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    if constexpr (C::BM == 256) {
+      // activation and this expert's weights as buffer resources
+      const int64_t wrows = p.N;
+      const auto xc = buf_rsrc(p.x_codes, p.act_rows * (p.K / 2)), xs = buf_rsrc(p.x_scales, p.act_rows * nblk);
+      const auto wc = buf_rsrc(p.w_codes + wbase * (p.K / 2), wrows * (p.K / 2));
+      const auto ws = buf_rsrc(p.w_scales + wbase * nblk, wrows * nblk);
+      uint32_t ablk[C::FA], bblk[C::FB];
+#pragma unroll
+      for (int q = 0; q < C::FA; ++q) ablk[q] = static_cast<uint32_t>(abase[q] + (threadIdx.x & 3));
+#pragma unroll
+      for (int q = 0; q < C::FB; ++q) bblk[q] = static_cast<uint32_t>(bbase[q] - wbase * nblk + (threadIdx.x & 3));
+      k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
+          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+          [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch_buf(st, xc, xs, ablk, nblk, kt, part); },
+          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch_buf(st, wc, ws, bblk, nblk, kt, part); },
+          [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
+          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    } else {
+      k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
+          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+          [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch(st, p.x_codes, p.x_scales, abase, nblk, kt, part); },
+          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
+          [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
+          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    }
     if constexpr (HAS_RES) {
       const float ratio = *p.x_g / *p.r_g;
 #pragma unroll
@@ -555,12 +616,29 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
 #pragma unroll
     for (int q = 0; q < C::FB; ++q)
       bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
-    k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
-        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-        [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt, part); },
-        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
-        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
-        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    if constexpr (C::BM == 256) {
+      const auto xa = buf_rsrc(p.x_f16, p.act_rows * p.K * 2);
+      const auto wc = buf_rsrc(p.w_codes + wbase * (p.K / 2), p.N * (p.K / 2));
+      const auto ws = buf_rsrc(p.w_scales + wbase * nblk, p.N * nblk);
+      uint32_t aofs[C::HA], bblk[C::FB];
+#pragma unroll
+      for (int q = 0; q < C::HA; ++q) aofs[q] = static_cast<uint32_t>(2 * (abase[q] + (threadIdx.x & 7) * 8));
+#pragma unroll
+      for (int q = 0; q < C::FB; ++q) bblk[q] = static_cast<uint32_t>(bbase[q] - wbase * nblk + (threadIdx.x & 3));
+      k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
+          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+          [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch_buf(st, xa, aofs, static_cast<int>(p.K), kt, part); },
+          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch_buf(st, wc, ws, bblk, nblk, kt, part); },
+          [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
+          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    } else {
+      k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
+          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+          [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt, part); },
+          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
+          [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
+          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
+    }
   } else if constexpr (MODE == 4) {
     const int nblk = static_cast<int>(p.K / 16);
     int64_t abase[C::HA], bbase[C::FB];
@@ -1471,9 +1549,19 @@ bool use_merged(const GemmLaunch &a) {
   return c == kL || c == kP;
 }
 
+// The large-tile NVFP4 kernel addresses the activation tensor and one
+// expert's weights through buffer resources: 32-bit byte offsets.
+bool buf_fits(const GemmLaunch &a, bool merged) {
+  constexpr int64_t kMax = int64_t(1) << 32;
+  const int64_t act = merged ? a.act_rows * a.K * 2 : a.act_rows * (a.K / 2);
+  return act < kMax && a.N * (a.K / 2) < kMax;
+}
+
 TileCfg pick_cfg_for(const GemmLaunch &a) {
   TileCfg c = pick_cfg(a);
-  if (use_merged(a) && c == kP) c = kL;  // kD and kL have a merged form
+  const bool merged = use_merged(a);
+  if (merged && c == kP) c = kL;  // kD and kL have a merged form
+  if (c == kL && !buf_fits(a, merged)) c = dma_fits(a) ? kD : kS;
   return c;
 }
 
@@ -1574,6 +1662,7 @@ hipError_t launch_gemm_main(const GemmLaunch &a, hipStream_t stream) {
   p.N = a.N;
   p.K = a.K;
   p.kpad = a.kpad;
+  p.act_rows = a.act_rows;
   p.row_token = a.row_token;
   p.x_codes = a.x_codes;
   p.x_scales = a.x_scales;
