@@ -307,6 +307,10 @@ __device__ __forceinline__ void load_frags(Frags<C> &f, const uint4 *As, const u
   for (int ni = 0; ni < C::NI; ++ni) f.b[ni] = Bs[swz(wn * C::TN + ni * 32 + (lane & 31), chunk)];
 }
 
+// The weight fragment is the MFMA's first operand and the activation the
+// second, so each accumulator holds a 32x32 block of Y transposed: lane l has
+// output row l % 32 and, in registers 4j..4j+3, the four consecutive columns
+// 8j + 4(l / 32) + 0..3, which the epilogue stores as one vector.
 template <class C, bool F16>
 __device__ __forceinline__ void mfmas(const Frags<C> &f, f32x16 (&acc)[C::MI][C::NI]) {
 #pragma unroll
@@ -314,11 +318,11 @@ __device__ __forceinline__ void mfmas(const Frags<C> &f, f32x16 (&acc)[C::MI][C:
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni) {
       if constexpr (F16)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, f.a[mi]),
-                                                             __builtin_bit_cast(h8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, f.b[ni]),
+                                                             __builtin_bit_cast(h8, f.a[mi]), acc[mi][ni], 0, 0, 0);
       else
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, f.a[mi]), __builtin_bit_cast(bf16x8, f.b[ni]), acc[mi][ni], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, f.b[ni]), __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni], 0, 0, 0);
     }
 }
 
@@ -453,13 +457,106 @@ __device__ __forceinline__ bool tile_setup(const Params &p, int &nt, int &e, int
 }
 
 // Scale, optional SwiGLU, and store one wave's accumulators.
-template <class C, int MODE, int EPI, bool HAS_RES>
+template <class C, int MODE, int EPI, bool HAS_RES, bool TRANS = false>
 __device__ __forceinline__ float epilogue(const Params &p, f32x16 (&acc)[C::MI][C::NI], int e, int m0, int mend,
-                                          int nt, int wm, int wn, int lane) {
+                                          int nt, int wm, int wn, int lane, float *stage = nullptr) {
   float hmax = 0.0f;  // largest |stored bf16 value| (NaN skipped), for the output's tensor scale
   float ascale = 1.0f;
   if constexpr (MODE == 0) ascale = HAS_RES ? *p.r_g : *p.x_g;
   if constexpr (MODE == 2) ascale = *p.x_g;
+  if constexpr (TRANS) {
+    // Accumulators hold Y transposed (see mfmas): four consecutive columns
+    // per register group, stored as one 16-byte (FP32) or 8-byte (bf16)
+    // vector.  Segments and SwiGLU halves are multiples of 32 columns, so a
+    // group never straddles them.
+    if constexpr (EPI == 0) {
+      // Through this wave's LDS stage, one 32-row block (mi) at a time: the
+      // scaled accumulators go in as 16-byte row pieces (rows padded by 16
+      // bytes so the 32 rows of a write fall in distinct banks), and come
+      // back out as whole row segments, TN/4 lanes per row, so each store
+      // instruction writes 64/(TN/4) full segments of TN columns.
+      const int64_t seg_len = p.N / p.n_seg;
+      constexpr int RS = C::TN + 4;         // floats per staged row
+      constexpr int LPR = C::TN / 4;        // lanes per row on the way out
+      constexpr int RPI = 64 / LPR;         // rows per store instruction
+      const int64_t col0 = static_cast<int64_t>(nt) * C::BN + wn * C::TN;
+      float sc[C::NI][4];
+#pragma unroll
+      for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[ni][j] = ascale;
+          if constexpr (MODE < 3 && MODE != 1)
+            sc[ni][j] = p.w_g[e * p.n_seg + (col0 + ni * 32 + 8 * j + 4 * (lane >> 5)) / seg_len] * ascale;
+        }
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(stage + (lane & 31) * RS + ni * 32 + 8 * j + 4 * (lane >> 5)) =
+                make_float4(acc[mi][ni][4 * j] * sc[ni][j], acc[mi][ni][4 * j + 1] * sc[ni][j],
+                            acc[mi][ni][4 * j + 2] * sc[ni][j], acc[mi][ni][4 * j + 3] * sc[ni][j]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int t = 0; t < 32 / RPI; ++t) {
+          const int r = t * RPI + lane / LPR, c4 = (lane % LPR) * 4;
+          const float4 v = *reinterpret_cast<const float4 *>(stage + r * RS + c4);
+          const int i = m0 + wm * C::TM + mi * 32 + r;
+          if (i < mend) {
+            const int64_t at = static_cast<int64_t>(i) * p.N + col0 + c4;
+            if (p.y_bf16) {
+              const uint32_t h0 = f32_to_bf16_bits(v.x), h1 = f32_to_bf16_bits(v.y), h2b = f32_to_bf16_bits(v.z),
+                             h3 = f32_to_bf16_bits(v.w);
+              hmax = fmaxf(fmaxf(fmaxf(hmax, fabsf(bf16_bits_to_f32(h0))), fabsf(bf16_bits_to_f32(h1))),
+                           fmaxf(fabsf(bf16_bits_to_f32(h2b)), fabsf(bf16_bits_to_f32(h3))));
+              *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + at) = make_uint2(h0 | (h1 << 16), h2b | (h3 << 16));
+            } else {
+              *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + at) = v;
+            }
+          }
+        }
+      }
+    } else {
+      static_assert(EPI == 0 || C::NI % 2 == 0, "SWIGLU needs an even number of 32-column tiles per wave");
+      const int64_t I = p.N / 2;
+      float sg = ascale, su = ascale;
+      if constexpr (MODE < 3 && MODE != 1) {
+        sg = p.w_g[e * 2] * ascale;
+        su = p.w_g[e * 2 + 1] * ascale;
+      }
+#pragma unroll
+      for (int ni = 0; ni < C::NI / 2; ++ni)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col =
+              static_cast<int64_t>(nt) * (C::BN / 2) + wn * (C::TN / 2) + ni * 32 + 8 * j + 4 * (lane >> 5);
+#pragma unroll
+          for (int mi = 0; mi < C::MI; ++mi) {
+            const int i = m0 + wm * C::TM + mi * 32 + (lane & 31);
+            if (i < mend) {
+              uint32_t hb[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const float g = acc[mi][ni][4 * j + u] * sg;
+                const float up = acc[mi][ni + C::NI / 2][4 * j + u] * su;
+                hb[u] = f32_to_bf16_bits(silu(g) * up);
+                hmax = fmaxf(hmax, fabsf(bf16_bits_to_f32(hb[u])));
+              }
+              *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + static_cast<int64_t>(i) * I + col) =
+                  make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+            }
+          }
+        }
+    }
+    return hmax;
+  }
   if constexpr (EPI == 0) {
     const int64_t seg_len = p.N / p.n_seg;
 #pragma unroll
@@ -688,7 +785,14 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
         [&](const RawStage<C::HB> &st, uint4 *tile, int part) { raw_store<C::HB, T>(st, tile, part); });
   }
 
-  const float hmax = epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  // Per-wave epilogue stages in the operand tiles (free after the last step):
+  // half the waves in As, half in Bs.
+  constexpr int kWaves = C::THREADS / 64, kPerArr = kWaves / 2;
+  static_assert(kPerArr * 32 * (C::TN + 4) * 4 <= static_cast<int>(sizeof(As)) &&
+                    kPerArr * 32 * (C::TN + 4) * 4 <= static_cast<int>(sizeof(Bs)),
+                "epilogue stages fit in the operand tiles");
+  float *stage = reinterpret_cast<float *>(wave < kPerArr ? &As[0][0] : &Bs[0][0]) + (wave % kPerArr) * 32 * (C::TN + 4);
+  const float hmax = epilogue<C, MODE, EPI, HAS_RES, true>(p, acc, e, m0, mend, nt, wm, wn, lane, stage);
   if (p.amax_ws != nullptr) amax_gather(p.amax_ws, hmax);
 }
 
@@ -915,7 +1019,9 @@ __global__ __launch_bounds__(CfgPP::THREADS, 1) void k_gemm_pp(Params p) {
                    [&]() __attribute__((always_inline)) { fetch(0); store(0); fetch(1); },
                    [&](int k, int buf) __attribute__((always_inline)) { store(buf); fetch(k + 2); });
   }
-  epilogue<C, MODE, EPI, HAS_RES>(p, acc, e, m0, mend, nt, wm, wn, lane);
+  // per-wave epilogue stages in the operand tiles, free after the last step
+  float *stage = reinterpret_cast<float *>(wave < 4 ? &As[0][0] : &Bs[0][0]) + (wave % 4) * 32 * (C::TN + 4);
+  epilogue<C, MODE, EPI, HAS_RES, true>(p, acc, e, m0, mend, nt, wm, wn, lane, stage);
 }
 
 // ---- DMA-staged NVFP4 kernel (128 x 64NI tiles, 8 waves) ---------------------
