@@ -517,8 +517,10 @@ __device__ __forceinline__ float epilogue(const Params &p, f32x16 (&acc)[C::MI][
               hmax = fmaxf(fmaxf(fmaxf(hmax, fabsf(bf16_bits_to_f32(h0))), fabsf(bf16_bits_to_f32(h1))),
                            fmaxf(fabsf(bf16_bits_to_f32(h2b)), fabsf(bf16_bits_to_f32(h3))));
               *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + at) = make_uint2(h0 | (h1 << 16), h2b | (h3 << 16));
-            } else {
-              *reinterpret_cast<float4 *>(static_cast<float *>(p.y) + at) = v;
+            } else {  // FP32 y leaves as a stream (a later kernel reads it back from HBM)
+              typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+              const f32x4_nt t = {v.x, v.y, v.z, v.w};
+              __builtin_nontemporal_store(t, reinterpret_cast<f32x4_nt *>(static_cast<float *>(p.y) + at));
             }
           }
         }
@@ -576,7 +578,7 @@ __device__ __forceinline__ float epilogue(const Params &p, f32x16 (&acc)[C::MI][
               static_cast<uint16_t *>(p.y)[static_cast<int64_t>(i) * p.N + col] = static_cast<uint16_t>(hb);
               hmax = fmaxf(hmax, fabsf(bf16_bits_to_f32(hb)));
             } else {
-              static_cast<float *>(p.y)[static_cast<int64_t>(i) * p.N + col] = v;
+              __builtin_nontemporal_store(v, static_cast<float *>(p.y) + static_cast<int64_t>(i) * p.N + col);
             }
           }
         }

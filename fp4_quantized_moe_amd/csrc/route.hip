@@ -341,7 +341,12 @@ __global__ __launch_bounds__(256) void k_combine_top(const float *y, int64_t T, 
   }
   float4 v[TOP];
 #pragma unroll
-  for (int j = 0; j < TOP; ++j) v[j] = reinterpret_cast<const float4 *>(y + static_cast<int64_t>(rows[j]) * N)[c];
+  for (int j = 0; j < TOP; ++j) {  // y is read once: streamed past the caches
+    typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+    const f32x4_nt t = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4_nt *>(y + static_cast<int64_t>(rows[j]) * N) + c);
+    v[j] = make_float4(t[0], t[1], t[2], t[3]);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < TOP; ++j) {
