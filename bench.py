@@ -752,12 +752,15 @@ def measure_qdq(Q, S, args):
     warm = stage_times(ql["stages"])
     cold = cold_stage_times(ql["stages"], [n for n, _ in ql["stages"]])
     ms_w, ms_c = sum(warm.values()), sum(cold.values())
+    traffic, tinfo = _traffic({"traffic_summary": os.path.join(ROOT, "profiles", "k_quantize_qdq_trainer_traffic.txt")})
     blk = {"config": {"workload": "trainer_qdq_layer", "matrices": "128 experts x (gate, up, down) of 2048x1024 bf16",
                       "elements": ql["elems"]},
            "algorithmic_bytes": ql["bytes"], "ms_warm": ms_w, "ms_cold": ms_c,
            "roofline": {"bound": "hbm", "kernel": "k_quantize<bf16, QDQ> (quads_weight_qdq)",
                         "achieved": ql["bytes"] / (ms_c * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": ql["bytes"] / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                        "frac": ql["bytes"] / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
+                        "traffic_note": (tinfo if traffic is None else
+                                         tinfo + "; the launch time here also holds the amax pass over the masters"),
                         "bytes_per_launch": ql["bytes"] / 2, "avg_launch_ms": ms_c / 2},
            "GBps_warm": ql["bytes"] / (ms_w * 1e-3) / 1e9}
     if not args.no_cpu_baseline:
