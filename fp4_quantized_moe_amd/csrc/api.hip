@@ -299,6 +299,9 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
       g.w_g = a->w_gscale;
     }
   }
+  if (!quads::gemm_shape_supported(g))
+    return fail(QUADS_ERR_SHAPE,
+                "gemm: W4A4 activation or one expert's weights beyond 4 GiB need K %% 128 == 0 and kpad %% 64 == 0");
   return QUADS_OK;
 }
 

@@ -660,31 +660,22 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
 #pragma unroll
     for (int q = 0; q < C::FB; ++q)
       bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
-    if constexpr (C::BM == 256) {
-      // activation and this expert's weights as buffer resources
-      const int64_t wrows = p.N;
-      const auto xc = buf_rsrc(p.x_codes, p.act_rows * (p.K / 2)), xs = buf_rsrc(p.x_scales, p.act_rows * nblk);
-      const auto wc = buf_rsrc(p.w_codes + wbase * (p.K / 2), wrows * (p.K / 2));
-      const auto ws = buf_rsrc(p.w_scales + wbase * nblk, wrows * nblk);
-      uint32_t ablk[C::FA], bblk[C::FB];
+    // activation and this expert's weights as buffer resources
+    const int64_t wrows = p.N;
+    const auto xc = buf_rsrc(p.x_codes, p.act_rows * (p.K / 2)), xs = buf_rsrc(p.x_scales, p.act_rows * nblk);
+    const auto wc = buf_rsrc(p.w_codes + wbase * (p.K / 2), wrows * (p.K / 2));
+    const auto ws = buf_rsrc(p.w_scales + wbase * nblk, wrows * nblk);
+    uint32_t ablk[C::FA], bblk[C::FB];
 #pragma unroll
-      for (int q = 0; q < C::FA; ++q) ablk[q] = static_cast<uint32_t>(abase[q] + (threadIdx.x & 3));
+    for (int q = 0; q < C::FA; ++q) ablk[q] = static_cast<uint32_t>(abase[q] + (threadIdx.x & 3));
 #pragma unroll
-      for (int q = 0; q < C::FB; ++q) bblk[q] = static_cast<uint32_t>(bbase[q] - wbase * nblk + (threadIdx.x & 3));
-      k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
-          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-          [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch_buf(st, xc, xs, ablk, nblk, kt, part); },
-          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch_buf(st, wc, ws, bblk, nblk, kt, part); },
-          [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
-          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
-    } else {
-      k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
-          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-          [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch(st, p.x_codes, p.x_scales, abase, nblk, kt, part); },
-          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
-          [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
-          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
-    }
+    for (int q = 0; q < C::FB; ++q) bblk[q] = static_cast<uint32_t>(bbase[q] - wbase * nblk + (threadIdx.x & 3));
+    k_loop<C, true, Fp4Stage<C::FA>, Fp4Stage<C::FB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](Fp4Stage<C::FA> &st, int kt, int part) { fp4_fetch_buf(st, xc, xs, ablk, nblk, kt, part); },
+        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch_buf(st, wc, ws, bblk, nblk, kt, part); },
+        [&](const Fp4Stage<C::FA> &st, uint4 *tile, int part) { fp4_store<C::FA, T>(st, tile, part); },
+        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
     if constexpr (HAS_RES) {
       const float ratio = *p.x_g / *p.r_g;
 #pragma unroll
@@ -715,29 +706,20 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void k_gemm(Params p) {
 #pragma unroll
     for (int q = 0; q < C::FB; ++q)
       bbase[q] = (wbase + w_row_of<C, EPI>(fp4_row(threadIdx.x) + q * (T / 4), nt, p.N)) * nblk;
-    if constexpr (C::BM == 256) {
-      const auto xa = buf_rsrc(p.x_f16, p.act_rows * p.K * 2);
-      const auto wc = buf_rsrc(p.w_codes + wbase * (p.K / 2), p.N * (p.K / 2));
-      const auto ws = buf_rsrc(p.w_scales + wbase * nblk, p.N * nblk);
-      uint32_t aofs[C::HA], bblk[C::FB];
+    const auto xa = buf_rsrc(p.x_f16, p.act_rows * p.K * 2);
+    const auto wc = buf_rsrc(p.w_codes + wbase * (p.K / 2), p.N * (p.K / 2));
+    const auto ws = buf_rsrc(p.w_scales + wbase * nblk, p.N * nblk);
+    uint32_t aofs[C::HA], bblk[C::FB];
 #pragma unroll
-      for (int q = 0; q < C::HA; ++q) aofs[q] = static_cast<uint32_t>(2 * (abase[q] + (threadIdx.x & 7) * 8));
+    for (int q = 0; q < C::HA; ++q) aofs[q] = static_cast<uint32_t>(2 * (abase[q] + (threadIdx.x & 7) * 8));
 #pragma unroll
-      for (int q = 0; q < C::FB; ++q) bblk[q] = static_cast<uint32_t>(bbase[q] - wbase * nblk + (threadIdx.x & 3));
-      k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
-          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-          [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch_buf(st, xa, aofs, static_cast<int>(p.K), kt, part); },
-          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch_buf(st, wc, ws, bblk, nblk, kt, part); },
-          [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
-          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
-    } else {
-      k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
-          static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
-          [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch(st, p.x_f16, abase, static_cast<int>(p.K), kt, part); },
-          [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch(st, p.w_codes, p.w_scales, bbase, nblk, kt, part); },
-          [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
-          [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
-    }
+    for (int q = 0; q < C::FB; ++q) bblk[q] = static_cast<uint32_t>(bbase[q] - wbase * nblk + (threadIdx.x & 3));
+    k_loop<C, true, RawStage<C::HA>, Fp4Stage<C::FB>>(
+        static_cast<int>((p.K + BK - 1) / BK), As, Bs, acc, wm, wn, lane,
+        [&](RawStage<C::HA> &st, int kt, int part) { raw_fetch_buf(st, xa, aofs, static_cast<int>(p.K), kt, part); },
+        [&](Fp4Stage<C::FB> &st, int kt, int part) { fp4_fetch_buf(st, wc, ws, bblk, nblk, kt, part); },
+        [&](const RawStage<C::HA> &st, uint4 *tile, int part) { raw_store<C::HA, T, false>(st, tile, part); },
+        [&](const Fp4Stage<C::FB> &st, uint4 *tile, int part) { fp4_store<C::FB, T>(st, tile, part); });
   } else if constexpr (MODE == 4) {
     const int nblk = static_cast<int>(p.K / 16);
     int64_t abase[C::HA], bbase[C::FB];
@@ -1657,7 +1639,7 @@ bool use_merged(const GemmLaunch &a) {
   return c == kL || c == kP;
 }
 
-// The large-tile NVFP4 kernel addresses the activation tensor and one
+// The register-staged NVFP4 kernels address the activation tensor and one
 // expert's weights through buffer resources: 32-bit byte offsets.
 bool buf_fits(const GemmLaunch &a, bool merged) {
   constexpr int64_t kMax = int64_t(1) << 32;
@@ -1668,8 +1650,13 @@ bool buf_fits(const GemmLaunch &a, bool merged) {
 TileCfg pick_cfg_for(const GemmLaunch &a) {
   TileCfg c = pick_cfg(a);
   const bool merged = use_merged(a);
-  if (merged && c == kP) c = kL;  // kD and kL have a merged form
-  if (c == kL && !buf_fits(a, merged)) c = dma_fits(a) ? kD : kS;
+  if (merged && c == kP) c = kL;  // kD, kS and kL have a merged form
+  // The merged fp16 operand on 128x128 tiles: the register-staged kernel
+  // (4096 x 1536 x 2048 step 73 against 78 us); NVFP4 activation codes and
+  // the extended-K form stay on the DMA-staged kernel (51 against 53 us,
+  // 91 against 93.5 us).
+  if (merged && c == kD) c = kS;
+  if (a.mode == 0 && (c == kL || c == kS) && !buf_fits(a, merged)) c = kD;  // dma_fits (gemm_shape_supported)
   return c;
 }
 
@@ -1699,6 +1686,10 @@ __global__ __launch_bounds__(64) void k_fold_amax(uint32_t *words, float *gscale
   if (threadIdx.x == 0) *gscale = tensor_scale_from_amax(__uint_as_float(t));
 }
 }  // namespace
+
+bool gemm_shape_supported(const GemmLaunch &a) {
+  return a.mode != 0 || gemm_use_small(a) || buf_fits(a, use_merged(a)) || dma_fits(a);
+}
 
 size_t gemm_ws_bytes(const GemmLaunch &a) {
   return gemm_ws_base(a) + (a.y_gscale != nullptr ? kAmaxWords * sizeof(uint32_t) : 0);

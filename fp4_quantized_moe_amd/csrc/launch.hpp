@@ -89,6 +89,10 @@ struct GemmLaunch {
   float *y_gscale;           // NVFP4 tensor scale of the bf16 output, formed by the GEMM, or null
 };
 size_t gemm_ws_bytes(const GemmLaunch &a);
+// False when the W4A4 operands exceed what every kernel able to run the call
+// can address (32-bit offsets of the register-staged kernels, and the
+// DMA-staged kernel's shape limits K % 128, N % 128).
+bool gemm_shape_supported(const GemmLaunch &a);
 // The workspace words gathering the output amax behind y_gscale, or null.
 uint32_t *gemm_amax_words(const GemmLaunch &a);
 // After the main kernel: y_gscale from the gathered amax (no-op without it).

@@ -234,7 +234,11 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  * the up projection) writes h [num_rows, N/2] BF16 with
  * h = silu(Y_gate) * Y_up.
  *
- * Shapes: K % 16 == 0, N % 128 == 0, num_experts in [1, 1024].  expert_offsets is a DEVICE array of num_experts + 1
+ * Shapes: K % 16 == 0, N % 128 == 0, num_experts in [1, 1024].  W4A4 calls
+ * whose activation operand (codes, or the merged fp16 operand: act_rows x K)
+ * or one expert's weight codes reach 4 GiB additionally need K % 128 == 0
+ * and kpad % 64 == 0 (else QUADS_ERR_SHAPE): the register-staged kernels
+ * address those tensors with 32-bit offsets.  expert_offsets is a DEVICE array of num_experts + 1
  * non-decreasing int32 with expert_offsets[0] = 0 and
  * expert_offsets[E] = num_rows (not checked on the host: reading it would
  * synchronize).
