@@ -168,8 +168,8 @@ def setup_expert_gemm(Q, S, k):
         return M * reps / secs, secs, (f"the whole step ({M} tokens, K={K}, N={N}, k={k}%) x {reps} repetitions: "
                                        "oracle quantize + RAC + fp64 GEMM (weights quantized beforehand)")
 
-    kern = ("k_gemm_dma<2, 0, false, true> (merged RAC operand x NVFP4 weights, 128x128 DMA-staged tiles)"
-            if merged else "k_gemm_dma<2, 0, true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)")
+    kern = ("k_gemm<Cfg<128, 128, 2, 2, 2>, 2, 0, false> (merged RAC operand x NVFP4 weights, 128x128 "
+            "register-staged tiles)" if merged else "k_gemm_dma<2, 0, true> (W4A4 + RAC segment, 128x128 DMA-staged tiles)")
     summary = (f"k_gemm_merged_expert_gemm_k{k}_traffic.txt" if merged else f"k_gemm_dma_expert_gemm_k{k}_traffic.txt")
     return dict(stages=stages, plain=plain, tokens=M, flops=flops_alg, dominant="gemm", bound="mfma",
                 dominant_work=flops_alg, dominant_exec=flops_exec, dominant_kernel=kern, config=cfg,
