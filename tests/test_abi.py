@@ -161,6 +161,27 @@ def test_gemm_rac_form_field(L):
     assert L.quads_moe_w4a4_gemm(ctypes.byref(_gemm_args(rac_form=2, x_merged=16, **big)), None) == -3
 
 
+def test_gemm_32bit_offset_limit(L):
+    """The register-staged NVFP4 kernels address the activation tensor through
+    32-bit byte offsets; a larger W4A4 activation runs on the DMA-staged kernel,
+    which needs K % 128 == 0 (and kpad % 64 == 0 with a residual), and is
+    rejected as a shape error otherwise."""
+    rows = dict(num_rows=65536, act_rows=1 << 21)  # 2^21 rows x K/2 bytes >= 4 GiB
+    bad = _gemm_args(K=4112, **rows)
+    assert L.quads_moe_gemm_workspace_bytes(ctypes.byref(bad)) == 0
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(bad), None) == -2 and b"4 GiB" in L.quads_last_error()
+    good = _gemm_args(K=4224, **rows)
+    assert L.quads_moe_gemm_workspace_bytes(ctypes.byref(good)) > 0
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(good), None) == -3  # accepted; no workspace
+    # below the limit any multiple of 16 is accepted
+    small = _gemm_args(K=4112, num_rows=65536, act_rows=65536)
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(small), None) == -3
+    # with a residual the DMA kernel also needs kpad % 64 == 0
+    res = dict(r_codes=16, r_scales=16, r_gscale=16, sel_idx=16, rac_form=1, **rows)
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(_gemm_args(K=4224, kpad=48, **res)), None) == -2
+    assert L.quads_moe_w4a4_gemm(ctypes.byref(_gemm_args(K=4224, kpad=64, **res)), None) == -3
+
+
 def test_qdq_route_combine_validation(L):
     dummy = ctypes.c_void_p(16)
     assert L.quads_weight_qdq(dummy, 1, 4, 24, dummy, None, 0, dummy, 1 << 20, None) == -2
