@@ -177,7 +177,7 @@ def test_expert_gemm_full_size_merged_pipeline(k):
     """The expert-GEMM workload at full size (X 4096 x 2048 bf16, W 1536 x 2048)
     through the calls and launch configuration the throughput benchmark
     times: quads_rac_select_merged, then the GEMM on the caller's merged
-    operand (128x128 DMA-staged tiles, merged steps). The operand is
+    operand (128x128 register-staged tiles, merged steps). The operand is
     bit-exact against the oracle's rac_merged_operand and Y is within 1e-3
     of its float64 extended-K product."""
     wl = S.expert_gemm()
