@@ -70,10 +70,11 @@ size_t quads_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
 }
 
 // Argument checks shared by quads_quantize_nvfp4 and its no-allocation
-// variant; QUADS_OK with *done set when there is nothing to enqueue.
+// variant; QUADS_OK with *empty set for a call with no rows (no workspace or
+// scratch needed).
 static quads_status_t quantize_check(const void *x, quads_dtype_t dt, const quads_nvfp4_t &out, uint32_t flags,
-                                     float *scores, bool *done) {
-  *done = false;
+                                     float *scores, bool *empty) {
+  *empty = false;
   if (dt != QUADS_F32 && dt != QUADS_BF16) return fail(QUADS_ERR_ARG, "quantize: bad dtype %d", dt);
   if (flags & ~(QUADS_GSCALE_GIVEN | QUADS_WANT_SCORES)) return fail(QUADS_ERR_ARG, "quantize: unknown flags");
   if (out.batch < 1 || out.rows < 0 || out.cols <= 0) return fail(QUADS_ERR_SHAPE, "quantize: bad shape");
@@ -82,11 +83,12 @@ static quads_status_t quantize_check(const void *x, quads_dtype_t dt, const quad
     return fail(QUADS_ERR_SHAPE, "quantize: size overflow");
   if ((flags & QUADS_WANT_SCORES) && (out.batch != 1 || scores == nullptr))
     return fail(QUADS_ERR_ARG, "quantize: QUADS_WANT_SCORES needs batch == 1 and a scores buffer");
+  if (!out.gscale) return fail(QUADS_ERR_ARG, "quantize: null gscale");
   if (out.rows == 0) {
-    *done = true;
-    return ok();
+    *empty = true;  // only the tensor scales and scores are written
+    return QUADS_OK;
   }
-  if (!x || !out.codes || !out.scales || !out.gscale) return fail(QUADS_ERR_ARG, "quantize: null pointer");
+  if (!x || !out.codes || !out.scales) return fail(QUADS_ERR_ARG, "quantize: null pointer");
   if (misaligned({x, out.codes, out.scales})) return fail(QUADS_ERR_ARG, "quantize: arrays must be 16-byte aligned");
   return QUADS_OK;
 }
@@ -111,9 +113,13 @@ static quads::QuantizeLaunch quantize_launch(const void *x, quads_dtype_t dt, co
 
 quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, quads_nvfp4_t out, uint32_t flags,
                                             float *scores, void *stream) {
-  bool done = false;
-  const quads_status_t st = quantize_check(x, dt, out, flags, scores, &done);
-  if (st != QUADS_OK || done) return st;
+  bool empty = false;
+  const quads_status_t st = quantize_check(x, dt, out, flags, scores, &empty);
+  if (st != QUADS_OK) return st;
+  if (empty)
+    return device_status(quads::launch_quantize(quantize_launch(x, dt, out, flags, scores, nullptr),
+                                                static_cast<hipStream_t>(stream)),
+                         "quantize_noalloc");
   const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
   float *ws = nullptr;
   if (!given) {
@@ -133,9 +139,13 @@ quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, qua
 
 quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4_t out, uint32_t flags,
                                     float *scores, void *ws, size_t ws_bytes, void *stream) {
-  bool done = false;
-  const quads_status_t st = quantize_check(x, dt, out, flags, scores, &done);
-  if (st != QUADS_OK || done) return st;
+  bool empty = false;
+  const quads_status_t st = quantize_check(x, dt, out, flags, scores, &empty);
+  if (st != QUADS_OK) return st;
+  if (empty)
+    return device_status(quads::launch_quantize(quantize_launch(x, dt, out, flags, scores, nullptr),
+                                                static_cast<hipStream_t>(stream)),
+                         "quantize");
   const bool given = (flags & QUADS_GSCALE_GIVEN) != 0;
   if (!given && (ws == nullptr || ws_bytes < quads::quantize_ws_bytes(out.batch, out.rows, out.cols)))
     return fail(QUADS_ERR_WORKSPACE, "quantize: workspace too small (need %zu)",
@@ -203,7 +213,8 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
                                        void *merged_f16, void *ws, size_t ws_bytes, void *stream) {
   (void)ws;
   (void)ws_bytes;
-  if (!merged_f16) return fail(QUADS_ERR_ARG, "rac_select_merged: null merged_f16");
+  if (!merged_f16 && !(xq && xq->rows == 0))  // no rows: nothing to merge
+    return fail(QUADS_ERR_ARG, "rac_select_merged: null merged_f16");
   return rac_select_impl("rac_select_merged", x, dt, xq, scores, k_percent, sel_idx, res, merged_f16, stream);
 }
 

@@ -153,6 +153,15 @@ __global__ __launch_bounds__(kThreads) void k_zero_f32(float *p, int64_t n) {
     p[i] = 0.0f;
 }
 
+// An activation with no rows: the largest of no magnitudes is taken as 0, so
+// the tensor scale is 1 (the all-zero convention) and every channel score 0.
+__global__ __launch_bounds__(kThreads) void k_empty_tensor(float *gscale, int64_t batch, float *scores, int64_t cols) {
+  if (gscale != nullptr)
+    for (int64_t b = threadIdx.x; b < batch; b += kThreads) gscale[b] = 1.0f;
+  if (scores != nullptr)
+    for (int64_t c = threadIdx.x; c < cols; c += kThreads) scores[c] = 0.0f;
+}
+
 struct QParams {
   const void *x;
   int64_t rows, cols, cb;  // cb = cols / 16
@@ -346,6 +355,12 @@ hipError_t quantize_scratch(float **out) {
 }
 
 hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
+  if (a.rows == 0) {  // nothing to quantize: the tensor scales (unless given) and the scores
+    if (a.gscale_given && a.scores == nullptr) return hipSuccess;
+    hipLaunchKernelGGL(k_empty_tensor, dim3(1), dim3(kThreads), 0, stream, a.gscale_given ? nullptr : a.gscale,
+                       a.batch, a.scores, a.cols);
+    return hipGetLastError();
+  }
   const int64_t n = a.rows * a.cols;
   const int P = amax_partials_per_tensor(n);
   float *partials = static_cast<float *>(a.ws);

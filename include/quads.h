@@ -104,6 +104,10 @@ int64_t quads_rac_kpad(int64_t nsel);
  *
  * ws: device workspace of at least quads_quantize_workspace_bytes(batch,
  * rows, cols) bytes (cross-workgroup amax partials).
+ *
+ * rows == 0: x, codes, scales and ws are neither read nor written (they may be
+ * NULL); the largest of no magnitudes is taken as 0, so gscale[b] = 1 (unless
+ * QUADS_GSCALE_GIVEN) and, with QUADS_WANT_SCORES, every score is 0.
  * ------------------------------------------------------------------------- */
 size_t quads_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
 quads_status_t quads_quantize_nvfp4(const void *x, quads_dtype_t dt, quads_nvfp4_t out,
@@ -140,7 +144,9 @@ quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, qua
  *      amax is the largest selected score.
  * x / dt: the activation that produced xq (batch 1); scores from
  * quads_quantize_nvfp4(QUADS_WANT_SCORES).  res.cols must equal kpad; with
- * k such that kpad == 0 only res.gscale[0] = 1 is written.
+ * k such that kpad == 0 only res.gscale[0] = 1 is written.  With rows == 0
+ * the mask still comes from the scores (all 0 for an empty activation:
+ * sel_idx = 0 .. nsel-1, res.gscale[0] = 1) and no row is touched.
  * Channel count limit: cols <= 16384 (larger shapes return QUADS_ERR_SHAPE
  * before anything is enqueued).  Two kernels are enqueued on `stream`: the
  * mask (one workgroup), then the rows.
@@ -160,7 +166,8 @@ quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvf
  * and one fp32 addition before the rounding.  Passing it to
  * quads_moe_w4a4_gemm (x_merged) lets the GEMM contract over K alone with no
  * merge pass of its own.  With kpad == 0 nothing is written (there is no
- * correction; the GEMM then takes the plain path). */
+ * correction; the GEMM then takes the plain path); with rows == 0
+ * merged_f16 may be NULL. */
 quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
                                        const float *scores, int32_t k_percent, int32_t *sel_idx,
                                        quads_nvfp4_t res, void *merged_f16, void *ws, size_t ws_bytes,

@@ -276,8 +276,13 @@ def rac_residual(x, q):
 
 def rac_scores(x, q):
     """Channel score: max over all rows of |ΔX[:, c]| (the residual magnitude
-    the channel mask ranks by)."""
-    return np.abs(rac_residual(x, q)).max(axis=0).astype(np.float32)
+    the channel mask ranks by).  Over zero rows every score is 0: the largest
+    of no magnitudes is taken as 0, as tensor_scale takes the amax of an empty
+    tensor (the pages do not speak of an empty batch)."""
+    r = np.abs(rac_residual(x, q))
+    if r.shape[0] == 0:
+        return np.zeros(r.shape[1], dtype=np.float32)
+    return r.max(axis=0).astype(np.float32)
 
 
 def rac_select(scores, k_percent):

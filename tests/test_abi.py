@@ -58,8 +58,10 @@ def test_quantize_validation(L):
     # scores need batch == 1
     assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16, batch=2), 2, dummy, dummy, 1 << 20, None) == -1
     assert L.quads_quantize_nvfp4(dummy, 0, _nv(4, 16), 1 << 7, None, dummy, 1 << 20, None) == -1
-    # zero rows: valid no-op
-    assert L.quads_quantize_nvfp4(dummy, 0, _nv(0, 16), 0, None, dummy, 1 << 20, None) == 0
+    # zero rows still write the tensor scale (a GPU test checks the values),
+    # so a NULL gscale is rejected before anything is enqueued
+    assert L.quads_quantize_nvfp4(None, 0, _lib._NVFP4(None, None, None, 1, 0, 16), 0, None, None, 0, None) == -1
+    assert b"gscale" in L.quads_last_error()
     # misaligned arrays are rejected before anything is enqueued
     st = L.quads_quantize_nvfp4(ctypes.c_void_p(24), 0, _nv(4, 16), 0, None, dummy, 1 << 20, None)
     assert st == -1 and b"aligned" in L.quads_last_error()
@@ -95,7 +97,7 @@ def test_quantize_noalloc_validation(L):
     # 300 matrices of 4096 x 4096: 1024 partials each, 1.2 MB > 1 MiB
     assert L.quads_quantize_nvfp4_noalloc(dummy, 1, _nv(4096, 4096, batch=300), 0, None, None) == -3
     assert b"scratch" in L.quads_last_error()
-    assert L.quads_quantize_nvfp4_noalloc(dummy, 1, _nv(0, 4096), 0, None, None) == 0  # nothing to do
+    assert L.quads_quantize_nvfp4_noalloc(None, 1, _lib._NVFP4(None, None, None, 1, 0, 4096), 0, None, None) == -1
 
 
 def _gemm_args(**kw):

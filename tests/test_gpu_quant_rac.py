@@ -181,3 +181,30 @@ def test_quantize_near_ties_random_scales():
     for i in range(len(blocks)):
         r = O.quantize_nvfp4(x[i], g=gs[i])
         assert codes[i].tobytes() == r.codes.tobytes() and scales[i].tobytes() == r.scales.tobytes(), i
+
+
+@pytest.mark.parametrize("cols,k", [(2048, 50), (768, 25), (64, 100)])
+def test_empty_activation(cols, k):
+    """No rows: the tensor scale is 1 and every channel score 0 (the oracle's
+    reading: the largest of no magnitudes is 0), then the mask is the first
+    nsel channels and the residual's tensor scale is 1, with the plain and the
+    merged select.  Outputs start out poisoned, so each is seen written."""
+    log(f"[quant] empty activation cols={cols} k={k}")
+    x = torch.empty(0, cols, dtype=torch.bfloat16, device="cuda")
+    qc = Q.QuantizeCall(x, want_scores=True)
+    qc.q.gscale.fill_(7.0)
+    qc.scores.fill_(float("nan"))
+    q, scores = qc()
+    empty = np.zeros((0, cols), np.float32)
+    ref = O.quantize_nvfp4(empty)
+    sref = O.rac_scores(empty, ref)
+    assert host(q.gscale)[0] == ref.g == np.float32(1.0)
+    assert np.array_equal(host(scores).view(np.uint32), sref.view(np.uint32))
+    osel, on = O.rac_select(sref, k)
+    for merged in (False, True):
+        call = Q.SelectCall(x, q, scores, k, merged=merged)
+        call.sel.fill_(-1)
+        call.res.gscale.fill_(7.0)
+        sel, res, nsel = call()
+        assert nsel == on and np.array_equal(host(sel), osel)
+        assert host(res.gscale)[0] == O.rac_quantize_residual(empty, ref, osel, on).g == np.float32(1.0)

@@ -108,6 +108,24 @@ def test_scores_are_column_max_of_abs_residual():
         assert sc[c] == np.float32(m)
 
 
+def test_empty_activation_matches_an_all_zero_row():
+    """Zero rows: every channel score is 0 (the brute-force maximum above
+    starts from 0 and sees no row), the tensor scales are 1, and the mask is
+    the first nsel channels, exactly what a single all-zero row gives (its
+    residual is zero everywhere)."""
+    for cols, k in [(64, 50), (48, 25), (32, 100)]:
+        empty, zero = np.zeros((0, cols), np.float32), np.zeros((1, cols), np.float32)
+        qe, qz = O.quantize_nvfp4(empty), O.quantize_nvfp4(zero)
+        assert qe.g == qz.g == np.float32(1.0)
+        se, sz = O.rac_scores(empty, qe), O.rac_scores(zero, qz)
+        assert se.shape == (cols,) and se.dtype == np.float32 and np.array_equal(se, sz) and not se.any()
+        (sel_e, n_e), (sel_z, n_z) = O.rac_select(se, k), O.rac_select(sz, k)
+        assert n_e == n_z == O.rac_nsel(cols, k) and np.array_equal(sel_e, sel_z)
+        assert np.array_equal(sel_e[:n_e], np.arange(n_e))
+        r = O.rac_quantize_residual(empty, qe, sel_e, n_e)
+        assert r.g == np.float32(1.0) and r.codes.shape == (0, sel_e.shape[0] // 2)
+
+
 def test_activation_error_never_grows():
     """P7 (activation level, a theorem): adding the second-pass residual never
     moves an element farther from x than the first pass left it, up to one
