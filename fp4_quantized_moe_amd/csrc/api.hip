@@ -238,7 +238,9 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
     return fail(QUADS_ERR_SHAPE, "gemm: row counts must fit int32");
   if (!mul_ok(a->num_rows, a->N, kMaxElems) || !mul_ok(int64_t(a->num_experts) * a->N, a->K, kMaxElems))
     return fail(QUADS_ERR_SHAPE, "gemm: size overflow");
-  if (!a->expert_offsets || !a->y) return fail(QUADS_ERR_ARG, "gemm: null expert_offsets or y");
+  // No rows: y and the activation operands are not touched (they may be NULL).
+  const bool rows = a->num_rows > 0;
+  if (!a->expert_offsets || (rows && !a->y)) return fail(QUADS_ERR_ARG, "gemm: null expert_offsets or y");
   if (misaligned({a->y, a->ws, a->x_codes, a->x_scales, a->r_codes, a->r_scales, a->w_codes, a->w_scales, a->x_bf16,
                   a->w_bf16, a->x_merged}))
     return fail(QUADS_ERR_ARG, "gemm: arrays must be 16-byte aligned");
@@ -271,7 +273,7 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
   g.y = a->y;
   g.ws = a->ws;
   if (g.mode == 0) {
-    if (!a->x_codes || !a->x_scales || !a->x_gscale || !a->w_codes || !a->w_scales || !a->w_gscale)
+    if (!a->w_codes || !a->w_scales || !a->w_gscale || (rows && (!a->x_codes || !a->x_scales || !a->x_gscale)))
       return fail(QUADS_ERR_ARG, "gemm: null W4A4 operand");
     g.x_codes = a->x_codes;
     g.x_scales = a->x_scales;
@@ -295,14 +297,14 @@ static quads_status_t gemm_fill(const quads_moe_gemm_args *a, quads::GemmLaunch 
                     (long long)a->K);
     }
   } else if (g.mode == 3) {
-    if (!a->x_bf16 || !a->w_codes || !a->w_scales || !a->w_gscale)
+    if ((rows && !a->x_bf16) || !a->w_codes || !a->w_scales || !a->w_gscale)
       return fail(QUADS_ERR_ARG, "gemm: BF16_W4 needs x_bf16 and the NVFP4 weights (w_codes, w_scales, w_gscale)");
     g.x_bf16 = static_cast<const uint16_t *>(a->x_bf16);
     g.w_codes = a->w_codes;
     g.w_scales = a->w_scales;
     g.w_g = a->w_gscale;
   } else {
-    if (!a->x_bf16 || !a->w_bf16) return fail(QUADS_ERR_ARG, "gemm: null bf16 operand");
+    if ((rows && !a->x_bf16) || !a->w_bf16) return fail(QUADS_ERR_ARG, "gemm: null bf16 operand");
     g.x_bf16 = static_cast<const uint16_t *>(a->x_bf16);
     g.w_bf16 = static_cast<const uint16_t *>(a->w_bf16);
     if (g.mode == 2) {

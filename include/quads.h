@@ -248,7 +248,9 @@ quads_status_t quads_rac_select_merged(const void *x, quads_dtype_t dt, const qu
  * address those tensors with 32-bit offsets.  expert_offsets is a DEVICE array of num_experts + 1
  * non-decreasing int32 with expert_offsets[0] = 0 and
  * expert_offsets[E] = num_rows (not checked on the host: reading it would
- * synchronize).
+ * synchronize).  num_rows == 0: y and the activation operands may be NULL
+ * and no row is written; y_gscale, if given, receives 1 (the tensor scale
+ * of an empty output).
  * ws: at least quads_moe_gemm_workspace_bytes(args) bytes.
  * ------------------------------------------------------------------------- */
 #define QUADS_OPERANDS_W4A4 0

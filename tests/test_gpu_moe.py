@@ -297,3 +297,31 @@ def test_prefill_merged_pipeline_full_size_sampled_experts():
         hr = O.swiglu(yr[:, :I], yr[:, I:])
         tol = 2.0 ** -8 * np.abs(hr) + 2e-3 * np.abs(yr).max() * (np.abs(yr[:, I:]) + np.abs(yr[:, :I]) + 1)
         assert (np.abs(h[a:b] - hr) <= tol).all()
+
+
+def test_moe_layer_no_tokens():
+    """A layer call with no tokens: routing writes all-zero expert offsets,
+    the activation's tensor scale is 1 and its scores 0, the select keeps the
+    first nsel channels, the GEMM (few-rows kernel at K = 256, 128-row
+    kernels at K = 272) writes only the output tensor scale (1) and combine
+    nothing; every call returns OK with empty (NULL) row buffers."""
+    E, I, top = 16, 256, 8
+    rng = np.random.default_rng(91)
+    ids, tw, offs, rt, inv = Q.moe_route(torch.empty(0, E, dtype=torch.float32, device="cuda"), top)
+    assert host(offs).tolist() == [0] * (E + 1)
+    for H in (256, 272):
+        log(f"[moe] no tokens E={E} H={H} I={I}")
+        x = torch.empty(0, H, dtype=torch.bfloat16, device="cuda")
+        q, scores = Q.quantize_nvfp4(x, want_scores=True)
+        assert host(q.gscale)[0] == np.float32(1.0) and not host(scores).any()
+        sel, res, nsel = Q.SelectCall(x, q, scores, 50, merged=True)()
+        assert np.array_equal(host(sel)[:nsel], np.arange(nsel))
+        wgu = S.weights(rng, (E, 2 * I, H), 0.02, bf16=True)
+        guc, gus, gug = quantize_weights_gpu(dev_act(wgu), 2)
+        g_h = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+        h = Q.moe_w4a4_gemm(w_codes=guc, w_scales=gus, w_gscale=gug, n_seg=2, N=2 * I, K=H, expert_offsets=offs,
+                            num_rows=0, x=q, res=res, sel_idx=sel, row_token=rt, epilogue=Q.EPI_SWIGLU, y_gscale=g_h)
+        assert tuple(h.shape) == (0, I) and host(g_h)[0] == np.float32(1.0)
+        out = Q.moe_combine(torch.empty(0, H, dtype=torch.float32, device="cuda"), inv, tw)
+        torch.cuda.synchronize()
+        assert tuple(out.shape) == (0, H)
