@@ -148,3 +148,41 @@ def test_bf16_operand_mode_trainer_forward():
             bits, _ = O.weight_qdq(wgu.f32[e, s * I:(s + 1) * I])
             got = host(wq[e, s * I:(s + 1) * I].contiguous().view(torch.int16)).view(np.uint16)
             assert np.array_equal(got, bits)
+
+
+@pytest.fixture(scope="module")
+def experts_1024():
+    """1024 experts (the largest count) of [128, 256] weights, quantized once."""
+    rng = np.random.default_rng(95)
+    wa = S.weights(rng, (1024, 128, 256), 0.02, bf16=True)
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    xa = S.activation(rng, 4096, 256, 3, 30.0, bf16=True)
+    return wa, we, xa
+
+
+@pytest.mark.parametrize("rows,form", [(3000, "merged"), (36000, "exact"), (36000, "merged")])
+def test_grouped_gemm_1024_experts(experts_1024, rows, form):
+    """The largest expert count: Zipf-skewed rows with every seventh expert
+    empty, gathered token rows.  3000 rows run the few-rows kernel, 36000
+    rows (more than 32 per expert) the 128-row kernels over a tile list of
+    1024 experts; both RAC forms."""
+    wa, we, xa = experts_1024
+    E, N, K = wa.f32.shape
+    T = xa.f32.shape[0]
+    rng = np.random.default_rng(96 + rows)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p[::7] = 0.0
+    counts = rng.multinomial(rows, rng.permutation(p / p.sum()))
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rt = rng.integers(0, T, rows).astype(np.int32)
+    log(f"[gemm] E=1024 rows={rows} ({int((counts == 0).sum())} empty experts) {form}")
+    x = dev_act(xa)
+    wc, ws_, wg = quantize_weights_gpu(dev_act(wa), 1)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    sel, res, nsel = Q.rac_select(x, q, scores, 50)
+    y = Q.moe_w4a4_gemm(w_codes=wc, w_scales=ws_, w_gscale=wg, N=N, K=K, expert_offsets=torch.from_numpy(offs).cuda(),
+                        num_rows=rows, x=q, res=res, sel_idx=sel, row_token=torch.from_numpy(rt).cuda(),
+                        rac_form=Q.RAC_FORM_MERGED if form == "merged" else Q.RAC_FORM_EXACT)
+    err = rel_err(host(y), O.rac_linear(xa.f32, we, 50, rt, offs)["y"])
+    log(f"  rel err {err:.2e}")
+    assert err <= TOL
