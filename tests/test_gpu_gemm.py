@@ -186,3 +186,28 @@ def test_grouped_gemm_1024_experts(experts_1024, rows, form):
     err = rel_err(host(y), O.rac_linear(xa.f32, we, 50, rt, offs)["y"])
     log(f"  rel err {err:.2e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("rows,form", [(40, "merged"), (300, "exact"), (300, "merged")])
+def test_grouped_gemm_largest_k(rows, form):
+    """K = 16384, the largest contraction the RAC select and the merge step
+    stage (k = 50: 8192 residual channels): 40 rows over two experts run the
+    few-rows kernel, 300 rows the 128-row kernels; both RAC forms."""
+    E, N, K, T = 2, 128, 16384, 200
+    rng = np.random.default_rng(97 + rows)
+    wa = S.weights(rng, (E, N, K), 0.02, bf16=True)
+    xa = S.activation(rng, T, K, K // 100, 30.0, bf16=True)
+    offs = np.array([0, rows // 3, rows], np.int32)
+    rt = rng.integers(0, T, rows).astype(np.int32)
+    log(f"[gemm] K={K} E={E} rows={rows} {form}")
+    x = dev_act(xa)
+    wc, ws_, wg = quantize_weights_gpu(dev_act(wa), 1)
+    q, scores = Q.quantize_nvfp4(x, want_scores=True)
+    sel, res, nsel = Q.rac_select(x, q, scores, 50)
+    y = Q.moe_w4a4_gemm(w_codes=wc, w_scales=ws_, w_gscale=wg, N=N, K=K, expert_offsets=torch.from_numpy(offs).cuda(),
+                        num_rows=rows, x=q, res=res, sel_idx=sel, row_token=torch.from_numpy(rt).cuda(),
+                        rac_form=Q.RAC_FORM_MERGED if form == "merged" else Q.RAC_FORM_EXACT)
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    err = rel_err(host(y), O.rac_linear(xa.f32, we, 50, rt, offs)["y"])
+    log(f"  rel err {err:.2e}")
+    assert err <= TOL
