@@ -36,6 +36,31 @@ __device__ __forceinline__ uint32_t route_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Wave-wide maximum of a 64-bit value with DPP moves (the row shifts and row
+// broadcasts of wave_scan): no LDS round trip per level, as a shuffle has.
+// Lanes whose DPP source lies outside the row take 0, the identity here.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_max64_step(uint32_t &hi, uint32_t &lo) {
+  const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), CTRL, ROW_MASK, 0xf, false));
+  const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), CTRL, ROW_MASK, 0xf, false));
+  if (h > hi || (h == hi && l > lo)) {
+    hi = h;
+    lo = l;
+  }
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
+  dpp_max64_step<0x111, 0xf>(hi, lo);
+  dpp_max64_step<0x112, 0xf>(hi, lo);
+  dpp_max64_step<0x114, 0xf>(hi, lo);
+  dpp_max64_step<0x118, 0xf>(hi, lo);
+  dpp_max64_step<0x142, 0xa>(hi, lo);
+  dpp_max64_step<0x143, 0xc>(hi, lo);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63))) << 32) |
+         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
+}
+
 // kMaxPer = ceil(E / 64) slots per lane (E <= 64 * kMaxPer <= 1024).
 template <int kMaxPer>
 __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t T, int E, int top,
@@ -65,31 +90,25 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *logits, int64_t
   for (int q = 0; q < kMaxPer; ++q) key[q] = route_key(v[q]);
   uint32_t taken = 0;  // bit q: slot q of this lane already chosen
   for (int j = 0; j < top; ++j) {
-    // (key 0, index INT_MAX) loses to every untaken expert, and top <= E
-    // leaves at least one, so bi ends as a valid expert index.
-    uint32_t bk = 0u;
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    // Each lane's best untaken expert packed as key << 32 | (2^32 - 1 - e),
+    // so that the larger value is the larger key, then the lower index; 0
+    // (no expert left in the lane) loses to every candidate, and top <= E
+    // leaves at least one, so bi is a valid expert index.
+    uint64_t c = 0;
 #pragma unroll
     for (int q = 0; q < kMaxPer; ++q) {
       const int e = q * 64 + lane;
-      if (e < E && !((taken >> q) & 1u) && (key[q] > bk || (key[q] == bk && e < bi))) {
-        bk = key[q];
-        bv = v[q];
-        bi = e;
-      }
+      const uint64_t cq = (static_cast<uint64_t>(key[q]) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+      if (e < E && !((taken >> q) & 1u) && cq > c) c = cq;
     }
+    c = wave_max_u64(c);
+    const int bi = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(c));
+    // its logit, from the lane and slot that hold it
+    float vs = v[0];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t ok = __shfl_xor(bk, off);
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ok > bk || (ok == bk && oi < bi)) {
-        bk = ok;
-        bv = ov;
-        bi = oi;
-      }
-    }
+    for (int q = 1; q < kMaxPer; ++q)
+      if ((bi >> 6) == q) vs = v[q];
+    const float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs), bi & 63));
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == 0) {
       ids[t * top + j] = bi;
