@@ -289,15 +289,22 @@ __global__ __launch_bounds__(kTokBlk) void k_route_one_block(const int32_t *ids,
   int32_t *pre = lds_i + E + E * W;
   __shared__ int32_t wsum[kTokBlk / 64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // This token's experts, loaded together (top <= 16) while the tables clear.
+  int32_t ex[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < top && t < T) ex[j] = ids[t * top + j];
   for (int i = t; i < E; i += kTokBlk) cnt[i] = 0;
   for (int i = t; i < E * W; i += kTokBlk) bits[i] = 0;
   __syncthreads();
-  if (t < T)
-    for (int j = 0; j < top; ++j) {
-      const int e = ids[t * top + j];
-      atomicAdd(&cnt[e], 1);
-      atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
-    }
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < top) {
+        atomicAdd(&cnt[ex[j]], 1);
+        atomicOr(&bits[ex[j] * W + (t >> 5)], 1u << (t & 31));
+      }
+  }
   __syncthreads();
   // Exclusive prefix of cnt over experts: thread t owns experts [4t, 4t + 4).
   int32_t c[4], own = 0;
@@ -307,12 +314,7 @@ __global__ __launch_bounds__(kTokBlk) void k_route_one_block(const int32_t *ids,
     c[q] = e < E ? cnt[e] : 0;
     own += c[q];
   }
-  int32_t incl = own;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int32_t incl = static_cast<int32_t>(wave_scan<false>(static_cast<uint32_t>(own)));
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int32_t run = incl - own;
@@ -329,14 +331,17 @@ __global__ __launch_bounds__(kTokBlk) void k_route_one_block(const int32_t *ids,
   if (t == kTokBlk - 1) offsets[E] = run;  // the last thread's running sum is the total
   __syncthreads();
   if (t >= T) return;
-  for (int j = 0; j < top; ++j) {
-    const int e = ids[t * top + j];
-    int rank = 0;
-    for (int w = 0; w < (t >> 5); ++w) rank += __popc(bits[e * W + w]);
-    rank += __popc(bits[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
-    const int32_t pos = pre[e] + rank;
-    row_token[pos] = t;
-    inverse[t * top + j] = pos;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < top) {
+      const int e = ex[j];
+      int rank = 0;
+      for (int w = 0; w < (t >> 5); ++w) rank += __popc(bits[e * W + w]);
+      rank += __popc(bits[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
+      const int32_t pos = pre[e] + rank;
+      row_token[pos] = t;
+      inverse[t * top + j] = pos;
+    }
   }
 }
 
