@@ -149,7 +149,9 @@ quads_status_t quads_quantize_nvfp4_noalloc(const void *x, quads_dtype_t dt, qua
  * sel_idx = 0 .. nsel-1, res.gscale[0] = 1) and no row is touched.
  * Channel count limit: cols <= 16384 (larger shapes return QUADS_ERR_SHAPE
  * before anything is enqueued).  Two kernels are enqueued on `stream`: the
- * mask (one workgroup), then the rows.
+ * mask (one workgroup), then the rows; calls of bf16 rows with cols <= 2048
+ * and at most one workgroup per CU (or many row groups per workgroup)
+ * enqueue one kernel in which every workgroup finds the mask itself.
  * ------------------------------------------------------------------------- */
 size_t quads_rac_select_workspace_bytes(int64_t rows, int64_t cols);
 quads_status_t quads_rac_select(const void *x, quads_dtype_t dt, const quads_nvfp4_t *xq,
