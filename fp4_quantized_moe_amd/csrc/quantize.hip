@@ -8,7 +8,9 @@
 // trainer's fake-quantized weight (section 2.2-A).
 //
 // Two launches per call, no atomics on floats and no memset:
-//   k_amax_partial  one max|x| partial per workgroup (P per tensor); also
+//   k_amax_partial  one max|x| partial per workgroup (P per tensor), over
+//                   contiguous chunks (weight batches) or, for one activation
+//                   matrix, over k_quantize's own tiles (k_amax_tiles); also
 //                   zeroes the score buffer when scores are requested;
 //   k_quantize      every workgroup folds its tensor's P partials into g, then
 //                   quantizes a [rows x 16*BC] tile: 16-element blocks,
@@ -33,17 +35,14 @@ struct Raw16 {
   uint4 u[BF16 ? 2 : 4];
 };
 
-template <bool BF16>
+// NT: nontemporal loads (weights, read once); plain loads keep an
+// activation in L2 for the pass that reads it next.
+template <bool BF16, bool NT>
 __device__ __forceinline__ void load_raw16(const void *base, int64_t elem, Raw16<BF16> &r) {
-  if constexpr (BF16) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
-    r.u[0] = load_nt16(p);
-    r.u[1] = load_nt16(p + 1);
-  } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
+  const uint4 *p = BF16 ? reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem)
+                        : reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.u[i] = load_nt16(p + i);
-  }
+  for (int i = 0; i < (BF16 ? 2 : 4); ++i) r.u[i] = NT ? load_nt16(p + i) : p[i];
 }
 
 template <bool BF16>
@@ -175,7 +174,7 @@ struct QParams {
   uint16_t *qdq;
 };
 
-template <bool BF16, bool SCORES, bool CODES, bool QDQ>
+template <bool BF16, bool SCORES, bool CODES, bool QDQ, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
   __shared__ float red[kThreads / 64];
   extern __shared__ float smax_lds[];  // [RG][BC*16] when SCORES
@@ -202,8 +201,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
     q.two = rr + p.RG < r_end;
     q.row[0] = static_cast<int64_t>(b) * p.rows + rr;
     q.row[1] = q.row[0] + (q.two ? p.RG : 0);
-    load_raw16<BF16>(p.x, q.row[0] * p.cols + gbc * 16, q.x[0]);
-    load_raw16<BF16>(p.x, q.row[1] * p.cols + gbc * 16, q.x[1]);
+    load_raw16<BF16, NT>(p.x, q.row[0] * p.cols + gbc * 16, q.x[0]);
+    load_raw16<BF16, NT>(p.x, q.row[1] * p.cols + gbc * 16, q.x[1]);
   };
   if (active && r < r_end) issue(pa, r);  // in flight while the tensor scale is folded
 
@@ -280,9 +279,46 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
   }
 }
 
-template <bool BF16, bool SCORES, bool CODES, bool QDQ>
+// The amax pass of one activation matrix over the quantizer's own tiles:
+// workgroup w folds tiles w, w + P, ... (the (row chunk, column chunk) tiles
+// k_quantize numbers the same way) into partial w, with plain loads.  With P
+// a multiple of 8 (4096 x 2048 with scores: 512 tiles and partials), each
+// tile is read on the XCD whose workgroup quantizes it next, so that read
+// comes from the XCD's L2 (expert-GEMM step 72.8 -> 69.4 us with the
+// quantizer's loads plain too; prefill quantize of h 59 -> 53 us).  Weight
+// batches keep the contiguous-chunk pass and nontemporal loads (590 against
+// 744 us per gate_up QDQ the other way).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_amax_tiles(QParams p, float *partials) {
+  __shared__ float red[kThreads / 64];
+  const int per_tensor = p.row_chunks * p.col_chunks;
+  const int b = blockIdx.x / p.P, w = blockIdx.x % p.P;
+  const int bcol = threadIdx.x % p.BC, rg = threadIdx.x / p.BC;
+  float m = 0.0f;
+  for (int t = w; t < per_tensor; t += p.P) {
+    const int rc = t / p.col_chunks, cc = t % p.col_chunks;
+    const int64_t gbc = static_cast<int64_t>(cc) * p.BC + bcol;
+    if (rg >= p.RG || gbc >= p.cb) continue;
+    const int64_t r_end = min(static_cast<int64_t>(rc + 1) * p.RW, p.rows);
+    for (int64_t r = static_cast<int64_t>(rc) * p.RW + rg; r < r_end; r += p.RG) {
+      const int64_t elem = (static_cast<int64_t>(b) * p.rows + r) * p.cols + gbc * 16;
+      Raw16<BF16> raw;
+      load_raw16<BF16, false>(p.x, elem, raw);
+      float v[16];
+      to_f32<BF16>(raw, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  if (p.scores != nullptr && blockIdx.x == 0)
+    for (int64_t c = threadIdx.x; c < p.cols; c += kThreads) p.scores[c] = 0.0f;
+}
+
+template <bool BF16, bool SCORES, bool CODES, bool QDQ, bool NT>
 void launch_q(const QParams &qp, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_quantize<BF16, SCORES, CODES, QDQ>), dim3(grid), dim3(kThreads), lds, s, qp);
+  hipLaunchKernelGGL((k_quantize<BF16, SCORES, CODES, QDQ, NT>), dim3(grid), dim3(kThreads), lds, s, qp);
 }
 
 }  // namespace
@@ -364,18 +400,6 @@ hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
   const int64_t n = a.rows * a.cols;
   const int P = amax_partials_per_tensor(n);
   float *partials = static_cast<float *>(a.ws);
-  if (!a.gscale_given) {
-    int64_t chunk = (n + P - 1) / P;
-    chunk = (chunk + 15) / 16 * 16;
-    if (a.x_bf16)
-      hipLaunchKernelGGL(k_amax_partial<true>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n,
-                         P, chunk, partials, a.scores, a.cols);
-    else
-      hipLaunchKernelGGL(k_amax_partial<false>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x,
-                         n, P, chunk, partials, a.scores, a.cols);
-  } else if (a.scores != nullptr) {
-    hipLaunchKernelGGL(k_zero_f32, dim3(1), dim3(kThreads), 0, stream, a.scores, a.cols);
-  }
 
   QParams qp{};
   qp.x = a.x;
@@ -410,27 +434,60 @@ hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
   qp.scales = a.scales;
   qp.scores = a.scores;
   qp.qdq = a.qdq_out;
+  // One matrix (an activation) whose tiles map onto the partials (at most
+  // two tiles per partial, P a multiple of 8): amax over the quantizer's
+  // tiles and plain loads in both passes.  Otherwise (weight batches, or
+  // small activations whose few partials would each fold many tiles:
+  // decode-sized calls measured 0.8 us slower that way) contiguous chunks
+  // and nontemporal loads.
+  const int64_t tiles = static_cast<int64_t>(qp.row_chunks) * qp.col_chunks;
+  const bool act = a.batch == 1 && P % 8 == 0 && tiles <= 2 * static_cast<int64_t>(P);
+  if (!a.gscale_given) {
+    if (act) {
+      if (a.x_bf16) hipLaunchKernelGGL(k_amax_tiles<true>, dim3(P), dim3(kThreads), 0, stream, qp, partials);
+      else hipLaunchKernelGGL(k_amax_tiles<false>, dim3(P), dim3(kThreads), 0, stream, qp, partials);
+    } else {
+      int64_t chunk = (n + P - 1) / P;
+      chunk = (chunk + 15) / 16 * 16;
+      if (a.x_bf16)
+        hipLaunchKernelGGL(k_amax_partial<true>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n, P, chunk,
+                           partials, a.scores, a.cols);
+      else
+        hipLaunchKernelGGL(k_amax_partial<false>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n, P, chunk,
+                           partials, a.scores, a.cols);
+    }
+  } else if (a.scores != nullptr) {
+    hipLaunchKernelGGL(k_zero_f32, dim3(1), dim3(kThreads), 0, stream, a.scores, a.cols);
+  }
   const int grid = static_cast<int>(a.batch * qp.row_chunks * qp.col_chunks);
   const bool scores = a.scores != nullptr, codes = a.codes != nullptr, qdq = a.qdq_out != nullptr;
   const size_t lds = scores ? static_cast<size_t>(qp.RG) * qp.BC * 16 * sizeof(float) : 0;
   if (a.x_bf16) {
-    if (scores)
-      launch_q<true, true, true, false>(qp, grid, lds, stream);
+    if (scores && act)  // (scores: batch 1)
+      launch_q<true, true, true, false, false>(qp, grid, lds, stream);
+    else if (scores)
+      launch_q<true, true, true, false, true>(qp, grid, lds, stream);
     else if (codes && qdq)
-      launch_q<true, false, true, true>(qp, grid, lds, stream);
+      launch_q<true, false, true, true, true>(qp, grid, lds, stream);
     else if (qdq)
-      launch_q<true, false, false, true>(qp, grid, lds, stream);
+      launch_q<true, false, false, true, true>(qp, grid, lds, stream);
+    else if (act)
+      launch_q<true, false, true, false, false>(qp, grid, lds, stream);
     else
-      launch_q<true, false, true, false>(qp, grid, lds, stream);
+      launch_q<true, false, true, false, true>(qp, grid, lds, stream);
   } else {
-    if (scores)
-      launch_q<false, true, true, false>(qp, grid, lds, stream);
+    if (scores && act)
+      launch_q<false, true, true, false, false>(qp, grid, lds, stream);
+    else if (scores)
+      launch_q<false, true, true, false, true>(qp, grid, lds, stream);
     else if (codes && qdq)
-      launch_q<false, false, true, true>(qp, grid, lds, stream);
+      launch_q<false, false, true, true, true>(qp, grid, lds, stream);
     else if (qdq)
-      launch_q<false, false, false, true>(qp, grid, lds, stream);
+      launch_q<false, false, false, true, true>(qp, grid, lds, stream);
+    else if (act)
+      launch_q<false, false, true, false, false>(qp, grid, lds, stream);
     else
-      launch_q<false, false, true, false>(qp, grid, lds, stream);
+      launch_q<false, false, true, false, true>(qp, grid, lds, stream);
   }
   return hipGetLastError();
 }
