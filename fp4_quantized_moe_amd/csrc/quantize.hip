@@ -283,11 +283,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QParams p) {
 // workgroup w folds tiles w, w + P, ... (the (row chunk, column chunk) tiles
 // k_quantize numbers the same way) into partial w, with plain loads.  With P
 // a multiple of 8 (4096 x 2048 with scores: 512 tiles and partials), each
-// tile is read on the XCD whose workgroup quantizes it next, so that read
-// comes from the XCD's L2 (expert-GEMM step 72.8 -> 69.4 us with the
-// quantizer's loads plain too; prefill quantize of h 59 -> 53 us).  Weight
-// batches keep the contiguous-chunk pass and nontemporal loads (590 against
-// 744 us per gate_up QDQ the other way).
+// tile is read by workgroups of the same index, on the same XCD, in both
+// passes.  Plain instead of nontemporal loads in both passes gave most of the
+// gain (expert-GEMM step 72.8 -> 71.0 us, prefill quantize of h 60 -> 54 us;
+// the quantizer's counted HBM-side fetch stays at 1.06x, so the second read
+// is served beyond L2), the tiled amax pass another 0.7 us (70.3 us).
+// Weight batches keep the contiguous-chunk pass and nontemporal loads (590
+// against 744 us per gate_up QDQ the other way).
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_amax_tiles(QParams p, float *partials) {
   __shared__ float red[kThreads / 64];
