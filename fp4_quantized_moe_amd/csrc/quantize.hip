@@ -85,7 +85,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
   return r;
 }
 
-template <bool BF16>
+template <bool BF16, bool NT = true>
 __global__ __launch_bounds__(kThreads) void k_amax_partial(const void *x, int64_t n_per_tensor,
                                                            int P, int64_t chunk, float *partials,
                                                            float *scores, int64_t cols) {
@@ -119,11 +119,12 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const void *x, int64_
   for (; i + (kUnroll - 1) * stride < end; i += kUnroll * stride) {
     uint4 u[kUnroll];
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) u[k] = load_nt16(addr(i + k * stride));
+    for (int k = 0; k < kUnroll; ++k)
+      u[k] = NT ? load_nt16(addr(i + k * stride)) : *reinterpret_cast<const uint4 *>(addr(i + k * stride));
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) fold(u[k]);
   }
-  for (; i < end; i += stride) fold(load_nt16(addr(i)));
+  for (; i < end; i += stride) fold(NT ? load_nt16(addr(i)) : *reinterpret_cast<const uint4 *>(addr(i)));
   m = block_max(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
   if (scores != nullptr && blockIdx.x == 0) {
@@ -436,27 +437,34 @@ hipError_t launch_quantize(const QuantizeLaunch &a, hipStream_t stream) {
   qp.scales = a.scales;
   qp.scores = a.scores;
   qp.qdq = a.qdq_out;
-  // One matrix (an activation) whose tiles map onto the partials (at most
-  // two tiles per partial, P a multiple of 8): amax over the quantizer's
-  // tiles and plain loads in both passes.  Otherwise (weight batches, or
-  // small activations whose few partials would each fold many tiles:
-  // decode-sized calls measured 0.8 us slower that way) contiguous chunks
-  // and nontemporal loads.
+  // One matrix (an activation, read again by the quantize pass and by RAC):
+  // plain loads in both passes, and the amax over the quantizer's tiles where
+  // they map onto the partials (at most two tiles per partial, P a multiple
+  // of 8; decode-sized calls, whose few partials would each fold many tiles,
+  // measured 0.8 us slower that way and keep contiguous chunks).  Weight
+  // batches (read once): contiguous chunks and nontemporal loads.
   const int64_t tiles = static_cast<int64_t>(qp.row_chunks) * qp.col_chunks;
-  const bool act = a.batch == 1 && P % 8 == 0 && tiles <= 2 * static_cast<int64_t>(P);
+  const bool act = a.batch == 1;  // plain loads
+  const bool tiled = act && P % 8 == 0 && tiles <= 2 * static_cast<int64_t>(P);
   if (!a.gscale_given) {
-    if (act) {
+    if (tiled) {
       if (a.x_bf16) hipLaunchKernelGGL(k_amax_tiles<true>, dim3(P), dim3(kThreads), 0, stream, qp, partials);
       else hipLaunchKernelGGL(k_amax_tiles<false>, dim3(P), dim3(kThreads), 0, stream, qp, partials);
     } else {
       int64_t chunk = (n + P - 1) / P;
       chunk = (chunk + 15) / 16 * 16;
-      if (a.x_bf16)
-        hipLaunchKernelGGL(k_amax_partial<true>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n, P, chunk,
+      if (a.x_bf16 && act)
+        hipLaunchKernelGGL((k_amax_partial<true, false>), dim3(P), dim3(kThreads), 0, stream, a.x, n, P, chunk,
+                           partials, a.scores, a.cols);
+      else if (a.x_bf16)
+        hipLaunchKernelGGL((k_amax_partial<true, true>), dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n, P,
+                           chunk, partials, a.scores, a.cols);
+      else if (act)
+        hipLaunchKernelGGL((k_amax_partial<false, false>), dim3(P), dim3(kThreads), 0, stream, a.x, n, P, chunk,
                            partials, a.scores, a.cols);
       else
-        hipLaunchKernelGGL(k_amax_partial<false>, dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n, P, chunk,
-                           partials, a.scores, a.cols);
+        hipLaunchKernelGGL((k_amax_partial<false, true>), dim3(a.batch * P), dim3(kThreads), 0, stream, a.x, n, P,
+                           chunk, partials, a.scores, a.cols);
     }
   } else if (a.scores != nullptr) {
     hipLaunchKernelGGL(k_zero_f32, dim3(1), dim3(kThreads), 0, stream, a.scores, a.cols);
