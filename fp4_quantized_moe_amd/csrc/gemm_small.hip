@@ -254,7 +254,7 @@ __device__ __forceinline__ float store_out(const SmallParams &p, int64_t row, in
     static_cast<uint16_t *>(p.y)[row * ld + col] = static_cast<uint16_t>(hb);
     return fabsf(bf16_bits_to_f32(hb));
   }
-  __builtin_nontemporal_store(v, static_cast<float *>(p.y) + row * ld + col);  // read back from HBM later
+  static_cast<float *>(p.y)[row * ld + col] = v;  // few rows: y stays in the caches for the combine
   return 0.0f;
 }
 
