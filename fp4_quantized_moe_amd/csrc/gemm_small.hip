@@ -78,13 +78,57 @@ struct SmallParams {
 
 // One LDS stage.  Rows of 128 bytes hold 8 chunks; chunk c of row r sits in
 // slot c ^ ((r >> 1) & 7) (32 merged-operand chunks per row: slot c ^ (r & 15)).
-template <bool RES>
-struct StageLds {
+// TAB: the weight block scales of the whole K come from a per-workgroup
+// table loaded once (below), not with every step; only the members a form
+// uses are declared, so that the merged-operand form with the table fills
+// exactly half of a CU's LDS and two workgroups fit.
+template <bool RES, bool TAB>
+struct StageLds;
+template <>
+struct StageLds<true, true> {
   uint4 w[kSW * 32 * 8];            // [wave][row][slot] weight codes
-  uint32_t ws[kSW * 32 * 4];        // [wave][row][4 words] weight block scales
-  uint4 x[RES ? 1 : 32 * 8];        // [row][slot] activation codes (plain W4A4)
-  uint32_t xs[RES ? 1 : 32 * 4];    // [row][4 words] activation block scales (plain W4A4)
-  uint4 r[RES ? 32 * 32 : 1];       // [row][slot] merged fp16 activation (RAC)
+  uint4 r[32 * 32];                 // [row][slot] merged fp16 activation (RAC)
+};
+template <>
+struct StageLds<true, false> {
+  uint4 w[kSW * 32 * 8];
+  uint32_t ws[kSW * 32 * 4];        // [wave][row][4 words] weight block scales of the step
+  uint4 r[32 * 32];
+};
+template <>
+struct StageLds<false, true> {
+  uint4 w[kSW * 32 * 8];
+  uint4 x[32 * 8];                  // [row][slot] activation codes (plain W4A4)
+  uint32_t xs[32 * 4];              // [row][4 words] activation block scales (plain W4A4)
+};
+template <>
+struct StageLds<false, false> {
+  uint4 w[kSW * 32 * 8];
+  uint32_t ws[kSW * 32 * 4];
+  uint4 x[32 * 8];
+  uint32_t xs[32 * 4];
+};
+
+// The scale table.  Each wave's 32 weight rows are consecutive rows of the
+// scale tensor, so their K/16 bytes each form one contiguous run of 2K
+// bytes, copied with whole-line loads at the start of the workgroup.  Per K
+// step the same bytes as 16-byte pieces of 32 rows on 32 lines cost more
+// load time than the codes they scale (a probe of the kernel's loads alone:
+// 55 us with per-step pieces, 49 us with the table, 41 us without scales).
+// Row r holds CPR = K/256 chunks of 16 bytes (one per step); step c of row r
+// sits at chunk c ^ ((r >> (4 - log2 CPR)) & (CPR - 1)), so the 32 rows read
+// at one step spread over the LDS banks (rows 16 apart share banks: 2-way).
+// K in {256, 512, 1024, 2048}.
+constexpr int kSTabK = 2048;
+constexpr int kSTabWords = kSW * 32 * (kSTabK / 64);
+
+inline bool small_tab(int64_t K) { return K == 256 || K == 512 || K == 1024 || K == 2048; }
+
+struct ScaleTab {
+  int cpr_log2;  // log2(K / 256)
+  __device__ __forceinline__ int chunk(int r, int c) const {
+    return c ^ ((r >> (4 - cpr_log2)) & ((1 << cpr_log2) - 1));
+  }
 };
 
 // Activation staging of a step is split into 8 (plain W4A4) or 16 (merged
@@ -99,9 +143,9 @@ constexpr int kSA = (RES ? 16 : 8) / kSW;
 static_assert((16 / kSW) * kSW == 16 && (8 / kSW) * kSW == 8, "activation jobs must split evenly over the waves");
 
 // DMA instructions per wave per step: 4 weight-code lines, 2 weight-scale
-// words and the activation jobs.
-template <bool RES>
-constexpr int kSP = 6 + kSA<RES>;
+// words (without the table) and the activation jobs.
+template <bool RES, bool TAB>
+constexpr int kSP = (TAB ? 4 : 6) + kSA<RES>;
 
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
@@ -123,8 +167,8 @@ __device__ __forceinline__ int act_job_row(int j, int lane, bool rows16) {
   }
 }
 
-template <bool RES>
-__device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, const SmallRows &rw, int kt,
+template <bool RES, bool TAB>
+__device__ __forceinline__ void issue(StageLds<RES, TAB> &st, const SmallParams &p, const SmallRows &rw, int kt,
                                       int wave, int lane, bool rows16) {
   const int64_t K = p.K;
   const int slot = lane & 7;
@@ -134,9 +178,11 @@ __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, c
     const int chunk = slot ^ swz8(r);
     dma(p.w_codes + rw.wrow[q] * (K / 2) + kt * 128 + chunk * 16, &st.w[(wave * 32 + 8 * q) * 8], 16);
   }
+  if constexpr (!TAB) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i], 4);
+    for (int i = 0; i < 2; ++i)
+      dma(p.w_scales + rw.wsrow[i] * (K / 16) + kt * 16 + (lane & 3) * 4, &st.ws[wave * 128 + 64 * i], 4);
+  }
 #pragma unroll
   for (int q = 0; q < kSA<RES>; ++q) {
     const int j = wave * kSA<RES> + q;  // wave-uniform
@@ -158,10 +204,33 @@ __device__ __forceinline__ void issue(StageLds<RES> &st, const SmallParams &p, c
   }
 }
 
-template <bool RES>
-__device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int lane, f32x16 &acc) {
+// This wave's part of the table: LDS chunk P of the wave (row P / CPR,
+// position P % CPR) holds step chunk(row, position) of that row.
+__device__ __forceinline__ void load_scale_table(uint32_t *tab, const ScaleTab &tb, const SmallParams &p,
+                                                 int64_t wrow0, int wave, int lane) {
+  const int cpr = 1 << tb.cpr_log2, chunks = 32 * cpr;
+  uint32_t *base = tab + wave * chunks * 4;
+  for (int off = 0; off < chunks; off += 64) {
+    const int P = off + lane;
+    const int r = P >> tb.cpr_log2, c = tb.chunk(r, P & (cpr - 1));
+    if (P < chunks) dma(p.w_scales + (wrow0 + r) * (p.K / 16) + c * 16, base + off * 4, 16);
+  }
+}
+
+// The 16 scale bytes of step kt for row r of this wave (4 words).
+template <bool RES, bool TAB>
+__device__ __forceinline__ const uint32_t *step_scales(const StageLds<RES, TAB> &st, const uint32_t *tab,
+                                                       const ScaleTab &tb, int wave, int r, int kt) {
+  if constexpr (TAB) return tab + ((wave * 32 + r) * (1 << tb.cpr_log2) + tb.chunk(r, kt)) * 4;
+  else return &st.ws[wave * 128 + r * 4];
+}
+
+template <bool RES, bool TAB>
+__device__ __forceinline__ void compute(const StageLds<RES, TAB> &st, const uint32_t *tab, const ScaleTab &tb, int kt,
+                                        int wave, int lane, f32x16 &acc) {
   const int r = lane & 31, h = lane >> 5;
-  const uint32_t ws0 = st.ws[wave * 128 + r * 4 + 2 * h], ws1 = st.ws[wave * 128 + r * 4 + 2 * h + 1];
+  const uint32_t *sw = step_scales<RES, TAB>(st, tab, tb, wave, r, kt);
+  const uint32_t ws0 = sw[2 * h], ws1 = sw[2 * h + 1];
 #pragma unroll
   for (int cq = 0; cq < 4; ++cq) {
     const int c = 4 * h + cq;
@@ -203,12 +272,13 @@ __device__ __forceinline__ void compute(const StageLds<RES> &st, int wave, int l
 // for both operands (and the merged operand).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <bool RES>
-__device__ __forceinline__ void compute16(const StageLds<RES> &st, int wave, int lane, f32x4 (&acc)[2]) {
+template <bool RES, bool TAB>
+__device__ __forceinline__ void compute16(const StageLds<RES, TAB> &st, const uint32_t *tab, const ScaleTab &tb,
+                                          int kt, int wave, int lane, f32x4 (&acc)[2]) {
   const int r = lane & 15, q = lane >> 4;
   uint32_t wsw[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) wsw[cb] = st.ws[wave * 128 + (16 * cb + r) * 4 + q];
+  for (int cb = 0; cb < 2; ++cb) wsw[cb] = step_scales<RES, TAB>(st, tab, tb, wave, 16 * cb + r, kt)[q];
 #pragma unroll
   for (int cq = 0; cq < 2; ++cq) {
     const int c = 2 * q + cq;
@@ -270,14 +340,14 @@ __device__ __forceinline__ float store_swiglu(const SmallParams &p, int64_t idx,
 // Step s lives in stage s % kSStages; step kt+kSStages-1 is issued into the
 // stage step kt-1 used, after the barrier that follows every wave's last read
 // of it.
-template <bool RES, class Comp>
-__device__ __forceinline__ void stream_k(StageLds<RES> (&st)[kSStages], const SmallParams &p, const SmallRows &rw,
-                                         int nk, int wave, int lane, bool rows16, Comp comp) {
-  constexpr int P = kSP<RES>;
+template <bool RES, bool TAB, class Comp>
+__device__ __forceinline__ void stream_k(StageLds<RES, TAB> (&st)[kSStages], const SmallParams &p,
+                                         const SmallRows &rw, int nk, int wave, int lane, bool rows16, Comp comp) {
+  constexpr int P = kSP<RES, TAB>;
   static_assert(kSStages >= 2 && kSStages <= 4, "stages");
 #pragma unroll
   for (int s = 0; s < kSStages - 1; ++s)
-    if (s < nk) issue<RES>(st[s], p, rw, s, wave, lane, rows16);
+    if (s < nk) issue<RES, TAB>(st[s], p, rw, s, wave, lane, rows16);
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // This wave's part of step kt has landed once at most its loads of the
@@ -290,9 +360,9 @@ __device__ __forceinline__ void stream_k(StageLds<RES> (&st)[kSStages], const Sm
     const int nxt = kt + kSStages - 1;
     if (nxt < nk) {
       const int b = cur + kSStages - 1 >= kSStages ? cur - 1 : cur + kSStages - 1;
-      issue<RES>(st[b], p, rw, nxt, wave, lane, rows16);
+      issue<RES, TAB>(st[b], p, rw, nxt, wave, lane, rows16);
     }
-    comp(st[cur]);
+    comp(st[cur], kt);
     cur = cur + 1 == kSStages ? 0 : cur + 1;
   }
 }
@@ -300,9 +370,10 @@ __device__ __forceinline__ void stream_k(StageLds<RES> (&st)[kSStages], const Sm
 // EPI 0: Y fp32/bf16 [rows, N].  EPI 1 (SwiGLU): the first half of the waves
 // own gate columns and the second half the matching up columns;
 // h = silu(gate) * up -> bf16 [rows, N/2].
-template <int EPI, bool RES>
+template <int EPI, bool RES, bool TAB>
 __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(SmallParams p) {
-  __shared__ StageLds<RES> st[kSStages];
+  __shared__ StageLds<RES, TAB> st[kSStages];
+  __shared__ uint32_t tab[TAB ? kSTabWords : 1];
   const int e = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -323,6 +394,8 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
   const float gw = p.w_g[e * p.n_seg + static_cast<int>(wcol0) / static_cast<int>(p.N / p.n_seg)];
   const float gx = *p.x_g;
   const int nk = static_cast<int>(p.K / kSK);
+  const ScaleTab tb{nk == 8 ? 3 : nk == 4 ? 2 : nk == 2 ? 1 : 0};
+  if constexpr (TAB) load_scale_table(tab, tb, p, wrow0, wave, lane);  // waited for with step 0's loads
 
   auto act_row = [&](int pm, int r) -> int64_t {
     const int i = min(pm + r, mend - 1);  // rows past the expert re-read a valid row, never stored
@@ -346,9 +419,10 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) ax[cb][v] = 0.0f;
-      stream_k<RES>(st, p, rw, nk, wave, lane, true, [&](const StageLds<RES> &s) __attribute__((always_inline)) {
-        compute16<RES>(s, wave, lane, ax);
-      });
+      stream_k<RES, TAB>(st, p, rw, nk, wave, lane, true,
+                         [&](const StageLds<RES, TAB> &s, int kt) __attribute__((always_inline)) {
+                           compute16<RES, TAB>(s, tab, tb, kt, wave, lane, ax);
+                         });
       // Element v of accumulator cb is row 4*(lane/16) + v of the pass,
       // column 16*cb + lane%16 of the wave's 32.
       const int q = lane >> 4;
@@ -395,9 +469,10 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
     f32x16 acc_x;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_x[r] = 0.0f;
-    stream_k<RES>(st, p, rw, nk, wave, lane, false, [&](const StageLds<RES> &s) __attribute__((always_inline)) {
-      compute<RES>(s, wave, lane, acc_x);
-    });
+    stream_k<RES, TAB>(st, p, rw, nk, wave, lane, false,
+                       [&](const StageLds<RES, TAB> &s, int kt) __attribute__((always_inline)) {
+                         compute<RES, TAB>(s, tab, tb, kt, wave, lane, acc_x);
+                       });
 
     // Element r of the accumulator is row 8*(r/4) + 4*h + r%4 of the pass,
     // column lane%32 of the wave's 32.
@@ -430,7 +505,14 @@ __global__ __launch_bounds__(kSW * 64, kSStages == 2 ? 2 : 1) void k_gemm_small(
       }
     }
   }
-  if (p.amax_ws != nullptr) amax_gather(p.amax_ws, hmax);
+  if (p.amax_ws != nullptr) {
+    if constexpr (TAB) {
+      __syncthreads();  // every wave is done with the table, which takes the per-wave partials
+      amax_gather(p.amax_ws, hmax, tab);
+    } else {
+      amax_gather(p.amax_ws, hmax);
+    }
+  }
 }
 
 }  // namespace
@@ -476,12 +558,17 @@ hipError_t launch_gemm_small(const GemmLaunch &a, const uint16_t *r_dense, hipSt
   p.amax_ws = gemm_amax_words(a);
   const bool res = r_dense != nullptr;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.E) * p.n_tiles)), block(kSW * 64);
+  const bool tab = small_tab(a.K);
   if (a.epilogue == 0) {
-    if (res) hipLaunchKernelGGL((k_gemm_small<0, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_gemm_small<0, false>), grid, block, 0, stream, p);
+    if (res && tab) hipLaunchKernelGGL((k_gemm_small<0, true, true>), grid, block, 0, stream, p);
+    else if (res) hipLaunchKernelGGL((k_gemm_small<0, true, false>), grid, block, 0, stream, p);
+    else if (tab) hipLaunchKernelGGL((k_gemm_small<0, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_gemm_small<0, false, false>), grid, block, 0, stream, p);
   } else {
-    if (res) hipLaunchKernelGGL((k_gemm_small<1, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((k_gemm_small<1, false>), grid, block, 0, stream, p);
+    if (res && tab) hipLaunchKernelGGL((k_gemm_small<1, true, true>), grid, block, 0, stream, p);
+    else if (res) hipLaunchKernelGGL((k_gemm_small<1, true, false>), grid, block, 0, stream, p);
+    else if (tab) hipLaunchKernelGGL((k_gemm_small<1, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_gemm_small<1, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -333,8 +333,8 @@ __device__ __forceinline__ uint32_t last_lane(uint32_t v) {
 // a barrier: every thread of the workgroup calls it.
 constexpr int kAmaxWords = 64;
 
-__device__ __forceinline__ void amax_gather(uint32_t *words, float m) {
-  __shared__ uint32_t red[16];
+// `red`: 16 words of LDS the caller is done with (every thread calls).
+__device__ __forceinline__ void amax_gather(uint32_t *words, float m, uint32_t *red) {
   const uint32_t wm = last_lane(wave_scan<true>(__float_as_uint(m)));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = wm;
   __syncthreads();
@@ -344,6 +344,11 @@ __device__ __forceinline__ void amax_gather(uint32_t *words, float m) {
     if (t != 0u)
       __hip_atomic_fetch_max(words + blockIdx.x % kAmaxWords, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
+}
+
+__device__ __forceinline__ void amax_gather(uint32_t *words, float m) {
+  __shared__ uint32_t red[16];
+  amax_gather(words, m, red);
 }
 
 // Dequantized FP32 value of one code given the block's d = fl32(dec(s) * g).
