@@ -7,7 +7,8 @@ chosen per call with the rac_form argument:
 Both are checked against the oracle's float64 extended-K reference at the
 1e-3 bar (the exact form also at the accumulation-only bar EXACT_TOL):
 dense and grouped shapes, ragged rows, a gathered row order, the SwiGLU
-epilogue, the few-rows (decode) shape in both forms, and the full-size
+epilogue, the few-rows (decode) shape in both forms, K tails (K % 64 != 0,
+an odd number of 64-wide steps) on both tile shapes, and the full-size
 expert-GEMM workload through the caller-built merged operand."""
 import numpy as np
 import pytest
@@ -73,6 +74,22 @@ def test_grouped_gathered_both_formulations(mode):
     y = host(_run(xa, wa, offs, rt, 50, rac_form=FORMS[mode]))
     _, _, _, we = O.quantize_weights(wa.f32, 1)
     _check(y, O.rac_linear(xa.f32, we, 50, rt, offs)["y"], mode)
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([300, 0, 257, 130], 784, 512),   # K % 64 != 0
+    ([300, 0, 257, 130], 832, 512),   # odd step count
+    ([4096, 4000], 832, 2048),        # 256x256 tiles, odd step count
+])
+def test_merged_k_tails(counts, K, N):
+    """K tails of the merged operand's GEMM: K % 64 != 0 (a ragged last
+    step whose blocks past K are zeroed) and an odd count of 64-wide steps
+    (the pipeline pads one all-zero step), on both tile shapes."""
+    xa, wa, offs, rt = _grouped(611, counts, 700, K, N)
+    log(f"[gemm-rac] merged experts {counts} K={K} N={N} k=50")
+    y = host(_run(xa, wa, offs, rt, 50, rac_form=Q.RAC_FORM_MERGED))
+    _, _, _, we = O.quantize_weights(wa.f32, 1)
+    _check(y, O.rac_linear(xa.f32, we, 50, rt, offs)["y"], "merged")
 
 
 @pytest.mark.parametrize("mode", ["exact", "merged"])
